@@ -1,0 +1,98 @@
+/*
+ * CPU oracle for the DeepSeek-V3.2 sparse-attention hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously-correct
+ * statement of what the hot path computes, written from the pages in fp64.
+ * Only the test-suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load it.  It shares no source, header, table or helper with the GPU
+ * library, and the GPU library never calls it.
+ *
+ * Sources (the pages this follows):
+ *  - atlas.klimoza.dev, DeepSeek-V3.2-Exp, MoE block, "All 43 steps": the index
+ *    score S^I = 1/(sqrt 64 * sqrt 128) * sum_h w_{t,h} ReLU(Q^I_{h,t} . k^I_s),
+ *    the causal mask M added to it, and the top-2048 selection mask M^sel.
+ *  - nnterp encyclopedia, deepseek_v32, section 03 ("Up to 2048 tokens the
+ *    sparse attention is plain causal attention") and section 04: unselected
+ *    keys get zero probability, rows sum to one over the selection, the
+ *    selection is int32 [batch, query, min(index_topk, keys)].
+ *  - the same MoE-block step list for latent attention: k^C = c^KV W_UK,
+ *    v = c^KV W_UV, K_i = [K^C_i ; k^R] with one rotary key shared by all heads.
+ *
+ * Conventions (readings where the pages are silent):
+ *  - query t of a sequence sits at position q_pos(t) = S - T + t and sees keys
+ *    s <= q_pos(t) (the diagonal included);
+ *  - top-K orders by (score descending, index ascending); -0 equals +0; NaN and
+ *    -inf are never selected; the chosen indices are written in ascending
+ *    order and the row is padded with -1 up to min(K, S);
+ *  - the index scale is applied after the head sum, in fp32;
+ *  - sparse attention over an index row skips entries that are -1 or outside
+ *    [0, S) and counts duplicates as given; a row with no valid entry yields
+ *    o = 0 and lse = -inf.
+ *
+ * Data types: DSA_ORC_F32 = 0, DSA_ORC_BF16 = 1 (uint16 bit patterns),
+ * DSA_ORC_FP8 = 2 (OCP E4M3FN bytes with one ue8m0 scale byte per 128-element
+ * block; value = e4m3 * 2^(byte - 127)).
+ *
+ * Row-list calling convention: each routine works on n query rows; row r of
+ * the call is query (row_b[r], row_t[r]).  Per-query inputs (q_idx, w, q) and
+ * outputs are passed compactly, [n, ...]; per-sequence tensors (k_idx, kv) are
+ * passed whole, [B, S, ...].  All routines return 0 on success, nonzero on a
+ * bad argument.
+ */
+#ifndef DSA_ORACLE_H
+#define DSA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { DSA_ORC_F32 = 0, DSA_ORC_BF16 = 1, DSA_ORC_FP8 = 2 };
+
+typedef struct {
+  int32_t B, T, S;      /* batch, queries per sequence, keys per sequence */
+  int32_t HI, DI;       /* indexer heads, indexer head width */
+  int32_t H, Dc, Dr;    /* MLA heads, latent width, rotary width */
+  int32_t K;            /* top-k */
+  float idx_scale;      /* index-score prefactor */
+  float sm_scale;       /* softmax scale */
+  int32_t idx_dtype;    /* q_idx / k_idx */
+  int32_t w_dtype;      /* w */
+  int32_t mla_dtype;    /* q / kv */
+} orc_shape;
+
+/* Index scores, [n, S] fp32, future keys -inf. */
+int orc_indexer_scores(const orc_shape* sh, int32_t n, const int32_t* row_b,
+                       const int32_t* row_t, const void* q_idx_rows,
+                       const uint8_t* q_sf_rows, const void* k_idx,
+                       const uint8_t* k_sf, const void* w_rows, float* scores);
+
+/* Top-K selection of n score rows of length S -> [n, min(K, S)] int32. */
+int orc_topk(const orc_shape* sh, int32_t n, const float* scores, int32_t* idx);
+
+/* Absorbed sparse latent attention over index rows of width W.
+ * o [n, H, Dc] fp64, lse [n, H] fp64, probs [n, H, W] fp64 (nullable). */
+int orc_sparse_mla(const orc_shape* sh, int32_t n, const int32_t* row_b,
+                   const void* q_rows, const void* kv, const int32_t* idx,
+                   int32_t W, double* o, double* lse, double* probs);
+
+/* Dense causal latent attention over every key s <= q_pos(t).
+ * o [n, H, Dc] fp64, lse [n, H] fp64. */
+int orc_dense_mla(const orc_shape* sh, int32_t n, const int32_t* row_b,
+                  const int32_t* row_t, const void* q_rows, const void* kv,
+                  double* o, double* lse);
+
+/* Explicit (non-absorbed) latent attention of one query over nkeys keys, fp64.
+ * qC [H, Dn], qR [H, Dr], c [nkeys, Dc], r [nkeys, Dr],
+ * W_UK [Dc, H*Dn] and W_UV [Dc, H*Dv] (column block h belongs to head h).
+ * out [H, Dv]. */
+int orc_explicit_mla(int32_t H, int32_t Dc, int32_t Dn, int32_t Dv, int32_t Dr,
+                     int32_t nkeys, double sm_scale, const double* qC,
+                     const double* qR, const double* c, const double* r,
+                     const double* W_UK, const double* W_UV, double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

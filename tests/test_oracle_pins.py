@@ -1,0 +1,466 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Each test ties one oracle routine to a hand-worked example, a closed form, an
+invariant, or a special case that reduces to a library routine (numpy matmul,
+numpy lexsort, torch's scaled_dot_product_attention in fp64).  The shapes are
+deliberately non-square (HI != DI, T != S, Dc != Dr) so that a transposed
+operand or a swapped index changes the result.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import dsa_inputs as g
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _cfg(**kw):
+    base = dict(name="pin", B=2, T=5, S=37, HI=3, DI=7, H=3, Dc=6, Dr=2, K=8,
+                idx_dtype="f32", w_dtype="f32", mla_dtype="f32", seed=11)
+    base.update(kw)
+    return g.Config(**base)
+
+
+def _rows(cfg):
+    rb = np.repeat(np.arange(cfg.B, dtype=np.int32), cfg.T)
+    rt = np.tile(np.arange(cfg.T, dtype=np.int32), cfg.B)
+    return rb, rt
+
+
+def _draw(cfg, rng, integer=False):
+    def d(*shape):
+        if integer:
+            return rng.integers(-3, 4, size=shape).astype(np.float32)
+        return rng.standard_normal(shape).astype(np.float32)
+    return dict(q_idx=d(cfg.B * cfg.T, cfg.HI, cfg.DI), k_idx=d(cfg.B, cfg.S, cfg.DI),
+                w=d(cfg.B * cfg.T, cfg.HI), q=d(cfg.B * cfg.T, cfg.H, cfg.D),
+                kv=d(cfg.B, cfg.S, cfg.D))
+
+
+def _scores(cfg, x):
+    rb, rt = _rows(cfg)
+    return oracle.indexer_scores(cfg, rb, rt, x["q_idx"], x["w"], x["k_idx"])
+
+
+def _causal_mask(cfg):
+    rb, rt = _rows(cfg)
+    qpos = cfg.S - cfg.T + rt
+    return np.arange(cfg.S)[None, :] <= qpos[:, None]
+
+
+# ---------------------------------------------------------------------------
+# hand-worked example
+# ---------------------------------------------------------------------------
+
+def _golden():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        return json.load(f)
+
+
+def _num(v):
+    if v == "-inf":
+        return -math.inf
+    if v == "ln3":
+        return math.log(3.0)
+    if v == "ln4":
+        return math.log(4.0)
+    return float(v)
+
+
+def test_worked_example_indexer(oracle_lib):
+    ex = _golden()["indexer"]
+    q = np.array(ex["q_idx"], np.float32)[None]
+    k = np.array(ex["k_idx"], np.float32)[None]
+    w = np.array(ex["w"], np.float32)[None]
+    dec = _cfg(B=1, T=1, S=3, HI=2, DI=2, K=2, idx_scale=ex["idx_scale"])
+    s = oracle.indexer_scores(dec, [0], [0], q, w, k)
+    assert s[0].tolist() == [_num(v) for v in ex["decode_scores"]]
+    assert oracle.topk(dec, s)[0].tolist() == ex["decode_topk"]
+    pre = dec.replace(T=3)
+    s = oracle.indexer_scores(pre, [0], [0], q, w, k)
+    assert s[0].tolist() == [_num(v) for v in ex["prefill_t0_scores"]]
+    assert oracle.topk(pre, s)[0].tolist() == ex["prefill_t0_topk"]
+
+
+def test_worked_example_attention(oracle_lib):
+    ex = _golden()["attention"]
+    cfg = _cfg(B=1, T=1, S=3, H=1, Dc=2, Dr=1, sm_scale=ex["sm_scale"])
+    kv = np.array(ex["kv"], np.float64)[None].astype(np.float32)
+    q = np.array([[[_num(v) for v in ex["q"]]]], np.float32)
+    idx = np.array([ex["idx"]], np.int32)
+    o, lse, p = oracle.sparse_mla(cfg, [0], q, kv, idx, want_probs=True)
+    np.testing.assert_allclose(o[0, 0], ex["o"], rtol=1e-6)
+    np.testing.assert_allclose(p[0, 0], ex["probs"], rtol=1e-6, atol=1e-12)
+    assert abs(lse[0, 0] - _num(ex["lse"])) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# index scores
+# ---------------------------------------------------------------------------
+
+def test_scores_single_head_unit_weight_is_relu_matmul(oracle_lib):
+    """HI = 1, w = 1: S = scale * ReLU(Q K^T) (numpy matmul), exact on integers."""
+    cfg = _cfg(HI=1)
+    rng = np.random.default_rng(1)
+    x = _draw(cfg, rng, integer=True)
+    x["w"][:] = 1.0
+    s = _scores(cfg, x)
+    rb, _ = _rows(cfg)
+    ref = np.einsum("nd,nsd->ns", x["q_idx"][:, 0].astype(np.int64),
+                    x["k_idx"][rb].astype(np.int64))
+    ref = np.float32(cfg.index_scale) * np.maximum(ref, 0).astype(np.float32)
+    mask = _causal_mask(cfg)
+    assert np.array_equal(s[mask], ref[mask])
+    assert np.all(np.isneginf(s[~mask]))
+
+
+def test_scores_relu_sits_between_dot_and_weight(oracle_lib):
+    """Heads (q, -q) with w = (1, -1) give scale*(q.k); with w = (1, 1), scale*|q.k|.
+
+    relu(x) - relu(-x) = x and relu(x) + relu(-x) = |x|: a missing ReLU, a
+    ReLU after the weight, or a dropped head changes one of the two."""
+    cfg = _cfg(HI=2, T=1)
+    rng = np.random.default_rng(2)
+    x = _draw(cfg, rng, integer=True)
+    x["q_idx"][:, 1] = -x["q_idx"][:, 0]
+    rb, _ = _rows(cfg)
+    dot = np.einsum("nd,nsd->ns", x["q_idx"][:, 0], x["k_idx"][rb]).astype(np.float32)
+    sc = np.float32(cfg.index_scale)
+    x["w"][:] = [1.0, -1.0]
+    assert np.array_equal(_scores(cfg, x), sc * dot)
+    x["w"][:] = [1.0, 1.0]
+    assert np.array_equal(_scores(cfg, x), sc * np.abs(dot))
+
+
+def test_scores_nonnegative_dots_are_linear_in_weighted_query(oracle_lib):
+    """All q.k >= 0: S = scale * ((sum_h w_h q_h) . k), a plain GEMV."""
+    cfg = _cfg(T=2)
+    rng = np.random.default_rng(3)
+    x = _draw(cfg, rng)
+    x["q_idx"] = np.abs(x["q_idx"])
+    x["k_idx"] = np.abs(x["k_idx"])
+    s = _scores(cfg, x).astype(np.float64)
+    rb, _ = _rows(cfg)
+    u = np.einsum("nh,nhd->nd", x["w"].astype(np.float64), x["q_idx"].astype(np.float64))
+    ref = cfg.index_scale * np.einsum("nd,nsd->ns", u, x["k_idx"][rb].astype(np.float64))
+    mask = _causal_mask(cfg)
+    np.testing.assert_allclose(s[mask], ref[mask], rtol=2e-6, atol=1e-6)
+
+
+def test_scores_causal_boundary_and_decode_alignment(oracle_lib):
+    """Query t sits at S - T + t and sees keys 0..S-T+t (diagonal included)."""
+    rng = np.random.default_rng(4)
+    for T, S in [(5, 37), (1, 9), (9, 9)]:
+        cfg = _cfg(T=T, S=S)
+        x = _draw(cfg, rng)
+        x["q_idx"] = np.abs(x["q_idx"])
+        x["k_idx"] = np.abs(x["k_idx"]) + 0.5
+        x["w"] = np.abs(x["w"]) + 0.5
+        s = _scores(cfg, x)
+        _, rt = _rows(cfg)
+        finite = np.isfinite(s).sum(axis=1)
+        assert np.array_equal(finite, S - T + rt + 1)
+        assert np.all(s[np.isfinite(s)] > 0)
+
+
+def test_scores_integer_mode_exact_against_int64(oracle_lib):
+    """Integer inputs in [-3, 3]: the score equals the int64 closed form, scaled."""
+    cfg = g.CONFIGS["tiny"]
+    qi = g.full(cfg, "q_idx")[0]
+    ki = g.full(cfg, "k_idx")
+    w = g.full(cfg, "w")[0]
+    rb = np.zeros(cfg.T, np.int32)
+    rt = np.arange(cfg.T, dtype=np.int32)
+    s = oracle.indexer_scores(cfg, rb, rt, qi, w, ki)
+    d = np.einsum("thd,sd->ths", qi.astype(np.int64), ki[0].astype(np.int64))
+    acc = np.einsum("th,ths->ts", w.astype(np.int64), np.maximum(d, 0))
+    ref = np.float32(cfg.index_scale) * acc.astype(np.float32)
+    mask = np.tril(np.ones((cfg.T, cfg.S), bool))
+    assert np.array_equal(s[mask], ref[mask])
+
+
+def test_scores_bf16_inputs_are_read_exactly(oracle_lib):
+    """bf16 storage decodes exactly: same scores as the fp32 copy of the values."""
+    cfg = _cfg(T=2)
+    rng = np.random.default_rng(5)
+    x = _draw(cfg, rng)
+    xb = {k: g.f32_to_bf16_bits(v) for k, v in x.items()}
+    xf = {k: g.bf16_bits_to_f32(v) for k, v in xb.items()}
+    s_b = _scores(cfg.replace(idx_dtype="bf16", w_dtype="bf16"), xb)
+    s_f = _scores(cfg, xf)
+    assert np.array_equal(s_b, s_f)
+
+
+def test_scores_fp8_block_scales(oracle_lib):
+    """e4m3 with ue8m0 scales: byte 127 reproduces the integer result exactly;
+    raising the query scale byte by a and the key byte by b multiplies every
+    score by 2^(a+b) exactly (two blocks per row: DI = 256)."""
+    cfg = _cfg(DI=256, T=2, idx_dtype="fp8")
+    rng = np.random.default_rng(6)
+    x = _draw(cfg, rng, integer=True)
+    qc, kc = g.f32_to_e4m3(x["q_idx"]), g.f32_to_e4m3(x["k_idx"])
+    qs = np.full(x["q_idx"].shape[:-1] + (2,), 127, np.uint8)
+    ks = np.full(x["k_idx"].shape[:-1] + (2,), 127, np.uint8)
+    rb, rt = _rows(cfg)
+    s8 = oracle.indexer_scores(cfg, rb, rt, qc, x["w"], kc, qs, ks)
+    s32 = _scores(cfg.replace(idx_dtype="f32"), x)
+    assert np.array_equal(s8, s32)
+    s8b = oracle.indexer_scores(cfg, rb, rt, qc, x["w"], kc, qs + 2, ks - 5)
+    mask = np.isfinite(s32)
+    assert np.array_equal(s8b[mask], s32[mask] * np.float32(2.0 ** -3))
+    # one block scaled on its own only scales that block's contribution
+    x2 = dict(x)
+    x2["q_idx"] = x["q_idx"].copy()
+    x2["q_idx"][..., 128:] *= 4.0
+    qs2 = qs.copy()
+    qs2[..., 1] += 2
+    s8c = oracle.indexer_scores(cfg, rb, rt, qc, x["w"], kc, qs2, ks)
+    s32c = _scores(cfg.replace(idx_dtype="f32"), x2)
+    assert np.array_equal(s8c, s32c)
+
+
+# ---------------------------------------------------------------------------
+# top-k
+# ---------------------------------------------------------------------------
+
+def _lexsort_topk(row, K):
+    """Reference selection with numpy.lexsort on (score desc, index asc)."""
+    idx = np.arange(row.size)
+    ok = ~(np.isnan(row) | np.isneginf(row))
+    r, i = row[ok].astype(np.float64), idx[ok]
+    r = np.where(r == 0.0, 0.0, r)  # -0 == +0
+    order = np.lexsort((i, -r))
+    sel = np.sort(i[order[:K]])
+    out = -np.ones(min(K, row.size), np.int64)
+    out[: sel.size] = sel
+    return out
+
+
+def test_topk_matches_lexsort_with_heavy_ties(oracle_lib):
+    rng = np.random.default_rng(7)
+    for S, K in [(37, 8), (64, 64), (100, 130), (257, 31)]:
+        cfg = _cfg(S=S, K=K, T=1)
+        sc = rng.integers(-4, 5, size=(20, S)).astype(np.float32)
+        sc[3] = 0.0
+        sc[4, ::3] = -0.0
+        sc[5, ::2] = -np.inf
+        sc[6, 1::4] = np.nan
+        sc[7] = -np.inf
+        sc[8, 5] = np.inf
+        got = oracle.topk(cfg, sc)
+        for r in range(sc.shape[0]):
+            assert np.array_equal(got[r], _lexsort_topk(sc[r], K)), (S, K, r)
+
+
+def test_topk_invariants_real_scores(oracle_lib):
+    """Every selected score >= every unselected one; equal scores at the
+    boundary go to the lower indices; output ascending then -1."""
+    rng = np.random.default_rng(8)
+    cfg = _cfg(S=500, K=64, T=1)
+    sc = rng.standard_normal((16, 500)).astype(np.float32)
+    sc[:, 300:310] = sc[:, 10:11]  # a block of equal values
+    got = oracle.topk(cfg, sc)
+    for r in range(16):
+        sel = got[r][got[r] >= 0]
+        assert np.all(np.diff(sel) > 0)
+        mask = np.zeros(500, bool)
+        mask[sel] = True
+        assert sel.size == 64
+        lo = sc[r][mask].min()
+        assert sc[r][~mask].max() <= lo
+        eq_sel = np.nonzero(mask & (sc[r] == lo))[0]
+        eq_uns = np.nonzero(~mask & (sc[r] == lo))[0]
+        if eq_uns.size:
+            assert eq_sel.max() < eq_uns.min()
+
+
+def test_topk_signed_zero_is_one_value(oracle_lib):
+    cfg = _cfg(S=6, K=3, T=1)
+    sc = np.array([[-0.0, 0.0, -0.0, 0.0, -1.0, 1.0]], np.float32)
+    assert oracle.topk(cfg, sc)[0].tolist() == [0, 1, 5]
+
+
+def test_topk_short_rows_pad_and_wide_k(oracle_lib):
+    cfg = _cfg(S=6, K=10, T=1)
+    sc = np.array([[1, -np.inf, 2, np.nan, -np.inf, 0]], np.float32)
+    assert oracle.topk(cfg, sc)[0].tolist() == [0, 2, 5, -1, -1, -1]
+
+
+# ---------------------------------------------------------------------------
+# latent attention
+# ---------------------------------------------------------------------------
+
+def _sdpa(q, k, v, mask=None):
+    """torch scaled_dot_product_attention in fp64 on the CPU, [H, Tq, D]."""
+    torch = pytest.importorskip("torch")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a, np.float64)) for a in (q, k, v))
+    m = None if mask is None else torch.from_numpy(mask)
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m, scale=1.0)
+    return out.numpy()
+
+
+def test_sparse_with_full_selection_is_dense_causal_sdpa(oracle_lib):
+    """K >= causal length: top-k keeps every visible key, and sparse attention
+    equals textbook causal softmax attention (torch SDPA, fp64) to 1e-12;
+    row t has exactly t + 1 nonzero probabilities."""
+    cfg = _cfg(B=1, T=24, S=24, K=24, H=3, Dc=6, Dr=2, sm_scale=0.37)
+    rng = np.random.default_rng(9)
+    x = _draw(cfg, rng)
+    rb, rt = _rows(cfg)
+    idx = oracle.topk(cfg, _scores(cfg, x))
+    o, lse, p = oracle.sparse_mla(cfg, rb, x["q"], x["kv"], idx, want_probs=True)
+    kv = x["kv"][0].astype(np.float64)
+    sm = np.float64(np.float32(cfg.sm_scale))                            # the scale is an fp32 argument
+    q = x["q"].astype(np.float64).transpose(1, 0, 2) * sm                # [H, T, D]
+    k = np.broadcast_to(kv[None], (cfg.H,) + kv.shape)                   # one key row for all heads
+    v = np.broadcast_to(kv[None, :, : cfg.Dc], (cfg.H, cfg.S, cfg.Dc))   # value = latent part
+    ref = _sdpa(q, k, v, mask=np.tril(np.ones((cfg.T, cfg.S), bool)))
+    np.testing.assert_allclose(o.transpose(1, 0, 2), ref, rtol=1e-12, atol=1e-12)
+    nz = (p[:, 0, :] != 0).sum(axis=1)
+    assert np.array_equal(nz, np.arange(1, cfg.T + 1))
+    do, dl = oracle.dense_mla(cfg, rb, rt, x["q"], x["kv"])
+    np.testing.assert_allclose(o, do, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, dl, rtol=1e-12, atol=1e-12)
+
+
+def test_absorbed_equals_explicit_form(oracle_lib):
+    """q_lat_h = W_UK,h q^C_h and out_h = o_lat_h W_UV,h reproduce the explicit
+    per-head keys c W_UK and values c W_UV, checked against both the oracle's
+    explicit routine and torch SDPA on explicitly expanded keys (fp64, 1e-12)."""
+    rng = np.random.default_rng(10)
+    H, Dc, Dn, Dv, Dr, S = 4, 16, 8, 6, 4, 13
+    sm = 0.29
+    qC = rng.standard_normal((H, Dn))
+    qR = rng.standard_normal((H, Dr))
+    kv = rng.standard_normal((S, Dc + Dr))
+    c, r = kv[:, :Dc], kv[:, Dc:]
+    W_UK = rng.standard_normal((Dc, H * Dn)) / 4
+    W_UV = rng.standard_normal((Dc, H * Dv)) / 4
+    explicit = oracle.explicit_mla(qC, qR, c, r, W_UK, W_UV, sm)
+    # library form: expand keys and values per head, then SDPA
+    KC = (c @ W_UK).reshape(S, H, Dn).transpose(1, 0, 2)
+    Kfull = np.concatenate([KC, np.broadcast_to(r[None], (H, S, Dr))], axis=-1)
+    V = (c @ W_UV).reshape(S, H, Dv).transpose(1, 0, 2)
+    qfull = np.concatenate([qC, qR], axis=-1)[:, None, :] * sm
+    ref = _sdpa(qfull, Kfull, V)[:, 0]
+    np.testing.assert_allclose(explicit, ref, rtol=1e-12, atol=1e-12)
+    # absorbed form through the sparse routine
+    q_lat = np.stack([W_UK[:, h * Dn:(h + 1) * Dn] @ qC[h] for h in range(H)])
+    q_abs = np.concatenate([q_lat, qR], axis=-1)[None].astype(np.float64)
+    cfg = _cfg(B=1, T=1, S=S, H=H, Dc=Dc, Dr=Dr, K=S, sm_scale=sm)
+    # the oracle reads fp32 storage: keep values exactly representable
+    q32 = q_abs.astype(np.float32)
+    kv32 = kv[None].astype(np.float32)
+    o_lat, _ = oracle.sparse_mla(cfg, [0], q32, kv32, np.arange(S, dtype=np.int32)[None])
+    out = np.stack([o_lat[0, h] @ W_UV[:, h * Dv:(h + 1) * Dv] for h in range(H)])
+    # same identity on the rounded inputs, through torch, to 1e-12
+    c32, r32 = kv32[0, :, :Dc].astype(np.float64), kv32[0, :, Dc:].astype(np.float64)
+    qa = q32[0].astype(np.float64)
+    ref_abs = _sdpa(qa[:, None, :] * np.float64(np.float32(sm)),
+                    np.broadcast_to(np.concatenate([c32, r32], 1)[None], (H, S, Dc + Dr)),
+                    np.broadcast_to(c32[None], (H, S, Dc)))[:, 0]
+    np.testing.assert_allclose(o_lat[0], ref_abs, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out, ref, rtol=2e-5, atol=2e-5)  # fp32 rounding of q, kv
+
+
+def test_softmax_rows_sum_to_one(oracle_lib):
+    cfg = _cfg(B=2, T=3, S=50, K=16)
+    rng = np.random.default_rng(12)
+    x = _draw(cfg, rng)
+    rb, _ = _rows(cfg)
+    idx = oracle.topk(cfg, _scores(cfg, x))
+    _, _, p = oracle.sparse_mla(cfg, rb, x["q"], x["kv"], idx, want_probs=True)
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert np.all(p[np.broadcast_to((idx < 0)[:, None, :], p.shape)] == 0)
+
+
+def test_zero_query_averages_selected_latents(oracle_lib):
+    """q = 0: every logit is 0, o = mean of the selected latent rows, lse = ln |J|."""
+    cfg = _cfg(B=1, T=1, S=40, K=9)
+    rng = np.random.default_rng(13)
+    kv = rng.standard_normal((1, 40, cfg.D)).astype(np.float32)
+    q = np.zeros((1, cfg.H, cfg.D), np.float32)
+    idx = np.array([[3, 7, 8, 11, 20, 21, 39, -1, -1]], np.int32)
+    o, lse = oracle.sparse_mla(cfg, [0], q, kv, idx)
+    ref = kv[0, idx[0][idx[0] >= 0], : cfg.Dc].astype(np.float64).mean(0)
+    for h in range(cfg.H):
+        np.testing.assert_allclose(o[0, h], ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse[0], math.log(7), rtol=1e-14)
+
+
+def test_single_key_and_duplicates_and_empty_rows(oracle_lib):
+    cfg = _cfg(B=1, T=1, S=10, K=4, sm_scale=0.5)
+    rng = np.random.default_rng(14)
+    kv = rng.standard_normal((1, 10, cfg.D)).astype(np.float32)
+    q = rng.standard_normal((1, cfg.H, cfg.D)).astype(np.float32)
+    logit = 0.5 * (q[0].astype(np.float64) @ kv[0, 6].astype(np.float64))
+    o, lse = oracle.sparse_mla(cfg, [0], q, kv, np.array([[6, -1, 55, -7]], np.int32))
+    np.testing.assert_allclose(o[0], np.broadcast_to(kv[0, 6, : cfg.Dc], (cfg.H, cfg.Dc)),
+                               rtol=1e-14)
+    np.testing.assert_allclose(lse[0], logit, rtol=1e-12)
+    # a duplicate counts twice: same output, lse + ln 2
+    o2, lse2 = oracle.sparse_mla(cfg, [0], q, kv, np.array([[6, 6, -1, -1]], np.int32))
+    np.testing.assert_allclose(o2, o, rtol=1e-14)
+    np.testing.assert_allclose(lse2[0], logit + math.log(2), rtol=1e-12)
+    o3, lse3 = oracle.sparse_mla(cfg, [0], q, kv, np.array([[-1, -1, 10, -2]], np.int32))
+    assert np.all(o3 == 0) and np.all(np.isneginf(lse3))
+
+
+def test_index_order_does_not_matter(oracle_lib):
+    cfg = _cfg(B=1, T=1, S=64, K=12)
+    rng = np.random.default_rng(15)
+    kv = rng.standard_normal((1, 64, cfg.D)).astype(np.float32)
+    q = rng.standard_normal((1, cfg.H, cfg.D)).astype(np.float32)
+    idx = np.sort(rng.choice(64, 12, replace=False)).astype(np.int32)[None]
+    o1, l1 = oracle.sparse_mla(cfg, [0], q, kv, idx)
+    o2, l2 = oracle.sparse_mla(cfg, [0], q, kv, idx[:, ::-1].copy())
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(l1, l2, rtol=1e-14)
+
+
+def test_rotary_part_enters_logits_not_values(oracle_lib):
+    """Zeroing q's latent part leaves logits from the rotary part only; the
+    output is still a mix of the latent columns (never the rotary ones)."""
+    cfg = _cfg(B=1, T=1, S=5, K=5, H=1, Dc=3, Dr=2, sm_scale=1.0)
+    kv = np.zeros((1, 5, 5), np.float32)
+    kv[0, :, :3] = np.arange(15, dtype=np.float32).reshape(5, 3)
+    kv[0, 2, 3:] = [1.0, 1.0]
+    q = np.array([[[0, 0, 0, 20.0, 20.0]]], np.float32)
+    o, lse = oracle.sparse_mla(cfg, [0], q, kv, np.arange(5, dtype=np.int32)[None])
+    np.testing.assert_allclose(o[0, 0], kv[0, 2, :3], rtol=1e-12)  # weight ~ 1 on key 2
+    np.testing.assert_allclose(lse[0, 0], 40.0, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# page constants
+# ---------------------------------------------------------------------------
+
+def test_page_constants_fix_the_shapes():
+    with open(os.path.join(GOLDEN, "page_constants.json")) as f:
+        pc = json.load(f)
+    v = {k: (d["value"] if isinstance(d, dict) else d) for k, d in pc.items() if not k.startswith("_")}
+    dim, qr, kr = v["dim"], v["q_lora_rank"], v["kv_lora_rank"]
+    H, dn, dr, dv = v["n_heads"], v["qk_nope_head_dim"], v["qk_rope_head_dim"], v["v_head_dim"]
+    HI, DI = v["index_n_heads"], v["index_head_dim"]
+    params = (dim * qr + qr + qr * H * (dn + dr) + dim * (kr + dr) + kr + kr * H * (dn + dv)
+              + H * dv * dim
+              + qr * HI * DI + dim * DI + 2 * DI + dim * HI)   # indexer: wq_b, wk, LayerNorm(w, b), weights_proj
+    assert params == v["sparse_latent_attention_params_per_block"]
+    # the shapes the workloads use
+    for name in ("decode_8k", "prefill_16k", "decode_128k", "decode_64k_fp8"):
+        c = g.CONFIGS[name]
+        assert (c.HI, c.DI, c.H, c.Dc, c.Dr, c.K) == (HI, DI, H, kr, dr, v["index_topk"])
+        assert abs(c.softmax_scale - (dn + dr) ** -0.5) < 1e-7
+        assert abs(c.index_scale - 1 / (math.sqrt(HI) * math.sqrt(DI))) < 1e-9
+    assert round((dn + dr) ** -0.5, 4) == v["softmax_scale_plain"]
+    for ver in ("v32", "v2"):
+        f = v[f"yarn_factor_{ver}"]
+        d = pc[f"yarn_factor_{ver}"]
+        m = (0.1 * d["mscale"] * math.log(d["rope_factor"]) + 1.0) ** 2
+        assert round(m, 2) == f
+        assert round(m * (dn + dr) ** -0.5, 4) == v[f"softmax_scale_yarn_{ver}"]
