@@ -1,0 +1,156 @@
+/*
+ * libdsa: DeepSeek-V3.2 sparse attention hot path on AMD Instinct MI355X
+ * (gfx950).  Lightning-indexer scores -> per-query top-K -> absorbed sparse
+ * latent attention, as hand-written HIP kernels behind a plain C ABI.
+ *
+ * Where each operation is defined:
+ *  - index score and causal mask: atlas.klimoza.dev, DeepSeek-V3.2-Exp, MoE
+ *    block, "All 43 steps": S^I_{t,s} = 1/(sqrt 64 sqrt 128) sum_h w_{t,h}
+ *    ReLU(Q^I_{h,t} . k^I_s); S~^I = S^I + M;
+ *  - selection: the same step list, M^sel keeps s in top_2048(S~^I_t); the
+ *    nnterp deepseek_v32 page, section 03, gives the result's layout, int32
+ *    [batch, query, min(index_topk, keys)];
+ *  - sparse latent attention: the same step list (k^C = c^KV W_UK, v = c^KV
+ *    W_UV, K_i = [K^C_i ; k^R], one rotary key shared by all heads), taken in
+ *    absorbed form (q_lat_h = W_UK,h q^C_h, output = per-head 512-wide latent
+ *    context before W_UV), with the nnterp deepseek_v32 semantics of section
+ *    03/04: zero probability outside the selection, rows summing to one over
+ *    it, a written index list used as written.
+ *
+ * Conventions shared by every entry point:
+ *  - Memory.  Every tensor pointer is caller-owned DEVICE memory, row-major
+ *    and contiguous, 16-byte aligned.  The library allocates nothing; scratch
+ *    comes from the caller's workspace, sized by dsa_workspace_bytes().
+ *  - Streams.  Work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream).  Calls return after enqueueing: results are valid once the
+ *    stream has reached them.  No call synchronises the host.
+ *  - Positions.  Query t of a sequence sits at position q_pos(t) = S - T + t
+ *    and sees keys s <= q_pos(t).  Decode is T = 1 (sees all S keys); causal
+ *    prefill is T = S.
+ *  - Errors.  A call returns DSA_OK or an error code and enqueues nothing on
+ *    error (argument errors are detected on the host before any launch).
+ *    dsa_last_error() gives a thread-local message for the last failure.
+ *  - Outputs are fully overwritten, so a failed call can simply be repeated.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer */
+  DSA_ERR_UNSUPPORTED = 2, /* dtype or shape combination without a kernel */
+  DSA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  DSA_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} dsa_status_t;
+
+typedef enum {
+  DSA_F32 = 0,
+  DSA_BF16 = 1,
+  DSA_FP8_E4M3 = 2 /* OCP E4M3FN bytes with one ue8m0 scale byte per 128 elements */
+} dsa_dtype_t;
+
+/* Problem description.  The DeepSeek-V3.2 sizes (config_671B_v3.2.json on the
+ * atlas block-input page) are HI x DI = 64 x 128, H = 128, Dc = 512, Dr = 64,
+ * K = 2048. */
+typedef struct {
+  int32_t B, T, S;   /* batch, queries per sequence, keys per sequence (T <= S) */
+  int32_t HI, DI;    /* indexer heads and head width */
+  int32_t H, Dc, Dr; /* latent-attention heads, latent width, rotary width */
+  int32_t K;         /* top-k; rows hold K_eff = min(K, S) indices */
+  float idx_scale;   /* index prefactor, 1/(sqrt(HI) sqrt(DI)) on the pages */
+  float sm_scale;    /* softmax scale on the logits (1/sqrt(192) for the V3.2 head) */
+  int32_t idx_dtype; /* dsa_dtype_t of q_idx and k_idx: F32, BF16 or FP8_E4M3 */
+  int32_t w_dtype;   /* dsa_dtype_t of w: F32 or BF16 */
+  int32_t mla_dtype; /* dsa_dtype_t of q, kv and o: F32 or BF16 */
+} dsa_shape_t;
+
+typedef enum {
+  DSA_ENTRY_TOPK = 0,
+  DSA_ENTRY_SPARSE_MLA = 1,
+  DSA_ENTRY_FORWARD = 2
+} dsa_entry_t;
+
+/*
+ * Index scores (the atlas MoE-block step list: S^I and the causal mask M).
+ *   q_idx  [B, T, HI, DI]  idx_dtype
+ *   q_sf   [B, T, HI, DI/128] uint8 ue8m0 scales (FP8 only, else NULL)
+ *   k_idx  [B, S, DI]      idx_dtype
+ *   k_sf   [B, S, DI/128]  uint8 ue8m0 scales (FP8 only, else NULL)
+ *   w      [B, T, HI]      w_dtype
+ *   scores [B, T, S]       fp32 output: idx_scale * sum_h w_h ReLU(q_h . k_s)
+ *                          for s <= q_pos(t), -inf for future keys.
+ * The head sum accumulates in fp32 and the prefactor multiplies it once, in
+ * fp32.  FP8 requires DI % 128 == 0.
+ */
+dsa_status_t dsa_indexer_scores(const dsa_shape_t* shape, const void* q_idx,
+                                const uint8_t* q_sf, const void* k_idx,
+                                const uint8_t* k_sf, const void* w, float* scores,
+                                void* stream);
+
+/*
+ * Top-K selection per score row (the step list's M^sel; layout from the
+ * nnterp deepseek_v32 page, section 03).
+ *   scores [B, T, S] fp32 (as written by dsa_indexer_scores, or any values)
+ *   idx    [B, T, K_eff] int32 output, K_eff = min(K, S)
+ * Selects the K_eff largest scores by (value descending, index ascending);
+ * -0 equals +0; NaN and -inf are never selected.  Each row lists the chosen
+ * indices in ascending order and is padded with -1 when fewer than K_eff
+ * scores are selectable.  The result is exact (no approximation).
+ * ws/ws_bytes: workspace of at least dsa_workspace_bytes(shape, DSA_ENTRY_TOPK)
+ * bytes (may be NULL/0 when that is 0).
+ */
+dsa_status_t dsa_topk(const dsa_shape_t* shape, const float* scores, int32_t* idx,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse latent attention in absorbed form over the listed keys.
+ *   q   [B, T, H, Dc+Dr] mla_dtype: per head, the absorbed latent query
+ *       (W_UK,h q^C_h, Dc wide) followed by the rotary query (Dr wide)
+ *   kv  [B, S, Dc+Dr]    mla_dtype: per key, the normalised latent c^KV (Dc)
+ *       followed by the rotary key k^R (Dr), shared by all heads
+ *   idx [B, T, K_eff]    int32 key indices; entries that are -1 or outside
+ *       [0, S) are skipped; duplicates count as written
+ *   o   [B, T, H, Dc]    mla_dtype output: sum_j p_j c_j with
+ *       p = softmax_j(sm_scale * (q_lat . c_j + q_rot . r_j))
+ *   lse [B, T, H]        fp32 output (nullable): log sum_j exp(logit_j)
+ * A row with no valid index gives o = 0 and lse = -inf.  Accumulation is in
+ * fp32.  ws: at least dsa_workspace_bytes(shape, DSA_ENTRY_SPARSE_MLA) bytes.
+ */
+dsa_status_t dsa_sparse_mla_fwd(const dsa_shape_t* shape, const void* q,
+                                const void* kv, const int32_t* idx, void* o,
+                                float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole hot path: index scores -> top-K -> sparse latent attention.
+ * Arguments as above; idx_out [B, T, K_eff] (nullable) receives the selection.
+ * ws: at least dsa_workspace_bytes(shape, DSA_ENTRY_FORWARD) bytes (it holds
+ * the [B, T, S] fp32 scores, the selection when idx_out is NULL, and the
+ * scratch of the two later steps).
+ */
+dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx,
+                         const uint8_t* q_sf, const void* k_idx, const uint8_t* k_sf,
+                         const void* w, const void* q, const void* kv,
+                         int32_t* idx_out, void* o, float* lse, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Workspace bytes an entry point needs for `shape` on the current device
+ * (0 if none).  Returns (size_t)-1 when the shape is invalid. */
+size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry);
+
+/* Static description of a status code. */
+const char* dsa_status_str(dsa_status_t status);
+
+/* Thread-local detail of the last failed call on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

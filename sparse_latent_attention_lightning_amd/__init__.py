@@ -1,0 +1,13 @@
+"""DeepSeek-V3.2 sparse attention hot path on MI355X (gfx950).
+
+Lightning-indexer scores -> per-query top-K -> absorbed sparse latent
+attention, as hand-written HIP kernels in ``libdsa.so`` behind the C ABI of
+``include/dsa.h``.  This package is the thin Python binding of that ABI.
+"""
+from ._binding import (DSA_BF16, DSA_F32, DSA_FP8_E4M3, ENTRY_FORWARD, ENTRY_SPARSE_MLA,
+                       ENTRY_TOPK, DsaError, DsaShape, dsa_forward, dsa_indexer_scores,
+                       dsa_sparse_mla_fwd, dsa_topk, lib, make_shape, workspace_bytes)
+
+__all__ = ["DSA_BF16", "DSA_F32", "DSA_FP8_E4M3", "ENTRY_FORWARD", "ENTRY_SPARSE_MLA",
+           "ENTRY_TOPK", "DsaError", "DsaShape", "dsa_forward", "dsa_indexer_scores",
+           "dsa_sparse_mla_fwd", "dsa_topk", "lib", "make_shape", "workspace_bytes"]

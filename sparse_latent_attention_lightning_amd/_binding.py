@@ -1,0 +1,215 @@
+"""ctypes binding of libdsa (include/dsa.h), same entry-point names.
+
+Argument marshalling only: shape checks, output/workspace allocation with
+torch, device pointers and the current HIP stream go to the C ABI; every step
+of the computation runs in the library's HIP kernels.  There is no fallback:
+if libdsa.so is missing or fails to load, the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+ENTRY_TOPK, ENTRY_SPARSE_MLA, ENTRY_FORWARD = 0, 1, 2
+STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
+          3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
+
+_ELEM = {DSA_F32: torch.float32, DSA_BF16: torch.bfloat16}
+
+
+class DsaShape(ctypes.Structure):
+    """Mirror of dsa_shape_t."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "T", "S", "HI", "DI", "H", "Dc", "Dr", "K")] + [
+        ("idx_scale", ctypes.c_float), ("sm_scale", ctypes.c_float),
+        ("idx_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("mla_dtype", ctypes.c_int32)]
+
+    @property
+    def K_eff(self) -> int:
+        return min(self.K, self.S)
+
+    def __repr__(self) -> str:
+        return "DsaShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def make_shape(B, T, S, HI, DI, H, Dc, Dr, K, idx_scale, sm_scale,
+               idx_dtype=DSA_BF16, w_dtype=DSA_BF16, mla_dtype=DSA_BF16) -> DsaShape:
+    return DsaShape(B, T, S, HI, DI, H, Dc, Dr, K, idx_scale, sm_scale, idx_dtype, w_dtype,
+                    mla_dtype)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libdsa (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              "`python -m sparse_latent_attention_lightning_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, sz = ctypes.c_void_p, ctypes.c_size_t
+        sp = ctypes.POINTER(DsaShape)
+        L.dsa_indexer_scores.argtypes = [sp, P, P, P, P, P, P, P]
+        L.dsa_topk.argtypes = [sp, P, P, P, sz, P]
+        L.dsa_sparse_mla_fwd.argtypes = [sp, P, P, P, P, P, P, sz, P]
+        L.dsa_forward.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_forward"):
+            getattr(L, f).restype = ctypes.c_int
+        L.dsa_workspace_bytes.argtypes = [sp, ctypes.c_int32]
+        L.dsa_workspace_bytes.restype = ctypes.c_size_t
+        L.dsa_status_str.argtypes = [ctypes.c_int]
+        L.dsa_status_str.restype = ctypes.c_char_p
+        L.dsa_last_error.argtypes = []
+        L.dsa_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise DsaError(status, lib().dsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _req(t: torch.Tensor, name: str, shape: Tuple[int, ...], dtypes, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _idx_dtypes(code):
+    if code == DSA_FP8_E4M3:
+        return (torch.uint8, torch.float8_e4m3fn)
+    return (_ELEM[code],)
+
+
+def workspace_bytes(shape: DsaShape, entry: int) -> int:
+    n = lib().dsa_workspace_bytes(ctypes.byref(shape), entry)
+    if n == ctypes.c_size_t(-1).value:
+        raise DsaError(1, lib().dsa_last_error().decode())
+    return n
+
+
+def _workspace(shape: DsaShape, entry: int, device) -> Optional[torch.Tensor]:
+    n = workspace_bytes(shape, entry)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _check_indexer(shape, q_idx, k_idx, w, q_sf, k_sf):
+    s = shape
+    dev = q_idx.device
+    _req(q_idx, "q_idx", (s.B, s.T, s.HI, s.DI), _idx_dtypes(s.idx_dtype))
+    _req(k_idx, "k_idx", (s.B, s.S, s.DI), _idx_dtypes(s.idx_dtype), dev)
+    _req(w, "w", (s.B, s.T, s.HI), (_ELEM[s.w_dtype],), dev)
+    if s.idx_dtype == DSA_FP8_E4M3:
+        _req(q_sf, "q_sf", (s.B, s.T, s.HI, s.DI // 128), (torch.uint8,), dev)
+        _req(k_sf, "k_sf", (s.B, s.S, s.DI // 128), (torch.uint8,), dev)
+    return dev
+
+
+def _check_mla(shape, q, kv, idx):
+    s = shape
+    dev = q.device
+    _req(q, "q", (s.B, s.T, s.H, s.Dc + s.Dr), (_ELEM[s.mla_dtype],))
+    _req(kv, "kv", (s.B, s.S, s.Dc + s.Dr), (_ELEM[s.mla_dtype],), dev)
+    if idx is not None:
+        _req(idx, "idx", (s.B, s.T, s.K_eff), (torch.int32,), dev)
+    return dev
+
+
+def dsa_indexer_scores(shape: DsaShape, q_idx, k_idx, w, q_sf=None, k_sf=None,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Index scores [B, T, S] fp32 (future keys -inf)."""
+    dev = _check_indexer(shape, q_idx, k_idx, w, q_sf, k_sf)
+    if out is None:
+        out = torch.empty((shape.B, shape.T, shape.S), dtype=torch.float32, device=dev)
+    _req(out, "scores", (shape.B, shape.T, shape.S), (torch.float32,), dev)
+    _check(lib().dsa_indexer_scores(ctypes.byref(shape), _ptr(q_idx), _ptr(q_sf), _ptr(k_idx),
+                                    _ptr(k_sf), _ptr(w), _ptr(out), _stream(dev)))
+    return out
+
+
+def dsa_topk(shape: DsaShape, scores, out: Optional[torch.Tensor] = None,
+             ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Top-K index rows [B, T, min(K, S)] int32, ascending, -1 padded."""
+    _req(scores, "scores", (shape.B, shape.T, shape.S), (torch.float32,))
+    dev = scores.device
+    if out is None:
+        out = torch.empty((shape.B, shape.T, shape.K_eff), dtype=torch.int32, device=dev)
+    _req(out, "idx", (shape.B, shape.T, shape.K_eff), (torch.int32,), dev)
+    if ws is None:
+        ws = _workspace(shape, ENTRY_TOPK, dev)
+    _check(lib().dsa_topk(ctypes.byref(shape), _ptr(scores), _ptr(out), _ptr(ws),
+                          0 if ws is None else ws.numel(), _stream(dev)))
+    return out
+
+
+def dsa_sparse_mla_fwd(shape: DsaShape, q, kv, idx, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                       ws: Optional[torch.Tensor] = None):
+    """Absorbed sparse latent attention: (o [B,T,H,Dc], lse [B,T,H] fp32 or None)."""
+    dev = _check_mla(shape, q, kv, idx)
+    if out is None:
+        out = torch.empty((shape.B, shape.T, shape.H, shape.Dc), dtype=q.dtype, device=dev)
+    _req(out, "o", (shape.B, shape.T, shape.H, shape.Dc), (q.dtype,), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((shape.B, shape.T, shape.H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _req(lse, "lse", (shape.B, shape.T, shape.H), (torch.float32,), dev)
+    if ws is None:
+        ws = _workspace(shape, ENTRY_SPARSE_MLA, dev)
+    _check(lib().dsa_sparse_mla_fwd(ctypes.byref(shape), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out),
+                                    _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(dev)))
+    return out, lse
+
+
+def dsa_forward(shape: DsaShape, q_idx, k_idx, w, q, kv, q_sf=None, k_sf=None,
+                want_idx: bool = True, want_lse: bool = True, ws: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None):
+    """The whole hot path: (o, lse or None, idx or None)."""
+    dev = _check_indexer(shape, q_idx, k_idx, w, q_sf, k_sf)
+    _check_mla(shape, q, kv, None)
+    if out is None:
+        out = torch.empty((shape.B, shape.T, shape.H, shape.Dc), dtype=q.dtype, device=dev)
+    if idx_out is None and want_idx:
+        idx_out = torch.empty((shape.B, shape.T, shape.K_eff), dtype=torch.int32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((shape.B, shape.T, shape.H), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(shape, ENTRY_FORWARD, dev)
+    _check(lib().dsa_forward(ctypes.byref(shape), _ptr(q_idx), _ptr(q_sf), _ptr(k_idx), _ptr(k_sf),
+                             _ptr(w), _ptr(q), _ptr(kv), _ptr(idx_out), _ptr(out), _ptr(lse),
+                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
+    return out, lse, idx_out

@@ -1,0 +1,231 @@
+// libdsa C ABI: argument validation, dispatch and workspace layout.
+// The operations are defined in include/dsa.h (with the passages of the pages
+// each one follows); the kernels live in indexer.hip, topk.hip and
+// sparse_mla.hip.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <vector>
+
+#include "dsa.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+thread_local char g_last_error[512] = "";
+
+constexpr size_t kAlign = 256;  // workspace sub-buffers start on 256-byte boundaries
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dtype_bytes(int32_t dt) {
+  switch (dt) {
+    case DSA_F32: return 4;
+    case DSA_BF16: return 2;
+    case DSA_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+dsa_status_t check_shape(const dsa_shape_t* s) {
+  if (s == nullptr) return fail(DSA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B <= 0 || s->T <= 0 || s->S <= 0)
+    return fail(DSA_ERR_INVALID_ARG, "B, T, S must be positive (got %d, %d, %d)", s->B, s->T, s->S);
+  if (s->T > s->S) return fail(DSA_ERR_INVALID_ARG, "T = %d exceeds S = %d", s->T, s->S);
+  if (s->HI <= 0 || s->DI <= 0) return fail(DSA_ERR_INVALID_ARG, "HI and DI must be positive");
+  if (s->H <= 0 || s->Dc <= 0 || s->Dr < 0)
+    return fail(DSA_ERR_INVALID_ARG, "H and Dc must be positive and Dr non-negative");
+  if (s->K <= 0) return fail(DSA_ERR_INVALID_ARG, "K must be positive (got %d)", s->K);
+  if (s->idx_dtype != DSA_F32 && s->idx_dtype != DSA_BF16 && s->idx_dtype != DSA_FP8_E4M3)
+    return fail(DSA_ERR_INVALID_ARG, "unknown idx_dtype %d", s->idx_dtype);
+  if (s->w_dtype != DSA_F32 && s->w_dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "w_dtype must be F32 or BF16 (got %d)", s->w_dtype);
+  if (s->mla_dtype != DSA_F32 && s->mla_dtype != DSA_BF16)
+    return fail(DSA_ERR_INVALID_ARG, "mla_dtype must be F32 or BF16 (got %d)", s->mla_dtype);
+  if (s->idx_dtype == DSA_FP8_E4M3 && s->DI % 128 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "fp8 indexer needs DI %% 128 == 0 (got %d)", s->DI);
+  const int64_t rows = static_cast<int64_t>(s->B) * s->T;
+  if (rows * s->S > (int64_t(1) << 40))
+    return fail(DSA_ERR_UNSUPPORTED, "B*T*S too large");
+  if ((static_cast<int64_t>(s->Dc + s->Dr) * dtype_bytes(s->mla_dtype)) % 16 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "(Dc + Dr) rows must be a multiple of 16 bytes");
+  return DSA_OK;
+}
+
+dsa_status_t need(const void* p, const char* name) {
+  if (p == nullptr) return fail(DSA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(DSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return DSA_OK;
+}
+
+dsa_status_t check_indexer_args(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
+                                const void* k_idx, const uint8_t* k_sf, const void* w,
+                                const float* scores) {
+  dsa_status_t st;
+  if ((st = need(q_idx, "q_idx")) || (st = need(k_idx, "k_idx")) || (st = need(w, "w")) ||
+      (st = need(scores, "scores")))
+    return st;
+  if (s.idx_dtype == DSA_FP8_E4M3) {
+    if (q_sf == nullptr || k_sf == nullptr)
+      return fail(DSA_ERR_INVALID_ARG, "fp8 indexer needs q_sf and k_sf");
+  }
+  return DSA_OK;
+}
+
+dsa_status_t check_mla_args(const void* q, const void* kv, const int32_t* idx, const void* o) {
+  dsa_status_t st;
+  if ((st = need(q, "q")) || (st = need(kv, "kv")) || (st = need(idx, "idx")) ||
+      (st = need(o, "o")))
+    return st;
+  return DSA_OK;
+}
+
+struct ForwardLayout {
+  size_t scores, idx, topk_ws, mla_ws, total;
+};
+
+ForwardLayout forward_layout(const dsa_shape_t& s) {
+  const size_t rows = static_cast<size_t>(s.B) * s.T;
+  ForwardLayout L{};
+  L.scores = 0;
+  L.idx = align_up(rows * s.S * sizeof(float));
+  L.topk_ws = L.idx + align_up(rows * k_eff(s) * sizeof(int32_t));
+  L.mla_ws = L.topk_ws + align_up(topk_workspace_bytes(s));
+  L.total = L.mla_ws + align_up(mla_workspace_bytes(s));
+  return L;
+}
+
+}  // namespace
+
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+dsa_status_t check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DSA_OK;
+}
+
+const DeviceInfo& device_info() {
+  static std::mutex mu;
+  static std::vector<DeviceInfo> cache;
+  static std::vector<bool> have;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<size_t>(dev) >= cache.size()) {
+    cache.resize(dev + 1);
+    have.resize(dev + 1, false);
+  }
+  if (!have[dev]) {
+    hipDeviceProp_t p{};
+    DeviceInfo info{256, 160 * 1024};
+    if (hipGetDeviceProperties(&p, dev) == hipSuccess) {
+      info.cu_count = p.multiProcessorCount;
+      info.max_lds = p.sharedMemPerBlock;
+    }
+    cache[dev] = info;
+    have[dev] = true;
+  }
+  return cache[dev];
+}
+
+}  // namespace dsa
+
+using namespace dsa;
+
+extern "C" {
+
+dsa_status_t dsa_indexer_scores(const dsa_shape_t* shape, const void* q_idx, const uint8_t* q_sf,
+                                const void* k_idx, const uint8_t* k_sf, const void* w,
+                                float* scores, void* stream) {
+  g_last_error[0] = '\0';
+  dsa_status_t st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if ((st = check_indexer_args(*shape, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
+  return launch_indexer(*shape, q_idx, q_sf, k_idx, k_sf, w, scores,
+                        static_cast<hipStream_t>(stream));
+}
+
+dsa_status_t dsa_topk(const dsa_shape_t* shape, const float* scores, int32_t* idx, void* ws,
+                      size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  dsa_status_t st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if ((st = need(scores, "scores")) || (st = need(idx, "idx"))) return st;
+  if (ws != nullptr && !aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  return launch_topk(*shape, scores, idx, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+dsa_status_t dsa_sparse_mla_fwd(const dsa_shape_t* shape, const void* q, const void* kv,
+                                const int32_t* idx, void* o, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  dsa_status_t st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  if ((st = check_mla_args(q, kv, idx, o)) != DSA_OK) return st;
+  if (ws != nullptr && !aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  return launch_sparse_mla(*shape, q, kv, idx, o, lse, ws, ws_bytes,
+                           static_cast<hipStream_t>(stream));
+}
+
+dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx, const uint8_t* q_sf,
+                         const void* k_idx, const uint8_t* k_sf, const void* w, const void* q,
+                         const void* kv, int32_t* idx_out, void* o, float* lse, void* ws,
+                         size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  dsa_status_t st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  const dsa_shape_t& s = *shape;
+  const ForwardLayout L = forward_layout(s);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(DSA_ERR_WORKSPACE, "forward: workspace of %zu bytes needed, %zu given", L.total,
+                ws_bytes);
+  if (!aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + L.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx);
+  if ((st = check_indexer_args(s, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
+  if ((st = check_mla_args(q, kv, idx, o)) != DSA_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if ((st = launch_indexer(s, q_idx, q_sf, k_idx, k_sf, w, scores, hs)) != DSA_OK) return st;
+  if ((st = launch_topk(s, scores, idx, base + L.topk_ws, L.mla_ws - L.topk_ws, hs)) != DSA_OK)
+    return st;
+  return launch_sparse_mla(s, q, kv, idx, o, lse, base + L.mla_ws, L.total - L.mla_ws, hs);
+}
+
+size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry) {
+  if (check_shape(shape) != DSA_OK) return static_cast<size_t>(-1);
+  switch (entry) {
+    case DSA_ENTRY_TOPK: return topk_workspace_bytes(*shape);
+    case DSA_ENTRY_SPARSE_MLA: return mla_workspace_bytes(*shape);
+    case DSA_ENTRY_FORWARD: return forward_layout(*shape).total;
+  }
+  fail(DSA_ERR_INVALID_ARG, "unknown entry %d", entry);
+  return static_cast<size_t>(-1);
+}
+
+const char* dsa_status_str(dsa_status_t status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_INVALID_ARG: return "DSA_ERR_INVALID_ARG";
+    case DSA_ERR_UNSUPPORTED: return "DSA_ERR_UNSUPPORTED";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP";
+  }
+  return "DSA_ERR_UNKNOWN";
+}
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

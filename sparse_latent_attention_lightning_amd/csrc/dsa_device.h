@@ -1,0 +1,92 @@
+// Device-side helpers shared by the libdsa kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// OCP E4M3FN byte -> fp32 (exact); used by the generic kernels only.
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+  const uint32_t s = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xfu;
+  const uint32_t m = c & 0x7u;
+  if (e == 0xfu && m == 0x7u) return __uint_as_float(0x7fc00000u);
+  float v;
+  if (e == 0)
+    v = static_cast<float>(m) * 0.001953125f;  // m/8 * 2^-6
+  else
+    v = __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1+m/8)*2^(e-7)
+  return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// ue8m0 scale byte -> 2^(byte-127) as fp32 (bytes 0 and 255 are not used by
+// the block quantiser; 0 maps to 2^-127 (a subnormal), 255 to NaN).
+__device__ __forceinline__ float ue8m0_to_f32(uint8_t b) {
+  if (b == 0xffu) return __uint_as_float(0x7fc00000u);
+  if (b == 0) return __uint_as_float(0x00400000u);
+  return __uint_as_float(static_cast<uint32_t>(b) << 23);
+}
+
+// Order-preserving key of an fp32 score: larger score -> larger key.
+// -0 is folded into +0; NaN and -inf map to 0, which no selectable score
+// reaches (the smallest selectable key, that of -FLT_MAX, is 0x00800000).
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;                      // -0 -> +0
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;    // NaN
+  if (u == 0xff800000u) return 0u;                   // -inf
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32_bf16(const bf16x8_t& a, const bf16x8_t& b,
+                                                     const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32_fp8(long a, long b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+}
+
+}  // namespace dsa

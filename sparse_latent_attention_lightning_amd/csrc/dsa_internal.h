@@ -1,0 +1,41 @@
+// Host-side declarations shared by the libdsa translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+// Device facts the launch heuristics need, cached once per device.
+struct DeviceInfo {
+  int cu_count;
+  size_t max_lds;
+};
+const DeviceInfo& device_info();
+
+// Records a failure detail for dsa_last_error() and returns `st`.
+dsa_status_t fail(dsa_status_t st, const char* fmt, ...);
+// Checks the last launch on this thread.
+dsa_status_t check_launch(const char* what);
+
+inline int32_t k_eff(const dsa_shape_t& s) { return s.K < s.S ? s.K : s.S; }
+
+// ---- index scores -------------------------------------------------------
+dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
+                            const void* k_idx, const uint8_t* k_sf, const void* w,
+                            float* scores, hipStream_t stream);
+
+// ---- top-k -------------------------------------------------------------
+size_t topk_workspace_bytes(const dsa_shape_t& s);
+dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+// ---- sparse latent attention ------------------------------------------
+size_t mla_workspace_bytes(const dsa_shape_t& s);
+dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* kv,
+                               const int32_t* idx, void* o, float* lse, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+}  // namespace dsa

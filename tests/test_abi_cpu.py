@@ -1,0 +1,119 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+entry point include/dsa.h declares, and rejects bad arguments before it
+touches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_latent_attention_lightning_amd as m
+    if not os.path.exists(m._binding.LIB_PATH):
+        from sparse_latent_attention_lightning_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_forward",
+              "dsa_workspace_bytes", "dsa_status_str", "dsa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(dsa):
+    lib = ctypes.CDLL(dsa._binding.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
+
+
+def test_status_strings(dsa):
+    L = dsa.lib()
+    assert L.dsa_status_str(0) == b"DSA_OK"
+    assert L.dsa_status_str(3) == b"DSA_ERR_WORKSPACE"
+    assert L.dsa_status_str(99) == b"DSA_ERR_UNKNOWN"
+
+
+def _v32(dsa, **kw):
+    base = dict(B=32, T=1, S=8192, HI=64, DI=128, H=128, Dc=512, Dr=64, K=2048,
+                idx_scale=1 / (8 * 128 ** 0.5), sm_scale=192 ** -0.5)
+    base.update(kw)
+    return dsa.make_shape(**base)
+
+
+def test_workspace_sizes(dsa):
+    s = _v32(dsa)
+    topk = dsa.workspace_bytes(s, dsa.ENTRY_TOPK)
+    mla = dsa.workspace_bytes(s, dsa.ENTRY_SPARSE_MLA)
+    fwd = dsa.workspace_bytes(s, dsa.ENTRY_FORWARD)
+    assert topk == 0                               # one workgroup per 8192-key row
+    assert mla % (32 * 128 * 513 * 4) == 0 and mla > 0   # split partials (o and lse)
+    assert fwd >= 32 * 8192 * 4 + 32 * 2048 * 4 + mla
+    long = _v32(dsa, B=8, S=131072)
+    assert dsa.workspace_bytes(long, dsa.ENTRY_TOPK) == 8 * 4 * 2048 * 8  # 4 chunks of candidates
+    prefill = _v32(dsa, B=1, T=16384, S=16384)
+    assert dsa.workspace_bytes(prefill, dsa.ENTRY_SPARSE_MLA) == 0         # no splits
+    with pytest.raises(dsa.DsaError):
+        dsa.workspace_bytes(_v32(dsa, K=0), dsa.ENTRY_TOPK)
+    with pytest.raises(dsa.DsaError):
+        dsa.workspace_bytes(s, 7)
+
+
+@pytest.mark.parametrize("bad,msg", [
+    (dict(B=0), "positive"), (dict(T=9, S=8), "exceeds"), (dict(K=0), "K must"),
+    (dict(idx_dtype=2, DI=100), "fp8"), (dict(w_dtype=2), "w_dtype"), (dict(mla_dtype=2), "mla_dtype"),
+    (dict(HI=-1), "HI"),
+])
+def test_bad_shapes_rejected_on_host(dsa, bad, msg):
+    L = dsa.lib()
+    s = _v32(dsa, **bad)
+    P = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    for rc in (L.dsa_indexer_scores(ctypes.byref(s), P, None, P, None, P, P, None),
+               L.dsa_topk(ctypes.byref(s), P, P, None, 0, None),
+               L.dsa_sparse_mla_fwd(ctypes.byref(s), P, P, P, P, None, None, 0, None),
+               L.dsa_forward(ctypes.byref(s), P, None, P, None, P, P, P, None, P, None, None, 0, None)):
+        assert rc == 1
+        assert msg in L.dsa_last_error().decode()
+
+
+def test_null_and_misaligned_pointers_rejected(dsa):
+    L = dsa.lib()
+    s = _v32(dsa)
+    P = ctypes.c_void_p(256)
+    rc = L.dsa_indexer_scores(ctypes.byref(s), None, None, P, None, P, P, None)
+    assert rc == 1 and "q_idx is NULL" in L.dsa_last_error().decode()
+    rc = L.dsa_sparse_mla_fwd(ctypes.byref(s), P, ctypes.c_void_p(258), P, P, None, None, 0, None)
+    assert rc == 1 and "kv is not 16-byte aligned" in L.dsa_last_error().decode()
+    rc = L.dsa_indexer_scores(ctypes.byref(_v32(dsa, idx_dtype=2)), P, None, P, None, P, P, None)
+    assert rc == 1 and "q_sf" in L.dsa_last_error().decode()
+    rc = L.dsa_topk(None, P, P, None, 0, None)
+    assert rc == 1 and "shape is NULL" in L.dsa_last_error().decode()
+
+
+def test_forward_workspace_too_small(dsa):
+    L = dsa.lib()
+    s = _v32(dsa)
+    P = ctypes.c_void_p(256)
+    rc = L.dsa_forward(ctypes.byref(s), P, None, P, None, P, P, P, None, P, None, P, 1024, None)
+    assert rc == 3 and "workspace" in L.dsa_last_error().decode()
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import sparse_latent_attention_lightning_amd._binding as b
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(b, "_lib", None)
+    with pytest.raises(ImportError):
+        b.lib()

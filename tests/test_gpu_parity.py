@@ -1,0 +1,292 @@
+"""GPU parity: every libdsa entry point against the CPU oracle (MI355X only).
+
+Inputs are the seeded synthetic workloads of ``dsa_inputs`` (or small
+variants of them), identical bytes on both sides.  The bar:
+  * index scores: bit-exact on integer-valued inputs (sums are exact in fp32
+    and fp64); otherwise within 1e-4 of the row's largest |score|;
+  * top-K: bit-exact against the oracle's selection on the SAME fp32 scores;
+    end to end (GPU scores vs oracle scores) a key may differ only within the
+    1e-5 relative gap of the K-th score;
+  * latent attention on the same indices: per (b, t, h) row within 1e-4
+    (fp32) / 2e-2 (bf16) of the row's largest |o|; lse within the same bar
+    in absolute terms.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import dsa_inputs as g
+import oracle
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_latent_attention_lightning_amd as m
+    m.lib()
+    oracle.build(force=False)
+    return m
+
+
+def _rows(cfg, rows=None):
+    if rows is None:
+        rb = np.repeat(np.arange(cfg.B, dtype=np.int32), cfg.T)
+        rt = np.tile(np.arange(cfg.T, dtype=np.int32), cfg.B)
+    else:
+        rb = np.array([r[0] for r in rows], np.int32)
+        rt = np.array([r[1] for r in rows], np.int32)
+    return rb, rt
+
+
+def _host_rows(cfg, tensor, rb, rt):
+    """Per-query rows of q_idx / w / q for the listed (b, t)."""
+    parts = [g.rows(cfg, tensor, int(b), int(t), int(t) + 1) for b, t in zip(rb, rt)]
+    if isinstance(parts[0], tuple):
+        return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+    return np.concatenate(parts)
+
+
+def _oracle_scores(cfg, rb, rt):
+    k = g.full(cfg, "k_idx")
+    qi = _host_rows(cfg, "q_idx", rb, rt)
+    w = _host_rows(cfg, "w", rb, rt)
+    if cfg.idx_dtype == "fp8":
+        return oracle.indexer_scores(cfg, rb, rt, qi[0], w, k[0], qi[1], k[1])
+    return oracle.indexer_scores(cfg, rb, rt, qi, w, k)
+
+
+def _inputs(cfg):
+    d = {n: U.upload(cfg, n) for n in ("q_idx", "k_idx", "w", "q", "kv")}
+    if cfg.idx_dtype == "fp8":
+        d["q_idx"], d["q_sf"] = d["q_idx"]
+        d["k_idx"], d["k_sf"] = d["k_idx"]
+    else:
+        d["q_sf"] = d["k_sf"] = None
+    return d
+
+
+def _gpu_scores(dsa, cfg, x):
+    return dsa.dsa_indexer_scores(U.shape_of(cfg), x["q_idx"], x["k_idx"], x["w"], x["q_sf"], x["k_sf"])
+
+
+# ---------------------------------------------------------------------------
+# index scores
+# ---------------------------------------------------------------------------
+
+SCORE_CASES = {
+    # generic VALU kernel (4 heads x 32 dims, fp32), integer inputs: bit-exact
+    "tiny": g.CONFIGS["tiny"],
+    # MFMA bf16 kernel, decode, integer twin: bit-exact
+    "decode_int": g.CONFIGS["decode_8k"].replace(B=3, integer=True),
+    # MFMA bf16 kernel, causal prefill with a ragged tail, integer: bit-exact
+    "prefill_int": g.CONFIGS["prefill_16k"].replace(T=300, S=1000, integer=True),
+    # MFMA e4m3 kernel, integer twin (scale byte 127): bit-exact
+    "fp8_int": g.CONFIGS["decode_64k_fp8"].replace(B=2, S=4200, integer=True),
+    # real-valued: within 1e-4 of the row max
+    "decode_real": g.CONFIGS["decode_8k"].replace(B=2, S=3000),
+    "fp8_real": g.CONFIGS["decode_64k_fp8"].replace(B=2, S=5000),
+    # generic kernel on bf16 with odd sizes
+    "generic_bf16": g.Config("generic_bf16", B=2, T=3, S=77, HI=5, DI=24, H=4, Dc=64, Dr=16, K=20,
+                             idx_dtype="bf16", w_dtype="bf16", mla_dtype="bf16", seed=5),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SCORE_CASES))
+def test_indexer_scores(dsa, case):
+    cfg = SCORE_CASES[case]
+    print(f"[indexer_scores] {case}: {cfg}", flush=True)
+    x = _inputs(cfg)
+    got = _gpu_scores(dsa, cfg, x).cpu().numpy().reshape(cfg.B * cfg.T, cfg.S)
+    rb, rt = _rows(cfg)
+    ref = _oracle_scores(cfg, rb, rt)
+    if cfg.integer:
+        assert np.array_equal(got, ref), f"{case}: integer-valued scores must be bit-exact"
+    else:
+        U.assert_scores_close(got, ref, what=case)
+
+
+# ---------------------------------------------------------------------------
+# top-k on identical scores: bit-exact
+# ---------------------------------------------------------------------------
+
+def _special_rows(S, K, rng):
+    rows = [rng.standard_normal(S).astype(np.float32),
+            rng.integers(-3, 4, S).astype(np.float32),              # heavy ties
+            np.zeros(S, np.float32),                                 # all equal
+            np.where(rng.random(S) < 0.5, -0.0, 0.0).astype(np.float32),  # signed zeros
+            np.full(S, -np.inf, np.float32)]                         # nothing selectable
+    r = rng.standard_normal(S).astype(np.float32)
+    r[rng.random(S) < 0.3] = np.nan
+    r[rng.random(S) < 0.3] = -np.inf
+    rows.append(r)
+    r = rng.standard_normal(S).astype(np.float32)
+    r[: S // 2] = -np.inf                                            # fewer than K selectable (for big K)
+    rows.append(r)
+    r = (rng.standard_normal(S) * 1e-30).astype(np.float32)          # subnormal-range values
+    rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("S,K", [(256, 32), (1000, 64), (3000, 2048), (8192, 2048),
+                                 (16384, 2048), (40000, 2048), (131072, 2048), (100, 300)])
+def test_topk_bit_exact(dsa, S, K):
+    print(f"[topk] S={S} K={K}", flush=True)
+    torch = U.torch()
+    rng = np.random.default_rng(S + K)
+    sc = _special_rows(S, K, rng)
+    cfg = g.CONFIGS["decode_8k"].replace(B=sc.shape[0], T=1, S=S, K=K)
+    got = dsa.dsa_topk(U.shape_of(cfg), torch.from_numpy(sc).cuda().view(cfg.B, 1, S))
+    got = got.cpu().numpy().reshape(cfg.B, -1)
+    ref = oracle.topk(cfg, sc)
+    for r in range(cfg.B):
+        assert np.array_equal(got[r], ref[r]), f"row {r} differs"
+
+
+def test_topk_on_gpu_scores(dsa):
+    """Selection from the GPU's own fp32 scores matches the oracle's selection
+    of those same scores exactly (decode 8k shape, real-valued)."""
+    cfg = g.CONFIGS["decode_8k"].replace(B=4)
+    x = _inputs(cfg)
+    sc = _gpu_scores(dsa, cfg, x)
+    got = dsa.dsa_topk(U.shape_of(cfg), sc).cpu().numpy().reshape(cfg.B, -1)
+    ref = oracle.topk(cfg, sc.cpu().numpy().reshape(cfg.B, -1))
+    assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# sparse latent attention on identical indices
+# ---------------------------------------------------------------------------
+
+def _mla_check(dsa, cfg, idx_np, rb, x=None):
+    torch = U.torch()
+    x = x or _inputs(cfg)
+    idx = torch.from_numpy(idx_np.reshape(cfg.B, cfg.T, -1)).cuda()
+    o, lse = dsa.dsa_sparse_mla_fwd(U.shape_of(cfg), x["q"], x["kv"], idx)
+    o = U.dev_to_np(o, cfg.mla_dtype).reshape(cfg.B * cfg.T, cfg.H, cfg.Dc)
+    if cfg.mla_dtype == "bf16":
+        o = g.bf16_bits_to_f32(o)
+    lse = lse.cpu().numpy().reshape(cfg.B * cfg.T, cfg.H)
+    q = g.full(cfg, "q").reshape(cfg.B * cfg.T, cfg.H, cfg.D)
+    kv = g.full(cfg, "kv")
+    ro, rl = oracle.sparse_mla(cfg, rb, q, kv, idx_np.reshape(cfg.B * cfg.T, -1))
+    U.assert_rows_close(o, ro, U.RTOL[cfg.mla_dtype], what=f"{cfg.name} o")
+    fin = np.isfinite(rl)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.all(np.abs(lse[fin] - rl[fin]) <= U.RTOL[cfg.mla_dtype] * np.maximum(1, np.abs(rl[fin])))
+    return o, lse
+
+
+def _random_idx(cfg, rng, frac_invalid=0.0):
+    W = cfg.K_eff
+    rows = []
+    for _ in range(cfg.B * cfg.T):
+        sel = np.sort(rng.choice(cfg.S, size=W, replace=False)).astype(np.int32)
+        if frac_invalid:
+            sel[rng.random(W) < frac_invalid] = -1
+        rows.append(sel)
+    return np.stack(rows)
+
+
+def test_mla_tiny_fp32(dsa):
+    cfg = g.CONFIGS["tiny"]
+    rb, rt = _rows(cfg)
+    idx = oracle.topk(cfg, _oracle_scores(cfg, rb, rt))
+    _mla_check(dsa, cfg, idx, rb)
+
+
+@pytest.mark.parametrize("B", [1, 4, 32])
+def test_mla_mfma_decode(dsa, B):
+    """MFMA kernel, decode split-K (B=1: 16-way ... B=32: 8-way) + combine."""
+    cfg = g.CONFIGS["decode_8k"].replace(B=B)
+    rb, _ = _rows(cfg)
+    _mla_check(dsa, cfg, _random_idx(cfg, np.random.default_rng(B)), rb)
+
+
+def test_mla_mfma_prefill_rows(dsa):
+    """MFMA kernel without splits (many query rows), causal-style short rows."""
+    cfg = g.CONFIGS["prefill_16k"].replace(T=300, S=2500)
+    rb, rt = _rows(cfg)
+    idx = oracle.topk(cfg, _oracle_scores(cfg, rb, rt))
+    _mla_check(dsa, cfg, idx, rb)
+
+
+def test_mla_mfma_edge_indices(dsa):
+    """-1 and out-of-range entries skipped, duplicates counted, empty rows give
+    o = 0 and lse = -inf, a ragged last tile."""
+    cfg = g.CONFIGS["decode_8k"].replace(B=6, S=4096, K=1000)
+    rng = np.random.default_rng(7)
+    idx = _random_idx(cfg, rng, frac_invalid=0.3)
+    idx[1, :] = -1                                     # empty row
+    idx[2, 5:] = -1                                    # five keys
+    idx[3, :500] = idx[3, 0]                           # one key many times
+    idx[4, ::7] = cfg.S + 5                            # out of range
+    idx[5, :] = rng.integers(0, 3, cfg.K_eff)          # three keys, heavy duplicates
+    rb, _ = _rows(cfg)
+    o, lse = _mla_check(dsa, cfg, idx, rb)
+    assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
+
+
+def test_mla_generic_bf16(dsa):
+    cfg = SCORE_CASES["generic_bf16"]
+    rb, _ = _rows(cfg)
+    _mla_check(dsa, cfg, _random_idx(cfg, np.random.default_rng(3), 0.2), rb)
+
+
+# ---------------------------------------------------------------------------
+# the whole path
+# ---------------------------------------------------------------------------
+
+def _forward(dsa, cfg, x):
+    o, lse, idx = dsa.dsa_forward(U.shape_of(cfg), x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"],
+                                  x["q_sf"], x["k_sf"])
+    return o, lse, idx
+
+
+def test_forward_tiny_exact_selection(dsa):
+    cfg = g.CONFIGS["tiny"]
+    x = _inputs(cfg)
+    o, lse, idx = _forward(dsa, cfg, x)
+    rb, rt = _rows(cfg)
+    ref_idx = oracle.topk(cfg, _oracle_scores(cfg, rb, rt))
+    assert np.array_equal(idx.cpu().numpy().reshape(cfg.T, -1), ref_idx)
+    ro, rl = oracle.sparse_mla(cfg, rb, g.full(cfg, "q")[0], g.full(cfg, "kv"), ref_idx)
+    U.assert_rows_close(o.cpu().numpy().reshape(cfg.T, cfg.H, cfg.Dc), ro, U.RTOL["f32"], "tiny o")
+
+
+def test_forward_dense_when_k_covers_causal(dsa):
+    """K >= causal length: the sparse path is plain causal attention."""
+    cfg = g.CONFIGS["tiny"].replace(K=256)
+    x = _inputs(cfg)
+    o, lse, idx = _forward(dsa, cfg, x)
+    rb, rt = _rows(cfg)
+    idx = idx.cpu().numpy().reshape(cfg.T, -1)
+    assert np.array_equal((idx >= 0).sum(1), rt + 1)
+    do, dl = oracle.dense_mla(cfg, rb, rt, g.full(cfg, "q")[0], g.full(cfg, "kv"))
+    U.assert_rows_close(o.cpu().numpy().reshape(cfg.T, cfg.H, cfg.Dc), do, U.RTOL["f32"], "dense")
+    np.testing.assert_allclose(lse.cpu().numpy().reshape(cfg.T, cfg.H), dl, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("case", ["decode_int", "decode_real"])
+def test_forward_decode(dsa, case):
+    cfg = {"decode_int": g.CONFIGS["decode_8k"].replace(B=4, integer=True),
+           "decode_real": g.CONFIGS["decode_8k"].replace(B=4)}[case]
+    x = _inputs(cfg)
+    o, lse, idx = _forward(dsa, cfg, x)
+    rb, rt = _rows(cfg)
+    ref_sc = _oracle_scores(cfg, rb, rt)
+    ref_idx = oracle.topk(cfg, ref_sc)
+    idx = idx.cpu().numpy().reshape(cfg.B, -1)
+    if cfg.integer:
+        assert np.array_equal(idx, ref_idx)
+    else:
+        U.assert_selection_within_gap(idx, ref_idx, ref_sc)
+    ro, rl = oracle.sparse_mla(cfg, rb, g.full(cfg, "q").reshape(cfg.B, cfg.H, cfg.D),
+                               g.full(cfg, "kv"), idx)
+    o = g.bf16_bits_to_f32(U.dev_to_np(o, "bf16")).reshape(cfg.B, cfg.H, cfg.Dc)
+    U.assert_rows_close(o, ro, U.RTOL["bf16"], f"{case} o")
