@@ -123,17 +123,21 @@ mla_generic(int T, int S, int H, int Dc, int Dr, int W, float sm_scale,
 //   B (16 x 32): lane holds column n, reduction elements 8G .. 8G+7
 //   C (32 x 32): register i holds row 8*(i/4) + 4G + (i%4) of column n
 //
-// Key tile in LDS: 32 selected rows of 576 bf16, 1152 B apart (no padding),
-// each row cut in 72 pieces of 16 B; piece c of row r sits at physical piece
-// c ^ (r & 7).  The tile is filled by direct global->LDS loads
-// (global_load_lds_dwordx4: lane l of a wave writes 16 B at the wave's LDS
-// base + 16 l), so the gather needs no registers and runs asynchronously
-// with the MFMAs of the previous tile.
+// Key tile in LDS (38 KiB): latent part of row m (64 pieces of 16 B) at byte
+// 1088 m, piece c stored at c ^ ((m >> 2) & 3); rotary part (8 pieces) in a
+// region of its own at byte 34816, row m at 128 m, piece c' at c' ^ ((m >> 1) & 7).
+// The LDS has 64 banks of 4 bytes (a 16-byte read pass serves 16 lanes, an
+// 8-byte pass 32 lanes).  The 1088-byte row stride shifts consecutive rows by
+// 4 bank quads and the 2-bit XOR spreads groups of 4 rows, so the logits
+// operand reads (16 rows, one piece) and the transposing value reads (4 rows x
+// 4 pieces) both touch every bank once per pass, and every read is one base
+// register plus a compile-time offset.  The tile is filled by direct
+// global->LDS copies (global_load_lds_dwordx4: lane l of a wave writes 16 B at
+// the wave's LDS base + 16 l); wave w copies the latent parts of tile rows
+// 8w .. 8w+7 (one 1 KiB run of global memory each) and their rotary parts.  The gather needs no registers and runs asynchronously with the MFMAs.
 //
 // logits^T (32 keys x 32 heads) = K_tile (A, from LDS) . Q^T (B, registers),
-// reduction over the 576 dims in 36 steps of 16.  MFMA row m reads the tile's
-// row pi(m), pi(8a + 4b + j) = 8a + 2j + b (a permutation inside each group
-// of 8 rows).
+// reduction over the 576 dims in 36 steps of 16.  MFMA row m is tile row m.
 //
 // O (32 heads x 512) += P (A) . V (B), reduction over the 32 keys in two
 // MFMAs (kk = 0, 1).  P comes straight from the logit accumulators: lane
@@ -145,20 +149,25 @@ mla_generic(int T, int S, int H, int Dc, int Dr, int W, float sm_scale,
 // j = 0..3.  So lane 4j + c of a group loads 4 latent dims (base + 4c) of the
 // key in slot (base slot + j), and each lane ends up with 4 consecutive key
 // slots of one latent dim: half of its B operand.
-//
-// With the row permutation and the piece swizzle, both LDS read patterns
-// (8 lanes x 16 B on 8 rows of one column; 4 rows x 32 B for the transposing
-// read) touch each of the 32 banks once per pass.
 // ---------------------------------------------------------------------------
 constexpr int kH = 128, kDc = 512, kDr = 64, kD = kDc + kDr;
 constexpr int kMlaWaves = 4;                 // wave w owns heads 32w .. 32w+31
 constexpr int kMlaThreads = kMlaWaves * 64;
 constexpr int kTileKeys = 32;
 constexpr int kPieces = kD / 8;              // 16-byte pieces per key row (72)
-constexpr int kTileLoads = kTileKeys * kPieces / 64;       // wave-wide 1 KiB loads per tile (36)
-constexpr int kLoadsPerWave = kTileLoads / kMlaWaves;      // 9
-constexpr int kMaxSplitKeys = 2048;          // index entries one workgroup stages in LDS
+constexpr int kTileLoads = kTileKeys * kPieces / 64;       // wave-wide 1 KiB copies per tile (36)
+constexpr int kLoadsPerWave = kTileLoads / kMlaWaves;      // 9: 8 latent rows + 8 rotary parts
+constexpr int kBuffers = 3;                  // LDS tile ring: 2 tiles in flight during compute
+constexpr int kLatStride = 1088;             // bytes per latent row in LDS (1024 + 64 pad)
+constexpr int kRopeBase = kTileKeys * kLatStride;       // byte offset of the rotary region
+constexpr int kTileBytes = kRopeBase + kTileKeys * kDr * 2;  // 38912
+constexpr int kReadAhead = 6;                // logits A-operand reads issued ahead of their MFMA
+constexpr int kVAhead = 4;                   // value B-operand (2 reads each) issued ahead
 constexpr float kRefSlack = 32.0f;           // log2 units: p <= 2^32 against the reference max
+// The query operand (36 steps x 8 bf16 per lane) does not fit in registers next
+// to the 512 fp32 accumulators of O; its last kQLdsSteps steps live in LDS.
+constexpr int kQLdsSteps = 11;
+constexpr int kQRegSteps = kD / 16 - kQLdsSteps;
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -168,7 +177,7 @@ typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[kD];
 
 struct MlaTile {
-  uint16_t k[kTileKeys * kD];
+  uint8_t bytes[kTileBytes];
 };
 
 // LDS byte address of a __shared__ object
@@ -180,7 +189,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 16-byte global -> LDS copy per lane: lane l writes LDS [lds + 16 l] (lds is
 // wave-uniform).  Issued through asm so the compiler does not hold back the
 // current tile's LDS reads behind it; completion is awaited explicitly with
-// s_waitcnt vmcnt(0) before the barrier that publishes the tile.
+// s_waitcnt vmcnt before the barrier that publishes a tile (loads retire in
+// issue order, so vmcnt(N) means all but the last N copies have landed).
 // m0 is declared clobbered; the compiler sets m0 itself before each of its own
 // uses and this kernel has no other, so the reserved-register warning is moot.
 #pragma clang diagnostic push
@@ -193,59 +203,81 @@ __device__ __forceinline__ void lds_dma_16(const void* src, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ int tile_row(int m) {  // pi(m)
-  return (m & ~7) | ((m & 3) << 1) | ((m >> 2) & 1);
+// wait until at most `groups` tiles' copies of this wave are still in flight
+__device__ __forceinline__ void wait_tiles_in_flight(int groups) {
+  static_assert(kLoadsPerWave == 9 && kBuffers == 3, "vmcnt immediates assume 9 copies per tile");
+  if (groups >= 1)
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// byte offset of (row r, logical piece c) in a tile
-__device__ __forceinline__ int tile_off(int r, int c) { return r * (kD * 2) + 16 * (c ^ (r & 7)); }
+__device__ __forceinline__ int lat_swz(int m) { return (m >> 2) & 3; }
+__device__ __forceinline__ int rope_swz(int m) { return (m >> 1) & 7; }
 
 __device__ __forceinline__ f32x16_t mfma32x32x16_bf16(const bf16x8_t& a, const bf16x8_t& b,
                                                       const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ short4_t lds_read_tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_short4_t*)((__attribute__((address_space(3))) char*)(p)));
+typedef __attribute__((address_space(3))) const char lds_char_t;
+
+// Address arithmetic on LDS pointers stays in the 32-bit LDS address space, so
+// constant offsets fold into the instructions' offset fields.
+__device__ __forceinline__ short4_t lds_read_tr16(lds_char_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p));
 }
 
-// grid: (splits, rows).  Split sp covers index entries [sp*kps, (sp+1)*kps).
-// splits == 1: writes o (bf16) and lse directly; otherwise writes fp32 partials
-// part_o [rows, splits, H, Dc] (already divided by the split's own sum) and
-// part_lse [rows, splits, H] (natural log; -inf for an empty split).
+// 1-D grid of rows * nsplit workgroups.  With xcd_map, the splits of one query
+// row share an XCD (workgroups are dealt to the 8 XCDs round-robin), so its
+// 147 KB query block is fetched once into that XCD's L2.
+// nsplit == 1: writes o (bf16) and lse directly; otherwise writes bf16
+// partials part_o [rows, nsplit, H, Dc] (already divided by the split's own
+// sum) and part_lse [rows, nsplit, H] (natural log; -inf for an empty split).
 __global__ void __launch_bounds__(kMlaThreads, 1)
-mla_mfma(int T, int S, int W, int kps, float sm_scale, const uint16_t* __restrict__ q,
-         const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
-         uint16_t* __restrict__ o, float* __restrict__ lse, float* __restrict__ part_o,
-         float* __restrict__ part_lse) {
-  __shared__ __attribute__((aligned(1024))) MlaTile tiles[2];
-  __shared__ int32_t sidx[kMaxSplitKeys];
+mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
+         const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+         const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse,
+         uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(1024))) MlaTile tiles[kBuffers];
+  __shared__ uint32_t vmask[kBuffers];  // per tile buffer: bit r = tile row r holds a valid key
+  // query steps kQRegSteps.. of each wave: [step][wave][G][head n][8 bf16]
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[kQLdsSteps][kMlaWaves][2][32][8];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = lane >> 5, n = lane & 31;
-  const int sp = blockIdx.x, nsplit = gridDim.x;
-  const int64_t row = blockIdx.y;
+  const int L = blockIdx.x;
+  int sp;
+  int64_t row;
+  if (xcd_map) {
+    sp = (L >> 3) % nsplit;
+    row = static_cast<int64_t>(L / (8 * nsplit)) * 8 + (L & 7);
+  } else {
+    sp = L % nsplit;
+    row = L / nsplit;
+  }
   const int b = static_cast<int>(row / T);
   const int j0 = sp * kps;
   const int nj = max(0, min(W, j0 + kps) - j0);
   const int ntiles = (nj + kTileKeys - 1) / kTileKeys;
   const uint16_t* kv_seq = kv + static_cast<int64_t>(b) * S * kD;
 
-  // stage this split's index entries (skipped entries become -1)
-  for (int j = tid; j < ntiles * kTileKeys; j += kMlaThreads) {
-    int s = j < nj ? idx[row * W + j0 + j] : -1;
-    sidx[j] = (s >= 0 && s < S) ? s : -1;
-  }
-
-  // query operand (B of logits^T): head 32*wave + n, dims 16ks + 8G .. +8
-  bf16x8_t qf[kD / 16];
+  // query operand (B of logits^T): head 32*wave + n, dims 16ks + 8G .. +8;
+  // steps < kQRegSteps stay in registers, the rest go to LDS
+  bf16x8_t qf[kQRegSteps];
   {
     const uint16_t* qh = q + (row * kH + 32 * wave + n) * kD;
 #pragma unroll
-    for (int ks = 0; ks < kD / 16; ++ks)
+    for (int ks = 0; ks < kQRegSteps; ++ks)
       qf[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 16 * ks + 8 * G);
+#pragma unroll
+    for (int ks = kQRegSteps; ks < kD / 16; ++ks)
+      *reinterpret_cast<bf16x8_t*>(qlds[ks - kQRegSteps][wave][G][n]) =
+          *reinterpret_cast<const bf16x8_t*>(qh + 16 * ks + 8 * G);
+    // consume the loads here: later vmcnt waits then only see the tile copies
+#pragma unroll
+    for (int ks = 0; ks < kQRegSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
 
   f32x16_t oacc[kDc / 32];
@@ -256,53 +288,87 @@ mla_mfma(int T, int S, int W, int kps, float sm_scale, const uint16_t* __restric
   float m_ref = -__builtin_inff();  // reference max (log2 units) of head 32*wave + n
   float l_run = 0.f;
   const float scale2 = sm_scale * kLog2e;
-  __syncthreads();  // sidx ready
 
-  // gather: wave-wide load k covers tile slots 64k .. 64k+63 (slot = row*72 + physical piece)
-  auto issue_tile = [&](int t, MlaTile& dst) {
+  // Wave w gathers tile rows 8w .. 8w+7.  Their index entries come through
+  // scalar loads one tile ahead (skipped or out-of-range entries become -1);
+  // the wave publishes their validity as byte w of the tile's mask word.
+  const int32_t* idx_row = idx + row * W;
+  const int j_end = j0 + nj;
+  typedef __attribute__((__vector_size__(8 * sizeof(int32_t)))) int32_t i32x8_t;
+  auto tile_rows = [&](int t, int (&sr)[8]) {
+    const int j = j0 + t * kTileKeys + 8 * wave;
+    if (j + 8 <= j_end) {  // one 32-byte scalar load
+      i32x8_t v;
+      __builtin_memcpy(&v, idx_row + j, sizeof v);
 #pragma unroll
-    for (int i = 0; i < kLoadsPerWave; ++i) {
-      const int k = wave + kMlaWaves * i;
-      const int L = 64 * k + lane;
-      const int r = L / kPieces, c = (L % kPieces) ^ (r & 7);
-      const int s = sidx[t * kTileKeys + r];
-      const uint16_t* src = (s >= 0 ? kv_seq + static_cast<int64_t>(s) * kD : g_zero_row) + 8 * c;
-      lds_dma_16(src, lds_addr(dst.k) + 1024 * k);
+      for (int e = 0; e < 8; ++e) sr[e] = (v[e] >= 0 && v[e] < S) ? v[e] : -1;
+    } else {               // the ragged end of the split
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int sv = idx_row[min(j + e, j_end - 1)];
+        if (j + e >= j_end || sv < 0 || sv >= S) sv = -1;
+        sr[e] = sv;
+      }
+    }
+  };
+  auto issue_tile = [&](int t, const int (&sr)[8]) {
+    MlaTile& dst = tiles[t % kBuffers];
+    // an opaque copy of the lane id: the per-copy address math below is redone
+    // at each issue instead of being kept live across the loop in registers
+    int lane = __lane_id();
+    asm volatile("" : "+v"(lane));
+    uint32_t mask8 = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mask8 |= static_cast<uint32_t>(sr[e] >= 0) << e;
+    if (lane == 0) reinterpret_cast<uint8_t*>(&vmask[t % kBuffers])[wave] = static_cast<uint8_t>(mask8);
+    // latent part of row r = 8w + e: its 16-byte slot `lane` holds piece lane ^ F(r)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int r = 8 * wave + e;
+      const uint16_t* src =
+          (sr[e] >= 0 ? kv_seq + static_cast<int64_t>(sr[e]) * kD : g_zero_row) + 8 * (lane ^ lat_swz(r));
+      lds_dma_16(src, lds_addr(dst.bytes) + kLatStride * r);
+    }
+    // rotary parts of rows 8w .. 8w+7: lane l takes row 8w + l/8
+    {
+      const int e = lane >> 3, r = 8 * wave + e;
+      int sv = sr[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) sv = e == k ? sr[k] : sv;
+      const uint16_t* src = (sv >= 0 ? kv_seq + static_cast<int64_t>(sv) * kD : g_zero_row) + kDc +
+                            8 * ((lane & 7) ^ rope_swz(r));
+      lds_dma_16(src, lds_addr(dst.bytes) + kRopeBase + 1024 * wave);
     }
   };
 
-  // LDS byte offsets.  Logits A operand: row pi(n), logical piece 2ks + G;
-  // with ks = 4a + bb, (2ks + G) ^ x = 8a + ((2bb + G) ^ x), x = row & 7.
-  const int ar = tile_row(n);
-  int aoff[4];
+  // LDS byte offsets.  Logits A operand of step ks: row n, piece 2ks + G.
+  // Latent steps: piece 4(ks/2) + (2(ks&1) + G), stored at 4(ks/2) + ((2(ks&1) + G) ^ F(n)).
+  int aoff[2], roff[4];
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) aoff[bb] = ar * (kD * 2) + 16 * ((2 * bb + G) ^ (ar & 7));
-  // Transposing reads: lane (q16, jq, cq) reads MFMA rows 16kk + 8h + 4(q16/2) + jq,
-  // latent dims d = 32nb + y*4 + 4(cq&1)... as piece 4nb + y, y = 2(q16&1) + cq/2,
-  // byte 8(cq&1).  (4nb + y) ^ x = 4(nb ^ (x>>2)) + ((y ^ x) & 3): even nb move by
-  // +64*(x>>2) bytes, odd nb by -64*(x>>2).
+  for (int par = 0; par < 2; ++par) aoff[par] = kLatStride * n + 16 * ((2 * par + G) ^ lat_swz(n));
+#pragma unroll
+  for (int kr = 0; kr < 4; ++kr) roff[kr] = kRopeBase + 128 * n + 16 * ((2 * kr + G) ^ rope_swz(n));
+  // Transposing reads: lane (q16, jq, cq) reads MFMA row m = 16kk + 8h + 4(q16/2) + jq,
+  // latent dims 32nb + 16(q16&1) + 4cq: piece 4nb + y, y = 2(q16&1) + cq/2, byte 8(cq&1);
+  // F(m) = (2h + q16/2) & 3, so the stored piece is 4nb + (y ^ F(m)).
   const int q16 = lane >> 4, jq = (lane & 15) >> 2, cq = lane & 3;
   const int y = 2 * (q16 & 1) + (cq >> 1);
-  int voff[2][2][2];  // [kk][h][nb parity]
+  int voff[2][2];  // [kk][h]
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int r = tile_row(16 * kk + 8 * h + 4 * (q16 >> 1) + jq);
-      const int x = r & 7;
-      const int base = r * (kD * 2) + 16 * ((y ^ x) & 3) + 8 * (cq & 1);
-      voff[kk][h][0] = base + 64 * (x >> 2);
-      voff[kk][h][1] = base - 64 * (x >> 2);
+      const int m = 16 * kk + 8 * h + 4 * (q16 >> 1) + jq;
+      voff[kk][h] = kLatStride * m + 16 * (y ^ lat_swz(m)) + 8 * (cq & 1);
     }
 
   // Online softmax with a fixed reference max per head: the first tile with a
-  // valid key sets it, and p = 2^(x - ref) stays below 2^kRefSlack after
-  // that as long as no later logit exceeds the reference by more than the
-  // slack.  If one does (never for sane data), the whole split is run once
-  // more with the true maximum as reference, so O is only ever zeroed, never
-  // rescaled.  The decision is workgroup-uniform (barriers stay matched).
+  // valid key sets it, and p = 2^(x - ref) stays below 2^kRefSlack as long as
+  // no later logit exceeds the reference by more than the slack.  If one does
+  // (never for sane data), the whole split is run once more with the true
+  // maximum as reference, so O is only ever zeroed, never rescaled.  The
+  // decision is workgroup-uniform (barriers stay matched).
   float m_seen = -__builtin_inff();
-  bool rerun = false;  // workgroup-uniform
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
 #pragma unroll
@@ -312,32 +378,64 @@ mla_mfma(int T, int S, int W, int kps, float sm_scale, const uint16_t* __restric
       l_run = 0.f;
       m_ref = m_seen;
     }
-    if (ntiles > 0) issue_tile(0, tiles[0]);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
     bool overflow = false;
+    int srn[8];  // index entries of the next tile to issue
+    if (ntiles > 0) tile_rows(0, srn);
+    for (int t = 0; t < kBuffers - 1 && t < ntiles; ++t) {
+      issue_tile(t, srn);
+      if (t + 1 < ntiles) tile_rows(t + 1, srn);
+    }
     for (int it = 0; it < ntiles; ++it) {
-      const char* cur = reinterpret_cast<const char*>(tiles[it & 1].k);
-      if (it + 1 < ntiles) issue_tile(it + 1, tiles[(it + 1) & 1]);
+      // tile `it` has landed once at most the copies of the later issued tiles remain
+      wait_tiles_in_flight(min(kBuffers - 2, ntiles - 1 - it));
+      __syncthreads();  // every wave's copies of tile `it` are in; tile it-1 is consumed
+      if (it + kBuffers - 1 < ntiles) {
+        issue_tile(it + kBuffers - 1, srn);
+        if (it + kBuffers < ntiles) tile_rows(it + kBuffers, srn);
+      }
+      lds_char_t* cur = (lds_char_t*)(tiles[it % kBuffers].bytes);
+      // validity of the tile rows; accumulator i sits on row 8(i/4) + 4G + i%4
+      const uint32_t valid = vmask[it % kBuffers] >> (4 * G);
 
       // ---- logits^T: 32 keys x 32 heads ----
       f32x16_t sacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      {
+        // software pipeline: the LDS read of step ks + kReadAhead is issued with
+        // the MFMA of step ks; sched_barrier keeps each pair in place
+        auto aload = [&](int ks) {
+          const int off = ks < kDc / 16 ? aoff[ks & 1] + 64 * (ks >> 1) : roff[ks - kDc / 16];
+          return *(__attribute__((address_space(3))) const bf16x8_t*)(cur + off);
+        };
+        auto qload = [&](int ks) {
+          return *reinterpret_cast<const bf16x8_t*>(qlds[ks - kQRegSteps][wave][G][n]);
+        };
+        bf16x8_t ka[kReadAhead], qb[kReadAhead];
 #pragma unroll
-      for (int ks = 0; ks < kD / 16; ++ks) {
-        const bf16x8_t ka =
-            *reinterpret_cast<const bf16x8_t*>(cur + aoff[ks & 3] + 128 * (ks >> 2));
-        sacc = mfma32x32x16_bf16(ka, qf[ks], sacc);
+        for (int ks = 0; ks < kReadAhead; ++ks) {
+          ka[ks] = aload(ks);
+          if (ks >= kQRegSteps) qb[ks] = qload(ks);
+        }
+#pragma unroll
+        for (int ks = 0; ks < kD / 16; ++ks) {
+          sacc = mfma32x32x16_bf16(ka[ks % kReadAhead],
+                                   ks < kQRegSteps ? qf[ks] : qb[ks % kReadAhead], sacc);
+          const int nx = ks + kReadAhead;
+          if (nx < kD / 16) {
+            ka[ks % kReadAhead] = aload(nx);
+            if (nx >= kQRegSteps) qb[ks % kReadAhead] = qload(nx);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 
-      // ---- softmax weights (lane: head n, MFMA rows 8(i/4) + 4G + i%4) ----
+      // ---- softmax weights (lane: head n, accumulator i = MFMA row 8(i/4) + 4G + i%4) ----
       float x[16];
       float tmax = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = 8 * (i >> 2) + 4 * G + (i & 3);
-        x[i] = sidx[it * kTileKeys + tile_row(m)] >= 0 ? sacc[i] * scale2 : -__builtin_inff();
+        x[i] = ((valid >> (8 * (i >> 2) + (i & 3))) & 1) ? sacc[i] * scale2 : -__builtin_inff();
         tmax = fmaxf(tmax, x[i]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
@@ -364,24 +462,43 @@ mla_mfma(int T, int S, int W, int kps, float sm_scale, const uint16_t* __restric
       l_run += psum;
 
       // ---- O += P . V ----
+      {
+        // software pipeline over the 32 (kk, nb) steps: the two transposing reads
+        // of step st + kVAhead are issued with the MFMA of step st
+        constexpr int kSteps = 2 * (kDc / 32);
+        // ds_read_b64_tr_b16 takes no folded offset: an opaque per-tile copy of
+        // the bases keeps each read's address add next to the read instead of
+        // 64 precomputed addresses living across the loop
+        int vbase[2][2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int nb = 0; nb < kDc / 32; ++nb) {
-          const short4_t lo = lds_read_tr16(cur + voff[kk][0][nb & 1] + 64 * nb);
-          const short4_t hi = lds_read_tr16(cur + voff[kk][1][nb & 1] + 64 * nb);
-          const bf16x8_t vb = __builtin_bit_cast(
+          for (int h = 0; h < 2; ++h) {
+            vbase[kk][h] = voff[kk][h];
+            asm volatile("" : "+v"(vbase[kk][h]));
+          }
+        bf16x8_t vb[kVAhead];
+        auto vload = [&](int st) {
+          const int kk = st / (kDc / 32), nb = st % (kDc / 32);
+          const short4_t lo = lds_read_tr16(cur + vbase[kk][0] + 64 * nb);
+          const short4_t hi = lds_read_tr16(cur + vbase[kk][1] + 64 * nb);
+          return __builtin_bit_cast(
               bf16x8_t, short8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-          oacc[nb] = mfma32x32x16_bf16(pa[kk], vb, oacc[nb]);
+        };
+#pragma unroll
+        for (int st = 0; st < kVAhead; ++st) vb[st] = vload(st);
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          const int kk = st / (kDc / 32), nb = st % (kDc / 32);
+          oacc[nb] = mfma32x32x16_bf16(pa[kk], vb[st % kVAhead], oacc[nb]);
+          if (st + kVAhead < kSteps) vb[st % kVAhead] = vload(st + kVAhead);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (__syncthreads_or(pass == 0 && overflow)) {
-        rerun = true;
-        break;
-      }
     }
-    if (!rerun || pass == 1) break;
+    // every copy has landed (the ring is reused by a second pass)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!__syncthreads_or(pass == 0 && overflow)) break;
   }
 
   // ---- epilogue: oacc[nb][i] = O[head 32*wave + 8(i/4) + 4G + i%4][32nb + n] ----
@@ -395,58 +512,56 @@ mla_mfma(int T, int S, int W, int kps, float sm_scale, const uint16_t* __restric
     lse_h[i] = l > 0.f ? (m + __log2f(l)) * kLn2 : -__builtin_inff();
   }
   const int hbase = 32 * wave + 4 * G;
-  if (nsplit == 1) {
+  uint16_t* dst = nsplit == 1 ? o + (row * kH) * kDc : part_o + ((row * nsplit + sp) * kH) * kDc;
+  float* dst_lse = nsplit == 1 ? lse : part_lse + (row * nsplit + sp - row) * kH;
 #pragma unroll
-    for (int nb = 0; nb < kDc / 32; ++nb)
+  for (int nb = 0; nb < kDc / 32; ++nb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = hbase + 8 * (i >> 2) + (i & 3);
-        o[(row * kH + h) * kDc + 32 * nb + n] = f32_to_bf16(oacc[nb][i] * inv_l[i]);
-      }
-    if (lse != nullptr && n == 0)
+    for (int i = 0; i < 16; ++i) {
+      const int h = hbase + 8 * (i >> 2) + (i & 3);
+      dst[h * kDc + 32 * nb + n] = f32_to_bf16(oacc[nb][i] * inv_l[i]);
+    }
+  if (dst_lse != nullptr && n == 0)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) lse[row * kH + hbase + 8 * (i >> 2) + (i & 3)] = lse_h[i];
-  } else {
-    float* po = part_o + ((row * nsplit + sp) * kH) * kDc;
-#pragma unroll
-    for (int nb = 0; nb < kDc / 32; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int h = hbase + 8 * (i >> 2) + (i & 3);
-        po[h * kDc + 32 * nb + n] = oacc[nb][i] * inv_l[i];
-      }
-    if (n == 0)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        part_lse[(row * nsplit + sp) * kH + hbase + 8 * (i >> 2) + (i & 3)] = lse_h[i];
-  }
+    for (int i = 0; i < 16; ++i) dst_lse[row * kH + hbase + 8 * (i >> 2) + (i & 3)] = lse_h[i];
 }
 
-// grid: (H, rows), 128 threads; thread handles Dc / 128 latent dims
+// Merge of the split partials: thread = 8 consecutive latent dims of one head.
+// lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.  Fixed split
+// order, no atomics: deterministic.
 template <int DT>
-__global__ void __launch_bounds__(128)
-mla_combine(int H, int Dc, int nsplit, const float* __restrict__ part_o,
+__global__ void __launch_bounds__(256)
+mla_combine(int H, int Dc, int nsplit, int64_t total_vec, const uint16_t* __restrict__ part_o,
             const float* __restrict__ part_lse, void* __restrict__ o, float* __restrict__ lse) {
-  const int h = blockIdx.x;
-  const int64_t row = blockIdx.y;
+  const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // 8-dim vector id
+  if (v >= total_vec) return;
+  const int per_row = H * Dc / 8;
+  const int64_t row = v / per_row;
+  const int rem = static_cast<int>(v % per_row);
+  const int h = rem / (Dc / 8), d0 = (rem % (Dc / 8)) * 8;
   float m = -__builtin_inff();
   for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, part_lse[(row * nsplit + sp) * H + h]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float ls = part_lse[(row * nsplit + sp) * H + h];
-    wsum += ls == -__builtin_inff() ? 0.f : __expf(ls - m);
-  }
-  const float lse_tot = wsum > 0.f ? m + __logf(wsum) : -__builtin_inff();
-  for (int d = threadIdx.x; d < Dc; d += blockDim.x) {
-    float acc = 0.f;
+  if (m != -__builtin_inff()) {
     for (int sp = 0; sp < nsplit; ++sp) {
       const float ls = part_lse[(row * nsplit + sp) * H + h];
       if (ls == -__builtin_inff()) continue;
-      acc = fmaf(__expf(ls - lse_tot), part_o[((row * nsplit + sp) * H + h) * Dc + d], acc);
+      const float wgt = __expf(ls - m);
+      wsum += wgt;
+      const u32x4_t pv = *reinterpret_cast<const u32x4_t*>(
+          part_o + ((row * nsplit + sp) * H + h) * Dc + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(wgt, __uint_as_float(pv[e] << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(wgt, __uint_as_float(pv[e] & 0xffff0000u), acc[2 * e + 1]);
+      }
     }
-    store_mla<DT>(o, (row * H + h) * Dc + d, acc);
   }
-  if (lse != nullptr && threadIdx.x == 0) lse[row * H + h] = lse_tot;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) store_mla<DT>(o, (row * H + h) * Dc + d0 + e, acc[e] * inv);
+  if (lse != nullptr && d0 == 0) lse[row * H + h] = wsum > 0.f ? m + __logf(wsum) : -__builtin_inff();
 }
 
 struct MlaPlan {
@@ -463,10 +578,9 @@ MlaPlan plan(const dsa_shape_t& s) {
   const int64_t rows = static_cast<int64_t>(s.B) * s.T;
   const int cus = device_info().cu_count;
   // one workgroup per CU: split until every CU has a workgroup, but keep at
-  // least 4 tiles per split and at most kMaxSplitKeys entries per workgroup
+  // least 4 tiles per split
   int splits = 1;
   while (rows * splits < cus && W / (splits * 2) >= 4 * kTileKeys) splits *= 2;
-  while ((W + splits - 1) / splits > kMaxSplitKeys) splits *= 2;
   int kps = (W + splits - 1) / splits;
   kps = (kps + kTileKeys - 1) / kTileKeys * kTileKeys;
   splits = (W + kps - 1) / kps;
@@ -481,7 +595,8 @@ size_t mla_workspace_bytes(const dsa_shape_t& s) {
   const MlaPlan p = plan(s);
   if (!p.mfma || p.splits == 1) return 0;
   const size_t rows = static_cast<size_t>(s.B) * s.T;
-  return rows * p.splits * s.H * (static_cast<size_t>(s.Dc) + 1) * sizeof(float);
+  const size_t po = rows * p.splits * s.H * static_cast<size_t>(s.Dc) * sizeof(uint16_t);
+  return (po + 255) / 256 * 256 + rows * p.splits * s.H * sizeof(float);
 }
 
 dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* kv,
@@ -494,25 +609,26 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
   const int W = k_eff(s);
   const MlaPlan p = plan(s);
   if (p.mfma) {
-    if (p.splits == 1) {
-      mla_mfma<<<dim3(1, rows), kMlaThreads, 0, stream>>>(
-          s.T, s.S, W, p.kps, s.sm_scale, static_cast<const uint16_t*>(q),
-          static_cast<const uint16_t*>(kv), idx, static_cast<uint16_t*>(o), lse, nullptr, nullptr);
-      return check_launch("mla_mfma");
+    uint16_t* part_o = nullptr;
+    float* part_lse = nullptr;
+    if (p.splits > 1) {
+      const size_t need = mla_workspace_bytes(s);
+      if (ws == nullptr || ws_bytes < need)
+        return fail(DSA_ERR_WORKSPACE, "sparse_mla: workspace of %zu bytes needed, %zu given",
+                    need, ws_bytes);
+      part_o = static_cast<uint16_t*>(ws);
+      const size_t po = static_cast<size_t>(rows) * p.splits * s.H * s.Dc * sizeof(uint16_t);
+      part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + (po + 255) / 256 * 256);
     }
-    const size_t need = mla_workspace_bytes(s);
-    if (ws == nullptr || ws_bytes < need)
-      return fail(DSA_ERR_WORKSPACE, "sparse_mla: workspace of %zu bytes needed, %zu given", need,
-                  ws_bytes);
-    float* part_o = static_cast<float*>(ws);
-    float* part_lse = part_o + static_cast<size_t>(rows) * p.splits * s.H * s.Dc;
-    mla_mfma<<<dim3(p.splits, rows), kMlaThreads, 0, stream>>>(
-        s.T, s.S, W, p.kps, s.sm_scale, static_cast<const uint16_t*>(q),
-        static_cast<const uint16_t*>(kv), idx, nullptr, nullptr, part_o, part_lse);
+    const int xcd_map = (p.splits > 1 && rows % 8 == 0) ? 1 : 0;
+    mla_mfma<<<dim3(static_cast<unsigned>(rows * p.splits)), kMlaThreads, 0, stream>>>(
+        s.T, s.S, W, p.kps, p.splits, xcd_map, s.sm_scale, static_cast<const uint16_t*>(q),
+        static_cast<const uint16_t*>(kv), idx, static_cast<uint16_t*>(o), lse, part_o, part_lse);
     dsa_status_t st = check_launch("mla_mfma");
-    if (st != DSA_OK) return st;
-    mla_combine<DSA_BF16><<<dim3(s.H, rows), 128, 0, stream>>>(s.H, s.Dc, p.splits, part_o,
-                                                               part_lse, o, lse);
+    if (st != DSA_OK || p.splits == 1) return st;
+    const int64_t total_vec = rows * s.H * s.Dc / 8;
+    mla_combine<DSA_BF16><<<dim3(static_cast<unsigned>((total_vec + 255) / 256)), 256, 0, stream>>>(
+        s.H, s.Dc, p.splits, total_vec, part_o, part_lse, o, lse);
     return check_launch("mla_combine");
   }
   const size_t lds = (static_cast<size_t>(s.Dc) + s.Dr + W) * sizeof(float);

@@ -60,7 +60,8 @@ def test_workspace_sizes(dsa):
     mla = dsa.workspace_bytes(s, dsa.ENTRY_SPARSE_MLA)
     fwd = dsa.workspace_bytes(s, dsa.ENTRY_FORWARD)
     assert topk == 0                               # one workgroup per 8192-key row
-    assert mla % (32 * 128 * 513 * 4) == 0 and mla > 0   # split partials (o and lse)
+    splits = 8                                      # 32 rows x 8 splits fill 256 CUs
+    assert mla == 32 * splits * 128 * 512 * 2 + 32 * splits * 128 * 4  # bf16 o and fp32 lse partials
     assert fwd >= 32 * 8192 * 4 + 32 * 2048 * 4 + mla
     long = _v32(dsa, B=8, S=131072)
     assert dsa.workspace_bytes(long, dsa.ENTRY_TOPK) == 8 * 4 * 2048 * 8  # 4 chunks of candidates
