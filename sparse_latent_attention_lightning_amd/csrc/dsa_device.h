@@ -16,12 +16,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN)
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN): gfx950 converts
+// in hardware (v_cvt_pk_bf16_f32), branch-free
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+// two fp32 -> packed bf16 pair (low half = a), round to nearest even
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
 // OCP E4M3FN byte -> fp32 (exact); used by the generic kernels only.

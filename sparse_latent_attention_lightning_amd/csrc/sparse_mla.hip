@@ -13,14 +13,14 @@
 // Kernels:
 //  * mla_mfma (H = 128, Dc = 512, Dr = 64, bf16): one workgroup of 8 waves
 //    takes one query row and one split of its index list.  All 128 heads share
-//    each gathered key tile: 32 selected rows are loaded with coalesced
-//    16-byte loads and written to LDS twice, row-major for the logits and
-//    transposed (latent part) for the value product.  Wave w owns heads
-//    16w..16w+15: logits^T = K_tile . Q^T on MFMA (keys on M, heads on N), an
-//    online softmax in fp32 with exp2, and O += P . V on MFMA (heads on M,
-//    latent dims on N) with P taken straight from the logit accumulators.
-//    LDS is double-buffered: the next tile's rows load into registers during
-//    the current tile's MFMAs.
+//    each gathered key tile: 32 selected rows are copied straight from global
+//    memory into LDS (row-major, swizzled) and read twice, directly for the
+//    logits and through transposing LDS reads for the value product.  Wave w
+//    owns heads 16w..16w+15: logits^T = K_tile . Q^T on MFMA (keys on M,
+//    heads on N), an online softmax in fp32 with exp2, and O^T += V^T . P^T on
+//    MFMA (latent dims on M, heads on N) with P^T taken straight from the
+//    logit accumulators.  A ring of 3 LDS tiles keeps the next tile's copies
+//    in flight during the current tile's MFMAs.
 //  * mla_combine: merges split partials (o_s, lse_s) with weights
 //    exp(lse_s - lse), deterministically (fixed split order, no atomics).
 //  * mla_generic: any shape, fp32 VALU loops, two passes over the index row.
@@ -118,60 +118,71 @@ mla_generic(int T, int S, int H, int Dc, int Dr, int W, float sm_scale,
 // ---------------------------------------------------------------------------
 // MFMA kernel, H = 128, Dc = 512, Dr = 64, bf16
 //
-// MFMA 32x32x16 bf16 operand layouts (lane l, G = l / 32, n = l % 32):
-//   A (32 x 16): lane holds row n, reduction elements 8G .. 8G+7
-//   B (16 x 32): lane holds column n, reduction elements 8G .. 8G+7
-//   C (32 x 32): register i holds row 8*(i/4) + 4G + (i%4) of column n
+// One workgroup of 8 waves (two per SIMD, so one wave's softmax and memory
+// waits overlap the other's MFMAs) takes one query row and one split of its
+// index list; wave w owns heads 16w .. 16w+15.  All 128 heads share each
+// gathered tile of 32 selected key rows.
 //
-// Key tile in LDS (38 KiB): latent part of row m (64 pieces of 16 B) at byte
-// 1088 m, piece c stored at c ^ ((m >> 2) & 3); rotary part (8 pieces) in a
-// region of its own at byte 34816, row m at 128 m, piece c' at c' ^ ((m >> 1) & 7).
-// The LDS has 64 banks of 4 bytes (a 16-byte read pass serves 16 lanes, an
-// 8-byte pass 32 lanes).  The 1088-byte row stride shifts consecutive rows by
-// 4 bank quads and the 2-bit XOR spreads groups of 4 rows, so the logits
-// operand reads (16 rows, one piece) and the transposing value reads (4 rows x
-// 4 pieces) both touch every bank once per pass, and every read is one base
-// register plus a compile-time offset.  The tile is filled by direct
-// global->LDS copies (global_load_lds_dwordx4: lane l of a wave writes 16 B at
-// the wave's LDS base + 16 l); wave w copies the latent parts of tile rows
-// 8w .. 8w+7 (one 1 KiB run of global memory each) and their rotary parts.  The gather needs no registers and runs asynchronously with the MFMAs.
+// MFMA 16x16x32 bf16 operand layouts (lane l, g = l / 16, n = l % 16):
+//   A (16 x 32): lane holds row n, reduction elements 8g .. 8g+7
+//   B (32 x 16): lane holds column n, reduction elements 8g .. 8g+7
+//   C (16 x 16): register i holds row 4g + i of column n
 //
-// logits^T (32 keys x 32 heads) = K_tile (A, from LDS) . Q^T (B, registers),
-// reduction over the 576 dims in 36 steps of 16.  MFMA row m is tile row m.
+// logits^T (2 blocks of 16 keys x 16 heads) = K_tile (A, from LDS) . Q^T (B),
+// reduced over the 576 dims in 18 steps of 32; the two key blocks are two
+// independent accumulation chains.  Lane (g, n) ends with head n and keys
+// 4g + i and 16 + 4g + i.
 //
-// O (32 heads x 512) += P (A) . V (B), reduction over the 32 keys in two
-// MFMAs (kk = 0, 1).  P comes straight from the logit accumulators: lane
-// (G, n) holds head n and MFMA rows 8*(i/4) + 4G + i%4; its A-operand slot
-// 8G + e of MFMA kk is accumulator i = 8kk + e, i.e. MFMA row
-// 16kk + 8(e/4) + 4G + e%4.  V is read from the same row-major tile with the
-// transposing LDS load ds_read_b64_tr_b16: within a 16-lane group, lane i
-// receives element (i % 4) of the 8-byte chunk loaded by lane 4j + i/4, for
-// j = 0..3.  So lane 4j + c of a group loads 4 latent dims (base + 4c) of the
-// key in slot (base slot + j), and each lane ends up with 4 consecutive key
-// slots of one latent dim: half of its B operand.
+// O^T (512 dims x 16 heads) += V^T (A) . P^T (B), reduced over the 32 keys in
+// one MFMA per 16 dims.  P^T comes straight from the logit accumulators: its
+// B-operand slot 8g + e holds key 4g + e (e < 4) or 16 + 4g + e - 4 (e >= 4).
+// V^T is read from the same row-major key tile with the transposing LDS load
+// ds_read_b64_tr_b16: within a 16-lane group, lane i receives element (i % 4)
+// of the 8-byte chunk loaded by lane 4j + i/4, for j = 0..3.  So lane 4j + c
+// of group g loads dims 16db + 4c .. +3 of tile row 4g + j (+16 for the
+// second half of its slots), and lane i ends up with 4 key slots of dim
+// 16db + i: half of its A operand.
+//
+// Key tile in LDS (38 KiB): latent part of row r (64 pieces of 16 B) at byte
+// 1088 r, piece c stored at c ^ f(r), f(r) = bit-reversed (r >> 2) & 3;
+// rotary part (8 pieces) in a region of its own at byte 34816, row r at 128 r,
+// piece c' at c' ^ ((r >> 1) & 7).  The LDS has 64 banks of 4 bytes (a 16-byte
+// read pass serves 16 lanes, an 8-byte pass 32 lanes); with this placement
+// the logits reads (16 rows, one piece), the transposing reads (8 rows x 2
+// pieces) and the epilogue staging all touch every bank once per pass, and
+// every read is one base register plus a compile-time offset.
+//
+// The tile is filled by direct global->LDS copies (global_load_lds_dwordx4:
+// lane l of a wave writes 16 B at the wave's LDS base + 16 l): wave w copies
+// the latent parts of rows 4w .. 4w+3 (one 1 KiB run of global memory each),
+// even waves also the rotary parts of rows 4w .. 4w+7.  A ring of 3 tiles
+// keeps the next tile's copies in flight during the current tile's MFMAs.
 // ---------------------------------------------------------------------------
 constexpr int kH = 128, kDc = 512, kDr = 64, kD = kDc + kDr;
-constexpr int kMlaWaves = 4;                 // wave w owns heads 32w .. 32w+31
+constexpr int kMlaWaves = 8;                 // wave w owns heads 16w .. 16w+15
 constexpr int kMlaThreads = kMlaWaves * 64;
 constexpr int kTileKeys = 32;
-constexpr int kPieces = kD / 8;              // 16-byte pieces per key row (72)
-constexpr int kTileLoads = kTileKeys * kPieces / 64;       // wave-wide 1 KiB copies per tile (36)
-constexpr int kLoadsPerWave = kTileLoads / kMlaWaves;      // 9: 8 latent rows + 8 rotary parts
-constexpr int kBuffers = 3;                  // LDS tile ring: 2 tiles in flight during compute
+constexpr int kBuffers = 3;                  // LDS tile ring: 1 tile in flight during compute
 constexpr int kLatStride = 1088;             // bytes per latent row in LDS (1024 + 64 pad)
-constexpr int kRopeBase = kTileKeys * kLatStride;       // byte offset of the rotary region
+constexpr int kRopeBase = kTileKeys * kLatStride;            // byte offset of the rotary region
 constexpr int kTileBytes = kRopeBase + kTileKeys * kDr * 2;  // 38912
-constexpr int kReadAhead = 6;                // logits A-operand reads issued ahead of their MFMA
-constexpr int kVAhead = 4;                   // value B-operand (2 reads each) issued ahead
+constexpr int kKSteps = kD / 32;             // 18 logits reduction steps
+constexpr int kLatSteps = kDc / 32;          // 16 of them over the latent part
+// The query operand (18 steps x 8 bf16 per lane) does not all fit in
+// registers next to the 128 fp32 accumulators of O; its last steps live in LDS.
+constexpr int kQLdsSteps = 5;
+constexpr int kQRegSteps = kKSteps - kQLdsSteps;
+constexpr int kReadAhead = 3;                // logits A-operand reads issued ahead of their MFMA
+constexpr int kVAhead = 2;                   // value A-operand (2 reads each) issued ahead
 constexpr float kRefSlack = 32.0f;           // log2 units: p <= 2^32 against the reference max
-// The query operand (36 steps x 8 bf16 per lane) does not fit in registers next
-// to the 512 fp32 accumulators of O; its last kQLdsSteps steps live in LDS.
-constexpr int kQLdsSteps = 11;
-constexpr int kQRegSteps = kD / 16 - kQLdsSteps;
+constexpr int kStageStride = 528;            // epilogue staging row: 256 bf16 + 16 B pad
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) const char lds_char_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(int32_t)))) int32_t i32x8_t;
 
 // a zero key row: skipped index entries load it, so their LDS rows are zero
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[kD];
@@ -203,24 +214,11 @@ __device__ __forceinline__ void lds_dma_16(const void* src, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-// wait until at most `groups` tiles' copies of this wave are still in flight
-__device__ __forceinline__ void wait_tiles_in_flight(int groups) {
-  static_assert(kLoadsPerWave == 9 && kBuffers == 3, "vmcnt immediates assume 9 copies per tile");
-  if (groups >= 1)
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+__device__ __forceinline__ int lat_swz(int r) {  // f(r): bit-reversed (r >> 2) & 3
+  const int k = (r >> 2) & 3;
+  return ((k & 1) << 1) | (k >> 1);
 }
-
-__device__ __forceinline__ int lat_swz(int m) { return (m >> 2) & 3; }
-__device__ __forceinline__ int rope_swz(int m) { return (m >> 1) & 7; }
-
-__device__ __forceinline__ f32x16_t mfma32x32x16_bf16(const bf16x8_t& a, const bf16x8_t& b,
-                                                      const f32x16_t& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-typedef __attribute__((address_space(3))) const char lds_char_t;
+__device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 
 // Address arithmetic on LDS pointers stays in the 32-bit LDS address space, so
 // constant offsets fold into the instructions' offset fields.
@@ -240,13 +238,16 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
          const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse,
          uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(1024))) MlaTile tiles[kBuffers];
-  __shared__ uint32_t vmask[kBuffers];  // per tile buffer: bit r = tile row r holds a valid key
-  // query steps kQRegSteps.. of each wave: [step][wave][G][head n][8 bf16]
-  __shared__ __attribute__((aligned(16))) uint16_t qlds[kQLdsSteps][kMlaWaves][2][32][8];
+  // query steps kQRegSteps.. : [step][wave][g][head n][8 bf16]
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[kQLdsSteps][kMlaWaves][4][16][8];
+  // validity of each tile's rows (bit r: tile row r holds a valid key); written
+  // one tile ahead of its copies, so it needs one more slot than the tile ring
+  __shared__ uint32_t vmask[kBuffers + 1];
+  __shared__ __attribute__((aligned(16))) int32_t ring_idx[kBuffers][kTileKeys];  // key row of each tile row (-1: none)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = lane >> 5, n = lane & 31;
+  const int g = lane >> 4, n = lane & 15;
   const int L = blockIdx.x;
   int sp;
   int64_t row;
@@ -263,40 +264,43 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   const int ntiles = (nj + kTileKeys - 1) / kTileKeys;
   const uint16_t* kv_seq = kv + static_cast<int64_t>(b) * S * kD;
 
-  // query operand (B of logits^T): head 32*wave + n, dims 16ks + 8G .. +8;
+  // query operand (B of logits^T): head 16*wave + n, dims 32ks + 8g .. +8;
   // steps < kQRegSteps stay in registers, the rest go to LDS
   bf16x8_t qf[kQRegSteps];
   {
-    const uint16_t* qh = q + (row * kH + 32 * wave + n) * kD;
+    const uint16_t* qh = q + (row * kH + 16 * wave + n) * kD;
 #pragma unroll
     for (int ks = 0; ks < kQRegSteps; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 16 * ks + 8 * G);
+      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * g);
 #pragma unroll
-    for (int ks = kQRegSteps; ks < kD / 16; ++ks)
-      *reinterpret_cast<bf16x8_t*>(qlds[ks - kQRegSteps][wave][G][n]) =
-          *reinterpret_cast<const bf16x8_t*>(qh + 16 * ks + 8 * G);
+    for (int ks = kQRegSteps; ks < kKSteps; ++ks)
+      *reinterpret_cast<bf16x8_t*>(qlds[ks - kQRegSteps][wave][g][n]) =
+          *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * g);
     // consume the loads here: later vmcnt waits then only see the tile copies
 #pragma unroll
     for (int ks = 0; ks < kQRegSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
   }
 
-  f32x16_t oacc[kDc / 32];
+  f32x4_t oacc[kDc / 16];  // O^T: oacc[db][i] = O[head 16*wave + n][16db + 4g + i]
 #pragma unroll
-  for (int nb = 0; nb < kDc / 32; ++nb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[nb][i] = 0.f;
-  float m_ref = -__builtin_inff();  // reference max (log2 units) of head 32*wave + n
+  for (int db = 0; db < kDc / 16; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -__builtin_inff();  // reference max (log2 units) of head 16*wave + n
   float l_run = 0.f;
   const float scale2 = sm_scale * kLog2e;
 
-  // Wave w gathers tile rows 8w .. 8w+7.  Their index entries come through
-  // scalar loads one tile ahead (skipped or out-of-range entries become -1);
-  // the wave publishes their validity as byte w of the tile's mask word.
+  // Wave w copies tile rows 4w .. 4w+3 (and, if even, the rotary parts of rows
+  // 4w .. 4w+7).  The index entries of the 8-row block w/2 come through one
+  // scalar load a tile ahead (skipped or out-of-range entries become -1); both
+  // waves of the block write them to the tile's index slots in LDS (the same
+  // values, each wave then reads back only what it wrote itself), and even
+  // waves publish the block's validity as byte w/2 of the tile's mask word.
   const int32_t* idx_row = idx + row * W;
   const int j_end = j0 + nj;
-  typedef __attribute__((__vector_size__(8 * sizeof(int32_t)))) int32_t i32x8_t;
-  auto tile_rows = [&](int t, int (&sr)[8]) {
-    const int j = j0 + t * kTileKeys + 8 * wave;
+  const int blk = wave >> 1;
+  const bool even = (wave & 1) == 0;
+  auto tile_rows = [&](int t) {
+    const int j = j0 + t * kTileKeys + 8 * blk;
+    int sr[8];
     if (j + 8 <= j_end) {  // one 32-byte scalar load
       i32x8_t v;
       __builtin_memcpy(&v, idx_row + j, sizeof v);
@@ -310,57 +314,74 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
         sr[e] = sv;
       }
     }
-  };
-  auto issue_tile = [&](int t, const int (&sr)[8]) {
-    MlaTile& dst = tiles[t % kBuffers];
-    // an opaque copy of the lane id: the per-copy address math below is redone
-    // at each issue instead of being kept live across the loop in registers
-    int lane = __lane_id();
-    asm volatile("" : "+v"(lane));
     uint32_t mask8 = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) mask8 |= static_cast<uint32_t>(sr[e] >= 0) << e;
-    if (lane == 0) reinterpret_cast<uint8_t*>(&vmask[t % kBuffers])[wave] = static_cast<uint8_t>(mask8);
-    // latent part of row r = 8w + e: its 16-byte slot `lane` holds piece lane ^ F(r)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int r = 8 * wave + e;
-      const uint16_t* src =
-          (sr[e] >= 0 ? kv_seq + static_cast<int64_t>(sr[e]) * kD : g_zero_row) + 8 * (lane ^ lat_swz(r));
-      lds_dma_16(src, lds_addr(dst.bytes) + kLatStride * r);
-    }
-    // rotary parts of rows 8w .. 8w+7: lane l takes row 8w + l/8
-    {
-      const int e = lane >> 3, r = 8 * wave + e;
-      int sv = sr[0];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) sv = e == k ? sr[k] : sv;
-      const uint16_t* src = (sv >= 0 ? kv_seq + static_cast<int64_t>(sv) * kD : g_zero_row) + kDc +
-                            8 * ((lane & 7) ^ rope_swz(r));
-      lds_dma_16(src, lds_addr(dst.bytes) + kRopeBase + 1024 * wave);
+    if (lane == 0) {
+      int32_t* slot = &ring_idx[t % kBuffers][8 * blk];
+      *reinterpret_cast<int4*>(slot) = make_int4(sr[0], sr[1], sr[2], sr[3]);
+      *reinterpret_cast<int4*>(slot + 4) = make_int4(sr[4], sr[5], sr[6], sr[7]);
+      if (even) reinterpret_cast<uint8_t*>(&vmask[t % (kBuffers + 1)])[blk] = static_cast<uint8_t>(mask8);
     }
   };
-
-  // LDS byte offsets.  Logits A operand of step ks: row n, piece 2ks + G.
-  // Latent steps: piece 4(ks/2) + (2(ks&1) + G), stored at 4(ks/2) + ((2(ks&1) + G) ^ F(n)).
-  int aoff[2], roff[4];
+  auto issue_tile = [&](int t) {
+    MlaTile& dst = tiles[t % kBuffers];
+    // an opaque copy of the lane id: the per-copy address math below is redone
+    // at each issue instead of being kept live across the loop in registers
+    int ln = __lane_id();
+    asm volatile("" : "+v"(ln));
+    const int4 s4 = *reinterpret_cast<const int4*>(&ring_idx[t % kBuffers][4 * wave]);
+    const int sl[4] = {s4.x, s4.y, s4.z, s4.w};
+    // latent part of row r: its 16-byte slot `ln` holds piece ln ^ f(r)
 #pragma unroll
-  for (int par = 0; par < 2; ++par) aoff[par] = kLatStride * n + 16 * ((2 * par + G) ^ lat_swz(n));
-#pragma unroll
-  for (int kr = 0; kr < 4; ++kr) roff[kr] = kRopeBase + 128 * n + 16 * ((2 * kr + G) ^ rope_swz(n));
-  // Transposing reads: lane (q16, jq, cq) reads MFMA row m = 16kk + 8h + 4(q16/2) + jq,
-  // latent dims 32nb + 16(q16&1) + 4cq: piece 4nb + y, y = 2(q16&1) + cq/2, byte 8(cq&1);
-  // F(m) = (2h + q16/2) & 3, so the stored piece is 4nb + (y ^ F(m)).
-  const int q16 = lane >> 4, jq = (lane & 15) >> 2, cq = lane & 3;
-  const int y = 2 * (q16 & 1) + (cq >> 1);
-  int voff[2][2];  // [kk][h]
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int m = 16 * kk + 8 * h + 4 * (q16 >> 1) + jq;
-      voff[kk][h] = kLatStride * m + 16 * (y ^ lat_swz(m)) + 8 * (cq & 1);
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * wave + e;
+      const uint16_t* src =
+          (sl[e] >= 0 ? kv_seq + static_cast<int64_t>(sl[e]) * kD : g_zero_row) + 8 * (ln ^ lat_swz(r));
+      lds_dma_16(src, lds_addr(dst.bytes) + kLatStride * r);
     }
+    if (even) {  // rotary parts of rows 8*blk .. +7: lane l takes row 8*blk + l/8
+      const int r = 8 * blk + (ln >> 3);
+      const int sv = ring_idx[t % kBuffers][r];
+      const uint16_t* src = (sv >= 0 ? kv_seq + static_cast<int64_t>(sv) * kD : g_zero_row) + kDc +
+                            8 * ((ln & 7) ^ rope_swz(r));
+      lds_dma_16(src, lds_addr(dst.bytes) + kRopeBase + 1024 * blk);
+    }
+  };
+  // wait until at most `pending` later tiles' copies of this wave are in flight
+  auto wait_tiles = [&](int pending) {
+    static_assert(kBuffers == 3, "vmcnt immediates assume one later tile in flight");
+    if (pending == 0)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (even)
+      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  };
+
+  // LDS byte offsets.  Logits A operand of step ks for key block mb: row
+  // 16mb + n, piece 4ks + g, stored at 4ks + (g ^ f(row)) (latent steps) or in
+  // the rotary region (steps 16, 17).
+  int aoff[2], roff[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int r = 16 * mb + n;
+    aoff[mb] = kLatStride * r + 16 * (g ^ lat_swz(r));
+#pragma unroll
+    for (int kr = 0; kr < 2; ++kr) roff[mb][kr] = kRopeBase + 128 * r + 16 * ((4 * kr + g) ^ rope_swz(r));
+  }
+  // Transposing reads: lane (g, jq, cq) reads tile row 4g + jq + 16h, dims
+  // 16db + 4cq: piece 2db + cq/2, byte 8(cq&1).  (2db + y) ^ f = 4(db/2) + ((2(db&1) + y) ^ f),
+  // so each (h, db parity) has one base and db/2 moves it by 64 bytes.
+  const int jq = n >> 2, cq = n & 3;
+  int voff[2][2];  // [h][db parity]
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 4 * g + jq + 16 * h;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      voff[h][par] = kLatStride * r + 16 * ((2 * par + (cq >> 1)) ^ lat_swz(r)) + 8 * (cq & 1);
+  }
 
   // Online softmax with a fixed reference max per head: the first tile with a
   // valid key sets it, and p = 2^(x - ref) stays below 2^kRefSlack as long as
@@ -372,126 +393,121 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
 #pragma unroll
-      for (int nb = 0; nb < kDc / 32; ++nb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[nb][i] = 0.f;
+      for (int db = 0; db < kDc / 16; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       l_run = 0.f;
       m_ref = m_seen;
     }
     bool overflow = false;
-    int srn[8];  // index entries of the next tile to issue
-    if (ntiles > 0) tile_rows(0, srn);
     for (int t = 0; t < kBuffers - 1 && t < ntiles; ++t) {
-      issue_tile(t, srn);
-      if (t + 1 < ntiles) tile_rows(t + 1, srn);
+      tile_rows(t);
+      issue_tile(t);
     }
+    if (kBuffers - 1 < ntiles) tile_rows(kBuffers - 1);
     for (int it = 0; it < ntiles; ++it) {
-      // tile `it` has landed once at most the copies of the later issued tiles remain
-      wait_tiles_in_flight(min(kBuffers - 2, ntiles - 1 - it));
+      wait_tiles(min(kBuffers - 2, ntiles - 1 - it));
       __syncthreads();  // every wave's copies of tile `it` are in; tile it-1 is consumed
       if (it + kBuffers - 1 < ntiles) {
-        issue_tile(it + kBuffers - 1, srn);
-        if (it + kBuffers < ntiles) tile_rows(it + kBuffers, srn);
+        issue_tile(it + kBuffers - 1);
+        if (it + kBuffers < ntiles) tile_rows(it + kBuffers);
       }
       lds_char_t* cur = (lds_char_t*)(tiles[it % kBuffers].bytes);
-      // validity of the tile rows; accumulator i sits on row 8(i/4) + 4G + i%4
-      const uint32_t valid = vmask[it % kBuffers] >> (4 * G);
+      // validity of rows 4g + i (block 0) and 16 + 4g + i (block 1)
+      const uint32_t valid = vmask[it % (kBuffers + 1)] >> (4 * g);
 
-      // ---- logits^T: 32 keys x 32 heads ----
-      f32x16_t sacc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      // ---- logits^T: 2 blocks of 16 keys x 16 heads, interleaved chains ----
+      f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
       {
-        // software pipeline: the LDS read of step ks + kReadAhead is issued with
-        // the MFMA of step ks; sched_barrier keeps each pair in place
-        auto aload = [&](int ks) {
-          const int off = ks < kDc / 16 ? aoff[ks & 1] + 64 * (ks >> 1) : roff[ks - kDc / 16];
+        // software pipeline over the 36 (ks, mb) steps: the LDS reads of step
+        // st + kReadAhead are issued with the MFMA of step st
+        constexpr int kSteps = 2 * kKSteps;
+        auto aload = [&](int st) {
+          const int ks = st >> 1, mb = st & 1;
+          const int off = ks < kLatSteps ? aoff[mb] + 64 * ks : roff[mb][ks - kLatSteps];
           return *(__attribute__((address_space(3))) const bf16x8_t*)(cur + off);
         };
         auto qload = [&](int ks) {
-          return *reinterpret_cast<const bf16x8_t*>(qlds[ks - kQRegSteps][wave][G][n]);
+          return *reinterpret_cast<const bf16x8_t*>(qlds[ks - kQRegSteps][wave][g][n]);
         };
-        bf16x8_t ka[kReadAhead], qb[kReadAhead];
+        // the LDS query step ks lives in qb[ks % 3], loaded with the first step
+        // (2ks) of its read-ahead window; its last use, step 2ks + 1, comes
+        // before slot ks % 3 is reloaded for ks + 3 as long as kReadAhead <= 5
+        static_assert(kReadAhead <= 5, "query ring of 3 slots");
+        bf16x8_t ka[kReadAhead], qb[3];
+        auto issue = [&](int nx) {
+          ka[nx % kReadAhead] = aload(nx);
+          if ((nx & 1) == 0 && (nx >> 1) >= kQRegSteps) qb[(nx >> 1) % 3] = qload(nx >> 1);
+        };
 #pragma unroll
-        for (int ks = 0; ks < kReadAhead; ++ks) {
-          ka[ks] = aload(ks);
-          if (ks >= kQRegSteps) qb[ks] = qload(ks);
-        }
+        for (int st = 0; st < kReadAhead; ++st) issue(st);
 #pragma unroll
-        for (int ks = 0; ks < kD / 16; ++ks) {
-          sacc = mfma32x32x16_bf16(ka[ks % kReadAhead],
-                                   ks < kQRegSteps ? qf[ks] : qb[ks % kReadAhead], sacc);
-          const int nx = ks + kReadAhead;
-          if (nx < kD / 16) {
-            ka[ks % kReadAhead] = aload(nx);
-            if (nx >= kQRegSteps) qb[ks % kReadAhead] = qload(nx);
-          }
+        for (int st = 0; st < kSteps; ++st) {
+          const int ks = st >> 1, mb = st & 1;
+          sacc[mb] = mfma16x16x32_bf16(ka[st % kReadAhead], ks < kQRegSteps ? qf[ks] : qb[ks % 3],
+                                       sacc[mb]);
+          if (st + kReadAhead < kSteps) issue(st + kReadAhead);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
 
-      // ---- softmax weights (lane: head n, accumulator i = MFMA row 8(i/4) + 4G + i%4) ----
-      float x[16];
+      // ---- softmax weights (lane: head n; keys 16mb + 4g + i) ----
+      float x[2][4];
       float tmax = -__builtin_inff();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = ((valid >> (8 * (i >> 2) + (i & 3))) & 1) ? sacc[i] * scale2 : -__builtin_inff();
-        tmax = fmaxf(tmax, x[i]);
-      }
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[mb][i] = ((valid >> (16 * mb + i)) & 1) ? sacc[mb][i] * scale2 : -__builtin_inff();
+          tmax = fmaxf(tmax, x[mb][i]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       m_seen = fmaxf(m_seen, tmax);
       if (m_ref == -__builtin_inff()) m_ref = tmax;  // O and l of this head are still 0
       overflow |= tmax > m_ref + kRefSlack;
       const float m_use = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
       float psum = 0.f;
-      bf16x8_t pa[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t pb;  // B operand of the value product: slot 8g + e
+      {
         u32x4_t pw;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = exp2f(x[8 * kk + e] - m_use);
-          const float p1 = exp2f(x[8 * kk + e + 1] - m_use);
+          // v_exp_f32 directly: arguments are <= kRefSlack, -inf gives 0
+          const float p0 = __builtin_amdgcn_exp2f(x[e >> 2][e & 3] - m_use);
+          const float p1 = __builtin_amdgcn_exp2f(x[e >> 2][(e & 3) + 1] - m_use);
           psum += p0 + p1;
-          pw[e >> 1] = static_cast<uint32_t>(f32_to_bf16(p0)) |
-                       (static_cast<uint32_t>(f32_to_bf16(p1)) << 16);
+          pw[e >> 1] = f32x2_to_bf16x2(p0, p1);
         }
-        pa[kk] = __builtin_bit_cast(bf16x8_t, pw);
+        pb = __builtin_bit_cast(bf16x8_t, pw);
       }
+      psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
       l_run += psum;
 
-      // ---- O += P . V ----
+      // ---- O^T += V^T . P^T ----
       {
-        // software pipeline over the 32 (kk, nb) steps: the two transposing reads
-        // of step st + kVAhead are issued with the MFMA of step st
-        constexpr int kSteps = 2 * (kDc / 32);
         // ds_read_b64_tr_b16 takes no folded offset: an opaque per-tile copy of
-        // the bases keeps each read's address add next to the read instead of
-        // 64 precomputed addresses living across the loop
+        // the bases keeps each read's address add next to the read
         int vbase[2][2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            vbase[kk][h] = voff[kk][h];
-            asm volatile("" : "+v"(vbase[kk][h]));
+          for (int par = 0; par < 2; ++par) {
+            vbase[h][par] = voff[h][par];
+            asm volatile("" : "+v"(vbase[h][par]));
           }
-        bf16x8_t vb[kVAhead];
-        auto vload = [&](int st) {
-          const int kk = st / (kDc / 32), nb = st % (kDc / 32);
-          const short4_t lo = lds_read_tr16(cur + vbase[kk][0] + 64 * nb);
-          const short4_t hi = lds_read_tr16(cur + vbase[kk][1] + 64 * nb);
+        auto vload = [&](int db) {
+          const short4_t lo = lds_read_tr16(cur + vbase[0][db & 1] + 64 * (db >> 1));
+          const short4_t hi = lds_read_tr16(cur + vbase[1][db & 1] + 64 * (db >> 1));
           return __builtin_bit_cast(
               bf16x8_t, short8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
         };
+        bf16x8_t va[kVAhead];
 #pragma unroll
-        for (int st = 0; st < kVAhead; ++st) vb[st] = vload(st);
+        for (int db = 0; db < kVAhead; ++db) va[db] = vload(db);
 #pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-          const int kk = st / (kDc / 32), nb = st % (kDc / 32);
-          oacc[nb] = mfma32x32x16_bf16(pa[kk], vb[st % kVAhead], oacc[nb]);
-          if (st + kVAhead < kSteps) vb[st % kVAhead] = vload(st + kVAhead);
+        for (int db = 0; db < kDc / 16; ++db) {
+          oacc[db] = mfma16x16x32_bf16(va[db % kVAhead], pb, oacc[db]);
+          if (db + kVAhead < kDc / 16) va[db % kVAhead] = vload(db + kVAhead);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -501,29 +517,33 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     if (!__syncthreads_or(pass == 0 && overflow)) break;
   }
 
-  // ---- epilogue: oacc[nb][i] = O[head 32*wave + 8(i/4) + 4G + i%4][32nb + n] ----
-  float inv_l[16], lse_h[16];
+  // ---- epilogue: normalise, stage [head][dims] through LDS, coalesced stores ----
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float lse_h = l_run > 0.f ? (m_ref + __log2f(l_run)) * kLn2 : -__builtin_inff();
+  const int h = 16 * wave + n;
+  uint16_t* dst = nsplit == 1 ? o + row * kH * kDc : part_o + (row * nsplit + sp) * kH * kDc;
+  char* stage = reinterpret_cast<char*>(tiles[0].bytes);  // 128 rows x 528 B (the ring is idle)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int src = 8 * (i >> 2) + 4 * G + (i & 3);
-    const float l = __shfl(l_run, src, 64);
-    const float m = __shfl(m_ref, src, 64);
-    inv_l[i] = l > 0.f ? 1.f / l : 0.f;
-    lse_h[i] = l > 0.f ? (m + __log2f(l)) * kLn2 : -__builtin_inff();
-  }
-  const int hbase = 32 * wave + 4 * G;
-  uint16_t* dst = nsplit == 1 ? o + (row * kH) * kDc : part_o + ((row * nsplit + sp) * kH) * kDc;
-  float* dst_lse = nsplit == 1 ? lse : part_lse + (row * nsplit + sp - row) * kH;
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();  // the ring / the previous half of the staging is free
 #pragma unroll
-  for (int nb = 0; nb < kDc / 32; ++nb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int h = hbase + 8 * (i >> 2) + (i & 3);
-      dst[h * kDc + 32 * nb + n] = f32_to_bf16(oacc[nb][i] * inv_l[i]);
+    for (int dq = 0; dq < kDc / 32; ++dq) {
+      const f32x4_t& a = oacc[16 * half + dq];
+      const u32x2_t v = {f32x2_to_bf16x2(a[0] * inv_l, a[1] * inv_l),
+                         f32x2_to_bf16x2(a[2] * inv_l, a[3] * inv_l)};
+      *reinterpret_cast<u32x2_t*>(stage + kStageStride * h + 2 * (16 * dq + 4 * g)) = v;
     }
-  if (dst_lse != nullptr && n == 0)
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dst_lse[row * kH + hbase + 8 * (i >> 2) + (i & 3)] = lse_h[i];
+    for (int k = 0; k < (kH * kDc / 2 * 2) / (16 * kMlaThreads); ++k) {  // 8 x 16 B per thread
+      const int c = tid + kMlaThreads * k;  // 16-byte chunk: head c / 32, part c % 32
+      const int hh = c >> 5, part = c & 31;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + kStageStride * hh + 16 * part);
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(dst + hh * kDc) + 512 * half + 16 * part) = v;
+    }
+  }
+  float* dst_lse = nsplit == 1 ? (lse ? lse + row * kH : nullptr) : part_lse + (row * nsplit + sp) * kH;
+  if (dst_lse != nullptr && g == 0) dst_lse[h] = lse_h;
 }
 
 // Merge of the split partials: thread = 8 consecutive latent dims of one head.
@@ -539,29 +559,36 @@ mla_combine(int H, int Dc, int nsplit, int64_t total_vec, const uint16_t* __rest
   const int64_t row = v / per_row;
   const int rem = static_cast<int>(v % per_row);
   const int h = rem / (Dc / 8), d0 = (rem % (Dc / 8)) * 8;
+  const float* ls_row = part_lse + row * nsplit * H + h;
   float m = -__builtin_inff();
-  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, part_lse[(row * nsplit + sp) * H + h]);
+  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, ls_row[sp * H]);
+  const float m_use = m == -__builtin_inff() ? 0.f : m;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  if (m != -__builtin_inff()) {
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float ls = part_lse[(row * nsplit + sp) * H + h];
-      if (ls == -__builtin_inff()) continue;
-      const float wgt = __expf(ls - m);
-      wsum += wgt;
-      const u32x4_t pv = *reinterpret_cast<const u32x4_t*>(
-          part_o + ((row * nsplit + sp) * H + h) * Dc + d0);
+  const uint16_t* po = part_o + (row * nsplit * H + h) * Dc + d0;
+  // every split's partial is written (an empty split holds zeros with weight 0),
+  // so all loads are issued unconditionally
+#pragma unroll 4
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float wgt = __expf(ls_row[sp * H] - m_use);  // exp(-inf) = 0
+    const u32x4_t pv = *reinterpret_cast<const u32x4_t*>(po + static_cast<int64_t>(sp) * H * Dc);
+    wsum += wgt;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] = fmaf(wgt, __uint_as_float(pv[e] << 16), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(wgt, __uint_as_float(pv[e] & 0xffff0000u), acc[2 * e + 1]);
-      }
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(wgt, __uint_as_float(pv[e] << 16), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(wgt, __uint_as_float(pv[e] & 0xffff0000u), acc[2 * e + 1]);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  if constexpr (DT == DSA_BF16) {
+    const u32x4_t ov = {f32x2_to_bf16x2(acc[0] * inv, acc[1] * inv), f32x2_to_bf16x2(acc[2] * inv, acc[3] * inv),
+                        f32x2_to_bf16x2(acc[4] * inv, acc[5] * inv), f32x2_to_bf16x2(acc[6] * inv, acc[7] * inv)};
+    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(o) + (row * H + h) * Dc + d0) = ov;
+  } else {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) store_mla<DT>(o, (row * H + h) * Dc + d0 + e, acc[e] * inv);
-  if (lse != nullptr && d0 == 0) lse[row * H + h] = wsum > 0.f ? m + __logf(wsum) : -__builtin_inff();
+    for (int e = 0; e < 8; ++e) store_mla<DT>(o, (row * H + h) * Dc + d0 + e, acc[e] * inv);
+  }
+  if (lse != nullptr && d0 == 0) lse[row * H + h] = wsum > 0.f ? m_use + __logf(wsum) : -__builtin_inff();
 }
 
 struct MlaPlan {
