@@ -40,6 +40,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size (0 = auto)")
     ap.add_argument("--only", default="", help="profile one entry point only: forward|indexer|topk|mla")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the run, copy a MIB-sized device buffer 5 times (the known-size "
+                         "kernel the HBM counters are scaled by)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
+                         "`--only forward --copy-calibration MIB` into profiles/hbm_counters.json")
+    ap.add_argument("--calibration-mib", type=int, default=256)
     return ap.parse_args()
 
 
@@ -59,6 +66,16 @@ def algorithmic(cfg):
     mla_flops = 2.0 * cfg.H * (cfg.D + cfg.Dc) * sel
     return dict(indexer_bytes=idx_bytes, mla_bytes=mla_bytes, bytes=idx_bytes + mla_bytes,
                 indexer_flops=idx_flops, mla_flops=mla_flops, flops=idx_flops + mla_flops)
+
+
+def roofline(decode, nbytes, nflops, seconds):
+    if decode:
+        achieved = nbytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    achieved = nflops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def source_hash():
@@ -82,6 +99,69 @@ def counters_for(kernel, workload):
     except (ValueError, KeyError):
         return None
     return None
+
+
+def _kernel_short_name(name):
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].split("<")[0].split("::")[-1].strip()
+
+
+def _pmc_rows(d, counter):
+    """{kernel: {dispatch id: counter value summed over its instances}}."""
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            k = per.setdefault(_kernel_short_name(r["Kernel_Name"]), {})
+            k[int(r["Dispatch_Id"])] = k.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def summarize_pmc(fetch_dir, write_dir, mib, workload):
+    """HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the counter reads for the calibration copy
+    (the last 5 device-copy dispatches of the run, `mib` MiB each)."""
+    fetch = _pmc_rows(fetch_dir, "FETCH_SIZE")
+    write = _pmc_rows(write_dir, "WRITE_SIZE")
+    ck = "__amd_rocclr_copyBuffer"
+    if ck not in fetch or ck not in write:
+        raise SystemExit("no copy kernel in the counter runs (run with --copy-calibration)")
+
+    def calib(per):
+        last = sorted(per[ck])[-5:]
+        return sum(per[ck][i] for i in last) / len(last)
+
+    known_kib = mib * 1024.0
+    cf, cw = calib(fetch), calib(write)
+    f_fetch, f_write = known_kib / cf, known_kib / cw
+    out = {}
+    lines = ["| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per launch (scaled) |",
+             "|---|---|---|---|---|"]
+    for k in sorted(fetch):
+        if k not in write or k == ck or not k:
+            continue
+        fv = sum(fetch[k].values()) / len(fetch[k])
+        wv = sum(write[k].values()) / len(write[k])
+        hbm = (fv * f_fetch + wv * f_write) * 1024.0
+        out[k] = {"fetch_kib": round(fv, 1), "write_kib": round(wv, 1),
+                  "hbm_bytes_per_launch": round(hbm), "source_hash": source_hash()}
+        lines.append(f"| {k} | {len(fetch[k])} | {fv:,.0f} | {wv:,.0f} | {hbm:,.0f} |")
+    p = os.path.join(ROOT, "profiles", "hbm_counters.json")
+    d = json.load(open(p)) if os.path.exists(p) else {}
+    d[workload] = out
+    d[workload]["_calibration"] = {"copy_kernel": ck, "copy_mib": mib, "fetch_kib": round(cf, 1),
+                                   "write_kib": round(cw, 1), "fetch_factor": round(f_fetch, 4),
+                                   "write_factor": round(f_write, 4)}
+    os.makedirs(os.path.dirname(p), exist_ok=True)
+    json.dump(d, open(p, "w"), indent=1, sort_keys=True)
+    print(f"calibration: {ck} copying {mib} MiB (last 5 dispatches) reads FETCH_SIZE {cf:,.0f} KiB "
+          f"and WRITE_SIZE {cw:,.0f} KiB: factors {f_fetch:.4f} (fetch), {f_write:.4f} (write)\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(cfg, rows):
@@ -132,6 +212,9 @@ def cpu_baseline(cfg, rows):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calibration_mib, args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -199,6 +282,17 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n  # ms
 
+    def copy_calibration():
+        if not args.copy_calibration:
+            return
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {args.copy_calibration} MiB 5 times", file=sys.stderr, flush=True)
+
     if args.only:
         fn = {"forward": step, "indexer": run_indexer, "topk": run_topk, "mla": run_mla}[args.only]
         if args.only in ("topk", "mla"):
@@ -206,51 +300,52 @@ def main():
             run_topk(0)
         ms = timed(fn, args.steps, args.warmup)
         print(json.dumps({"only": args.only, "ms_per_call": ms}))
+        copy_calibration()
         return
 
     ms = timed(step, args.steps, args.warmup)
     print(f"[bench] forward: {ms * 1e3:.1f} us per step", file=sys.stderr, flush=True)
 
-    # per-entry-point timing (same stream, same rotation)
-    run_indexer(0)
-    run_topk(0)
-    kern = {
-        "indexer_mfma": (timed(run_indexer, args.steps, 3), "dsa_indexer_scores"),
-        "topk_select": (timed(run_topk, args.steps, 3), "dsa_topk"),
-        "sparse_mla": (timed(run_mla, args.steps, 3), "dsa_sparse_mla_fwd"),
-    }
-    for k, (t, _) in kern.items():
-        print(f"[bench] {k}: {t * 1e3:.1f} us per launch", file=sys.stderr, flush=True)
+    # The same K steps once more with the library's kernel timing on: HIP
+    # events around each kernel launch, recorded on the stream it runs on.
+    dsa.dsa_timing_begin()
+    ms_timed = timed(step, args.steps, 0)
+    kt = dsa.dsa_timing_end()
+    for k, r in kt.items():
+        print(f"[bench] {k}: {r['avg_us']:.2f} us per launch ({r['launches']} launches)",
+              file=sys.stderr, flush=True)
 
     A = algorithmic(cfg)
     q = cfg.B * cfg.T
     step_s = ms / 1e3
     value = q / step_s
-    # the dominant single kernel: the indexer (one launch per entry-point call)
-    # or the attention entry point, whichever takes longer
-    dom = max(("indexer_mfma", "sparse_mla"), key=lambda k: kern[k][0])
-    t_dom = kern[dom][0] / 1e3
-    if dom == "indexer_mfma":
-        bytes_launch = A["indexer_bytes"] * q
-        flops_launch = A["indexer_flops"] * q
-    else:
-        bytes_launch = A["mla_bytes"] * q
-        flops_launch = A["mla_flops"] * q
     decode = cfg.T == 1
-    if decode:
-        achieved = bytes_launch / t_dom / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    # the dominant kernel: the longest average launch of the step
+    dom = max(kt, key=lambda k: kt[k]["avg_us"])
+    t_dom = kt[dom]["avg_us"] / 1e6
+    if dom.startswith("indexer"):
+        bytes_launch, flops_launch = A["indexer_bytes"] * q, A["indexer_flops"] * q
+    elif dom.startswith("mla") and dom != "mla_combine":
+        bytes_launch, flops_launch = A["mla_bytes"] * q, A["mla_flops"] * q
     else:
-        achieved = flops_launch / t_dom / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+        raise SystemExit(f"bench: no algorithmic model for dominant kernel {dom}")
+    roof = roofline(decode, bytes_launch, flops_launch, t_dom)
     roof["kernel"] = dom
-    roof["entry_point"] = kern[dom][1]
     roof["launch_us"] = round(t_dom * 1e6, 2)
     roof["algorithmic_per_launch"] = round(bytes_launch if decode else flops_launch)
-    traffic = counters_for(dom, cfg.name)
-    roof["traffic"] = traffic
+    roof["traffic"] = counters_for(dom, cfg.name)
+    # each stage of the path against its own bound (the attention stage is
+    # mla_mfma plus the split merge)
+    stage_us = {"indexer": sum(r["avg_us"] for k, r in kt.items() if k.startswith("indexer")),
+                "topk": sum(r["avg_us"] for k, r in kt.items() if k.startswith("topk")),
+                "sparse_mla": sum(r["avg_us"] for k, r in kt.items() if k.startswith("mla"))}
+    stages = {
+        "indexer": roofline(decode, A["indexer_bytes"] * q, A["indexer_flops"] * q, stage_us["indexer"] / 1e6),
+        "sparse_mla": roofline(decode, A["mla_bytes"] * q, A["mla_flops"] * q, stage_us["sparse_mla"] / 1e6),
+    }
+    for k, v in stages.items():
+        v["us"] = round(stage_us[k], 2)
+    stages["topk"] = {"us": round(stage_us["topk"], 2), "bound": "alu"}
 
     result = {
         "metric": "indexer+sparse-MLA queries/sec",
@@ -270,7 +365,9 @@ def main():
                    "rope": cfg.Dr, "topk": cfg.K, "idx_dtype": cfg.idx_dtype},
         "step_hbm_frac": round(A["bytes"] * q / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_tokens_per_s": round(value, 1),
-        "kernel_us": {k: round(v[0] * 1e3, 2) for k, v in kern.items()},
+        "kernel_us": {k: round(r["avg_us"], 2) for k, r in kt.items()},
+        "ms_per_step_kernel_timing": round(ms_timed, 5),
+        "stages": stages,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

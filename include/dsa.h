@@ -144,6 +144,32 @@ dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx,
  * (0 if none).  Returns (size_t)-1 when the shape is invalid. */
 size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry);
 
+/*
+ * Kernel timing, for measurement only.  Between dsa_timing_begin() and
+ * dsa_timing_end(), each kernel the library launches (from any host thread)
+ * carries a pair of HIP events that the runtime stamps with that dispatch's
+ * own begin and end on the device (hipExtLaunchKernel), on the stream it is
+ * launched on; outside a session launches carry none.  dsa_timing_end()
+ * waits for the recorded events, ends the session and writes one record per
+ * kernel name, in order of first launch, into out[0 .. max_out-1];
+ * *n_out (nullable) receives the number of distinct kernels.  The first
+ * 65536 launches of a session are timed; later ones are only counted, in
+ * `dropped` of their kernel's record.  Events come from a pool the library
+ * keeps for the life of the process.
+ * Errors: DSA_ERR_INVALID_ARG if a session is already active (begin) or none
+ * is (end), or out is NULL with max_out > 0; DSA_ERR_HIP if an event call
+ * fails (the session is ended).
+ */
+typedef struct {
+  char name[48];    /* kernel name, e.g. "mla_mfma" */
+  int32_t launches; /* timed launches */
+  int32_t dropped;  /* launches beyond the session's capacity (not timed) */
+  double total_ms, min_ms, max_ms;
+} dsa_kernel_time_t;
+
+dsa_status_t dsa_timing_begin(void);
+dsa_status_t dsa_timing_end(dsa_kernel_time_t* out, int32_t max_out, int32_t* n_out);
+
 /* Static description of a status code. */
 const char* dsa_status_str(dsa_status_t status);
 

@@ -38,6 +38,13 @@ class DsaShape(ctypes.Structure):
         return "DsaShape(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
 
 
+class DsaKernelTime(ctypes.Structure):
+    """Mirror of dsa_kernel_time_t."""
+    _fields_ = [("name", ctypes.c_char * 48), ("launches", ctypes.c_int32),
+                ("dropped", ctypes.c_int32), ("total_ms", ctypes.c_double),
+                ("min_ms", ctypes.c_double), ("max_ms", ctypes.c_double)]
+
+
 class DsaError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
@@ -71,6 +78,11 @@ def lib() -> ctypes.CDLL:
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_bytes.argtypes = [sp, ctypes.c_int32]
         L.dsa_workspace_bytes.restype = ctypes.c_size_t
+        L.dsa_timing_begin.argtypes = []
+        L.dsa_timing_begin.restype = ctypes.c_int
+        L.dsa_timing_end.argtypes = [ctypes.POINTER(DsaKernelTime), ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_int32)]
+        L.dsa_timing_end.restype = ctypes.c_int
         L.dsa_status_str.argtypes = [ctypes.c_int]
         L.dsa_status_str.restype = ctypes.c_char_p
         L.dsa_last_error.argtypes = []
@@ -213,3 +225,23 @@ def dsa_forward(shape: DsaShape, q_idx, k_idx, w, q, kv, q_sf=None, k_sf=None,
                              _ptr(w), _ptr(q), _ptr(kv), _ptr(idx_out), _ptr(out), _ptr(lse),
                              _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
     return out, lse, idx_out
+
+
+def dsa_timing_begin() -> None:
+    """Start a kernel-timing session: the library brackets each of its kernel
+    launches with HIP events on the launch's stream."""
+    _check(lib().dsa_timing_begin())
+
+
+def dsa_timing_end(max_kernels: int = 32) -> dict:
+    """End the session; {kernel name: {launches, dropped, total_ms, min_ms,
+    max_ms, avg_us}} in order of first launch."""
+    recs = (DsaKernelTime * max_kernels)()
+    n = ctypes.c_int32(0)
+    _check(lib().dsa_timing_end(recs, max_kernels, ctypes.byref(n)))
+    out = {}
+    for r in recs[:min(n.value, max_kernels)]:
+        out[r.name.decode()] = dict(launches=r.launches, dropped=r.dropped, total_ms=r.total_ms,
+                                    min_ms=r.min_ms, max_ms=r.max_ms,
+                                    avg_us=1e3 * r.total_ms / r.launches if r.launches else None)
+    return out

@@ -4,9 +4,13 @@
 // sparse_mla.hip.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "dsa.h"
@@ -116,6 +120,72 @@ dsa_status_t check_launch(const char* what) {
   return DSA_OK;
 }
 
+// ---- kernel timing sessions ----------------------------------------------
+namespace {
+constexpr size_t kTimingCap = 65536;
+
+struct TimedLaunch {
+  const char* name;  // set by done(); nullptr while the launch is being enqueued
+  hipEvent_t start, stop;
+};
+
+struct TimingSession {
+  std::mutex mu;
+  std::atomic<bool> active{false};
+  long generation = 0;
+  std::vector<TimedLaunch> launches;
+  std::vector<hipEvent_t> pool;  // 2 events per launch slot, reused across sessions
+  std::vector<std::pair<const char*, int>> dropped;
+};
+
+TimingSession& timing() {
+  static TimingSession t;
+  return t;
+}
+}  // namespace
+
+LaunchTimer::LaunchTimer() {
+  TimingSession& T = timing();
+  if (!T.active.load(std::memory_order_relaxed)) return;
+  std::lock_guard<std::mutex> lock(T.mu);
+  if (!T.active.load(std::memory_order_relaxed)) return;
+  gen_ = T.generation;
+  if (T.launches.size() >= kTimingCap) {
+    slot_ = -2;  // counted in done()
+    return;
+  }
+  const size_t i = T.launches.size();
+  while (T.pool.size() < 2 * (i + 1)) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return;
+    T.pool.push_back(e);
+  }
+  TimedLaunch rec{nullptr, T.pool[2 * i], T.pool[2 * i + 1]};
+  T.launches.push_back(rec);
+  start_ = rec.start;
+  stop_ = rec.stop;
+  slot_ = static_cast<long>(i);
+}
+
+dsa_status_t LaunchTimer::done(const char* what) {
+  const dsa_status_t st = check_launch(what);
+  if (slot_ == -1) return st;
+  TimingSession& T = timing();
+  std::lock_guard<std::mutex> lock(T.mu);
+  if (!T.active.load(std::memory_order_relaxed) || gen_ != T.generation) return st;
+  if (slot_ == -2) {
+    for (auto& d : T.dropped)
+      if (d.first == what) {
+        ++d.second;
+        return st;
+      }
+    T.dropped.emplace_back(what, 1);
+    return st;
+  }
+  if (st == DSA_OK) T.launches[static_cast<size_t>(slot_)].name = what;
+  return st;
+}
+
 const DeviceInfo& device_info() {
   static std::mutex mu;
   static std::vector<DeviceInfo> cache;
@@ -213,6 +283,58 @@ size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry) {
   }
   fail(DSA_ERR_INVALID_ARG, "unknown entry %d", entry);
   return static_cast<size_t>(-1);
+}
+
+dsa_status_t dsa_timing_begin(void) {
+  g_last_error[0] = '\0';
+  TimingSession& T = timing();
+  std::lock_guard<std::mutex> lock(T.mu);
+  if (T.active.load()) return fail(DSA_ERR_INVALID_ARG, "timing: a session is already active");
+  T.launches.clear();
+  T.dropped.clear();
+  ++T.generation;
+  T.active.store(true);
+  return DSA_OK;
+}
+
+dsa_status_t dsa_timing_end(dsa_kernel_time_t* out, int32_t max_out, int32_t* n_out) {
+  g_last_error[0] = '\0';
+  if (out == nullptr && max_out > 0) return fail(DSA_ERR_INVALID_ARG, "timing: out is NULL");
+  TimingSession& T = timing();
+  std::lock_guard<std::mutex> lock(T.mu);
+  if (!T.active.load()) return fail(DSA_ERR_INVALID_ARG, "timing: no active session");
+  T.active.store(false);
+  std::vector<dsa_kernel_time_t> recs;
+  auto find = [&](const char* name) -> dsa_kernel_time_t& {
+    for (auto& r : recs)
+      if (std::strncmp(r.name, name, sizeof r.name - 1) == 0) return r;
+    dsa_kernel_time_t r{};
+    std::snprintf(r.name, sizeof r.name, "%s", name);
+    recs.push_back(r);
+    return recs.back();
+  };
+  dsa_status_t st = DSA_OK;
+  for (const TimedLaunch& L : T.launches) {
+    if (L.name == nullptr) continue;  // its stop event was never recorded
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(L.stop);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, L.start, L.stop);
+    if (e != hipSuccess) {
+      st = fail(DSA_ERR_HIP, "timing: %s: %s", L.name, hipGetErrorString(e));
+      continue;
+    }
+    dsa_kernel_time_t& r = find(L.name);
+    r.min_ms = r.launches == 0 ? ms : std::min(r.min_ms, static_cast<double>(ms));
+    r.max_ms = std::max(r.max_ms, static_cast<double>(ms));
+    r.total_ms += ms;
+    ++r.launches;
+  }
+  for (const auto& d : T.dropped) find(d.first).dropped += d.second;
+  T.launches.clear();
+  T.dropped.clear();
+  for (int32_t i = 0; i < max_out && i < static_cast<int32_t>(recs.size()); ++i) out[i] = recs[i];
+  if (n_out != nullptr) *n_out = static_cast<int32_t>(recs.size());
+  return st;
 }
 
 const char* dsa_status_str(dsa_status_t status) {

@@ -1,5 +1,6 @@
 // Host-side declarations shared by the libdsa translation units.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -19,6 +20,24 @@ const DeviceInfo& device_info();
 dsa_status_t fail(dsa_status_t st, const char* fmt, ...);
 // Checks the last launch on this thread.
 dsa_status_t check_launch(const char* what);
+
+// Times one kernel launch for dsa_timing_*: construct it right before the
+// launch, pass start()/stop() to hipExtLaunchKernelGGL (the runtime stamps
+// them with the dispatch's own begin and end), call done() right after (it
+// checks the launch like check_launch).  Outside a timing session the events
+// are null and the launch is a plain one.
+class LaunchTimer {
+ public:
+  LaunchTimer();
+  hipEvent_t start() const { return start_; }
+  hipEvent_t stop() const { return stop_; }
+  dsa_status_t done(const char* what);
+
+ private:
+  hipEvent_t start_ = nullptr, stop_ = nullptr;
+  long slot_ = -1;  // record index in the session; -1 not timed, -2 beyond the capacity
+  long gen_ = 0;    // the session the slot belongs to
+};
 
 inline int32_t k_eff(const dsa_shape_t& s) { return s.K < s.S ? s.K : s.S; }
 

@@ -264,9 +264,11 @@ dsa_status_t run_generic(const dsa_shape_t& s, const void* q_idx, const uint8_t*
     return fail(DSA_ERR_UNSUPPORTED, "indexer: HI*DI = %d too large for the generic kernel",
                 s.HI * s.DI);
   dim3 grid((s.S + 255) / 256, s.B * s.T);
-  indexer_generic<IDT, WDT><<<grid, 256, lds, stream>>>(s.T, s.S, s.HI, s.DI, s.idx_scale, q_idx,
-                                                         q_sf, k_idx, k_sf, w, scores);
-  return check_launch("indexer_generic");
+  LaunchTimer timer;
+  hipExtLaunchKernelGGL(indexer_generic<IDT, WDT>, grid, dim3(256), lds, stream, timer.start(),
+                        timer.stop(), 0, s.T, s.S, s.HI, s.DI, s.idx_scale, q_idx, q_sf, k_idx,
+                        k_sf, w, scores);
+  return timer.done("indexer_generic");
 }
 
 template <bool FP8, int WDT>
@@ -275,9 +277,11 @@ dsa_status_t run_mfma(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_
                       hipStream_t stream) {
   const int keys_per_block = kIdxWaves * kKeysPerWave;
   dim3 grid((s.S + keys_per_block - 1) / keys_per_block, s.B * s.T);
-  indexer_mfma<FP8, WDT><<<grid, kIdxWaves * 64, 0, stream>>>(s.T, s.S, s.idx_scale, q_idx, q_sf,
-                                                               k_idx, k_sf, w, scores);
-  return check_launch("indexer_mfma");
+  LaunchTimer timer;
+  hipExtLaunchKernelGGL(indexer_mfma<FP8, WDT>, grid, dim3(kIdxWaves * 64), 0, stream,
+                        timer.start(), timer.stop(), 0, s.T, s.S, s.idx_scale, q_idx, q_sf, k_idx,
+                        k_sf, w, scores);
+  return timer.done("indexer_mfma");
 }
 
 }  // namespace

@@ -648,27 +648,34 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
       part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + (po + 255) / 256 * 256);
     }
     const int xcd_map = (p.splits > 1 && rows % 8 == 0) ? 1 : 0;
-    mla_mfma<<<dim3(static_cast<unsigned>(rows * p.splits)), kMlaThreads, 0, stream>>>(
-        s.T, s.S, W, p.kps, p.splits, xcd_map, s.sm_scale, static_cast<const uint16_t*>(q),
-        static_cast<const uint16_t*>(kv), idx, static_cast<uint16_t*>(o), lse, part_o, part_lse);
-    dsa_status_t st = check_launch("mla_mfma");
+    LaunchTimer timer;
+    hipExtLaunchKernelGGL(mla_mfma, dim3(static_cast<unsigned>(rows * p.splits)), dim3(kMlaThreads), 0,
+                          stream, timer.start(), timer.stop(), 0, s.T, s.S, W, p.kps, p.splits, xcd_map,
+                          s.sm_scale, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
+                          idx, static_cast<uint16_t*>(o), lse, part_o, part_lse);
+    dsa_status_t st = timer.done("mla_mfma");
     if (st != DSA_OK || p.splits == 1) return st;
     const int64_t total_vec = rows * s.H * s.Dc / 8;
-    mla_combine<DSA_BF16><<<dim3(static_cast<unsigned>((total_vec + 255) / 256)), 256, 0, stream>>>(
-        s.H, s.Dc, p.splits, total_vec, part_o, part_lse, o, lse);
-    return check_launch("mla_combine");
+    LaunchTimer ctimer;
+    hipExtLaunchKernelGGL(mla_combine<DSA_BF16>, dim3(static_cast<unsigned>((total_vec + 255) / 256)),
+                          dim3(256), 0, stream, ctimer.start(), ctimer.stop(), 0, s.H, s.Dc, p.splits,
+                          total_vec, static_cast<const uint16_t*>(part_o),
+                          static_cast<const float*>(part_lse), o, lse);
+    return ctimer.done("mla_combine");
   }
   const size_t lds = (static_cast<size_t>(s.Dc) + s.Dr + W) * sizeof(float);
   if (lds > 64 * 1024)
     return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: D + K = %d too large for the generic kernel",
                 s.Dc + s.Dr + W);
+  LaunchTimer timer;
+  const dim3 grid(s.H, static_cast<unsigned>(rows));
   if (s.mla_dtype == DSA_BF16)
-    mla_generic<DSA_BF16><<<dim3(s.H, rows), 256, lds, stream>>>(s.T, s.S, s.H, s.Dc, s.Dr, W,
-                                                                 s.sm_scale, q, kv, idx, o, lse);
+    hipExtLaunchKernelGGL(mla_generic<DSA_BF16>, grid, dim3(256), lds, stream, timer.start(),
+                          timer.stop(), 0, s.T, s.S, s.H, s.Dc, s.Dr, W, s.sm_scale, q, kv, idx, o, lse);
   else
-    mla_generic<DSA_F32><<<dim3(s.H, rows), 256, lds, stream>>>(s.T, s.S, s.H, s.Dc, s.Dr, W,
-                                                                s.sm_scale, q, kv, idx, o, lse);
-  return check_launch("mla_generic");
+    hipExtLaunchKernelGGL(mla_generic<DSA_F32>, grid, dim3(256), lds, stream, timer.start(),
+                          timer.stop(), 0, s.T, s.S, s.H, s.Dc, s.Dr, W, s.sm_scale, q, kv, idx, o, lse);
+  return timer.done("mla_generic");
 }
 
 }  // namespace dsa

@@ -180,14 +180,16 @@ template <bool SRC_CAND, bool OUT_CAND>
 dsa_status_t run_select(int per_wg, dim3 grid, int n_in, int64_t in_stride, int chunk_elems,
                         const float* scores, const uint32_t* ck_in, const int32_t* ci_in,
                         int K_out, int32_t* idx_out, uint32_t* ck_out, hipStream_t stream) {
-#define DSA_TOPK_LAUNCH(EV)                                                              \
-  topk_select<EV, SRC_CAND, OUT_CAND><<<grid, kTopkThreads, 0, stream>>>(              \
-      n_in, in_stride, chunk_elems, scores, ck_in, ci_in, K_out, idx_out, ck_out)
+#define DSA_TOPK_LAUNCH(EV)                                                               \
+  hipExtLaunchKernelGGL(topk_select<EV, SRC_CAND, OUT_CAND>, grid, dim3(kTopkThreads), 0, stream, \
+                        timer.start(), timer.stop(), 0, n_in, in_stride, chunk_elems, scores,     \
+                        ck_in, ci_in, K_out, idx_out, ck_out)
+  LaunchTimer timer;
   if (per_wg <= 8 * kTopkThreads) DSA_TOPK_LAUNCH(8);
   else if (per_wg <= 16 * kTopkThreads) DSA_TOPK_LAUNCH(16);
   else DSA_TOPK_LAUNCH(32);
 #undef DSA_TOPK_LAUNCH
-  return check_launch("topk_select");
+  return timer.done(SRC_CAND ? "topk_merge" : OUT_CAND ? "topk_chunk" : "topk_select");
 }
 
 struct TopkPlan {

@@ -112,6 +112,21 @@ def test_forward_workspace_too_small(dsa):
     assert rc == 3 and "workspace" in L.dsa_last_error().decode()
 
 
+def test_timing_session_on_host(dsa):
+    # no launches happen, so no event is created and no device is touched
+    with pytest.raises(dsa.DsaError, match="no active session"):
+        dsa.dsa_timing_end()
+    dsa.dsa_timing_begin()
+    with pytest.raises(dsa.DsaError, match="already active"):
+        dsa.dsa_timing_begin()
+    assert dsa.dsa_timing_end() == {}
+    # a launch rejected on the host is not timed and leaves no record
+    dsa.dsa_timing_begin()
+    L = dsa.lib()
+    assert L.dsa_topk(ctypes.byref(_v32(dsa, K=0)), ctypes.c_void_p(256), ctypes.c_void_p(256), None, 0, None) == 1
+    assert dsa.dsa_timing_end() == {}
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import sparse_latent_attention_lightning_amd._binding as b
     monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "missing.so"))
