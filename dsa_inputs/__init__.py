@@ -120,9 +120,10 @@ CONFIGS: Dict[str, Config] = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns, round to nearest even (NaN kept quiet)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # u + 0x8000 cannot wrap for any non-NaN pattern (the largest, -inf, is
+    # 0xff800000); NaN lanes are overwritten below
+    r = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = 0x7FC0
@@ -316,12 +317,31 @@ def full(cfg: Config, tensor: str):
     return np.stack(per_b)
 
 
-def iter_blocks(cfg: Config, tensor: str, rows_per_chunk: int = 4096):
-    """Yield (b, r0, r1, stored) chunks covering ``tensor`` (bounded memory)."""
+def iter_blocks(cfg: Config, tensor: str, values_per_chunk: int = 1 << 24, threads: int = 0):
+    """Yield (b, r0, r1, stored) chunks covering ``tensor`` in order, each
+    about ``values_per_chunk`` values (bounded memory).  Chunks are drawn by
+    ``threads`` worker threads (0 = up to 16); the draws do not depend on it."""
+    import concurrent.futures as cf
+    import os
     n = _nrows(cfg, tensor)
-    step = max(ROW_BLOCK, (rows_per_chunk // ROW_BLOCK) * ROW_BLOCK)
-    for b in range(cfg.B):
-        for r0 in range(0, n, step):
-            r1 = min(n, r0 + step)
+    row_vals = int(np.prod(_shape_tail(cfg, tensor)))
+    step = max(ROW_BLOCK, (values_per_chunk // row_vals // ROW_BLOCK) * ROW_BLOCK)
+    jobs = [(b, r0, min(n, r0 + step)) for b in range(cfg.B) for r0 in range(0, n, step)]
+    threads = threads or min(16, os.cpu_count() or 1)
+    if threads <= 1 or len(jobs) <= 1:
+        for b, r0, r1 in jobs:
             yield b, r0, r1, rows(cfg, tensor, b, r0, r1)
-
+        return
+    with cf.ThreadPoolExecutor(threads) as ex:
+        pending = []
+        it = iter(jobs)
+        for job in it:
+            pending.append((job, ex.submit(rows, cfg, tensor, *job)))
+            if len(pending) >= 2 * threads:
+                break
+        while pending:
+            (b, r0, r1), fut = pending.pop(0)
+            nxt = next(it, None)
+            if nxt is not None:
+                pending.append((nxt, ex.submit(rows, cfg, tensor, *nxt)))
+            yield b, r0, r1, fut.result()

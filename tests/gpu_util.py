@@ -91,7 +91,8 @@ def assert_scores_close(got, ref, rtol=SCORE_RTOL, what="scores"):
     assert np.array_equal(fin, np.isfinite(got)), f"{what}: -inf pattern differs"
     assert np.all(np.isneginf(got[~fin])), f"{what}: masked entries must be -inf"
     scale = np.where(fin, np.abs(ref), 0).max(axis=-1, keepdims=True)
-    err = np.where(fin, np.abs(got - ref), 0)
+    with np.errstate(invalid="ignore"):  # -inf - -inf on masked entries
+        err = np.where(fin, np.abs(got - ref), 0)
     bad = err > rtol * scale + 1e-30
     if bad.any():
         i = np.unravel_index(np.argmax(err), err.shape)
