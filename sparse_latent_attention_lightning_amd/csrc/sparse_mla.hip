@@ -176,13 +176,15 @@ constexpr int kReadAhead = 3;                // logits A-operand reads issued ah
 constexpr int kVAhead = 2;                   // value A-operand (2 reads each) issued ahead
 constexpr float kRefSlack = 32.0f;           // log2 units: p <= 2^32 against the reference max
 constexpr int kStageStride = 528;            // epilogue staging row: 256 bf16 + 16 B pad
+constexpr int kIdxWin = 1024;                // index entries staged in LDS at a time
+constexpr int kWinTiles = kIdxWin / kTileKeys;
+constexpr int kWinPerThread = kIdxWin / (kMlaWaves * 64);
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) const char lds_char_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
-typedef __attribute__((__vector_size__(8 * sizeof(int32_t)))) int32_t i32x8_t;
 
 // a zero key row: skipped index entries load it, so their LDS rows are zero
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[kD];
@@ -220,6 +222,26 @@ __device__ __forceinline__ int lat_swz(int r) {  // f(r): bit-reversed (r >> 2) 
 }
 __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 
+// Butterfly steps across lane distance 16 and 32 on the VALU (v_permlane16_swap
+// / v_permlane32_swap with both operands the same value: each lane ends with
+// its own value and its partner's, in some order, so any symmetric op works).
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Address arithmetic on LDS pointers stays in the 32-bit LDS address space, so
 // constant offsets fold into the instructions' offset fields.
 __device__ __forceinline__ short4_t lds_read_tr16(lds_char_t* p) {
@@ -240,10 +262,11 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   __shared__ __attribute__((aligned(1024))) MlaTile tiles[kBuffers];
   // query steps kQRegSteps.. : [step][wave][g][head n][8 bf16]
   __shared__ __attribute__((aligned(16))) uint16_t qlds[kQLdsSteps][kMlaWaves][4][16][8];
-  // validity of each tile's rows (bit r: tile row r holds a valid key); written
-  // one tile ahead of its copies, so it needs one more slot than the tile ring
+  // a window of the split's index entries as key rows (-1: skipped entry)
+  __shared__ __attribute__((aligned(16))) int32_t idxw[kIdxWin];
+  // validity of each tile's rows (bit r: tile row r holds a valid key), written
+  // when the tile's copies are issued, two iterations before its use
   __shared__ uint32_t vmask[kBuffers + 1];
-  __shared__ __attribute__((aligned(16))) int32_t ring_idx[kBuffers][kTileKeys];  // key row of each tile row (-1: none)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -264,9 +287,30 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   const int ntiles = (nj + kTileKeys - 1) / kTileKeys;
   const uint16_t* kv_seq = kv + static_cast<int64_t>(b) * S * kD;
 
+  // The split's index entries go through LDS a window at a time: thread i
+  // loads entries i, i + 512 of the window (past the split's end: -1).
+  const int32_t* idx_row = idx + row * W;
+  const int j_end = j0 + nj;
+  int win[kWinPerThread];
+  auto load_window = [&](int w) {
+#pragma unroll
+    for (int u = 0; u < kWinPerThread; ++u) {
+      const int j = j0 + w * kIdxWin + tid + u * kMlaThreads;
+      win[u] = j < j_end ? idx_row[j] : -1;
+    }
+  };
+  auto store_window = [&]() {
+#pragma unroll
+    for (int u = 0; u < kWinPerThread; ++u)
+      idxw[tid + u * kMlaThreads] = (win[u] >= 0 && win[u] < S) ? win[u] : -1;
+  };
+
   // query operand (B of logits^T): head 16*wave + n, dims 32ks + 8g .. +8;
-  // steps < kQRegSteps stay in registers, the rest go to LDS
-  bf16x8_t qf[kQRegSteps];
+  // steps < kQRegSteps stay in registers, the rest go to LDS.  The loads are
+  // issued with the first index window and consumed after the first tiles'
+  // copies are on their way, so the three latencies overlap.
+  bf16x8_t qf[kQRegSteps], qs[kQLdsSteps];
+  load_window(0);
   {
     const uint16_t* qh = q + (row * kH + 16 * wave + n) * kD;
 #pragma unroll
@@ -274,12 +318,10 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       qf[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * g);
 #pragma unroll
     for (int ks = kQRegSteps; ks < kKSteps; ++ks)
-      *reinterpret_cast<bf16x8_t*>(qlds[ks - kQRegSteps][wave][g][n]) =
-          *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * g);
-    // consume the loads here: later vmcnt waits then only see the tile copies
-#pragma unroll
-    for (int ks = 0; ks < kQRegSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
+      qs[ks - kQRegSteps] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * g);
   }
+  store_window();
+  __syncthreads();
 
   f32x4_t oacc[kDc / 16];  // O^T: oacc[db][i] = O[head 16*wave + n][16db + 4g + i]
 #pragma unroll
@@ -289,49 +331,23 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   const float scale2 = sm_scale * kLog2e;
 
   // Wave w copies tile rows 4w .. 4w+3 (and, if even, the rotary parts of rows
-  // 4w .. 4w+7).  The index entries of the 8-row block w/2 come through one
-  // scalar load a tile ahead (skipped or out-of-range entries become -1); both
-  // waves of the block write them to the tile's index slots in LDS (the same
-  // values, each wave then reads back only what it wrote itself), and even
-  // waves publish the block's validity as byte w/2 of the tile's mask word.
-  const int32_t* idx_row = idx + row * W;
-  const int j_end = j0 + nj;
+  // 4w .. 4w+7), reading their key rows from the index window; wave 0 also
+  // publishes the tile's validity mask.
   const int blk = wave >> 1;
   const bool even = (wave & 1) == 0;
-  auto tile_rows = [&](int t) {
-    const int j = j0 + t * kTileKeys + 8 * blk;
-    int sr[8];
-    if (j + 8 <= j_end) {  // one 32-byte scalar load
-      i32x8_t v;
-      __builtin_memcpy(&v, idx_row + j, sizeof v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sr[e] = (v[e] >= 0 && v[e] < S) ? v[e] : -1;
-    } else {               // the ragged end of the split
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int sv = idx_row[min(j + e, j_end - 1)];
-        if (j + e >= j_end || sv < 0 || sv >= S) sv = -1;
-        sr[e] = sv;
-      }
-    }
-    uint32_t mask8 = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) mask8 |= static_cast<uint32_t>(sr[e] >= 0) << e;
-    if (lane == 0) {
-      int32_t* slot = &ring_idx[t % kBuffers][8 * blk];
-      *reinterpret_cast<int4*>(slot) = make_int4(sr[0], sr[1], sr[2], sr[3]);
-      *reinterpret_cast<int4*>(slot + 4) = make_int4(sr[4], sr[5], sr[6], sr[7]);
-      if (even) reinterpret_cast<uint8_t*>(&vmask[t % (kBuffers + 1)])[blk] = static_cast<uint8_t>(mask8);
-    }
-  };
   auto issue_tile = [&](int t) {
     MlaTile& dst = tiles[t % kBuffers];
     // an opaque copy of the lane id: the per-copy address math below is redone
     // at each issue instead of being kept live across the loop in registers
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
-    const int4 s4 = *reinterpret_cast<const int4*>(&ring_idx[t % kBuffers][4 * wave]);
+    const int32_t* wrow = &idxw[(t % kWinTiles) * kTileKeys];
+    const int4 s4 = *reinterpret_cast<const int4*>(wrow + 4 * wave);
     const int sl[4] = {s4.x, s4.y, s4.z, s4.w};
+    if (wave == 0) {
+      const uint32_t m = static_cast<uint32_t>(__ballot(wrow[ln & 31] >= 0));
+      if (ln == 0) vmask[t % (kBuffers + 1)] = m;
+    }
     // latent part of row r: its 16-byte slot `ln` holds piece ln ^ f(r)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -342,7 +358,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     }
     if (even) {  // rotary parts of rows 8*blk .. +7: lane l takes row 8*blk + l/8
       const int r = 8 * blk + (ln >> 3);
-      const int sv = ring_idx[t % kBuffers][r];
+      const int sv = wrow[r];
       const uint16_t* src = (sv >= 0 ? kv_seq + static_cast<int64_t>(sv) * kD : g_zero_row) + kDc +
                             8 * ((ln & 7) ^ rope_swz(r));
       lds_dma_16(src, lds_addr(dst.bytes) + kRopeBase + 1024 * blk);
@@ -398,17 +414,30 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       m_ref = m_seen;
     }
     bool overflow = false;
-    for (int t = 0; t < kBuffers - 1 && t < ntiles; ++t) {
-      tile_rows(t);
-      issue_tile(t);
+    if (pass == 1 && ntiles > kWinTiles) {  // the window moved on: back to the first
+      load_window(0);
+      store_window();
+      __syncthreads();
     }
-    if (kBuffers - 1 < ntiles) tile_rows(kBuffers - 1);
+    for (int t = 0; t < kBuffers - 1 && t < ntiles; ++t) issue_tile(t);
+    if (pass == 0) {
+#pragma unroll
+      for (int ks = kQRegSteps; ks < kKSteps; ++ks)
+        *reinterpret_cast<bf16x8_t*>(qlds[ks - kQRegSteps][wave][g][n]) = qs[ks - kQRegSteps];
+#pragma unroll
+      for (int ks = 0; ks < kQRegSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
+    }
     for (int it = 0; it < ntiles; ++it) {
       wait_tiles(min(kBuffers - 2, ntiles - 1 - it));
       __syncthreads();  // every wave's copies of tile `it` are in; tile it-1 is consumed
       if (it + kBuffers - 1 < ntiles) {
-        issue_tile(it + kBuffers - 1);
-        if (it + kBuffers < ntiles) tile_rows(it + kBuffers);
+        const int t = it + kBuffers - 1;
+        if (t % kWinTiles == 0) {  // next index window (splits longer than kIdxWin)
+          load_window(t / kWinTiles);
+          store_window();
+          __syncthreads();
+        }
+        issue_tile(t);
       }
       lds_char_t* cur = (lds_char_t*)(tiles[it % kBuffers].bytes);
       // validity of rows 4g + i (block 0) and 16 + 4g + i (block 1)
@@ -459,8 +488,8 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
           x[mb][i] = ((valid >> (16 * mb + i)) & 1) ? sacc[mb][i] * scale2 : -__builtin_inff();
           tmax = fmaxf(tmax, x[mb][i]);
         }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      tmax = xor16_max(tmax);
+      tmax = xor32_max(tmax);
       m_seen = fmaxf(m_seen, tmax);
       if (m_ref == -__builtin_inff()) m_ref = tmax;  // O and l of this head are still 0
       overflow |= tmax > m_ref + kRefSlack;
@@ -479,8 +508,8 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
         }
         pb = __builtin_bit_cast(bf16x8_t, pw);
       }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
+      psum = xor16_sum(psum);
+      psum = xor32_sum(psum);
       l_run += psum;
 
       // ---- O^T += V^T . P^T ----
