@@ -24,6 +24,8 @@
 //  * mla_combine: merges split partials (o_s, lse_s) with weights
 //    exp(lse_s - lse), deterministically (fixed split order, no atomics).
 //  * mla_generic: any shape, fp32 VALU loops, two passes over the index row.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -118,30 +120,31 @@ mla_generic(int T, int S, int H, int Dc, int Dr, int W, float sm_scale,
 // ---------------------------------------------------------------------------
 // MFMA kernel, H = 128, Dc = 512, Dr = 64, bf16
 //
-// One workgroup of 8 waves (two per SIMD, so one wave's softmax and memory
-// waits overlap the other's MFMAs) takes one query row and one split of its
-// index list; wave w owns heads 16w .. 16w+15.  All 128 heads share each
-// gathered tile of 32 selected key rows.
+// One workgroup of 4 waves (one per SIMD, 512 registers each) takes one query
+// row and one split of its index list; wave w owns heads 32w .. 32w+31 as two
+// groups of 16 (group c: heads 32w + 16c .. +15).  All 128 heads share each
+// gathered tile of 32 selected key rows, and every operand a wave reads from
+// LDS feeds two MFMAs, one per group.
 //
 // MFMA 16x16x32 bf16 operand layouts (lane l, g = l / 16, n = l % 16):
 //   A (16 x 32): lane holds row n, reduction elements 8g .. 8g+7
 //   B (32 x 16): lane holds column n, reduction elements 8g .. 8g+7
 //   C (16 x 16): register i holds row 4g + i of column n
 //
-// logits^T (2 blocks of 16 keys x 16 heads) = K_tile (A, from LDS) . Q^T (B),
-// reduced over the 576 dims in 18 steps of 32; the two key blocks are two
-// independent accumulation chains.  Lane (g, n) ends with head n and keys
-// 4g + i and 16 + 4g + i.
+// logits^T (2 blocks of 16 keys x 16 heads, per group) = K_tile (A, from LDS)
+// . Q^T (B, registers), reduced over the 576 dims in 18 steps of 32: four
+// independent accumulation chains.  Lane (g, n) ends with head n of each
+// group and keys 4g + i and 16 + 4g + i.
 //
-// O^T (512 dims x 16 heads) += V^T (A) . P^T (B), reduced over the 32 keys in
-// one MFMA per 16 dims.  P^T comes straight from the logit accumulators: its
-// B-operand slot 8g + e holds key 4g + e (e < 4) or 16 + 4g + e - 4 (e >= 4).
-// V^T is read from the same row-major key tile with the transposing LDS load
-// ds_read_b64_tr_b16: within a 16-lane group, lane i receives element (i % 4)
-// of the 8-byte chunk loaded by lane 4j + i/4, for j = 0..3.  So lane 4j + c
-// of group g loads dims 16db + 4c .. +3 of tile row 4g + j (+16 for the
-// second half of its slots), and lane i ends up with 4 key slots of dim
-// 16db + i: half of its A operand.
+// O^T (512 dims x 16 heads, per group) += V^T (A) . P^T (B), reduced over the
+// 32 keys in one MFMA per 16 dims.  P^T comes straight from the logit
+// accumulators: its B-operand slot 8g + e holds key 4g + e (e < 4) or
+// 16 + 4g + e - 4 (e >= 4).  V^T is read from the same row-major key tile with
+// the transposing LDS load ds_read_b64_tr_b16: within a 16-lane group, lane i
+// receives element (i % 4) of the 8-byte chunk loaded by lane 4j + i/4, for
+// j = 0..3.  So lane 4j + c of group g loads dims 16db + 4c .. +3 of tile row
+// 4g + j (+16 for the second half of its slots), and lane i ends up with 4 key
+// slots of dim 16db + i: half of its A operand.
 //
 // Key tile in LDS (38 KiB): latent part of row r (64 pieces of 16 B) at byte
 // 1088 r, piece c stored at c ^ f(r), f(r) = bit-reversed (r >> 2) & 3;
@@ -154,31 +157,30 @@ mla_generic(int T, int S, int H, int Dc, int Dr, int W, float sm_scale,
 //
 // The tile is filled by direct global->LDS copies (global_load_lds_dwordx4:
 // lane l of a wave writes 16 B at the wave's LDS base + 16 l): wave w copies
-// the latent parts of rows 4w .. 4w+3 (one 1 KiB run of global memory each),
-// even waves also the rotary parts of rows 4w .. 4w+7.  A ring of 3 tiles
-// keeps the next tile's copies in flight during the current tile's MFMAs.
+// the latent parts of rows 8w .. 8w+7 (one 1 KiB run of global memory each)
+// and the rotary parts of the same rows.  A ring of 4 tiles keeps up to three
+// later tiles' copies in flight during the current tile's MFMAs.
 // ---------------------------------------------------------------------------
 constexpr int kH = 128, kDc = 512, kDr = 64, kD = kDc + kDr;
-constexpr int kMlaWaves = 8;                 // wave w owns heads 16w .. 16w+15
+constexpr int kMlaWaves = 4;                 // wave w owns heads 32w .. 32w+31
 constexpr int kMlaThreads = kMlaWaves * 64;
 constexpr int kTileKeys = 32;
-constexpr int kBuffers = 3;                  // LDS tile ring: 1 tile in flight during compute
+constexpr int kBuffers = 4;                  // LDS tile ring
+constexpr int kCopiesPerTile = 9;            // copies per wave per tile: 8 latent rows + rotary parts
 constexpr int kLatStride = 1088;             // bytes per latent row in LDS (1024 + 64 pad)
 constexpr int kRopeBase = kTileKeys * kLatStride;            // byte offset of the rotary region
 constexpr int kTileBytes = kRopeBase + kTileKeys * kDr * 2;  // 38912
 constexpr int kKSteps = kD / 32;             // 18 logits reduction steps
 constexpr int kLatSteps = kDc / 32;          // 16 of them over the latent part
-// The query operand (18 steps x 8 bf16 per lane) does not all fit in
-// registers next to the 128 fp32 accumulators of O; its last steps live in LDS.
-constexpr int kQLdsSteps = 5;
-constexpr int kQRegSteps = kKSteps - kQLdsSteps;
-constexpr int kReadAhead = 3;                // logits A-operand reads issued ahead of their MFMA
-constexpr int kVAhead = 2;                   // value A-operand (2 reads each) issued ahead
+constexpr int kReadAhead = 6;                // logits A-operand reads issued ahead of their MFMAs
+constexpr int kVAhead = 4;                   // value A operands (2 reads each) issued ahead
 constexpr float kRefSlack = 32.0f;           // log2 units: p <= 2^32 against the reference max
 constexpr int kStageStride = 528;            // epilogue staging row: 256 bf16 + 16 B pad
 constexpr int kIdxWin = 1024;                // index entries staged in LDS at a time
 constexpr int kWinTiles = kIdxWin / kTileKeys;
-constexpr int kWinPerThread = kIdxWin / (kMlaWaves * 64);
+constexpr int kWinPerThread = kIdxWin / kMlaThreads;
+constexpr int kQStageBytes = 32 * kD * 2;    // one wave's query rows, staged in the tile ring
+static_assert(kMlaWaves * kQStageBytes <= kBuffers * kTileBytes, "query staging fits the ring");
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -222,6 +224,15 @@ __device__ __forceinline__ int lat_swz(int r) {  // f(r): bit-reversed (r >> 2) 
 }
 __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 
+// Slot of 16-byte piece p (0..71) within a staged query row of head hq: the
+// latent pieces are XOR-swizzled within aligned groups of 16 by hq & 15, the
+// rotary pieces within their group of 8 by hq & 7 (an involution, so the same
+// function maps slots back to pieces).  16 lanes reading piece p of heads
+// hq .. hq+15 (rows 1152 B apart, i.e. 32 banks apart) then cover all 64 banks.
+__device__ __forceinline__ int qpiece_slot(int p, int hq) {
+  return p < 64 ? ((p & ~15) | ((p ^ hq) & 15)) : (64 | ((p - 64) ^ (hq & 7)));
+}
+
 // Butterfly steps across lane distance 16 and 32 on the VALU (v_permlane16_swap
 // / v_permlane32_swap with both operands the same value: each lane ends with
 // its own value and its partner's, in some order, so any symmetric op works).
@@ -260,12 +271,10 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
          const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse,
          uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(1024))) MlaTile tiles[kBuffers];
-  // query steps kQRegSteps.. : [step][wave][g][head n][8 bf16]
-  __shared__ __attribute__((aligned(16))) uint16_t qlds[kQLdsSteps][kMlaWaves][4][16][8];
   // a window of the split's index entries as key rows (-1: skipped entry)
   __shared__ __attribute__((aligned(16))) int32_t idxw[kIdxWin];
   // validity of each tile's rows (bit r: tile row r holds a valid key), written
-  // when the tile's copies are issued, two iterations before its use
+  // when the tile's copies are issued, kBuffers - 1 iterations before its use
   __shared__ uint32_t vmask[kBuffers + 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -288,7 +297,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   const uint16_t* kv_seq = kv + static_cast<int64_t>(b) * S * kD;
 
   // The split's index entries go through LDS a window at a time: thread i
-  // loads entries i, i + 512 of the window (past the split's end: -1).
+  // loads entries i, i + 256, ... of the window (past the split's end: -1).
   const int32_t* idx_row = idx + row * W;
   const int j_end = j0 + nj;
   int win[kWinPerThread];
@@ -305,74 +314,111 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       idxw[tid + u * kMlaThreads] = (win[u] >= 0 && win[u] < S) ? win[u] : -1;
   };
 
-  // query operand (B of logits^T): head 16*wave + n, dims 32ks + 8g .. +8;
-  // steps < kQRegSteps stay in registers, the rest go to LDS.  The loads are
-  // issued with the first index window and consumed after the first tiles'
-  // copies are on their way, so the three latencies overlap.
-  bf16x8_t qf[kQRegSteps], qs[kQLdsSteps];
+  // Query operand (B of logits^T): qf[c][ks] = head 32w + 16c + n, dims
+  // 32ks + 8g .. +8.  Wave w's 32 heads are one contiguous 36 KiB run of q;
+  // it goes through the (still idle) tile ring with whole-line copies, placed
+  // so that the operand reads are free of bank conflicts: head hq (0..31) at
+  // byte 1152 hq, its 16-byte piece p at slot qpiece_slot(p, hq).  The first
+  // index window loads with it.
+  bf16x8_t qf[2][kKSteps];
   load_window(0);
   {
-    const uint16_t* qh = q + (row * kH + 16 * wave + n) * kD;
-#pragma unroll
-    for (int ks = 0; ks < kQRegSteps; ++ks)
-      qf[ks] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * g);
-#pragma unroll
-    for (int ks = kQRegSteps; ks < kKSteps; ++ks)
-      qs[ks - kQRegSteps] = *reinterpret_cast<const bf16x8_t*>(qh + 32 * ks + 8 * g);
-  }
-  store_window();
-  __syncthreads();
-
-  f32x4_t oacc[kDc / 16];  // O^T: oacc[db][i] = O[head 16*wave + n][16db + 4g + i]
-#pragma unroll
-  for (int db = 0; db < kDc / 16; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -__builtin_inff();  // reference max (log2 units) of head 16*wave + n
-  float l_run = 0.f;
-  const float scale2 = sm_scale * kLog2e;
-
-  // Wave w copies tile rows 4w .. 4w+3 (and, if even, the rotary parts of rows
-  // 4w .. 4w+7), reading their key rows from the index window; wave 0 also
-  // publishes the tile's validity mask.
-  const int blk = wave >> 1;
-  const bool even = (wave & 1) == 0;
-  auto issue_tile = [&](int t) {
-    MlaTile& dst = tiles[t % kBuffers];
-    // an opaque copy of the lane id: the per-copy address math below is redone
-    // at each issue instead of being kept live across the loop in registers
+    const char* qsrc = reinterpret_cast<const char*>(q + (row * kH + 32 * wave) * kD);
+    const uint32_t qlds = lds_addr(tiles) + wave * kQStageBytes;
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
+#pragma unroll 4
+    for (int i = 0; i < kQStageBytes / 1024; ++i) {
+      const int x = 1024 * i + 16 * ln;  // staging byte this lane's copy lands on
+      const int hq = x / (kD * 2), slot = (x - hq * kD * 2) >> 4;
+      lds_dma_16(qsrc + hq * (kD * 2) + 16 * qpiece_slot(slot, hq), qlds + 1024 * i);
+    }
+  }
+  store_window();  // the compiler's wait for the window covers the copies issued after it
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  {
+    lds_char_t* qst = (lds_char_t*)(tiles[0].bytes) + wave * kQStageBytes;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks)
+        qf[c][ks] = *(__attribute__((address_space(3))) const bf16x8_t*)(
+            qst + (16 * c + n) * (kD * 2) + 16 * qpiece_slot(4 * ks + g, 16 * c + n));
+  }
+  __syncthreads();  // the window is published and every wave has its query: the ring is free
+
+  f32x4_t oacc[2][kDc / 16];  // O^T: oacc[c][db][i] = O[head 32w + 16c + n][16db + 4g + i]
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int db = 0; db < kDc / 16; ++db) oacc[c][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};  // reference max (log2 units) per group
+  float l_run[2] = {0.f, 0.f};
+  const float scale2 = sm_scale * kLog2e;
+
+  // Wave w copies tile rows 8w .. 8w+7 (latent and rotary parts), reading
+  // their key rows from the index window; wave 0 also publishes the tile's
+  // validity mask.
+  // Byte offset, from the sequence's first key row, of the zero row that
+  // skipped entries copy: one select per copy instead of a branch.
+  const int64_t zero_off = reinterpret_cast<const char*>(g_zero_row) - reinterpret_cast<const char*>(kv_seq);
+  // A tile's copies: prep_tile reads the wave's 8 key rows from the index
+  // window (two broadcast reads, one LDS round trip) and publishes the tile's
+  // validity mask (wave 0); copy_row(k) then issues copy k of 9 (8 latent
+  // rows, then the rotary parts).  Each lane forms its own source address, so
+  // no value goes through SGPRs.  The main loop spreads the nine copies over
+  // the logits MFMAs, so their issue cost hides under matrix work.
+  struct TileCopies {
+    int sl[8];  // key rows of tile rows 8w .. 8w+7 (-1: skipped)
+    int sr;     // key row of tile row 8w + lane/8 (rotary copy)
+    uint32_t lds;
+  };
+  auto prep_tile = [&](int t) {
+    TileCopies c;
     const int32_t* wrow = &idxw[(t % kWinTiles) * kTileKeys];
-    const int4 s4 = *reinterpret_cast<const int4*>(wrow + 4 * wave);
-    const int sl[4] = {s4.x, s4.y, s4.z, s4.w};
+    const int ln = __lane_id();
     if (wave == 0) {
       const uint32_t m = static_cast<uint32_t>(__ballot(wrow[ln & 31] >= 0));
       if (ln == 0) vmask[t % (kBuffers + 1)] = m;
     }
-    // latent part of row r: its 16-byte slot `ln` holds piece ln ^ f(r)
+    const int4 s4a = *reinterpret_cast<const int4*>(wrow + 8 * wave);
+    const int4 s4b = *reinterpret_cast<const int4*>(wrow + 8 * wave + 4);
+    c.sl[0] = s4a.x; c.sl[1] = s4a.y; c.sl[2] = s4a.z; c.sl[3] = s4a.w;
+    c.sl[4] = s4b.x; c.sl[5] = s4b.y; c.sl[6] = s4b.z; c.sl[7] = s4b.w;
+    c.sr = wrow[8 * wave + (ln >> 3)];
+    c.lds = lds_addr(tiles[t % kBuffers].bytes);
+    return c;
+  };
+  const char* kvb = reinterpret_cast<const char*>(kv_seq);
+  auto copy_row = [&](const TileCopies& c, int k) {
+    // an opaque copy of the lane id: the per-copy address math is redone at
+    // each copy instead of being kept live across the loop in registers
+    int ln = __lane_id();
+    asm volatile("" : "+v"(ln));
+    if (k < 8) {  // latent part of row r: its 16-byte slot `ln` holds piece ln ^ f(r)
+      const int r = 8 * wave + k;
+      const int64_t off = c.sl[k] >= 0 ? static_cast<int64_t>(c.sl[k]) * (kD * 2) : zero_off;
+      lds_dma_16(kvb + off + 16 * (ln ^ lat_swz(r)), c.lds + kLatStride * r);
+    } else {  // rotary parts of rows 8w .. 8w+7: lane l takes row 8w + l/8
+      const int r = 8 * wave + (ln >> 3);
+      const int64_t off = c.sr >= 0 ? static_cast<int64_t>(c.sr) * (kD * 2) : zero_off;
+      lds_dma_16(kvb + off + 2 * kDc + 16 * ((ln & 7) ^ rope_swz(r)), c.lds + kRopeBase + 1024 * wave);
+    }
+  };
+  auto issue_tile = [&](int t) {
+    const TileCopies c = prep_tile(t);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 4 * wave + e;
-      const uint16_t* src =
-          (sl[e] >= 0 ? kv_seq + static_cast<int64_t>(sl[e]) * kD : g_zero_row) + 8 * (ln ^ lat_swz(r));
-      lds_dma_16(src, lds_addr(dst.bytes) + kLatStride * r);
-    }
-    if (even) {  // rotary parts of rows 8*blk .. +7: lane l takes row 8*blk + l/8
-      const int r = 8 * blk + (ln >> 3);
-      const int sv = wrow[r];
-      const uint16_t* src = (sv >= 0 ? kv_seq + static_cast<int64_t>(sv) * kD : g_zero_row) + kDc +
-                            8 * ((ln & 7) ^ rope_swz(r));
-      lds_dma_16(src, lds_addr(dst.bytes) + kRopeBase + 1024 * blk);
-    }
+    for (int k = 0; k < kCopiesPerTile; ++k) copy_row(c, k);
   };
   // wait until at most `pending` later tiles' copies of this wave are in flight
   auto wait_tiles = [&](int pending) {
-    static_assert(kBuffers == 3, "vmcnt immediates assume one later tile in flight");
-    if (pending == 0)
+    static_assert(kBuffers == 4 && kCopiesPerTile == 9, "vmcnt immediates");
+    if (pending <= 0)
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (even)
-      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else if (pending == 1)
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     else
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
   };
 
   // LDS byte offsets.  Logits A operand of step ks for key block mb: row
@@ -405,13 +451,16 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   // (never for sane data), the whole split is run once more with the true
   // maximum as reference, so O is only ever zeroed, never rescaled.  The
   // decision is workgroup-uniform (barriers stay matched).
-  float m_seen = -__builtin_inff();
+  float m_seen[2] = {-__builtin_inff(), -__builtin_inff()};
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
 #pragma unroll
-      for (int db = 0; db < kDc / 16; ++db) oacc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      l_run = 0.f;
-      m_ref = m_seen;
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int db = 0; db < kDc / 16; ++db) oacc[c][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        l_run[c] = 0.f;
+        m_ref[c] = m_seen[c];
+      }
     }
     bool overflow = false;
     if (pass == 1 && ntiles > kWinTiles) {  // the window moved on: back to the first
@@ -420,83 +469,74 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       __syncthreads();
     }
     for (int t = 0; t < kBuffers - 1 && t < ntiles; ++t) issue_tile(t);
-    if (pass == 0) {
-#pragma unroll
-      for (int ks = kQRegSteps; ks < kKSteps; ++ks)
-        *reinterpret_cast<bf16x8_t*>(qlds[ks - kQRegSteps][wave][g][n]) = qs[ks - kQRegSteps];
-#pragma unroll
-      for (int ks = 0; ks < kQRegSteps; ++ks) asm volatile("" : "+v"(qf[ks]));
-    }
     for (int it = 0; it < ntiles; ++it) {
       wait_tiles(min(kBuffers - 2, ntiles - 1 - it));
       __syncthreads();  // every wave's copies of tile `it` are in; tile it-1 is consumed
-      if (it + kBuffers - 1 < ntiles) {
+      const bool copies = it + kBuffers - 1 < ntiles;
+      TileCopies nxt;
+      if (copies) {
         const int t = it + kBuffers - 1;
         if (t % kWinTiles == 0) {  // next index window (splits longer than kIdxWin)
           load_window(t / kWinTiles);
           store_window();
           __syncthreads();
         }
-        issue_tile(t);
+        nxt = prep_tile(t);
       }
       lds_char_t* cur = (lds_char_t*)(tiles[it % kBuffers].bytes);
       // validity of rows 4g + i (block 0) and 16 + 4g + i (block 1)
       const uint32_t valid = vmask[it % (kBuffers + 1)] >> (4 * g);
 
-      // ---- logits^T: 2 blocks of 16 keys x 16 heads, interleaved chains ----
-      f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      // ---- logits^T: 2 key blocks x 2 head groups, four chains ----
+      f32x4_t sacc[2][2];  // [mb][c]
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) sacc[mb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
-        // software pipeline over the 36 (ks, mb) steps: the LDS reads of step
-        // st + kReadAhead are issued with the MFMA of step st
+        // software pipeline over the 36 (ks, mb) key-tile reads: the read of
+        // step st + kReadAhead is issued with the two MFMAs of step st
         constexpr int kSteps = 2 * kKSteps;
         auto aload = [&](int st) {
           const int ks = st >> 1, mb = st & 1;
           const int off = ks < kLatSteps ? aoff[mb] + 64 * ks : roff[mb][ks - kLatSteps];
           return *(__attribute__((address_space(3))) const bf16x8_t*)(cur + off);
         };
-        auto qload = [&](int ks) {
-          return *reinterpret_cast<const bf16x8_t*>(qlds[ks - kQRegSteps][wave][g][n]);
-        };
-        // the LDS query step ks lives in qb[ks % 3], loaded with the first step
-        // (2ks) of its read-ahead window; its last use, step 2ks + 1, comes
-        // before slot ks % 3 is reloaded for ks + 3 as long as kReadAhead <= 5
-        static_assert(kReadAhead <= 5, "query ring of 3 slots");
-        bf16x8_t ka[kReadAhead], qb[3];
-        auto issue = [&](int nx) {
-          ka[nx % kReadAhead] = aload(nx);
-          if ((nx & 1) == 0 && (nx >> 1) >= kQRegSteps) qb[(nx >> 1) % 3] = qload(nx >> 1);
-        };
+        bf16x8_t ka[kReadAhead];
 #pragma unroll
-        for (int st = 0; st < kReadAhead; ++st) issue(st);
+        for (int st = 0; st < kReadAhead; ++st) ka[st] = aload(st);
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
           const int ks = st >> 1, mb = st & 1;
-          sacc[mb] = mfma16x16x32_bf16(ka[st % kReadAhead], ks < kQRegSteps ? qf[ks] : qb[ks % 3],
-                                       sacc[mb]);
-          if (st + kReadAhead < kSteps) issue(st + kReadAhead);
+          sacc[mb][0] = mfma16x16x32_bf16(ka[st % kReadAhead], qf[0][ks], sacc[mb][0]);
+          sacc[mb][1] = mfma16x16x32_bf16(ka[st % kReadAhead], qf[1][ks], sacc[mb][1]);
+          if (st + kReadAhead < kSteps) ka[st % kReadAhead] = aload(st + kReadAhead);
+          // copy k of the tile kBuffers - 1 ahead goes out with step 4k + 1
+          if (st % 4 == 1 && st / 4 < kCopiesPerTile && copies) copy_row(nxt, st / 4);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
 
-      // ---- softmax weights (lane: head n; keys 16mb + 4g + i) ----
-      float x[2][4];
-      float tmax = -__builtin_inff();
+      // ---- softmax weights (lane: head n of each group; keys 16mb + 4g + i) ----
+      bf16x8_t pb[2];  // B operands of the value product: slot 8g + e
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int c = 0; c < 2; ++c) {
+        float x[2][4];
+        float tmax = -__builtin_inff();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[mb][i] = ((valid >> (16 * mb + i)) & 1) ? sacc[mb][i] * scale2 : -__builtin_inff();
-          tmax = fmaxf(tmax, x[mb][i]);
-        }
-      tmax = xor16_max(tmax);
-      tmax = xor32_max(tmax);
-      m_seen = fmaxf(m_seen, tmax);
-      if (m_ref == -__builtin_inff()) m_ref = tmax;  // O and l of this head are still 0
-      overflow |= tmax > m_ref + kRefSlack;
-      const float m_use = (m_ref == -__builtin_inff()) ? 0.f : m_ref;
-      float psum = 0.f;
-      bf16x8_t pb;  // B operand of the value product: slot 8g + e
-      {
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[mb][i] = ((valid >> (16 * mb + i)) & 1) ? sacc[mb][c][i] * scale2 : -__builtin_inff();
+            tmax = fmaxf(tmax, x[mb][i]);
+          }
+        tmax = xor16_max(tmax);
+        tmax = xor32_max(tmax);
+        m_seen[c] = fmaxf(m_seen[c], tmax);
+        if (m_ref[c] == -__builtin_inff()) m_ref[c] = tmax;  // O and l of this head are still 0
+        overflow |= tmax > m_ref[c] + kRefSlack;
+        const float m_use = (m_ref[c] == -__builtin_inff()) ? 0.f : m_ref[c];
+        float psum = 0.f;
         u32x4_t pw;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -506,13 +546,13 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
           psum += p0 + p1;
           pw[e >> 1] = f32x2_to_bf16x2(p0, p1);
         }
-        pb = __builtin_bit_cast(bf16x8_t, pw);
+        pb[c] = __builtin_bit_cast(bf16x8_t, pw);
+        psum = xor16_sum(psum);
+        psum = xor32_sum(psum);
+        l_run[c] += psum;
       }
-      psum = xor16_sum(psum);
-      psum = xor32_sum(psum);
-      l_run += psum;
 
-      // ---- O^T += V^T . P^T ----
+      // ---- O^T += V^T . P^T, both groups per V^T operand ----
       {
         // ds_read_b64_tr_b16 takes no folded offset: an opaque per-tile copy of
         // the bases keeps each read's address add next to the read
@@ -535,7 +575,8 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
         for (int db = 0; db < kVAhead; ++db) va[db] = vload(db);
 #pragma unroll
         for (int db = 0; db < kDc / 16; ++db) {
-          oacc[db] = mfma16x16x32_bf16(va[db % kVAhead], pb, oacc[db]);
+          oacc[0][db] = mfma16x16x32_bf16(va[db % kVAhead], pb[0], oacc[0][db]);
+          oacc[1][db] = mfma16x16x32_bf16(va[db % kVAhead], pb[1], oacc[1][db]);
           if (db + kVAhead < kDc / 16) va[db % kVAhead] = vload(db + kVAhead);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -547,32 +588,39 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   }
 
   // ---- epilogue: normalise, stage [head][dims] through LDS, coalesced stores ----
-  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-  const float lse_h = l_run > 0.f ? (m_ref + __log2f(l_run)) * kLn2 : -__builtin_inff();
-  const int h = 16 * wave + n;
   uint16_t* dst = nsplit == 1 ? o + row * kH * kDc : part_o + (row * nsplit + sp) * kH * kDc;
   char* stage = reinterpret_cast<char*>(tiles[0].bytes);  // 128 rows x 528 B (the ring is idle)
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();  // the ring / the previous half of the staging is free
 #pragma unroll
-    for (int dq = 0; dq < kDc / 32; ++dq) {
-      const f32x4_t& a = oacc[16 * half + dq];
-      const u32x2_t v = {f32x2_to_bf16x2(a[0] * inv_l, a[1] * inv_l),
-                         f32x2_to_bf16x2(a[2] * inv_l, a[3] * inv_l)};
-      *reinterpret_cast<u32x2_t*>(stage + kStageStride * h + 2 * (16 * dq + 4 * g)) = v;
+    for (int c = 0; c < 2; ++c) {
+      const float inv_l = l_run[c] > 0.f ? 1.f / l_run[c] : 0.f;
+      const int h = 32 * wave + 16 * c + n;
+#pragma unroll
+      for (int dq = 0; dq < kDc / 32; ++dq) {
+        const f32x4_t& a = oacc[c][16 * half + dq];
+        const u32x2_t v = {f32x2_to_bf16x2(a[0] * inv_l, a[1] * inv_l),
+                           f32x2_to_bf16x2(a[2] * inv_l, a[3] * inv_l)};
+        *reinterpret_cast<u32x2_t*>(stage + kStageStride * h + 2 * (16 * dq + 4 * g)) = v;
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < (kH * kDc / 2 * 2) / (16 * kMlaThreads); ++k) {  // 8 x 16 B per thread
-      const int c = tid + kMlaThreads * k;  // 16-byte chunk: head c / 32, part c % 32
-      const int hh = c >> 5, part = c & 31;
+    for (int k = 0; k < (kH * kDc / 2 * 2) / (16 * kMlaThreads); ++k) {  // 16 x 16 B per thread
+      const int cidx = tid + kMlaThreads * k;  // 16-byte chunk: head cidx / 32, part cidx % 32
+      const int hh = cidx >> 5, part = cidx & 31;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + kStageStride * hh + 16 * part);
       *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(dst + hh * kDc) + 512 * half + 16 * part) = v;
     }
   }
   float* dst_lse = nsplit == 1 ? (lse ? lse + row * kH : nullptr) : part_lse + (row * nsplit + sp) * kH;
-  if (dst_lse != nullptr && g == 0) dst_lse[h] = lse_h;
+  if (dst_lse != nullptr && g == 0) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      dst_lse[32 * wave + 16 * c + n] =
+          l_run[c] > 0.f ? (m_ref[c] + __log2f(l_run[c])) * kLn2 : -__builtin_inff();
+  }
 }
 
 // Merge of the split partials: thread = 8 consecutive latent dims of one head.
