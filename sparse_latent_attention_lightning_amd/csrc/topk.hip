@@ -9,10 +9,13 @@
 // One 1024-thread workgroup selects from up to 32768 elements held in
 // registers (thread i owns a contiguous run of E elements, so the output is
 // compacted in index order by a block-wide prefix sum).  The K-th largest key
-// is found exactly by a 3-pass radix select over the order-preserving 32-bit
-// key (12 + 10 + 10 bits, MSB first) with LDS histograms; the first pass uses
-// 12 bits (sign, exponent and 3 mantissa bits) so that score distributions
-// concentrated in a few binades still spread over many bins.
+// is found exactly by a radix select over the order-preserving 32-bit key
+// (12 + 10 + 10 bits, MSB first) with LDS histograms; the first pass uses 12
+// bits (sign, exponent and 3 mantissa bits) so that score distributions
+// concentrated in a few binades still spread over many bins.  As soon as the
+// bin holding the K-th key has at most 16 elements, those are ranked
+// directly (by key, then index) instead of running the remaining passes; the
+// count of selectable keys comes from the first histogram.
 //
 // Rows longer than one workgroup's capacity are reduced in two stages: each
 // chunk of the row yields its own exact top-K candidates (key, index), in
@@ -28,43 +31,74 @@ namespace {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 constexpr int kChunkElems = 32 * kTopkThreads;  // stage-1 chunk (E = 32)
+constexpr int kPass1Bins = 4096;                 // 12 bits
+constexpr int kPassBins = 1024;                  // 10 bits (passes 2 and 3)
+constexpr int kSmallCand = 16;                   // boundary bins this small are ranked by one wave
 
-struct BlockScanLds {
-  uint32_t wave_tot[kTopkWaves];
+struct TopkLds {
+  uint32_t hist[2][kPass1Bins];     // ping-pong: pass p counts into hist[p & 1]
+  uint32_t wave_tot[2][kTopkWaves];  // ping-pong scan scratch
+  uint32_t sel[3][2];                // per pass: boundary bin, count above it
+  uint32_t cand_key[kSmallCand];
+  int32_t cand_idx[kSmallCand];
+  uint32_t cand_take[kSmallCand];
+  uint32_t total;
+  uint32_t ncand;
 };
 
-// Exclusive prefix sum over the workgroup in thread order; returns the sum of
-// the values of all lower threads and sets *total.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, BlockScanLds& lds,
+// Exclusive prefix sum over the workgroup in thread order: the sum of the
+// values of all lower threads; *total gets the sum over all threads.  One
+// barrier; `wave_tot` must not be reused before the next barrier.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wave_tot,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_inclusive_scan(v);
-  if (lane == 63) lds.wave_tot[wave] = inc;
+  if (lane == 63) wave_tot[wave] = inc;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < kTopkWaves; ++i) {
-    const uint32_t t = lds.wave_tot[i];
+    const uint32_t t = wave_tot[i];
     before += (i < wave) ? t : 0u;
     tot += t;
   }
-  __syncthreads();  // wave_tot is reused by the next scan
   *total = tot;
   return before + inc - v;
 }
 
+// Bins [nb - (t+1)*per, nb - t*per) belong to thread t (scanned from the top):
+// find the bin where the running count from the top reaches k_rem; the owner
+// thread records it and the count above it in sel.  Returns the histogram's
+// total (no bin is recorded when it is below k_rem).
+__device__ __forceinline__ uint32_t find_boundary(const uint32_t* hist, int nb, uint32_t k_rem,
+                                                  uint32_t* wave_tot, uint32_t* sel) {
+  const int per = nb / kTopkThreads;
+  const int hi_bin = nb - static_cast<int>(threadIdx.x) * per;  // exclusive
+  uint32_t local = 0;
+  for (int k = 1; k <= per; ++k) local += hist[hi_bin - k];
+  uint32_t tot;
+  uint32_t acc = block_exclusive_scan(local, wave_tot, &tot);
+  for (int k = 1; k <= per; ++k) {
+    const uint32_t c = hist[hi_bin - k];
+    if (acc < k_rem && k_rem <= acc + c) {
+      sel[0] = static_cast<uint32_t>(hi_bin - k);
+      sel[1] = acc;
+    }
+    acc += c;
+  }
+  return tot;
+}
+
 // SRC_CAND: elements come from a candidate list (key, index) instead of fp32
 // scores.  OUT_CAND: the result is a candidate list (key and index written).
-template <int E, bool SRC_CAND, bool OUT_CAND>
+// VEC: every thread's run of E inputs starts 16-byte aligned (16-byte loads).
+template <int E, bool SRC_CAND, bool OUT_CAND, bool VEC>
 __global__ void __launch_bounds__(kTopkThreads)
 topk_select(int n_in, int64_t in_stride, int chunk_elems,
             const float* __restrict__ scores, const uint32_t* __restrict__ cand_key_in,
             const int32_t* __restrict__ cand_idx_in, int K_out, int32_t* __restrict__ idx_out,
             uint32_t* __restrict__ cand_key_out) {
-  __shared__ uint32_t hist[4096];
-  __shared__ BlockScanLds scan_lds;
-  __shared__ uint32_t sel_bin, sel_above;
-
+  __shared__ TopkLds lds;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -74,97 +108,160 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
   const int64_t in_base = row * in_stride + elem0;
   const int64_t out_base = (row * gridDim.x + chunk) * static_cast<int64_t>(K_out);
 
+  // ---- thread t owns elements [E t, E t + E): keys in registers ----
   uint32_t key[E];
   int32_t id[E];
+  const int i0 = tid * E;
+  if (VEC && i0 + E <= n) {
 #pragma unroll
-  for (int j = 0; j < E; ++j) {
-    const int i = tid * E + j;
-    if (i < n) {
+    for (int j = 0; j < E; j += 4) {
       if constexpr (SRC_CAND) {
-        key[j] = cand_key_in[in_base + i];
-        id[j] = cand_idx_in[in_base + i];
+        const uint4 k4 = *reinterpret_cast<const uint4*>(cand_key_in + in_base + i0 + j);
+        const int4 d4 = *reinterpret_cast<const int4*>(cand_idx_in + in_base + i0 + j);
+        key[j] = k4.x; key[j + 1] = k4.y; key[j + 2] = k4.z; key[j + 3] = k4.w;
+        id[j] = d4.x; id[j + 1] = d4.y; id[j + 2] = d4.z; id[j + 3] = d4.w;
       } else {
-        key[j] = score_key(scores[in_base + i]);
-        id[j] = elem0 + i;
+        const float4 f4 = *reinterpret_cast<const float4*>(scores + in_base + i0 + j);
+        key[j] = score_key(f4.x); key[j + 1] = score_key(f4.y);
+        key[j + 2] = score_key(f4.z); key[j + 3] = score_key(f4.w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) id[j + e] = elem0 + i0 + j + e;
       }
-    } else {
-      key[j] = 0u;
-      id[j] = -1;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = i0 + j;
+      if (i < n) {
+        if constexpr (SRC_CAND) {
+          key[j] = cand_key_in[in_base + i];
+          id[j] = cand_idx_in[in_base + i];
+        } else {
+          key[j] = score_key(scores[in_base + i]);
+          id[j] = elem0 + i;
+        }
+      } else {
+        key[j] = 0u;
+        id[j] = -1;
+      }
+    }
+  }
+  // clear both histograms while the loads are in flight
+  for (int i = tid; i < 2 * kPass1Bins; i += kTopkThreads) (&lds.hist[0][0])[i] = 0u;
+  if (tid == 0) lds.ncand = 0u;
+  __syncthreads();
+
+  // ---- pass 1: 12-bit histogram of the selectable keys (key 0 is not) ----
+#pragma unroll
+  for (int j = 0; j < E; ++j)
+    if (key[j] != 0u) atomicAdd(&lds.hist[0][key[j] >> 20], 1u);
+  __syncthreads();
+  // the boundary bin of the K-th largest key; the total is the count of
+  // selectable keys
+  const uint32_t nvalid =
+      find_boundary(lds.hist[0], kPass1Bins, static_cast<uint32_t>(K_out), lds.wave_tot[0], lds.sel[0]);
+  __syncthreads();
+  const uint32_t ksel = min(static_cast<uint32_t>(K_out), nvalid);
+
+  // Selection rule, set below: keys > thr_hi are taken; keys with
+  // (key & mask) == prefix are the boundary candidates, of which k_rem are
+  // taken (by larger key, then lower index).
+  uint32_t prefix = 0u, mask = 0u, k_rem = ksel;
+  uint32_t cnt = 0u;  // candidates in the boundary bin
+  bool all = nvalid <= static_cast<uint32_t>(K_out);
+  if (!all) {
+    prefix = lds.sel[0][0] << 20;
+    mask = 0xfff00000u;
+    k_rem -= lds.sel[0][1];
+    cnt = lds.hist[0][lds.sel[0][0]];
+    constexpr int kShift[2] = {10, 0};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (cnt <= kSmallCand) break;  // workgroup-uniform
+      uint32_t* h = lds.hist[(p + 1) & 1];
+      if (p == 1)  // hist[0] is free again once pass 2's boundary is known
+        for (int i = tid; i < kPassBins; i += kTopkThreads) h[i] = 0u;
+      if (p == 1) __syncthreads();
+#pragma unroll
+      for (int j = 0; j < E; ++j)
+        if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> kShift[p]) & (kPassBins - 1)], 1u);
+      __syncthreads();
+      (void)find_boundary(h, kPassBins, k_rem, lds.wave_tot[(p + 1) & 1], lds.sel[p + 1]);
+      __syncthreads();
+      const uint32_t bin = lds.sel[p + 1][0];
+      prefix |= bin << kShift[p];
+      mask |= static_cast<uint32_t>(kPassBins - 1) << kShift[p];
+      k_rem -= lds.sel[p + 1][1];
+      cnt = h[bin];
     }
   }
 
-  // ---- how many selectable elements, and how many to take ----
-  uint32_t nvalid_local = 0;
+  // ---- decide which elements are taken ----
+  uint32_t take = 0;  // bit j: element j of this thread is taken
+  // the compaction scan's scratch: the one not read since the last barrier
+  uint32_t* cscan = lds.wave_tot[1];
+  if (all) {
 #pragma unroll
-  for (int j = 0; j < E; ++j) nvalid_local += key[j] != 0u;
-  uint32_t nvalid;
-  (void)block_exclusive_scan(nvalid_local, scan_lds, &nvalid);
-
-  uint32_t thr = 0u;      // keys > thr are taken ...
-  uint32_t take_eq = 0u;  // ... and the first take_eq keys == thr (by index)
-  const uint32_t ksel = min(static_cast<uint32_t>(K_out), nvalid);
-  if (nvalid > static_cast<uint32_t>(K_out)) {
-    uint32_t prefix = 0u, mask = 0u, k_rem = ksel;
-    constexpr int kShift[3] = {20, 10, 0};
-    constexpr int kBits[3] = {12, 10, 10};
+    for (int j = 0; j < E; ++j) take |= static_cast<uint32_t>(key[j] != 0u) << j;
+  } else if (cnt <= kSmallCand) {
+    // rank the few boundary candidates directly
+    int slot[E];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const int shift = kShift[p], nb = 1 << kBits[p];
-      for (int i = tid; i < nb; i += kTopkThreads) hist[i] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < E; ++j)
-        if (key[j] != 0u && (key[j] & mask) == prefix)
-          atomicAdd(&hist[(key[j] >> shift) & (nb - 1)], 1u);
-      __syncthreads();
-      // thread t owns bins [nb - (t+1)*per, nb - t*per), scanned from the top
-      const int per = (nb + kTopkThreads - 1) / kTopkThreads;
-      const int hi_bin = nb - tid * per;  // exclusive
-      uint32_t local = 0;
-      for (int k = 1; k <= per; ++k)
-        if (hi_bin - k >= 0) local += hist[hi_bin - k];
-      uint32_t tot;
-      uint32_t acc = block_exclusive_scan(local, scan_lds, &tot);
-      for (int k = 1; k <= per; ++k) {
-        const int bin = hi_bin - k;
-        if (bin < 0) break;
-        const uint32_t c = hist[bin];
-        if (acc < k_rem && k_rem <= acc + c) {
-          sel_bin = static_cast<uint32_t>(bin);
-          sel_above = acc;
-        }
-        acc += c;
+    for (int j = 0; j < E; ++j) {
+      slot[j] = -1;
+      if (key[j] != 0u && (key[j] & mask) == prefix) {
+        const uint32_t s = atomicAdd(&lds.ncand, 1u);
+        lds.cand_key[s] = key[j];
+        lds.cand_idx[s] = id[j];
+        slot[j] = static_cast<int>(s);
       }
-      __syncthreads();
-      prefix |= sel_bin << shift;
-      mask |= static_cast<uint32_t>(nb - 1) << shift;
-      k_rem -= sel_above;
-      __syncthreads();  // sel_bin / hist reused by the next pass
     }
-    thr = prefix;
-    take_eq = k_rem;
+    __syncthreads();
+    if (tid < 64) {  // wave 0: lane i holds candidate i; the others come by readlane
+      const bool have = tid < static_cast<int>(cnt);
+      const uint32_t mk = have ? lds.cand_key[tid] : 0u;
+      const int32_t mi = have ? lds.cand_idx[tid] : 0;
+      uint32_t rank = 0;
+      for (uint32_t u = 0; u < cnt; ++u) {
+        const uint32_t uk = __builtin_amdgcn_readlane(mk, u);
+        const int32_t ui = __builtin_amdgcn_readlane(mi, u);
+        rank += (uk > mk || (uk == mk && ui < mi)) ? 1u : 0u;
+      }
+      if (have) lds.cand_take[tid] = rank < k_rem;
+    }
+    __syncthreads();
+    const uint32_t thr_hi = prefix | ~mask;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const bool t = key[j] > thr_hi || (slot[j] >= 0 && lds.cand_take[slot[j]] != 0u);
+      take |= static_cast<uint32_t>(t) << j;
+    }
+  } else {
+    // three full passes: prefix is the exact boundary key; the first k_rem of
+    // its equal keys (in index order) are taken
+    uint32_t n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) n_eq += key[j] == prefix;
+    uint32_t tot;
+    uint32_t eq_before = block_exclusive_scan(n_eq, lds.wave_tot[1], &tot);
+    cscan = lds.wave_tot[0];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      bool t = key[j] > prefix;
+      if (key[j] == prefix) {
+        t = eq_before < k_rem;
+        ++eq_before;
+      }
+      take |= static_cast<uint32_t>(t) << j;
+    }
   }
 
   // ---- compaction in index order ----
-  uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int j = 0; j < E; ++j) {
-    n_gt += key[j] > thr;
-    n_eq += (key[j] == thr) && (thr != 0u);
-  }
   uint32_t tot;
-  const uint32_t packed_before = block_exclusive_scan((n_gt << 16) | n_eq, scan_lds, &tot);
-  uint32_t eq_before = packed_before & 0xffffu;
-  const uint32_t gt_before = packed_before >> 16;
-  uint32_t pos = gt_before + min(eq_before, take_eq);
+  uint32_t pos = block_exclusive_scan(__builtin_popcount(take), cscan, &tot);
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    bool take = key[j] > thr;
-    if (key[j] == thr && thr != 0u) {
-      take = eq_before < take_eq;
-      ++eq_before;
-    }
-    if (take && pos < static_cast<uint32_t>(K_out)) {  // pos < ksel <= K_out by construction
+    if (((take >> j) & 1u) && pos < static_cast<uint32_t>(K_out)) {  // pos < ksel <= K_out by construction
       idx_out[out_base + pos] = id[j];
       if constexpr (OUT_CAND) cand_key_out[out_base + pos] = key[j];
       ++pos;
@@ -177,17 +274,22 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
 }
 
 template <bool SRC_CAND, bool OUT_CAND>
-dsa_status_t run_select(int per_wg, dim3 grid, int n_in, int64_t in_stride, int chunk_elems,
-                        const float* scores, const uint32_t* ck_in, const int32_t* ci_in,
-                        int K_out, int32_t* idx_out, uint32_t* ck_out, hipStream_t stream) {
-#define DSA_TOPK_LAUNCH(EV)                                                               \
-  hipExtLaunchKernelGGL(topk_select<EV, SRC_CAND, OUT_CAND>, grid, dim3(kTopkThreads), 0, stream, \
-                        timer.start(), timer.stop(), 0, n_in, in_stride, chunk_elems, scores,     \
-                        ck_in, ci_in, K_out, idx_out, ck_out)
+dsa_status_t run_select(int per_wg, bool vec, dim3 grid, int n_in, int64_t in_stride,
+                        int chunk_elems, const float* scores, const uint32_t* ck_in,
+                        const int32_t* ci_in, int K_out, int32_t* idx_out, uint32_t* ck_out,
+                        hipStream_t stream) {
   LaunchTimer timer;
-  if (per_wg <= 8 * kTopkThreads) DSA_TOPK_LAUNCH(8);
-  else if (per_wg <= 16 * kTopkThreads) DSA_TOPK_LAUNCH(16);
-  else DSA_TOPK_LAUNCH(32);
+#define DSA_TOPK_LAUNCH(EV, VEC)                                                                \
+  hipExtLaunchKernelGGL(topk_select<EV, SRC_CAND, OUT_CAND, VEC>, grid, dim3(kTopkThreads), 0,  \
+                        stream, timer.start(), timer.stop(), 0, n_in, in_stride, chunk_elems,   \
+                        scores, ck_in, ci_in, K_out, idx_out, ck_out)
+  if (per_wg <= 8 * kTopkThreads) {
+    if (vec) DSA_TOPK_LAUNCH(8, true); else DSA_TOPK_LAUNCH(8, false);
+  } else if (per_wg <= 16 * kTopkThreads) {
+    if (vec) DSA_TOPK_LAUNCH(16, true); else DSA_TOPK_LAUNCH(16, false);
+  } else {
+    if (vec) DSA_TOPK_LAUNCH(32, true); else DSA_TOPK_LAUNCH(32, false);
+  }
 #undef DSA_TOPK_LAUNCH
   return timer.done(SRC_CAND ? "topk_merge" : OUT_CAND ? "topk_chunk" : "topk_select");
 }
@@ -224,8 +326,8 @@ dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx
   const int K = k_eff(s);
   const TopkPlan p = plan(s);
   if (p.chunks == 1) {
-    return run_select<false, false>(s.S, dim3(1, rows), s.S, s.S, s.S, scores, nullptr, nullptr,
-                                    K, idx, nullptr, stream);
+    return run_select<false, false>(s.S, s.S % 4 == 0, dim3(1, rows), s.S, s.S, s.S, scores,
+                                    nullptr, nullptr, K, idx, nullptr, stream);
   }
   const int64_t n2 = static_cast<int64_t>(p.chunks) * K;
   if (n2 > kChunkElems || K >= p.chunk_elems)
@@ -235,13 +337,13 @@ dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx
     return fail(DSA_ERR_WORKSPACE, "topk: workspace of %zu bytes needed, %zu given", need, ws_bytes);
   int32_t* cand_idx = static_cast<int32_t*>(ws);
   uint32_t* cand_key = reinterpret_cast<uint32_t*>(cand_idx + rows * n2);
-  dsa_status_t st = run_select<false, true>(p.chunk_elems, dim3(p.chunks, rows), s.S, s.S,
-                                            p.chunk_elems, scores, nullptr, nullptr, K, cand_idx,
-                                            cand_key, stream);
+  dsa_status_t st = run_select<false, true>(p.chunk_elems, s.S % 4 == 0, dim3(p.chunks, rows), s.S,
+                                            s.S, p.chunk_elems, scores, nullptr, nullptr, K,
+                                            cand_idx, cand_key, stream);
   if (st != DSA_OK) return st;
-  return run_select<true, false>(static_cast<int>(n2), dim3(1, rows), static_cast<int>(n2), n2,
-                                 static_cast<int>(n2), nullptr, cand_key, cand_idx, K, idx,
-                                 nullptr, stream);
+  return run_select<true, false>(static_cast<int>(n2), n2 % 4 == 0, dim3(1, rows),
+                                 static_cast<int>(n2), n2, static_cast<int>(n2), nullptr, cand_key,
+                                 cand_idx, K, idx, nullptr, stream);
 }
 
 }  // namespace dsa
