@@ -264,7 +264,7 @@ __device__ __forceinline__ short4_t lds_read_tr16(lds_char_t* p) {
 // 147 KB query block is fetched once into that XCD's L2.
 // nsplit == 1: writes o (bf16) and lse directly; otherwise writes bf16
 // partials part_o [rows, nsplit, H, Dc] (already divided by the split's own
-// sum) and part_lse [rows, nsplit, H] (natural log; -inf for an empty split).
+// sum) and part_lse [rows, H, nsplit] (natural log; -inf for an empty split).
 __global__ void __launch_bounds__(kMlaThreads, 1)
 mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
          const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -614,41 +614,45 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(dst + hh * kDc) + 512 * half + 16 * part) = v;
     }
   }
-  float* dst_lse = nsplit == 1 ? (lse ? lse + row * kH : nullptr) : part_lse + (row * nsplit + sp) * kH;
-  if (dst_lse != nullptr && g == 0) {
+  if (g == 0) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-      dst_lse[32 * wave + 16 * c + n] =
-          l_run[c] > 0.f ? (m_ref[c] + __log2f(l_run[c])) * kLn2 : -__builtin_inff();
+    for (int c = 0; c < 2; ++c) {
+      const int h = 32 * wave + 16 * c + n;
+      const float v = l_run[c] > 0.f ? (m_ref[c] + __log2f(l_run[c])) * kLn2 : -__builtin_inff();
+      if (nsplit > 1)
+        part_lse[(row * kH + h) * nsplit + sp] = v;
+      else if (lse != nullptr)
+        lse[row * kH + h] = v;
+    }
   }
 }
 
-// Merge of the split partials: thread = 8 consecutive latent dims of one head.
-// lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.  Fixed split
-// order, no atomics: deterministic.
-template <int DT>
+// Merge of the split partials: one wave per (query row, head), lane l covers
+// latent dims 8l .. 8l+7 (Dc = 512).  lse = log sum_s exp(lse_s);
+// o = sum_s exp(lse_s - lse) o_s.  Fixed split order, no atomics:
+// deterministic.  The wave's split lse values are one contiguous run, read
+// through the scalar cache.
 __global__ void __launch_bounds__(256)
-mla_combine(int H, int Dc, int nsplit, int64_t total_vec, const uint16_t* __restrict__ part_o,
-            const float* __restrict__ part_lse, void* __restrict__ o, float* __restrict__ lse) {
-  const int64_t v = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // 8-dim vector id
-  if (v >= total_vec) return;
-  const int per_row = H * Dc / 8;
-  const int64_t row = v / per_row;
-  const int rem = static_cast<int>(v % per_row);
-  const int h = rem / (Dc / 8), d0 = (rem % (Dc / 8)) * 8;
-  const float* ls_row = part_lse + row * nsplit * H + h;
+mla_combine(int nsplit, int64_t total_heads, const uint16_t* __restrict__ part_o,
+            const float* __restrict__ part_lse, uint16_t* __restrict__ o, float* __restrict__ lse) {
+  const int64_t rh = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));  // row * H + head
+  if (rh >= total_heads) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = rh / kH;
+  const int h = static_cast<int>(rh - row * kH);
+  const float* ls = part_lse + rh * nsplit;
   float m = -__builtin_inff();
-  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, ls_row[sp * H]);
+  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, ls[sp]);
   const float m_use = m == -__builtin_inff() ? 0.f : m;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  const uint16_t* po = part_o + (row * nsplit * H + h) * Dc + d0;
-  // every split's partial is written (an empty split holds zeros with weight 0),
-  // so all loads are issued unconditionally
-#pragma unroll 4
+  const uint16_t* po = part_o + (row * nsplit * kH + h) * kDc + 8 * lane;
+  // every split's partial is written (an empty split holds zeros with weight
+  // 0), so all loads are issued unconditionally
+#pragma unroll 8
   for (int sp = 0; sp < nsplit; ++sp) {
-    const float wgt = __expf(ls_row[sp * H] - m_use);  // exp(-inf) = 0
-    const u32x4_t pv = *reinterpret_cast<const u32x4_t*>(po + static_cast<int64_t>(sp) * H * Dc);
+    const float wgt = __expf(ls[sp] - m_use);  // exp(-inf) = 0
+    const u32x4_t pv = *reinterpret_cast<const u32x4_t*>(po + static_cast<int64_t>(sp) * kH * kDc);
     wsum += wgt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -657,15 +661,10 @@ mla_combine(int H, int Dc, int nsplit, int64_t total_vec, const uint16_t* __rest
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  if constexpr (DT == DSA_BF16) {
-    const u32x4_t ov = {f32x2_to_bf16x2(acc[0] * inv, acc[1] * inv), f32x2_to_bf16x2(acc[2] * inv, acc[3] * inv),
-                        f32x2_to_bf16x2(acc[4] * inv, acc[5] * inv), f32x2_to_bf16x2(acc[6] * inv, acc[7] * inv)};
-    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(o) + (row * H + h) * Dc + d0) = ov;
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) store_mla<DT>(o, (row * H + h) * Dc + d0 + e, acc[e] * inv);
-  }
-  if (lse != nullptr && d0 == 0) lse[row * H + h] = wsum > 0.f ? m_use + __logf(wsum) : -__builtin_inff();
+  const u32x4_t ov = {f32x2_to_bf16x2(acc[0] * inv, acc[1] * inv), f32x2_to_bf16x2(acc[2] * inv, acc[3] * inv),
+                      f32x2_to_bf16x2(acc[4] * inv, acc[5] * inv), f32x2_to_bf16x2(acc[6] * inv, acc[7] * inv)};
+  *reinterpret_cast<u32x4_t*>(o + rh * kDc + 8 * lane) = ov;
+  if (lse != nullptr && lane == 0) lse[rh] = wsum > 0.f ? m_use + __logf(wsum) : -__builtin_inff();
 }
 
 struct MlaPlan {
@@ -732,12 +731,12 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
                           idx, static_cast<uint16_t*>(o), lse, part_o, part_lse);
     dsa_status_t st = timer.done("mla_mfma");
     if (st != DSA_OK || p.splits == 1) return st;
-    const int64_t total_vec = rows * s.H * s.Dc / 8;
+    const int64_t total_heads = rows * kH;
     LaunchTimer ctimer;
-    hipExtLaunchKernelGGL(mla_combine<DSA_BF16>, dim3(static_cast<unsigned>((total_vec + 255) / 256)),
-                          dim3(256), 0, stream, ctimer.start(), ctimer.stop(), 0, s.H, s.Dc, p.splits,
-                          total_vec, static_cast<const uint16_t*>(part_o),
-                          static_cast<const float*>(part_lse), o, lse);
+    hipExtLaunchKernelGGL(mla_combine, dim3(static_cast<unsigned>((total_heads + 3) / 4)), dim3(256), 0,
+                          stream, ctimer.start(), ctimer.stop(), 0, p.splits, total_heads,
+                          static_cast<const uint16_t*>(part_o), static_cast<const float*>(part_lse),
+                          static_cast<uint16_t*>(o), lse);
     return ctimer.done("mla_combine");
   }
   const size_t lds = (static_cast<size_t>(s.Dc) + s.Dr + W) * sizeof(float);
