@@ -128,6 +128,35 @@ indexer_mfma(int T, int S, float idx_scale, const void* __restrict__ q_idx,
   const int q_pos = S - T + t;
   const int s_lim = min(S, q_pos + 1);  // keys [0, s_lim) are visible
 
+  const int s_begin = (blockIdx.x * kIdxWaves + wave) * kKeysPerWave;
+  const int s_end = min(S, s_begin + kKeysPerWave);
+  const bool active = s_begin < S && s_begin < s_lim;  // this wave has visible keys
+  const int64_t kbase = static_cast<int64_t>(b) * S;
+  // Key rows of a group of kTilesPerGroup 16-key tiles (keys past the visible
+  // range load row s_lim - 1, so every address stays in bounds).
+  auto load_group = [&](int s0, u32x4_t (&kb)[kTilesPerGroup][4], float (&ksc)[kTilesPerGroup]) {
+#pragma unroll
+    for (int j = 0; j < kTilesPerGroup; ++j) {
+      const int s = min(s0 + 16 * j + n, s_lim - 1);
+      if constexpr (!FP8) {
+        const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(
+            static_cast<const uint16_t*>(k_idx) + (kbase + s) * kIdxDim);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kb[j][ks] = __builtin_nontemporal_load(kr + 4 * ks + g);
+      } else {
+        const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(
+            static_cast<const uint8_t*>(k_idx) + (kbase + s) * kIdxDim);
+        kb[j][0] = __builtin_nontemporal_load(kr + 2 * g);
+        kb[j][1] = __builtin_nontemporal_load(kr + 2 * g + 1);
+        ksc[j] = ue8m0_to_f32(k_sf[kbase + s]);
+      }
+    }
+  };
+  // the first key group goes out before the query is staged: both latencies overlap
+  u32x4_t kb0[kTilesPerGroup][4], kb1[kTilesPerGroup][4];
+  float ksc0[kTilesPerGroup] = {}, ksc1[kTilesPerGroup] = {};
+  if (active) load_group(s_begin, kb0, ksc0);
+
   // ---- stage the query row (and w, times the query scales for fp8) ----
   if constexpr (!FP8) {
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
@@ -151,9 +180,7 @@ indexer_mfma(int T, int S, float idx_scale, const void* __restrict__ q_idx,
   }
   __syncthreads();
 
-  const int s_begin = (blockIdx.x * kIdxWaves + wave) * kKeysPerWave;
   if (s_begin >= S) return;
-  const int s_end = min(S, s_begin + kKeysPerWave);
   float* out_row = scores + row * S;
 
   if (s_begin >= s_lim) {  // every key of this wave is in the future
@@ -179,27 +206,6 @@ indexer_mfma(int T, int S, float idx_scale, const void* __restrict__ q_idx,
     for (int i = 0; i < 4; ++i) wreg[mb][i] = w_lds[mb * 16 + 4 * g + i];
   }
 
-  const int64_t kbase = static_cast<int64_t>(b) * S;
-  // Key rows of a group of kTilesPerGroup 16-key tiles (keys past the visible
-  // range load row s_lim - 1, so every address stays in bounds).
-  auto load_group = [&](int s0, u32x4_t (&kb)[kTilesPerGroup][4], float (&ksc)[kTilesPerGroup]) {
-#pragma unroll
-    for (int j = 0; j < kTilesPerGroup; ++j) {
-      const int s = min(s0 + 16 * j + n, s_lim - 1);
-      if constexpr (!FP8) {
-        const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(
-            static_cast<const uint16_t*>(k_idx) + (kbase + s) * kIdxDim);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[j][ks] = __builtin_nontemporal_load(kr + 4 * ks + g);
-      } else {
-        const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(
-            static_cast<const uint8_t*>(k_idx) + (kbase + s) * kIdxDim);
-        kb[j][0] = __builtin_nontemporal_load(kr + 2 * g);
-        kb[j][1] = __builtin_nontemporal_load(kr + 2 * g + 1);
-        ksc[j] = ue8m0_to_f32(k_sf[kbase + s]);
-      }
-    }
-  };
   auto score_group = [&](int s0, const u32x4_t (&kb)[kTilesPerGroup][4],
                          const float (&ksc)[kTilesPerGroup]) {
 #pragma unroll
@@ -227,8 +233,8 @@ indexer_mfma(int T, int S, float idx_scale, const void* __restrict__ q_idx,
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) part = fmaf(wreg[mb][i], fmaxf(acc[mb][i], 0.f), part);
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
+      part = xor16_sum(part);
+      part = xor32_sum(part);
       const int s = s0 + 16 * j + n;
       if (g == 0 && s < s_end) {
         float v;
@@ -241,9 +247,6 @@ indexer_mfma(int T, int S, float idx_scale, const void* __restrict__ q_idx,
 
   // two-stage pipeline: the next group's key rows load while this group scores
   constexpr int kGroupKeys = 16 * kTilesPerGroup;
-  u32x4_t kb0[kTilesPerGroup][4], kb1[kTilesPerGroup][4];
-  float ksc0[kTilesPerGroup] = {}, ksc1[kTilesPerGroup] = {};
-  load_group(s_begin, kb0, ksc0);
 #pragma unroll
   for (int grp = 0; grp < kKeysPerWave / kGroupKeys; grp += 2) {
     const int s0 = s_begin + grp * kGroupKeys;

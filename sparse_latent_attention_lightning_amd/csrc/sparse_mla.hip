@@ -233,26 +233,6 @@ __device__ __forceinline__ int qpiece_slot(int p, int hq) {
   return p < 64 ? ((p & ~15) | ((p ^ hq) & 15)) : (64 | ((p - 64) ^ (hq & 7)));
 }
 
-// Butterfly steps across lane distance 16 and 32 on the VALU (v_permlane16_swap
-// / v_permlane32_swap with both operands the same value: each lane ends with
-// its own value and its partner's, in some order, so any symmetric op works).
-__device__ __forceinline__ float xor16_max(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor32_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float xor16_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // Address arithmetic on LDS pointers stays in the 32-bit LDS address space, so
 // constant offsets fold into the instructions' offset fields.
 __device__ __forceinline__ short4_t lds_read_tr16(lds_char_t* p) {
