@@ -147,13 +147,15 @@ mla_generic(int T, int S, int H, int Dc, int Dr, int W, float sm_scale,
 // slots of dim 16db + i: half of its A operand.
 //
 // Key tile in LDS (38 KiB): latent part of row r (64 pieces of 16 B) at byte
-// 1088 r, piece c stored at c ^ f(r), f(r) = bit-reversed (r >> 2) & 3;
-// rotary part (8 pieces) in a region of its own at byte 34816, row r at 128 r,
-// piece c' at c' ^ ((r >> 1) & 7).  The LDS has 64 banks of 4 bytes (a 16-byte
-// read pass serves 16 lanes, an 8-byte pass 32 lanes); with this placement
-// the logits reads (16 rows, one piece), the transposing reads (8 rows x 2
-// pieces) and the epilogue staging all touch every bank once per pass, and
-// every read is one base register plus a compile-time offset.
+// 1088 r, piece c stored at c ^ f(r), f(r) = 2 ((r >> 2) & 1); rotary part (8
+// pieces) in a region of its own at byte 34816, row r at 128 r, piece c' at
+// c' ^ ((r >> 1) & 7).  The LDS has 64 banks of 4 bytes.  A 16-byte read takes
+// 4 cycles, each serving two groups of 8 lanes: lanes 0-7 with 24-31, 8-15
+// with 16-23, 32-39 with 56-63 and 40-47 with 48-55 (measured with the bank
+// conflict counter on gfx950); a transposing 8-byte read serves 32 lanes per
+// cycle.  With this placement the logits reads, the transposing reads and the
+// epilogue staging touch every bank once per cycle, and every read is one
+// base register plus a compile-time offset.
 //
 // The tile is filled by direct global->LDS copies (global_load_lds_dwordx4:
 // lane l of a wave writes 16 B at the wave's LDS base + 16 l): wave w copies
@@ -179,8 +181,8 @@ constexpr int kStageStride = 528;            // epilogue staging row: 256 bf16 +
 constexpr int kIdxWin = 1024;                // index entries staged in LDS at a time
 constexpr int kWinTiles = kIdxWin / kTileKeys;
 constexpr int kWinPerThread = kIdxWin / kMlaThreads;
-constexpr int kQStageBytes = 32 * kD * 2;    // one wave's query rows, staged in the tile ring
-static_assert(kMlaWaves * kQStageBytes <= kBuffers * kTileBytes, "query staging fits the ring");
+constexpr int kQStageBytes = 16 * kD * 2;    // one wave's query rows of one group, staged in the ring
+static_assert(kMlaWaves * kQStageBytes <= 2 * kTileBytes, "query staging fits ring buffers 0-1");
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -218,19 +220,17 @@ __device__ __forceinline__ void lds_dma_16(const void* src, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ int lat_swz(int r) {  // f(r): bit-reversed (r >> 2) & 3
-  const int k = (r >> 2) & 3;
-  return ((k & 1) << 1) | (k >> 1);
-}
+__device__ __forceinline__ int lat_swz(int r) { return ((r >> 2) & 1) << 1; }  // f(r)
 __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
 
-// Slot of 16-byte piece p (0..71) within a staged query row of head hq: the
-// latent pieces are XOR-swizzled within aligned groups of 16 by hq & 15, the
-// rotary pieces within their group of 8 by hq & 7 (an involution, so the same
-// function maps slots back to pieces).  16 lanes reading piece p of heads
-// hq .. hq+15 (rows 1152 B apart, i.e. 32 banks apart) then cover all 64 banks.
+// Slot of 16-byte piece p (0..71) within a staged query row of head hq
+// (0..15): the latent pieces are XOR-swizzled within aligned groups of 16 by
+// hq >> 1, the rotary pieces within their group of 8 likewise (an involution,
+// so the same function maps slots back to pieces).  The operand reads (lane
+// (g, n): head n, piece 4ks + g; rows 1152 B = 32 banks apart) then touch
+// every bank once per cycle of the 16-byte read.
 __device__ __forceinline__ int qpiece_slot(int p, int hq) {
-  return p < 64 ? ((p & ~15) | ((p ^ hq) & 15)) : (64 | ((p - 64) ^ (hq & 7)));
+  return p < 64 ? ((p & ~15) | ((p ^ (hq >> 1)) & 15)) : (64 | ((p - 64) ^ ((hq >> 1) & 7)));
 }
 
 // Address arithmetic on LDS pointers stays in the 32-bit LDS address space, so
@@ -295,38 +295,35 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   };
 
   // Query operand (B of logits^T): qf[c][ks] = head 32w + 16c + n, dims
-  // 32ks + 8g .. +8.  Wave w's 32 heads are one contiguous 36 KiB run of q;
-  // it goes through the (still idle) tile ring with whole-line copies, placed
-  // so that the operand reads are free of bank conflicts: head hq (0..31) at
-  // byte 1152 hq, its 16-byte piece p at slot qpiece_slot(p, hq).  The first
-  // index window loads with it.
+  // 32ks + 8g .. +8.  Wave w's 16 heads of group c are one contiguous 18 KiB
+  // run of q; each group goes through ring buffers 0-1 with whole-line copies,
+  // placed so that the operand reads are free of bank conflicts: head hq
+  // (0..15) at byte 1152 hq, its 16-byte piece p at slot qpiece_slot(p, hq).
+  // Meanwhile tiles 0 and 1 land in buffers 2 and 3 (tile t uses ring buffer
+  // (t + 2) % 4).
   bf16x8_t qf[2][kKSteps];
   load_window(0);
-  {
-    const char* qsrc = reinterpret_cast<const char*>(q + (row * kH + 32 * wave) * kD);
+  store_window();
+  __syncthreads();  // the first index window is published
+  const char* qsrc = reinterpret_cast<const char*>(q + (row * kH + 32 * wave) * kD);
+  auto stage_q = [&](int c) {
     const uint32_t qlds = lds_addr(tiles) + wave * kQStageBytes;
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
-#pragma unroll 4
+#pragma unroll 2
     for (int i = 0; i < kQStageBytes / 1024; ++i) {
       const int x = 1024 * i + 16 * ln;  // staging byte this lane's copy lands on
       const int hq = x / (kD * 2), slot = (x - hq * kD * 2) >> 4;
-      lds_dma_16(qsrc + hq * (kD * 2) + 16 * qpiece_slot(slot, hq), qlds + 1024 * i);
+      lds_dma_16(qsrc + (16 * c + hq) * (kD * 2) + 16 * qpiece_slot(slot, hq), qlds + 1024 * i);
     }
-  }
-  store_window();  // the compiler's wait for the window covers the copies issued after it
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  {
+  };
+  auto read_q = [&](int c) {
     lds_char_t* qst = (lds_char_t*)(tiles[0].bytes) + wave * kQStageBytes;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks)
-        qf[c][ks] = *(__attribute__((address_space(3))) const bf16x8_t*)(
-            qst + (16 * c + n) * (kD * 2) + 16 * qpiece_slot(4 * ks + g, 16 * c + n));
-  }
-  __syncthreads();  // the window is published and every wave has its query: the ring is free
-
+    for (int ks = 0; ks < kKSteps; ++ks)
+      qf[c][ks] = *(__attribute__((address_space(3))) const bf16x8_t*)(
+          qst + n * (kD * 2) + 16 * qpiece_slot(4 * ks + g, n));
+  };
   f32x4_t oacc[2][kDc / 16];  // O^T: oacc[c][db][i] = O[head 32w + 16c + n][16db + 4g + i]
 #pragma unroll
   for (int c = 0; c < 2; ++c)
@@ -366,7 +363,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     c.sl[0] = s4a.x; c.sl[1] = s4a.y; c.sl[2] = s4a.z; c.sl[3] = s4a.w;
     c.sl[4] = s4b.x; c.sl[5] = s4b.y; c.sl[6] = s4b.z; c.sl[7] = s4b.w;
     c.sr = wrow[8 * wave + (ln >> 3)];
-    c.lds = lds_addr(tiles[t % kBuffers].bytes);
+    c.lds = lds_addr(tiles[(t + 2) % kBuffers].bytes);
     return c;
   };
   const char* kvb = reinterpret_cast<const char*>(kv_seq);
@@ -425,6 +422,23 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       voff[h][par] = kLatStride * r + 16 * ((2 * par + (cq >> 1)) ^ lat_swz(r)) + 8 * (cq & 1);
   }
 
+  // start-up: the query in two halves, tiles 0 and 1 meanwhile
+  stage_q(0);
+  for (int t = 0; t < 2 && t < ntiles; ++t) issue_tile(t);
+  // loads complete in issue order: wait for the query half, not the tiles
+  if (ntiles >= 2)
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+  else if (ntiles == 1)
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  read_q(0);
+  __syncthreads();  // every wave has read its first half: the staging is free
+  stage_q(1);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  read_q(1);
+  __syncthreads();  // buffers 0-1 are free again; tiles 0 and 1 are in
+
   // Online softmax with a fixed reference max per head: the first tile with a
   // valid key sets it, and p = 2^(x - ref) stays below 2^kRefSlack as long as
   // no later logit exceeds the reference by more than the slack.  If one does
@@ -448,7 +462,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       store_window();
       __syncthreads();
     }
-    for (int t = 0; t < kBuffers - 1 && t < ntiles; ++t) issue_tile(t);
+    for (int t = pass == 0 ? 2 : 0; t < kBuffers - 1 && t < ntiles; ++t) issue_tile(t);
     for (int it = 0; it < ntiles; ++it) {
       wait_tiles(min(kBuffers - 2, ntiles - 1 - it));
       __syncthreads();  // every wave's copies of tile `it` are in; tile it-1 is consumed
@@ -463,7 +477,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
         }
         nxt = prep_tile(t);
       }
-      lds_char_t* cur = (lds_char_t*)(tiles[it % kBuffers].bytes);
+      lds_char_t* cur = (lds_char_t*)(tiles[(it + 2) % kBuffers].bytes);
       // validity of rows 4g + i (block 0) and 16 + 4g + i (block 1)
       const uint32_t valid = vmask[it % (kBuffers + 1)] >> (4 * g);
 
