@@ -103,6 +103,30 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS byte address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const char*)(p)));
+}
+
+// 16-byte global -> LDS copy per lane: lane l writes LDS [lds + 16 l] (lds is
+// wave-uniform).  Issued through asm so the compiler does not hold back the
+// current tile's LDS reads behind it; completion is awaited explicitly with
+// s_waitcnt vmcnt before the barrier that publishes a tile (loads retire in
+// issue order, so vmcnt(N) means all but the last N copies have landed).
+// m0 is declared clobbered; the compiler sets m0 itself before each of its own
+// uses and the kernels that call this have no other, so the reserved-register
+// warning is moot.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma_16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 __device__ __forceinline__ f32x4_t mfma16x16x32_bf16(const bf16x8_t& a, const bf16x8_t& b,
                                                      const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

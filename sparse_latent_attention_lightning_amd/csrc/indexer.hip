@@ -258,6 +258,181 @@ indexer_mfma(int T, int S, float idx_scale, const void* __restrict__ q_idx,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Query-blocked MFMA kernel for many queries per sequence (prefill), bf16,
+// HI = 64, DI = 128.
+//
+// The index scores of a prefill chunk are a dense contraction: [T queries x
+// 64 heads] x [128 dims] x [S keys], with the ReLU-weighted head sum applied
+// to every 64-head column.  Streaming the key rows once per query (as the
+// decode kernel does) would make the kernel bound by key traffic, so here a
+// block of 8 waves takes 8 consecutive queries of one sequence, one per wave,
+// and streams every key the 8 of them see through LDS once:
+//  * keys move in 64-key chunks (16 KB) through a ring of 4 LDS buffers,
+//    copied global -> LDS by the DMA path, two 1 KB copies per wave per chunk;
+//    a key row is 256 bytes = 16 pieces of 16 bytes, and piece c of row r sits
+//    in slot c ^ ((r & 7) << 1) of the row, so that the operand reads (lane
+//    (g, n): row n, piece 4 ks + g) touch all 64 banks in every cycle;
+//  * each wave keeps its query's 64 x 128 Q^I tile as MFMA A operands (64
+//    VGPRs) and its 64 head weights for the block's whole key range;
+//  * per 16-key tile: 16 MFMAs (4 head blocks x 4 reduction steps), then ReLU,
+//    weight and the in-lane part of the head sum on the accumulators (each
+//    lane holds 16 heads of one key); the MFMAs of tile u + 1 are issued
+//    before the VALU work of tile u, so the two overlap;
+//  * the cross-lane part of the head sum of a chunk's 4 tiles is one
+//    reduce-scatter (3 lane swaps, 3 adds) that leaves the 64 scores of the
+//    chunk one per lane, stored as one 256-byte run.
+// Blocks run longest first (the causal key range grows with the query index),
+// which balances the triangular work over the CUs.
+// ---------------------------------------------------------------------------
+constexpr int kPfWaves = 8;                                  // queries per block
+constexpr int kPfChunkKeys = 64;
+constexpr int kPfRowBytes = kIdxDim * 2;                     // 256
+constexpr int kPfChunkBytes = kPfChunkKeys * kPfRowBytes;    // 16 KB
+constexpr int kPfBuffers = 4;
+constexpr int kPfMinQueries = 8;   // fewer queries per sequence use the per-query kernel
+static_assert(kPfChunkBytes == kPfWaves * 2 * 1024, "two 1 KB copies per wave per chunk");
+
+template <int WDT>
+__global__ void __launch_bounds__(kPfWaves * 64)
+indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __restrict__ q_idx,
+                const uint16_t* __restrict__ k_idx, const void* __restrict__ w,
+                float* __restrict__ scores) {
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPfBuffers * kPfChunkBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int nb = gridDim.x / n_qblk;                 // sequences
+  const int qb = n_qblk - 1 - static_cast<int>(blockIdx.x) / nb;   // longest first
+  const int b = static_cast<int>(blockIdx.x) % nb;
+  const int t0 = qb * kPfWaves;
+  const int t = t0 + wave;
+  const bool has_q = t < T;
+  const int tq = min(t, T - 1);
+  const int q_pos = S - T + tq;
+  const int kend = S - T + min(t0 + kPfWaves, T);    // keys [0, kend) are visible to some query
+  const int nchunks = (kend + kPfChunkKeys - 1) / kPfChunkKeys;
+  const int64_t kbase = static_cast<int64_t>(b) * S;
+  const uint32_t kb_lds = lds_addr(kbuf);
+
+  // chunk c -> buffer c % kPfBuffers; this wave copies rows 8 wave .. 8 wave + 7
+  // (keys past S - 1 load row S - 1: every address stays in bounds)
+  auto issue_chunk = [&](int c) {
+    const uint32_t dst = kb_lds + (c % kPfBuffers) * kPfChunkBytes + wave * 2048;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = wave * 8 + i * 4 + (lane >> 4);
+      const int piece = (lane & 15) ^ ((r & 7) << 1);
+      const int key = min(c * kPfChunkKeys + r, S - 1);
+      lds_dma_16(k_idx + (kbase + key) * kIdxDim + piece * 8, dst + i * 1024);
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < kPfBuffers - 1; ++c)
+    if (c < nchunks) issue_chunk(c);
+
+  // ---- the query tile (A operands) and head weights, in registers ----
+  const int64_t row = static_cast<int64_t>(b) * T + tq;
+  const bf16x8_t* qrow = reinterpret_cast<const bf16x8_t*>(q_idx + row * kIdxHeads * kIdxDim);
+  bf16x8_t qa[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qa[mb][ks] = __builtin_nontemporal_load(qrow + (16 * mb + n) * (kIdxDim / 8) + 4 * ks + g);
+  float wreg[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wreg[mb][i] = load_w<WDT>(w, row * kIdxHeads + 16 * mb + 4 * g + i);
+
+  float* out_row = scores + row * S;
+
+  // one 16-key tile: 16 MFMAs into acc (key operands read from LDS)
+  auto tile_mfma = [&](const uint8_t* buf, int u, f32x4_t (&acc)[4]) {
+    bf16x8_t kb[4];
+    const uint8_t* rp = buf + (16 * u + n) * kPfRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kb[ks] = *reinterpret_cast<const bf16x8_t*>(rp + 16 * ((4 * ks + g) ^ ((n & 7) << 1)));
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x16x32_bf16(qa[mb][ks], kb[ks], acc[mb]);
+  };
+  // ReLU, head weights and the in-lane part of the head sum
+  auto tile_part = [&](const f32x4_t (&acc)[4]) -> float {
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      p0 = fmaf(wreg[mb][0], fmaxf(acc[mb][0], 0.f), p0);
+      p1 = fmaf(wreg[mb][1], fmaxf(acc[mb][1], 0.f), p1);
+      p0 = fmaf(wreg[mb][2], fmaxf(acc[mb][2], 0.f), p0);
+      p1 = fmaf(wreg[mb][3], fmaxf(acc[mb][3], 0.f), p1);
+    }
+    return p0 + p1;
+  };
+  // cross-lane part of the head sum for the 4 tiles of chunk c: afterwards
+  // lane l holds the full sum of part[l / 16] for key n, i.e. key 64 c + l
+  auto chunk_store = [&](int c, const float (&part)[4]) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+    const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+    const float h0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const float h1 = __uint_as_float(d[0]) + __uint_as_float(d[1]);
+    const auto e = __builtin_amdgcn_permlane16_swap(__float_as_uint(h0), __float_as_uint(h1), false, false);
+    const float v = idx_scale * (__uint_as_float(e[0]) + __uint_as_float(e[1]));
+    const int key = c * kPfChunkKeys + lane;
+    if (has_q && key < S) __builtin_nontemporal_store(key <= q_pos ? v : -__builtin_inff(), out_row + key);
+  };
+
+  f32x4_t acc0[4], acc1[4];
+  float part[4];
+  for (int c = 0; c < nchunks; ++c) {
+    // chunk c has landed: the copies issued after it are those of chunks
+    // c + 1 .. min(c + kPfBuffers - 2, nchunks - 1), two per chunk (the first
+    // chunk also waits for the query loads, issued after the copies)
+    const int later = min(kPfBuffers - 2, nchunks - 1 - c);
+    if (c == 0 || later <= 0)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    __syncthreads();   // every wave's copies of chunk c are in; chunk c - 1 is consumed
+    if (c + kPfBuffers - 1 < nchunks) issue_chunk(c + kPfBuffers - 1);
+    const uint8_t* buf = kbuf + (c % kPfBuffers) * kPfChunkBytes;
+    tile_mfma(buf, 0, acc0);
+    if (c > 0) {
+      part[3] = tile_part(acc1);
+      chunk_store(c - 1, part);
+    }
+    tile_mfma(buf, 1, acc1);
+    part[0] = tile_part(acc0);
+    tile_mfma(buf, 2, acc0);
+    part[1] = tile_part(acc1);
+    tile_mfma(buf, 3, acc1);
+    part[2] = tile_part(acc0);
+  }
+  if (nchunks > 0) {
+    part[3] = tile_part(acc1);
+    chunk_store(nchunks - 1, part);
+  }
+  // keys past the block's last chunk are in every query's future
+  if (has_q) {
+    const int k0 = nchunks * kPfChunkKeys;
+    if ((S & 3) == 0) {
+      const f32x4_t ninf = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+      for (int k = k0 + 4 * lane; k < S; k += 256)
+        __builtin_nontemporal_store(ninf, reinterpret_cast<f32x4_t*>(out_row + k));
+    } else {
+      for (int k = k0 + lane; k < S; k += 64) __builtin_nontemporal_store(-__builtin_inff(), out_row + k);
+    }
+  }
+}
+
 template <int IDT, int WDT>
 dsa_status_t run_generic(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                          const void* k_idx, const uint8_t* k_sf, const void* w, float* scores,
@@ -287,16 +462,35 @@ dsa_status_t run_mfma(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_
   return timer.done("indexer_mfma");
 }
 
+template <int WDT>
+dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_idx,
+                         const void* w, float* scores, hipStream_t stream) {
+  const int n_qblk = (s.T + kPfWaves - 1) / kPfWaves;
+  const int64_t blocks = static_cast<int64_t>(n_qblk) * s.B;
+  if (blocks > 0x7fffffff)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: %lld query blocks", static_cast<long long>(blocks));
+  LaunchTimer timer;
+  hipExtLaunchKernelGGL(indexer_prefill<WDT>, dim3(static_cast<unsigned>(blocks)),
+                        dim3(kPfWaves * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
+                        n_qblk, s.idx_scale, static_cast<const uint16_t*>(q_idx),
+                        static_cast<const uint16_t*>(k_idx), w, scores);
+  return timer.done("indexer_prefill");
+}
+
 }  // namespace
 
 dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                             const void* k_idx, const uint8_t* k_sf, const void* w,
                             float* scores, hipStream_t stream) {
+  const bool v32 = s.HI == kIdxHeads && s.DI == kIdxDim;
+  const bool wbf = s.w_dtype == DSA_BF16;
+  if (v32 && s.idx_dtype == DSA_BF16 && s.T >= kPfMinQueries)
+    return wbf ? run_prefill<DSA_BF16>(s, q_idx, k_idx, w, scores, stream)
+               : run_prefill<DSA_F32>(s, q_idx, k_idx, w, scores, stream);
+  // the per-query kernels put the query row on grid.y
   if (static_cast<int64_t>(s.B) * s.T > 65535)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: B*T = %lld exceeds 65535 query rows",
                 static_cast<long long>(s.B) * s.T);
-  const bool v32 = s.HI == kIdxHeads && s.DI == kIdxDim;
-  const bool wbf = s.w_dtype == DSA_BF16;
   if (v32 && s.idx_dtype == DSA_BF16)
     return wbf ? run_mfma<false, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
                : run_mfma<false, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);

@@ -197,28 +197,6 @@ struct MlaTile {
   uint8_t bytes[kTileBytes];
 };
 
-// LDS byte address of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const char*)(p)));
-}
-
-// 16-byte global -> LDS copy per lane: lane l writes LDS [lds + 16 l] (lds is
-// wave-uniform).  Issued through asm so the compiler does not hold back the
-// current tile's LDS reads behind it; completion is awaited explicitly with
-// s_waitcnt vmcnt before the barrier that publishes a tile (loads retire in
-// issue order, so vmcnt(N) means all but the last N copies have landed).
-// m0 is declared clobbered; the compiler sets m0 itself before each of its own
-// uses and this kernel has no other, so the reserved-register warning is moot.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_dma_16(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 __device__ __forceinline__ int lat_swz(int r) { return ((r >> 2) & 1) << 1; }  // f(r)
 __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }

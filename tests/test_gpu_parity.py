@@ -84,8 +84,17 @@ SCORE_CASES = {
     "tiny": g.CONFIGS["tiny"],
     # MFMA bf16 kernel, decode, integer twin: bit-exact
     "decode_int": g.CONFIGS["decode_8k"].replace(B=3, integer=True),
-    # MFMA bf16 kernel, causal prefill with a ragged tail, integer: bit-exact
+    # query-blocked MFMA bf16 kernel, causal prefill with ragged query blocks
+    # and key chunks, integer: bit-exact
     "prefill_int": g.CONFIGS["prefill_16k"].replace(T=300, S=1000, integer=True),
+    # the same kernel at its smallest T (one query block per sequence), fp32
+    # head weights, S not a multiple of 4 (scalar fill of the future keys)
+    "prefill_int_w32": g.CONFIGS["prefill_16k"].replace(B=3, T=8, S=517, w_dtype="f32",
+                                                        integer=True),
+    # one query short of it: the per-query kernel
+    "prefill_int_t7": g.CONFIGS["prefill_16k"].replace(B=2, T=7, S=64, integer=True),
+    # real-valued prefill, two sequences, T = S (every key chunk reaches the diagonal)
+    "prefill_real": g.CONFIGS["prefill_16k"].replace(B=2, T=203, S=203),
     # MFMA e4m3 kernel, integer twin (scale byte 127): bit-exact
     "fp8_int": g.CONFIGS["decode_64k_fp8"].replace(B=2, S=4200, integer=True),
     # real-valued: within 1e-4 of the row max
