@@ -121,47 +121,51 @@ mla_generic(int T, int S, int H, int Dc, int Dr, int W, float sm_scale,
 // MFMA kernel, H = 128, Dc = 512, Dr = 64, bf16
 //
 // One workgroup of 4 waves (one per SIMD, 512 registers each) takes one query
-// row and one split of its index list; wave w owns heads 32w .. 32w+31 as two
-// groups of 16 (group c: heads 32w + 16c .. +15).  All 128 heads share each
-// gathered tile of 32 selected key rows, and every operand a wave reads from
-// LDS feeds two MFMAs, one per group.
+// row and one split of its index list; wave w owns heads 32w .. 32w+31.  All
+// 128 heads share each gathered tile of 32 selected key rows.
 //
-// MFMA 16x16x32 bf16 operand layouts (lane l, g = l / 16, n = l % 16):
-//   A (16 x 32): lane holds row n, reduction elements 8g .. 8g+7
-//   B (32 x 16): lane holds column n, reduction elements 8g .. 8g+7
-//   C (16 x 16): register i holds row 4g + i of column n
+// Both products run on v_mfma_f32_32x32x16_bf16 (lane l, h = l / 32,
+// m = l % 32):
+//   A (32 x 16): lane holds row m, reduction elements 8h .. 8h+7
+//   B (16 x 32): lane holds column m, reduction elements 8h .. 8h+7
+//   C (32 x 32): register i holds row 8(i/4) + 4h + i%4 of column m
+// A wave issues about one instruction per 4 cycles and this MFMA holds the
+// matrix pipe for 32 cycles (also as one dependent accumulation chain), so
+// the loop is laid out to spend well under 8 other instructions per MFMA.
 //
-// logits^T (2 blocks of 16 keys x 16 heads, per group) = K_tile (A, from LDS)
-// . Q^T (B, registers), reduced over the 576 dims in 18 steps of 32: four
-// independent accumulation chains.  Lane (g, n) ends with head n of each
-// group and keys 4g + i and 16 + 4g + i.
+// logits^T (32 keys x 32 heads) = K_tile (A, from LDS) . Q^T (B, registers),
+// 36 steps of 16 dims in one chain: lane (h, m) ends with head m and keys
+// 8(i/4) + 4h + i%4.  The softmax is per lane (one head, 16 keys) plus one
+// lane swap across the halves.  O^T (512 dims x 32 heads) += V^T (A) . P^T
+// (B) in 16 dim blocks x 2 key steps: P^T is the lane's own probabilities
+// (key step s takes registers 8s .. 8s+7, so B slot 8h + e holds key
+// 16s + 8(e/4) + 4h + e%4), and V^T comes from the row-major key tile through
+// the transposing read ds_read_b64_tr_b16 (within 16 lanes, lane i receives
+// element i%4 of the 8-byte chunks loaded by lanes 4j + i/4, j = 0..3): lane
+// 4j + q of 16-lane group (h, d) loads dims 32db + 16d + 4q .. +3 of key
+// 16s + 4h + j, and of key 16s + 8 + 4h + j for the other half of its slots.
 //
-// O^T (512 dims x 16 heads, per group) += V^T (A) . P^T (B), reduced over the
-// 32 keys in one MFMA per 16 dims.  P^T comes straight from the logit
-// accumulators: its B-operand slot 8g + e holds key 4g + e (e < 4) or
-// 16 + 4g + e - 4 (e >= 4).  V^T is read from the same row-major key tile with
-// the transposing LDS load ds_read_b64_tr_b16: within a 16-lane group, lane i
-// receives element (i % 4) of the 8-byte chunk loaded by lane 4j + i/4, for
-// j = 0..3.  So lane 4j + c of group g loads dims 16db + 4c .. +3 of tile row
-// 4g + j (+16 for the second half of its slots), and lane i ends up with 4 key
-// slots of dim 16db + i: half of its A operand.
+// Iteration t computes logits(t), then the softmax of tile t interleaved with
+// the value product of tile t - 1: with a fixed reference max (below) the two
+// are independent, and the softmax's VALU work fills the issue slots the
+// value MFMAs leave free.
 //
-// Key tile in LDS (38 KiB): latent part of row r (64 pieces of 16 B) at byte
-// 1088 r, piece c stored at c ^ f(r), f(r) = 2 ((r >> 2) & 1); rotary part (8
-// pieces) in a region of its own at byte 34816, row r at 128 r, piece c' at
-// c' ^ ((r >> 1) & 7).  The LDS has 64 banks of 4 bytes.  A 16-byte read takes
-// 4 cycles, each serving two groups of 8 lanes: lanes 0-7 with 24-31, 8-15
-// with 16-23, 32-39 with 56-63 and 40-47 with 48-55 (measured with the bank
-// conflict counter on gfx950); a transposing 8-byte read serves 32 lanes per
-// cycle.  With this placement the logits reads, the transposing reads and the
-// epilogue staging touch every bank once per cycle, and every read is one
-// base register plus a compile-time offset.
+// Key tile in LDS (38 KiB): latent part of row r at byte 1088 r (1 KiB + 64 B
+// pad), 16-byte piece p at (p & ~3) | ((p & 3) ^ ((r >> 2) & 3)); rotary part
+// in a region of its own at byte 34816, row r at 128 r, piece p' at
+// p' ^ ((r >> 1) & 7).  The LDS has 64 banks of 4 bytes; a 16-byte read
+// serves two 8-lane groups per cycle (lanes 0-7 with 24-31, 8-15 with 16-23,
+// 32-39 with 56-63, 40-47 with 48-55) and a transposing 8-byte read lanes
+// 0-31, then 32-63 (measured with the bank conflict counter on gfx950).  With
+// this placement every read of the loop touches each bank once per cycle.
 //
-// The tile is filled by direct global->LDS copies (global_load_lds_dwordx4:
+// Tiles are filled by direct global->LDS copies (global_load_lds_dwordx4:
 // lane l of a wave writes 16 B at the wave's LDS base + 16 l): wave w copies
-// the latent parts of rows 8w .. 8w+7 (one 1 KiB run of global memory each)
-// and the rotary parts of the same rows.  A ring of 4 tiles keeps up to three
-// later tiles' copies in flight during the current tile's MFMAs.
+// the latent parts of rows 8w .. 8w+7 (one 1 KiB run each) and the rotary
+// parts of the same rows.  A ring of 4 tiles holds the tile of the value
+// product, the tile of the logits and two tiles in flight.  Before the first
+// tile the ring stages the query (one buffer per wave), after the last one
+// the output (bf16 [head][dims], stored as whole 1 KiB head rows).
 // ---------------------------------------------------------------------------
 constexpr int kH = 128, kDc = 512, kDr = 64, kD = kDc + kDr;
 constexpr int kMlaWaves = 4;                 // wave w owns heads 32w .. 32w+31
@@ -172,49 +176,71 @@ constexpr int kCopiesPerTile = 9;            // copies per wave per tile: 8 late
 constexpr int kLatStride = 1088;             // bytes per latent row in LDS (1024 + 64 pad)
 constexpr int kRopeBase = kTileKeys * kLatStride;            // byte offset of the rotary region
 constexpr int kTileBytes = kRopeBase + kTileKeys * kDr * 2;  // 38912
-constexpr int kKSteps = kD / 32;             // 18 logits reduction steps
-constexpr int kLatSteps = kDc / 32;          // 16 of them over the latent part
-constexpr int kReadAhead = 6;                // logits A-operand reads issued ahead of their MFMAs
-constexpr int kVAhead = 4;                   // value A operands (2 reads each) issued ahead
+constexpr int kKSteps = kD / 16;             // 36 logits reduction steps of 16 dims
+constexpr int kLatSteps = kDc / 16;          // 32 of them over the latent part
+constexpr int kDimBlocks = kDc / 32;         // 16 value blocks of 32 dims
+constexpr int kPvSteps = 2 * kDimBlocks;     // value MFMAs per tile (2 key steps)
+constexpr int kReadAhead = 3;                // logits A-operand reads issued ahead of their MFMAs
+constexpr int kVAhead = 3;                   // value A operands (2 reads each) issued ahead
 constexpr float kRefSlack = 32.0f;           // log2 units: p <= 2^32 against the reference max
-constexpr int kStageStride = 528;            // epilogue staging row: 256 bf16 + 16 B pad
 constexpr int kIdxWin = 1024;                // index entries staged in LDS at a time
 constexpr int kWinTiles = kIdxWin / kTileKeys;
 constexpr int kWinPerThread = kIdxWin / kMlaThreads;
-constexpr int kQStageBytes = 16 * kD * 2;    // one wave's query rows of one group, staged in the ring
-static_assert(kMlaWaves * kQStageBytes <= 2 * kTileBytes, "query staging fits ring buffers 0-1");
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 typedef __attribute__((address_space(3))) const char lds_char_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
-
-// a zero key row: skipped index entries load it, so their LDS rows are zero
-__device__ __attribute__((aligned(16))) uint16_t g_zero_row[kD];
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 
 struct MlaTile {
   uint8_t bytes[kTileBytes];
 };
 
-
-__device__ __forceinline__ int lat_swz(int r) { return ((r >> 2) & 1) << 1; }  // f(r)
+// slot of 16-byte piece p in a row whose 4-piece groups are permuted by f
+__device__ __forceinline__ int swz4(int p, int f) { return (p & ~3) | ((p & 3) ^ f); }
+__device__ __forceinline__ int lat_f(int r) { return (r >> 2) & 3; }
 __device__ __forceinline__ int rope_swz(int r) { return (r >> 1) & 7; }
-
-// Slot of 16-byte piece p (0..71) within a staged query row of head hq
-// (0..15): the latent pieces are XOR-swizzled within aligned groups of 16 by
-// hq >> 1, the rotary pieces within their group of 8 likewise (an involution,
-// so the same function maps slots back to pieces).  The operand reads (lane
-// (g, n): head n, piece 4ks + g; rows 1152 B = 32 banks apart) then touch
-// every bank once per cycle of the 16-byte read.
-__device__ __forceinline__ int qpiece_slot(int p, int hq) {
-  return p < 64 ? ((p & ~15) | ((p ^ (hq >> 1)) & 15)) : (64 | ((p - 64) ^ ((hq >> 1) & 7)));
-}
 
 // Address arithmetic on LDS pointers stays in the 32-bit LDS address space, so
 // constant offsets fold into the instructions' offset fields.
 __device__ __forceinline__ short4_t lds_read_tr16(lds_char_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p));
+}
+
+__device__ __forceinline__ f32x16_t mfma32x32x16_bf16(const bf16x8_t& a, const bf16x8_t& b,
+                                                      const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The logits chain keeps its accumulator in VGPRs (the value product holds
+// all AGPRs): issued through asm, whose register constraints pin the class.
+// Consecutive MFMAs of one chain (same destination and srcC) need no wait
+// states; the closing nops cover those before VALU reads of the result.
+__device__ __forceinline__ void mfma32_first(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_acc(f32x16_t& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+// (the result passes through the nops, so no reader can move above them)
+__device__ __forceinline__ void mfma32_drain(f32x16_t& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+}
+
+// max of three without the NaN-quieting the compiler adds around maxnum on
+// values it cannot prove canonical (the logits are finite or -inf)
+__device__ __forceinline__ float max3_f32(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// two fp32 -> packed bf16 pair (low half = a), round to nearest even, one instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{a, b}, bf16x2v_t));
 }
 
 // 1-D grid of rows * nsplit workgroups.  With xcd_map, the splits of one query
@@ -232,12 +258,12 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   // a window of the split's index entries as key rows (-1: skipped entry)
   __shared__ __attribute__((aligned(16))) int32_t idxw[kIdxWin];
   // validity of each tile's rows (bit r: tile row r holds a valid key), written
-  // when the tile's copies are issued, kBuffers - 1 iterations before its use
+  // when the tile's copies are issued, two iterations before its use
   __shared__ uint32_t vmask[kBuffers + 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, n = lane & 15;
+  const int hl = lane >> 5, m = lane & 31;
   const int L = blockIdx.x;
   int sp;
   int64_t row;
@@ -272,150 +298,128 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       idxw[tid + u * kMlaThreads] = (win[u] >= 0 && win[u] < S) ? win[u] : -1;
   };
 
-  // Query operand (B of logits^T): qf[c][ks] = head 32w + 16c + n, dims
-  // 32ks + 8g .. +8.  Wave w's 16 heads of group c are one contiguous 18 KiB
-  // run of q; each group goes through ring buffers 0-1 with whole-line copies,
-  // placed so that the operand reads are free of bank conflicts: head hq
-  // (0..15) at byte 1152 hq, its 16-byte piece p at slot qpiece_slot(p, hq).
-  // Meanwhile tiles 0 and 1 land in buffers 2 and 3 (tile t uses ring buffer
-  // (t + 2) % 4).
-  bf16x8_t qf[2][kKSteps];
-  load_window(0);
-  store_window();
-  __syncthreads();  // the first index window is published
-  const char* qsrc = reinterpret_cast<const char*>(q + (row * kH + 32 * wave) * kD);
-  auto stage_q = [&](int c) {
-    const uint32_t qlds = lds_addr(tiles) + wave * kQStageBytes;
+  // Query operand (B of logits^T): qf[ks] = head 32w + m, dims 16ks + 8h .. +8,
+  // i.e. 16-byte piece 2ks + h of the head's row.  Wave w's 32 heads are one
+  // contiguous 36 KiB run of q, copied with whole-line copies into ring buffer
+  // w (head n at byte 1152 n, piece p in slot p ^ ((n >> 1) & 7): rows 72
+  // slots apart, so the operand reads touch every bank once per cycle).  The
+  // copies go out before the index window's loads, so both latencies overlap;
+  // the 8 splits of a query row share an XCD and 7 of them find it in L2.
+  bf16x8_t qf[kKSteps];
+  {
+    const char* qsrc = reinterpret_cast<const char*>(q + (row * kH + 32 * wave) * kD);
+    const uint32_t qlds = lds_addr(tiles[wave].bytes);
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
-#pragma unroll 2
-    for (int i = 0; i < kQStageBytes / 1024; ++i) {
+#pragma unroll 4
+    for (int i = 0; i < 32 * kD * 2 / 1024; ++i) {
       const int x = 1024 * i + 16 * ln;  // staging byte this lane's copy lands on
-      const int hq = x / (kD * 2), slot = (x - hq * kD * 2) >> 4;
-      lds_dma_16(qsrc + (16 * c + hq) * (kD * 2) + 16 * qpiece_slot(slot, hq), qlds + 1024 * i);
+      const int n = x / (kD * 2), slot = (x - n * (kD * 2)) >> 4;
+      lds_dma_16(qsrc + n * (kD * 2) + 16 * (slot ^ ((n >> 1) & 7)), qlds + 1024 * i);
     }
-  };
-  auto read_q = [&](int c) {
-    lds_char_t* qst = (lds_char_t*)(tiles[0].bytes) + wave * kQStageBytes;
+  }
+  load_window(0);
+  store_window();   // waits for the window's loads, and so for the query copies issued before them
+  __syncthreads();  // the first index window is published
+  {
+    lds_char_t* qst = (lds_char_t*)(tiles[wave].bytes) + m * (kD * 2);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
-      qf[c][ks] = *(__attribute__((address_space(3))) const bf16x8_t*)(
-          qst + n * (kD * 2) + 16 * qpiece_slot(4 * ks + g, n));
-  };
-  f32x4_t oacc[2][kDc / 16];  // O^T: oacc[c][db][i] = O[head 32w + 16c + n][16db + 4g + i]
+      qf[ks] = *(__attribute__((address_space(3))) const bf16x8_t*)(
+          qst + 16 * ((2 * ks + hl) ^ ((m >> 1) & 7)));
+  }
+  f32x16_t oacc[kDimBlocks];  // O^T: oacc[db][i] = O[head 32w + m][32db + 8(i/4) + 4h + i%4]
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-    for (int db = 0; db < kDc / 16; ++db) oacc[c][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref[2] = {-__builtin_inff(), -__builtin_inff()};  // reference max (log2 units) per group
-  float l_run[2] = {0.f, 0.f};
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_ref = -__builtin_inff();  // reference max (log2 units) of head 32w + m
+  float l_run = 0.f;
   const float scale2 = sm_scale * kLog2e;
 
   // Wave w copies tile rows 8w .. 8w+7 (latent and rotary parts), reading
   // their key rows from the index window; wave 0 also publishes the tile's
-  // validity mask.
-  // Byte offset, from the sequence's first key row, of the zero row that
-  // skipped entries copy: one select per copy instead of a branch.
-  const int64_t zero_off = reinterpret_cast<const char*>(g_zero_row) - reinterpret_cast<const char*>(kv_seq);
-  // A tile's copies: prep_tile reads the wave's 8 key rows from the index
-  // window (two broadcast reads, one LDS round trip) and publishes the tile's
-  // validity mask (wave 0); copy_row(k) then issues copy k of 9 (8 latent
-  // rows, then the rotary parts).  Each lane forms its own source address, so
-  // no value goes through SGPRs.  The main loop spreads the nine copies over
-  // the logits MFMAs, so their issue cost hides under matrix work.
+  // validity mask.  Skipped entries copy key row 0 of the sequence: their
+  // logits are replaced by -inf, so their probabilities are exactly zero and
+  // (finite) rows add nothing to O.
+  // the sequence's base address, wave-uniform (the copies take it in SGPRs)
+  const char* kvb;
+  {
+    const uint64_t a = reinterpret_cast<uint64_t>(kv_seq);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    kvb = reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+  }
+  // latent copy of row 8w + k: lane ln's 16-byte slot holds piece swz4(ln, f),
+  // f = lat_f(8w + k) = (2w + k/4) & 3
+  const int lat_lo[2] = {16 * swz4(lane, (2 * wave) & 3), 16 * swz4(lane, (2 * wave + 1) & 3)};
+  // rotary copy: lane ln takes row 8w + ln/8, slot ln % 8
+  const int rope_r = 8 * wave + (lane >> 3);
+  const int rope_lo = 2 * kDc + 16 * ((lane & 7) ^ rope_swz(rope_r));
   struct TileCopies {
-    int sl[8];  // key rows of tile rows 8w .. 8w+7 (-1: skipped)
-    int sr;     // key row of tile row 8w + lane/8 (rotary copy)
+    const int32_t* wrow;  // the tile's 32 index entries in the window
     uint32_t lds;
   };
   auto prep_tile = [&](int t) {
     TileCopies c;
-    const int32_t* wrow = &idxw[(t % kWinTiles) * kTileKeys];
-    const int ln = __lane_id();
+    c.wrow = &idxw[(t % kWinTiles) * kTileKeys];
     if (wave == 0) {
-      const uint32_t m = static_cast<uint32_t>(__ballot(wrow[ln & 31] >= 0));
-      if (ln == 0) vmask[t % (kBuffers + 1)] = m;
+      const uint32_t vm = static_cast<uint32_t>(__ballot(c.wrow[lane & 31] >= 0));
+      if (lane == 0) vmask[t % (kBuffers + 1)] = vm;
     }
-    const int4 s4a = *reinterpret_cast<const int4*>(wrow + 8 * wave);
-    const int4 s4b = *reinterpret_cast<const int4*>(wrow + 8 * wave + 4);
-    c.sl[0] = s4a.x; c.sl[1] = s4a.y; c.sl[2] = s4a.z; c.sl[3] = s4a.w;
-    c.sl[4] = s4b.x; c.sl[5] = s4b.y; c.sl[6] = s4b.z; c.sl[7] = s4b.w;
-    c.sr = wrow[8 * wave + (ln >> 3)];
     c.lds = lds_addr(tiles[(t + 2) % kBuffers].bytes);
     return c;
   };
-  const char* kvb = reinterpret_cast<const char*>(kv_seq);
-  auto copy_row = [&](const TileCopies& c, int k) {
-    // an opaque copy of the lane id: the per-copy address math is redone at
-    // each copy instead of being kept live across the loop in registers
-    int ln = __lane_id();
-    asm volatile("" : "+v"(ln));
-    if (k < 8) {  // latent part of row r: its 16-byte slot `ln` holds piece ln ^ f(r)
-      const int r = 8 * wave + k;
-      const int64_t off = c.sl[k] >= 0 ? static_cast<int64_t>(c.sl[k]) * (kD * 2) : zero_off;
-      lds_dma_16(kvb + off + 16 * (ln ^ lat_swz(r)), c.lds + kLatStride * r);
-    } else {  // rotary parts of rows 8w .. 8w+7: lane l takes row 8w + l/8
-      const int r = 8 * wave + (ln >> 3);
-      const int64_t off = c.sr >= 0 ? static_cast<int64_t>(c.sr) * (kD * 2) : zero_off;
-      lds_dma_16(kvb + off + 2 * kDc + 16 * ((ln & 7) ^ rope_swz(r)), c.lds + kRopeBase + 1024 * wave);
-    }
+  // key row of copy k (0..7: tile row 8w + k, all lanes; 8: row 8w + lane/8),
+  // read from the index window just before the copy goes out (skipped: row 0)
+  auto copy_key = [&](const TileCopies& c, int k) {
+    int s = k < 8 ? c.wrow[8 * wave + k] : c.wrow[rope_r & 31];
+    // opaque: the row offsets are formed per lane on the VALU, not through
+    // the scalar unit
+    asm volatile("" : "+v"(s));
+    return max(s, 0);
+  };
+  // byte offsets within the sequence fit 32 bits (S * 1152 < 2^32, checked on the host)
+  auto copy_row = [&](const TileCopies& c, int k, int s) {
+    const int lo = k < 8 ? lat_lo[k >> 2] : rope_lo;
+    const uint32_t dst = k < 8 ? c.lds + kLatStride * (8 * wave + k) : c.lds + kRopeBase + 1024 * wave;
+    lds_dma_16_sbase(kvb, static_cast<uint32_t>(s) * static_cast<uint32_t>(kD * 2) + lo, dst);
   };
   auto issue_tile = [&](int t) {
     const TileCopies c = prep_tile(t);
 #pragma unroll
-    for (int k = 0; k < kCopiesPerTile; ++k) copy_row(c, k);
+    for (int k = 0; k < kCopiesPerTile; ++k) copy_row(c, k, copy_key(c, k));
   };
   // wait until at most `pending` later tiles' copies of this wave are in flight
   auto wait_tiles = [&](int pending) {
-    static_assert(kBuffers == 4 && kCopiesPerTile == 9, "vmcnt immediates");
+    static_assert(kCopiesPerTile == 9, "vmcnt immediates");
     if (pending <= 0)
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (pending == 1)
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     else
-      asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
   };
 
-  // LDS byte offsets.  Logits A operand of step ks for key block mb: row
-  // 16mb + n, piece 4ks + g, stored at 4ks + (g ^ f(row)) (latent steps) or in
-  // the rotary region (steps 16, 17).
-  int aoff[2], roff[2][2];
+  // LDS byte offsets.  Logits A operand of step ks: row m, piece 2ks + h:
+  // latent steps at aoff[ks & 1] + 64 (ks >> 1), rotary steps at roff[ks - 32].
+  int aoff[2], roff[4];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int r = 16 * mb + n;
-    aoff[mb] = kLatStride * r + 16 * (g ^ lat_swz(r));
+  for (int par = 0; par < 2; ++par) aoff[par] = kLatStride * m + 16 * ((2 * par + hl) ^ lat_f(m));
 #pragma unroll
-    for (int kr = 0; kr < 2; ++kr) roff[mb][kr] = kRopeBase + 128 * r + 16 * ((4 * kr + g) ^ rope_swz(r));
-  }
-  // Transposing reads: lane (g, jq, cq) reads tile row 4g + jq + 16h, dims
-  // 16db + 4cq: piece 2db + cq/2, byte 8(cq&1).  (2db + y) ^ f = 4(db/2) + ((2(db&1) + y) ^ f),
-  // so each (h, db parity) has one base and db/2 moves it by 64 bytes.
-  const int jq = n >> 2, cq = n & 3;
-  int voff[2][2];  // [h][db parity]
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = 4 * g + jq + 16 * h;
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-      voff[h][par] = kLatStride * r + 16 * ((2 * par + (cq >> 1)) ^ lat_swz(r)) + 8 * (cq & 1);
+  for (int k = 0; k < 4; ++k) roff[k] = kRopeBase + 128 * m + 16 * ((2 * k + hl) ^ rope_swz(m));
+  // Transposing reads of key step s, dim block db: lane (h, d, j, q) reads
+  // dims 32db + 16d + 4q of key 16s + 4h + j (vbase[0]) or 16s + 8 + 4h + j
+  // (vbase[1]); lat_f of those rows is h, resp. 2 + h.
+  int vbase[2];
+  {
+    const int dh = (lane >> 4) & 1, j = (lane >> 2) & 3, qd = lane & 3;
+    vbase[0] = kLatStride * (4 * hl + j) + 16 * ((2 * dh + (qd >> 1)) ^ hl) + 8 * (qd & 1);
+    vbase[1] = kLatStride * (8 + 4 * hl + j) + 16 * ((2 * dh + (qd >> 1)) ^ (2 + hl)) + 8 * (qd & 1);
   }
 
-  // start-up: the query in two halves, tiles 0 and 1 meanwhile
-  stage_q(0);
+  // start-up: every wave has its query in registers, the ring is free; tiles
+  // 0 and 1 go out
+  __syncthreads();
   for (int t = 0; t < 2 && t < ntiles; ++t) issue_tile(t);
-  // loads complete in issue order: wait for the query half, not the tiles
-  if (ntiles >= 2)
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else if (ntiles == 1)
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  read_q(0);
-  __syncthreads();  // every wave has read its first half: the staging is free
-  stage_q(1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  read_q(1);
-  __syncthreads();  // buffers 0-1 are free again; tiles 0 and 1 are in
 
   // Online softmax with a fixed reference max per head: the first tile with a
   // valid key sets it, and p = 2^(x - ref) stays below 2^kRefSlack as long as
@@ -423,16 +427,15 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   // (never for sane data), the whole split is run once more with the true
   // maximum as reference, so O is only ever zeroed, never rescaled.  The
   // decision is workgroup-uniform (barriers stay matched).
-  float m_seen[2] = {-__builtin_inff(), -__builtin_inff()};
+  float m_seen = -__builtin_inff();
   for (int pass = 0; pass < 2; ++pass) {
     if (pass == 1) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-        for (int db = 0; db < kDc / 16; ++db) oacc[c][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        l_run[c] = 0.f;
-        m_ref[c] = m_seen[c];
-      }
+        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+      l_run = 0.f;
+      m_ref = m_seen;
     }
     bool overflow = false;
     if (pass == 1 && ntiles > kWinTiles) {  // the window moved on: back to the first
@@ -440,14 +443,125 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       store_window();
       __syncthreads();
     }
-    for (int t = pass == 0 ? 2 : 0; t < kBuffers - 1 && t < ntiles; ++t) issue_tile(t);
-    for (int it = 0; it < ntiles; ++it) {
-      wait_tiles(min(kBuffers - 2, ntiles - 1 - it));
-      __syncthreads();  // every wave's copies of tile `it` are in; tile it-1 is consumed
-      const bool copies = it + kBuffers - 1 < ntiles;
+    if (pass == 1)
+      for (int t = 0; t < 2 && t < ntiles; ++t) issue_tile(t);
+
+    f32x16_t sacc;   // logits^T of the current tile (raw dot products)
+    bf16x8_t pb[2];  // P^T of the previous tile, key steps 0 and 1
+    u32x4_t pn[2];   // P^T of the current tile, being formed (bf16 pairs)
+
+    // ---- logits^T of tile it, with the copies of tile it + 2 ----
+    // COPIES: with the copies of the tile two ahead (all but the last two tiles)
+    auto logits = [&](auto copies_tag, lds_char_t* cur, const TileCopies& nxt) {
+      constexpr bool copies = decltype(copies_tag)::value;
+      auto aload = [&](int ks) {
+        const int off = ks < kLatSteps ? aoff[ks & 1] + 64 * (ks >> 1) : roff[ks - kLatSteps];
+        return *(__attribute__((address_space(3))) const bf16x8_t*)(cur + off);
+      };
+      bf16x8_t ka[kReadAhead];
+#pragma unroll
+      for (int ks = 0; ks < kReadAhead; ++ks) ka[ks] = aload(ks);
+      int key = copies ? copy_key(nxt, 0) : 0;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        if (ks == 0)
+          mfma32_first(sacc, ka[0], qf[0]);
+        else
+          mfma32_acc(sacc, ka[ks % kReadAhead], qf[ks]);
+        if (ks + kReadAhead < kKSteps) ka[ks % kReadAhead] = aload(ks + kReadAhead);
+        // copy k of the tile two ahead goes out with step 4k + 1, its key row
+        // is read with step 4k - 1
+        if (ks % 4 == 3 && ks / 4 + 1 < kCopiesPerTile && copies) key = copy_key(nxt, ks / 4 + 1);
+        if (ks % 4 == 1 && ks / 4 < kCopiesPerTile && copies) copy_row(nxt, ks / 4, key);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma32_drain(sacc);
+    };
+
+    // ---- softmax of the current tile in 15 phases, interleaved with the
+    // value product of the previous tile (phase k runs with value step 2k) ----
+    float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f, t4 = 0.f, negm = 0.f, ps0 = 0.f, ps1 = 0.f;
+    auto sm_phase = [&](int k) {
+      switch (k) {
+        case 0: t0 = max3_f32(sacc[0], sacc[1], sacc[2]); t1 = max3_f32(sacc[3], sacc[4], sacc[5]); break;
+        case 1: t2 = max3_f32(sacc[6], sacc[7], sacc[8]); t3 = max3_f32(sacc[9], sacc[10], sacc[11]); break;
+        case 2: t4 = max3_f32(sacc[12], sacc[13], sacc[14]); t0 = max3_f32(t0, t1, sacc[15]); break;
+        case 3: t0 = max3_f32(t0, t2, t3); t0 = max3_f32(t0, t4, t4); break;
+        case 4: {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0), __float_as_uint(t0), false, false);
+          t0 = max3_f32(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+          break;
+        }
+        case 5: {
+          const float tmax = t0 * scale2;  // -inf when the tile has no valid key
+          m_seen = max3_f32(m_seen, tmax, tmax);
+          if (m_ref == -__builtin_inff()) m_ref = tmax;  // O and l of this head are still 0
+          overflow |= tmax > m_ref + kRefSlack;
+          negm = (m_ref == -__builtin_inff()) ? 0.f : -m_ref;
+          break;
+        }
+        case 14: {
+          float ps = ps0 + ps1;
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+          l_run += __uint_as_float(r[0]) + __uint_as_float(r[1]);
+          break;
+        }
+        default: {  // k = 6 .. 13: probabilities of registers 2(k-6), 2(k-6)+1
+          const int e = 2 * (k - 6);
+          // v_exp_f32 directly: arguments are <= kRefSlack, -inf gives 0
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], scale2, negm));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e + 1], scale2, negm));
+          ps0 = e == 0 ? p0 : ps0 + p0;
+          ps1 = e == 0 ? p1 : ps1 + p1;
+          pn[e >> 3][(e >> 1) & 3] = pack_bf16x2(p0, p1);
+          break;
+        }
+      }
+    };
+    constexpr int kSmPhases = 15;
+
+    // ---- value product of the previous tile (in buffer `prv`), with the
+    // softmax phases of the current tile when SM ----
+    auto sm_pv = [&](auto sm_tag, auto pv_tag, lds_char_t* prv) {
+      constexpr bool SM = decltype(sm_tag)::value;
+      constexpr bool PV = decltype(pv_tag)::value;
+      if constexpr (PV) {
+        auto vload = [&](int st) {
+          const int s = st >> 4, db = st & 15;
+          const short4_t lo = lds_read_tr16(prv + vbase[0] + kLatStride * 16 * s + 64 * db);
+          const short4_t hi = lds_read_tr16(prv + vbase[1] + kLatStride * 16 * s + 64 * db);
+          return __builtin_bit_cast(
+              bf16x8_t, short8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        };
+        bf16x8_t va[kVAhead];
+#pragma unroll
+        for (int st = 0; st < kVAhead; ++st) va[st] = vload(st);
+#pragma unroll
+        for (int st = 0; st < kPvSteps; ++st) {
+          const int s = st >> 4, db = st & 15;
+          oacc[db] = mfma32x32x16_bf16(va[st % kVAhead], pb[s], oacc[db]);
+          if (st + kVAhead < kPvSteps) va[st % kVAhead] = vload(st + kVAhead);
+          if constexpr (SM)
+            if ((st & 1) == 0 && st / 2 < kSmPhases) sm_phase(st / 2);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kSmPhases; ++k) sm_phase(k);
+      }
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+
+    // wait for tile it, publish it, send out the copies of tile it + 2 and
+    // compute its logits (skipped rows: -inf)
+    auto front = [&](int it) {
+      wait_tiles(min(1, ntiles - 1 - it));
+      __syncthreads();  // every wave's copies of tile `it` are in; tile it-2 is consumed
+      const bool copies = it + 2 < ntiles;
       TileCopies nxt;
       if (copies) {
-        const int t = it + kBuffers - 1;
+        const int t = it + 2;
         if (t % kWinTiles == 0) {  // next index window (splits longer than kIdxWin)
           load_window(t / kWinTiles);
           store_window();
@@ -456,146 +570,70 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
         nxt = prep_tile(t);
       }
       lds_char_t* cur = (lds_char_t*)(tiles[(it + 2) % kBuffers].bytes);
-      // validity of rows 4g + i (block 0) and 16 + 4g + i (block 1)
-      const uint32_t valid = vmask[it % (kBuffers + 1)] >> (4 * g);
-
-      // ---- logits^T: 2 key blocks x 2 head groups, four chains ----
-      f32x4_t sacc[2][2];  // [mb][c]
+      const uint32_t vm = __builtin_amdgcn_readfirstlane(vmask[it % (kBuffers + 1)]);
+      if (copies)
+        logits(std::true_type{}, cur, nxt);
+      else
+        logits(std::false_type{}, cur, nxt);
+      if (vm != 0xffffffffu) {  // skipped rows in this tile: their logits are -inf
+        const uint32_t bits = (vm >> (4 * hl)) & 0x0f0f0f0fu;  // bit 8(i/4) + i%4: key of register i
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) sacc[mb][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      {
-        // software pipeline over the 36 (ks, mb) key-tile reads: the read of
-        // step st + kReadAhead is issued with the two MFMAs of step st
-        constexpr int kSteps = 2 * kKSteps;
-        auto aload = [&](int st) {
-          const int ks = st >> 1, mb = st & 1;
-          const int off = ks < kLatSteps ? aoff[mb] + 64 * ks : roff[mb][ks - kLatSteps];
-          return *(__attribute__((address_space(3))) const bf16x8_t*)(cur + off);
-        };
-        bf16x8_t ka[kReadAhead];
-#pragma unroll
-        for (int st = 0; st < kReadAhead; ++st) ka[st] = aload(st);
-#pragma unroll
-        for (int st = 0; st < kSteps; ++st) {
-          const int ks = st >> 1, mb = st & 1;
-          sacc[mb][0] = mfma16x16x32_bf16(ka[st % kReadAhead], qf[0][ks], sacc[mb][0]);
-          sacc[mb][1] = mfma16x16x32_bf16(ka[st % kReadAhead], qf[1][ks], sacc[mb][1]);
-          if (st + kReadAhead < kSteps) ka[st % kReadAhead] = aload(st + kReadAhead);
-          // copy k of the tile kBuffers - 1 ahead goes out with step 4k + 1
-          if (st % 4 == 1 && st / 4 < kCopiesPerTile && copies) copy_row(nxt, st / 4);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int i = 0; i < 16; ++i)
+          if (!((bits >> (8 * (i >> 2) + (i & 3))) & 1u)) sacc[i] = -__builtin_inff();
       }
-
-      // ---- softmax weights (lane: head n of each group; keys 16mb + 4g + i) ----
-      bf16x8_t pb[2];  // B operands of the value product: slot 8g + e
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float x[2][4];
-        float tmax = -__builtin_inff();
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[mb][i] = ((valid >> (16 * mb + i)) & 1) ? sacc[mb][c][i] * scale2 : -__builtin_inff();
-            tmax = fmaxf(tmax, x[mb][i]);
-          }
-        tmax = xor16_max(tmax);
-        tmax = xor32_max(tmax);
-        m_seen[c] = fmaxf(m_seen[c], tmax);
-        if (m_ref[c] == -__builtin_inff()) m_ref[c] = tmax;  // O and l of this head are still 0
-        overflow |= tmax > m_ref[c] + kRefSlack;
-        const float m_use = (m_ref[c] == -__builtin_inff()) ? 0.f : m_ref[c];
-        float psum = 0.f;
-        u32x4_t pw;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          // v_exp_f32 directly: arguments are <= kRefSlack, -inf gives 0
-          const float p0 = __builtin_amdgcn_exp2f(x[e >> 2][e & 3] - m_use);
-          const float p1 = __builtin_amdgcn_exp2f(x[e >> 2][(e & 3) + 1] - m_use);
-          psum += p0 + p1;
-          pw[e >> 1] = f32x2_to_bf16x2(p0, p1);
-        }
-        pb[c] = __builtin_bit_cast(bf16x8_t, pw);
-        psum = xor16_sum(psum);
-        psum = xor32_sum(psum);
-        l_run[c] += psum;
-      }
-
-      // ---- O^T += V^T . P^T, both groups per V^T operand ----
-      {
-        // ds_read_b64_tr_b16 takes no folded offset: an opaque per-tile copy of
-        // the bases keeps each read's address add next to the read
-        int vbase[2][2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int par = 0; par < 2; ++par) {
-            vbase[h][par] = voff[h][par];
-            asm volatile("" : "+v"(vbase[h][par]));
-          }
-        auto vload = [&](int db) {
-          const short4_t lo = lds_read_tr16(cur + vbase[0][db & 1] + 64 * (db >> 1));
-          const short4_t hi = lds_read_tr16(cur + vbase[1][db & 1] + 64 * (db >> 1));
-          return __builtin_bit_cast(
-              bf16x8_t, short8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        };
-        bf16x8_t va[kVAhead];
-#pragma unroll
-        for (int db = 0; db < kVAhead; ++db) va[db] = vload(db);
-#pragma unroll
-        for (int db = 0; db < kDc / 16; ++db) {
-          oacc[0][db] = mfma16x16x32_bf16(va[db % kVAhead], pb[0], oacc[0][db]);
-          oacc[1][db] = mfma16x16x32_bf16(va[db % kVAhead], pb[1], oacc[1][db]);
-          if (db + kVAhead < kDc / 16) va[db % kVAhead] = vload(db + kVAhead);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+    };
+    if (ntiles > 0) {
+      front(0);
+      sm_pv(yes{}, no{}, nullptr);
+      pb[0] = __builtin_bit_cast(bf16x8_t, pn[0]);
+      pb[1] = __builtin_bit_cast(bf16x8_t, pn[1]);
     }
+    for (int it = 1; it < ntiles; ++it) {
+      front(it);
+      sm_pv(yes{}, yes{}, (lds_char_t*)(tiles[(it + 1) % kBuffers].bytes));  // tile it - 1
+      pb[0] = __builtin_bit_cast(bf16x8_t, pn[0]);
+      pb[1] = __builtin_bit_cast(bf16x8_t, pn[1]);
+    }
+    // the last tile's value product
+    if (ntiles > 0) sm_pv(no{}, yes{}, (lds_char_t*)(tiles[(ntiles + 1) % kBuffers].bytes));
     // every copy has landed (the ring is reused by a second pass)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (!__syncthreads_or(pass == 0 && overflow)) break;
   }
 
-  // ---- epilogue: normalise, stage [head][dims] through LDS, coalesced stores ----
-  uint16_t* dst = nsplit == 1 ? o + row * kH * kDc : part_o + (row * nsplit + sp) * kH * kDc;
-  char* stage = reinterpret_cast<char*>(tiles[0].bytes);  // 128 rows x 528 B (the ring is idle)
+  // ---- epilogue: normalise, stage [head][dims] in bf16 through the idle
+  // ring (rows 1040 B apart), then store whole 1 KiB head rows: wave w reads
+  // back only the rows it wrote, so no barrier separates the two ----
+  constexpr int kStageStride = 1040;
+  static_assert(kH * kStageStride <= kBuffers * kTileBytes, "output staging fits the ring");
+  char* stage = reinterpret_cast<char*>(tiles[0].bytes);
+  {
+    const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+    char* srow = stage + kStageStride * (32 * wave + m) + 8 * hl;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    __syncthreads();  // the ring / the previous half of the staging is free
+    for (int db = 0; db < kDimBlocks; ++db)
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const float inv_l = l_run[c] > 0.f ? 1.f / l_run[c] : 0.f;
-      const int h = 32 * wave + 16 * c + n;
-#pragma unroll
-      for (int dq = 0; dq < kDc / 32; ++dq) {
-        const f32x4_t& a = oacc[c][16 * half + dq];
-        const u32x2_t v = {f32x2_to_bf16x2(a[0] * inv_l, a[1] * inv_l),
-                           f32x2_to_bf16x2(a[2] * inv_l, a[3] * inv_l)};
-        *reinterpret_cast<u32x2_t*>(stage + kStageStride * h + 2 * (16 * dq + 4 * g)) = v;
+      for (int u = 0; u < 4; ++u) {
+        const f32x16_t& a = oacc[db];
+        const u32x2_t v = {pack_bf16x2(a[4 * u] * inv_l, a[4 * u + 1] * inv_l),
+                           pack_bf16x2(a[4 * u + 2] * inv_l, a[4 * u + 3] * inv_l)};
+        *reinterpret_cast<u32x2_t*>(srow + 64 * db + 16 * u) = v;
       }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < (kH * kDc / 2 * 2) / (16 * kMlaThreads); ++k) {  // 16 x 16 B per thread
-      const int cidx = tid + kMlaThreads * k;  // 16-byte chunk: head cidx / 32, part cidx % 32
-      const int hh = cidx >> 5, part = cidx & 31;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + kStageStride * hh + 16 * part);
-      *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(dst + hh * kDc) + 512 * half + 16 * part) = v;
+    uint16_t* dst = nsplit == 1 ? o + row * kH * kDc : part_o + (row * nsplit + sp) * kH * kDc;
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {
+      const int hh = 32 * wave + k;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + kStageStride * hh + 16 * lane);
+      *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(dst + hh * kDc) + 16 * lane) = v;
     }
   }
-  if (g == 0) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int h = 32 * wave + 16 * c + n;
-      const float v = l_run[c] > 0.f ? (m_ref[c] + __log2f(l_run[c])) * kLn2 : -__builtin_inff();
-      if (nsplit > 1)
-        part_lse[(row * kH + h) * nsplit + sp] = v;
-      else if (lse != nullptr)
-        lse[row * kH + h] = v;
-    }
+  if (hl == 0) {
+    const int h = 32 * wave + m;
+    const float v = l_run > 0.f ? (m_ref + __log2f(l_run)) * kLn2 : -__builtin_inff();
+    if (nsplit > 1)
+      part_lse[(row * kH + h) * nsplit + sp] = v;
+    else if (lse != nullptr)
+      lse[row * kH + h] = v;
   }
 }
 
@@ -684,6 +722,8 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
   const int W = k_eff(s);
   const MlaPlan p = plan(s);
   if (p.mfma) {
+    if (static_cast<int64_t>(s.S) * kD * 2 > 0xffffffffLL)
+      return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: S = %d key rows exceed 4 GiB per sequence", s.S);
     uint16_t* part_o = nullptr;
     float* part_lse = nullptr;
     if (p.splits > 1) {
