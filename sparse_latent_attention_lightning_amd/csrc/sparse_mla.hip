@@ -359,34 +359,41 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   struct TileCopies {
     const int32_t* wrow;  // the tile's 32 index entries in the window
     uint32_t lds;
+    int t;
+  };
+  // the tile's validity mask, published by wave 0 (`entry`: its index entry
+  // lane & 31, read earlier so that the read's latency stays hidden)
+  auto publish_mask = [&](int t, int entry) {
+    if (wave == 0) {
+      const uint32_t vm = static_cast<uint32_t>(__ballot(entry >= 0));
+      if (lane == 0) vmask[t % (kBuffers + 1)] = vm;
+    }
   };
   auto prep_tile = [&](int t) {
     TileCopies c;
     c.wrow = &idxw[(t % kWinTiles) * kTileKeys];
-    if (wave == 0) {
-      const uint32_t vm = static_cast<uint32_t>(__ballot(c.wrow[lane & 31] >= 0));
-      if (lane == 0) vmask[t % (kBuffers + 1)] = vm;
-    }
     c.lds = lds_addr(tiles[(t + 2) % kBuffers].bytes);
+    c.t = t;
     return c;
   };
   // key row of copy k (0..7: tile row 8w + k, all lanes; 8: row 8w + lane/8),
   // read from the index window just before the copy goes out (skipped: row 0)
   auto copy_key = [&](const TileCopies& c, int k) {
-    int s = k < 8 ? c.wrow[8 * wave + k] : c.wrow[rope_r & 31];
-    // opaque: the row offsets are formed per lane on the VALU, not through
-    // the scalar unit
-    asm volatile("" : "+v"(s));
-    return max(s, 0);
+    return k < 8 ? c.wrow[8 * wave + k] : c.wrow[rope_r & 31];
   };
   // byte offsets within the sequence fit 32 bits (S * 1152 < 2^32, checked on the host)
   auto copy_row = [&](const TileCopies& c, int k, int s) {
+    // opaque, here at the use: the key read stays in flight until the copy,
+    // and the row offset is formed per lane on the VALU, not the scalar unit
+    asm volatile("" : "+v"(s));
+    s = max(s, 0);
     const int lo = k < 8 ? lat_lo[k >> 2] : rope_lo;
     const uint32_t dst = k < 8 ? c.lds + kLatStride * (8 * wave + k) : c.lds + kRopeBase + 1024 * wave;
     lds_dma_16_sbase(kvb, static_cast<uint32_t>(s) * static_cast<uint32_t>(kD * 2) + lo, dst);
   };
   auto issue_tile = [&](int t) {
     const TileCopies c = prep_tile(t);
+    publish_mask(t, c.wrow[lane & 31]);
 #pragma unroll
     for (int k = 0; k < kCopiesPerTile; ++k) copy_row(c, k, copy_key(c, k));
   };
@@ -462,6 +469,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
 #pragma unroll
       for (int ks = 0; ks < kReadAhead; ++ks) ka[ks] = aload(ks);
       int key = copies ? copy_key(nxt, 0) : 0;
+      const int entry = copies && wave == 0 ? nxt.wrow[lane & 31] : 0;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         if (ks == 0)
@@ -473,52 +481,62 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
         // is read with step 4k - 1
         if (ks % 4 == 3 && ks / 4 + 1 < kCopiesPerTile && copies) key = copy_key(nxt, ks / 4 + 1);
         if (ks % 4 == 1 && ks / 4 < kCopiesPerTile && copies) copy_row(nxt, ks / 4, key);
+        if (ks == 6 && copies) publish_mask(nxt.t, entry);
         __builtin_amdgcn_sched_barrier(0);
       }
       mfma32_drain(sacc);
     };
 
-    // ---- softmax of the current tile in 15 phases, interleaved with the
-    // value product of the previous tile (phase k runs with value step 2k) ----
-    float t0 = 0.f, t1 = 0.f, t2 = 0.f, t3 = 0.f, t4 = 0.f, negm = 0.f, ps0 = 0.f, ps1 = 0.f;
+    // ---- softmax of the current tile in small phases, one per value step of
+    // the previous tile, each a few independent instructions (the wave issues
+    // in order, so a phase must not wait on its own results): two max chains,
+    // the lane swap, the reference update, then a three-stage pipeline over
+    // the 16 probabilities (scale and shift, exp2, sum and pack) ----
+    float t0 = 0.f, t1 = 0.f, tm = 0.f, negm = 0.f, ps0 = 0.f, ps1 = 0.f;
+    float xq[2] = {0.f, 0.f}, pq[2] = {0.f, 0.f};  // in-flight arguments / probabilities
+    bool first = false;
     auto sm_phase = [&](int k) {
-      switch (k) {
-        case 0: t0 = max3_f32(sacc[0], sacc[1], sacc[2]); t1 = max3_f32(sacc[3], sacc[4], sacc[5]); break;
-        case 1: t2 = max3_f32(sacc[6], sacc[7], sacc[8]); t3 = max3_f32(sacc[9], sacc[10], sacc[11]); break;
-        case 2: t4 = max3_f32(sacc[12], sacc[13], sacc[14]); t0 = max3_f32(t0, t1, sacc[15]); break;
-        case 3: t0 = max3_f32(t0, t2, t3); t0 = max3_f32(t0, t4, t4); break;
-        case 4: {
-          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0), __float_as_uint(t0), false, false);
-          t0 = max3_f32(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
-          break;
+      if (k < 7) {  // max over the 16 logits, chains t0 (even phases) and t1 (odd)
+        const int i = k < 2 ? 3 * k : 2 * k + 2;  // first register of this phase
+        if (k == 0) t0 = max3_f32(sacc[0], sacc[1], sacc[2]);
+        else if (k == 1) t1 = max3_f32(sacc[3], sacc[4], sacc[5]);
+        else if (k & 1) t1 = max3_f32(t1, sacc[i], sacc[i + 1]);
+        else t0 = max3_f32(t0, sacc[i], sacc[i + 1]);
+      } else if (k == 7) {
+        t0 = max3_f32(t0, t1, t1);
+      } else if (k == 8) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(t0), __float_as_uint(t0), false, false);
+        t0 = max3_f32(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+      } else if (k == 9) {
+        tm = t0 * scale2;  // -inf when the tile has no valid key
+        first = m_ref == -__builtin_inff();
+      } else if (k == 10) {
+        m_seen = max3_f32(m_seen, tm, tm);
+        if (first) m_ref = tm;  // O and l of this head are still 0
+      } else if (k == 11) {
+        overflow |= tm > m_ref + kRefSlack;
+        negm = (m_ref == -__builtin_inff()) ? 0.f : -m_ref;
+      } else if (k < 12 + 18) {  // j = k - 12: argument of j, exp2 of j - 1, sum of j - 2
+        const int j = k - 12;
+        if (j >= 2) {
+          const int e = j - 2;
+          if (e & 1) {
+            ps1 = e == 1 ? pq[1] : ps1 + pq[1];
+            pn[e >> 3][(e >> 1) & 3] = pack_bf16x2(pq[0], pq[1]);
+          } else {
+            ps0 = e == 0 ? pq[0] : ps0 + pq[0];
+          }
         }
-        case 5: {
-          const float tmax = t0 * scale2;  // -inf when the tile has no valid key
-          m_seen = max3_f32(m_seen, tmax, tmax);
-          if (m_ref == -__builtin_inff()) m_ref = tmax;  // O and l of this head are still 0
-          overflow |= tmax > m_ref + kRefSlack;
-          negm = (m_ref == -__builtin_inff()) ? 0.f : -m_ref;
-          break;
-        }
-        case 14: {
-          float ps = ps0 + ps1;
-          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
-          l_run += __uint_as_float(r[0]) + __uint_as_float(r[1]);
-          break;
-        }
-        default: {  // k = 6 .. 13: probabilities of registers 2(k-6), 2(k-6)+1
-          const int e = 2 * (k - 6);
-          // v_exp_f32 directly: arguments are <= kRefSlack, -inf gives 0
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], scale2, negm));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e + 1], scale2, negm));
-          ps0 = e == 0 ? p0 : ps0 + p0;
-          ps1 = e == 0 ? p1 : ps1 + p1;
-          pn[e >> 3][(e >> 1) & 3] = pack_bf16x2(p0, p1);
-          break;
-        }
+        // v_exp_f32 directly: arguments are <= kRefSlack, -inf gives 0
+        if (j >= 1 && j <= 16) pq[(j - 1) & 1] = __builtin_amdgcn_exp2f(xq[(j - 1) & 1]);
+        if (j < 16) xq[j & 1] = __builtin_fmaf(sacc[j], scale2, negm);
+      } else {
+        const float ps = ps0 + ps1;
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+        l_run += __uint_as_float(r[0]) + __uint_as_float(r[1]);
       }
     };
-    constexpr int kSmPhases = 15;
+    constexpr int kSmPhases = 12 + 18 + 1;
 
     // ---- value product of the previous tile (in buffer `prv`), with the
     // softmax phases of the current tile when SM ----
@@ -542,9 +560,12 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
           oacc[db] = mfma32x32x16_bf16(va[st % kVAhead], pb[s], oacc[db]);
           if (st + kVAhead < kPvSteps) va[st % kVAhead] = vload(st + kVAhead);
           if constexpr (SM)
-            if ((st & 1) == 0 && st / 2 < kSmPhases) sm_phase(st / 2);
+            if (st < kSmPhases) sm_phase(st);
           __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (SM)
+#pragma unroll
+          for (int k = kPvSteps; k < kSmPhases; ++k) sm_phase(k);
       } else {
 #pragma unroll
         for (int k = 0; k < kSmPhases; ++k) sm_phase(k);
