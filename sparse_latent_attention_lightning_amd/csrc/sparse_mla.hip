@@ -391,11 +391,15 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     const uint32_t dst = k < 8 ? c.lds + kLatStride * (8 * wave + k) : c.lds + kRopeBase + 1024 * wave;
     lds_dma_16_sbase(kvb, static_cast<uint32_t>(s) * static_cast<uint32_t>(kD * 2) + lo, dst);
   };
+  // all of a tile's copies at once (start-up): the key reads go out together
   auto issue_tile = [&](int t) {
     const TileCopies c = prep_tile(t);
+    int keys[kCopiesPerTile];
+#pragma unroll
+    for (int k = 0; k < kCopiesPerTile; ++k) keys[k] = copy_key(c, k);
     publish_mask(t, c.wrow[lane & 31]);
 #pragma unroll
-    for (int k = 0; k < kCopiesPerTile; ++k) copy_row(c, k, copy_key(c, k));
+    for (int k = 0; k < kCopiesPerTile; ++k) copy_row(c, k, keys[k]);
   };
   // wait until at most `pending` later tiles' copies of this wave are in flight
   auto wait_tiles = [&](int pending) {
