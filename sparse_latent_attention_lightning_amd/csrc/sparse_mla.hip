@@ -665,35 +665,51 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
 // Merge of the split partials: one wave per (query row, head), lane l covers
 // latent dims 8l .. 8l+7 (Dc = 512).  lse = log sum_s exp(lse_s);
 // o = sum_s exp(lse_s - lse) o_s.  Fixed split order, no atomics:
-// deterministic.  The wave's split lse values are one contiguous run, read
-// through the scalar cache.
+// deterministic.  NS (the split count, a template argument for the counts the
+// planner uses) unrolls everything: the NS partial loads and the wave's NS
+// contiguous lse values (scalar loads) are all issued before the first wait.
+// Every split's partial is written (an empty split holds zeros with weight 0).
+template <int NS>
 __global__ void __launch_bounds__(256)
-mla_combine(int nsplit, int64_t total_heads, const uint16_t* __restrict__ part_o,
+mla_combine(int nsplit_rt, int64_t total_heads, const uint16_t* __restrict__ part_o,
             const float* __restrict__ part_lse, uint16_t* __restrict__ o, float* __restrict__ lse) {
   const int64_t rh = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));  // row * H + head
   if (rh >= total_heads) return;
+  const int nsplit = NS > 0 ? NS : nsplit_rt;
   const int lane = threadIdx.x & 63;
   const int64_t row = rh / kH;
   const int h = static_cast<int>(rh - row * kH);
   const float* ls = part_lse + rh * nsplit;
-  float m = -__builtin_inff();
-  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, ls[sp]);
-  const float m_use = m == -__builtin_inff() ? 0.f : m;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
   const uint16_t* po = part_o + (row * nsplit * kH + h) * kDc + 8 * lane;
-  // every split's partial is written (an empty split holds zeros with weight
-  // 0), so all loads are issued unconditionally
-#pragma unroll 8
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float wgt = __expf(ls[sp] - m_use);  // exp(-inf) = 0
-    const u32x4_t pv = *reinterpret_cast<const u32x4_t*>(po + static_cast<int64_t>(sp) * kH * kDc);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f, m_use = 0.f;
+  auto add = [&](float wgt, const u32x4_t& pv) {
     wsum += wgt;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc[2 * e] = fmaf(wgt, __uint_as_float(pv[e] << 16), acc[2 * e]);
       acc[2 * e + 1] = fmaf(wgt, __uint_as_float(pv[e] & 0xffff0000u), acc[2 * e + 1]);
     }
+  };
+  if constexpr (NS > 0) {
+    u32x4_t pv[NS];
+    float lv[NS];
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) pv[sp] = *reinterpret_cast<const u32x4_t*>(po + static_cast<int64_t>(sp) * kH * kDc);
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) lv[sp] = ls[sp];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) m = fmaxf(m, lv[sp]);
+    m_use = m == -__builtin_inff() ? 0.f : m;
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) add(__expf(lv[sp] - m_use), pv[sp]);  // exp(-inf) = 0
+  } else {
+    float m = -__builtin_inff();
+    for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, ls[sp]);
+    m_use = m == -__builtin_inff() ? 0.f : m;
+    for (int sp = 0; sp < nsplit; ++sp)
+      add(__expf(ls[sp] - m_use), *reinterpret_cast<const u32x4_t*>(po + static_cast<int64_t>(sp) * kH * kDc));
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   const u32x4_t ov = {f32x2_to_bf16x2(acc[0] * inv, acc[1] * inv), f32x2_to_bf16x2(acc[2] * inv, acc[3] * inv),
@@ -770,10 +786,19 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
     if (st != DSA_OK || p.splits == 1) return st;
     const int64_t total_heads = rows * kH;
     LaunchTimer ctimer;
-    hipExtLaunchKernelGGL(mla_combine, dim3(static_cast<unsigned>((total_heads + 3) / 4)), dim3(256), 0,
-                          stream, ctimer.start(), ctimer.stop(), 0, p.splits, total_heads,
-                          static_cast<const uint16_t*>(part_o), static_cast<const float*>(part_lse),
-                          static_cast<uint16_t*>(o), lse);
+    const dim3 cgrid(static_cast<unsigned>((total_heads + 3) / 4));
+    auto combine = [&](auto kernel) {
+      hipExtLaunchKernelGGL(kernel, cgrid, dim3(256), 0, stream, ctimer.start(), ctimer.stop(), 0,
+                            p.splits, total_heads, static_cast<const uint16_t*>(part_o),
+                            static_cast<const float*>(part_lse), static_cast<uint16_t*>(o), lse);
+    };
+    switch (p.splits) {
+      case 2: combine(mla_combine<2>); break;
+      case 4: combine(mla_combine<4>); break;
+      case 8: combine(mla_combine<8>); break;
+      case 16: combine(mla_combine<16>); break;
+      default: combine(mla_combine<0>); break;
+    }
     return ctimer.done("mla_combine");
   }
   const size_t lds = (static_cast<size_t>(s.Dc) + s.Dr + W) * sizeof(float);
