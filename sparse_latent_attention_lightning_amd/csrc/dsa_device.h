@@ -125,6 +125,14 @@ __device__ __forceinline__ void lds_dma_16(const void* src, uint32_t lds) {
                : "v"(src), "s"(lds)
                : "memory", "m0");
 }
+// The same copy with the nontemporal hint: data streamed once does not
+// displace cached data of the kernels that follow.
+__device__ __forceinline__ void lds_dma_16_nt(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
 // The same copy from a wave-uniform 64-bit base plus a 32-bit per-lane byte
 // offset (the saddr form: no 64-bit address arithmetic per lane).
 __device__ __forceinline__ void lds_dma_16_sbase(const void* base, uint32_t off, uint32_t lds) {

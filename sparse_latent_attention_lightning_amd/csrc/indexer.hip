@@ -433,6 +433,158 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming MFMA kernel for few queries per sequence (decode), bf16, HI = 64,
+// DI = 128.
+//
+// Decode reads every key row of the sequence once per query: the kernel is a
+// stream of k^I from HBM.  Each wave owns 256 consecutive keys and moves them
+// through a private ring of four 8 KB LDS buffers with whole-line direct
+// copies (global_load_lds_dwordx4: 1 KB of contiguous key rows per
+// instruction), three 32-key chunks in flight while one is scored; per-lane
+// operand loads, whose 16 lanes per key row touch 64-byte pieces, stream
+// slower.  No barrier is needed after the query is staged (each wave reads
+// only what it copied).  The operands are read as in the prefill kernel (row
+// r's piece c in slot c ^ ((r & 7) << 1)), and every two chunks (4 tiles)
+// finish with the same reduce-scatter, so each wave keeps its 256 scores in 4
+// registers and stores them at the end, after its last load.
+// ---------------------------------------------------------------------------
+constexpr int kStWaves = 4;
+constexpr int kStChunkKeys = 32;                              // keys per chunk
+constexpr int kStChunkBytes = kStChunkKeys * kIdxDim * 2;     // 8 KB
+constexpr int kStBuffers = 4;                                 // per wave
+constexpr int kStChunks = 8;                                  // chunks per wave
+constexpr int kStKeysPerBlock = kStWaves * kStChunks * kStChunkKeys;  // 1024
+constexpr int kStCopies = kStChunkBytes / 1024;               // 8 copies per chunk
+
+template <int WDT>
+__global__ void __launch_bounds__(kStWaves * 64)
+indexer_stream(int T, int S, int nkb, float idx_scale, const uint16_t* __restrict__ q_idx,
+               const uint16_t* __restrict__ k_idx, const void* __restrict__ w,
+               float* __restrict__ scores) {
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kStWaves * kStBuffers * kStChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kIdxHeads * kQStrideBf16 * 2];
+  __shared__ float w_lds[kIdxHeads];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int64_t row = blockIdx.x / nkb;  // b * T + t
+  const int kb = static_cast<int>(blockIdx.x % nkb);
+  const int b = static_cast<int>(row / T);
+  const int t = static_cast<int>(row % T);
+  const int s_lim = min(S, S - T + t + 1);  // keys [0, s_lim) are visible
+  const int s_begin = (kb * kStWaves + wave) * (kStChunks * kStChunkKeys);
+  const int s_end = min(S, s_begin + kStChunks * kStChunkKeys);
+  const int s_vis = min(s_end, s_lim);  // this wave scores [s_begin, s_vis)
+  const int nch = s_vis > s_begin ? (s_vis - s_begin + kStChunkKeys - 1) / kStChunkKeys : 0;
+  const int64_t kbase = static_cast<int64_t>(b) * S;
+  const uint32_t wlds = lds_addr(kbuf) + wave * kStBuffers * kStChunkBytes;
+
+  // chunk c -> buffer c % 4; copy i covers chunk rows 4i .. 4i+3 (keys past
+  // the visible range load row s_vis - 1: every address stays in bounds)
+  auto issue_chunk = [&](int c) {
+    const uint32_t dst = wlds + (c % kStBuffers) * kStChunkBytes;
+#pragma unroll
+    for (int i = 0; i < kStCopies; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int piece = (lane & 15) ^ ((r & 7) << 1);
+      const int key = min(s_begin + c * kStChunkKeys + r, s_vis - 1);
+      lds_dma_16_nt(k_idx + (kbase + key) * kIdxDim + piece * 8, dst + 1024 * i);
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < kStBuffers - 1; ++c)
+    if (c < nch) issue_chunk(c);
+
+  // ---- stage the query row and the head weights ----
+  {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(q_idx + row * kIdxHeads * kIdxDim);
+    for (int i = threadIdx.x; i < kIdxHeads * kIdxDim / 8; i += blockDim.x) {
+      const int h = i / (kIdxDim / 8), c = i % (kIdxDim / 8);
+      *reinterpret_cast<u32x4_t*>(q_lds + (h * kQStrideBf16 + c * 8) * 2) = src[i];
+    }
+    for (int h = threadIdx.x; h < kIdxHeads; h += blockDim.x) w_lds[h] = load_w<WDT>(w, row * kIdxHeads + h);
+  }
+  __syncthreads();
+
+  float* out_row = scores + row * S;
+  if (nch == 0) {  // every key of this wave is in the future (or past S)
+    for (int s = s_begin + lane; s < s_end; s += 64) out_row[s] = -__builtin_inff();
+    return;
+  }
+  bf16x8_t qa[4][4];
+  float wreg[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int h = mb * 16 + n;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qa[mb][ks] = *reinterpret_cast<const bf16x8_t*>(q_lds + (h * kQStrideBf16 + 32 * ks + 8 * g) * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wreg[mb][i] = w_lds[mb * 16 + 4 * g + i];
+  }
+
+  float res[kStChunks / 2];  // chunks 2j, 2j+1: 64 scores, key s_begin + 64 j + lane
+  float part[4];
+#pragma unroll
+  for (int c = 0; c < kStChunks; ++c) {
+    if (c < nch) {  // wave-uniform
+      // chunk c has landed; chunks up to c + 3 go out behind it
+      const int ahead = min(kStBuffers - 2, nch - 1 - c);  // copies issued after chunk c
+      if (ahead >= 2)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else if (ahead == 1)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (c + kStBuffers - 1 < nch) issue_chunk(c + kStBuffers - 1);
+      const uint8_t* buf = kbuf + (wave * kStBuffers + (c % kStBuffers)) * kStChunkBytes;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t kv[4];
+        const uint8_t* rp = buf + (16 * u + n) * (kIdxDim * 2);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          kv[ks] = *reinterpret_cast<const bf16x8_t*>(rp + 16 * ((4 * ks + g) ^ ((n & 7) << 1)));
+        f32x4_t acc[4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x16x32_bf16(qa[mb][ks], kv[ks], acc[mb]);
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          p0 = fmaf(wreg[mb][0], fmaxf(acc[mb][0], 0.f), p0);
+          p1 = fmaf(wreg[mb][1], fmaxf(acc[mb][1], 0.f), p1);
+          p0 = fmaf(wreg[mb][2], fmaxf(acc[mb][2], 0.f), p0);
+          p1 = fmaf(wreg[mb][3], fmaxf(acc[mb][3], 0.f), p1);
+        }
+        part[2 * (c & 1) + u] = p0 + p1;
+      }
+    } else {
+      part[2 * (c & 1)] = 0.f;
+      part[2 * (c & 1) + 1] = 0.f;
+    }
+    if (c & 1) {  // cross-lane head sum of 4 tiles: lane l ends with key 64 (c / 2) + l
+      const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const float h0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+      const float h1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(h0), __float_as_uint(h1), false, false);
+      res[c >> 1] = idx_scale * (__uint_as_float(z[0]) + __uint_as_float(z[1]));
+    }
+  }
+  // ---- the wave's scores: one 256-byte run per two chunks; future keys -inf ----
+#pragma unroll
+  for (int j = 0; j < kStChunks / 2; ++j) {
+    const int s = s_begin + 64 * j + lane;
+    if (s < s_end) __builtin_nontemporal_store(s < s_lim ? res[j] : -__builtin_inff(), out_row + s);
+  }
+}
+
 template <int IDT, int WDT>
 dsa_status_t run_generic(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                          const void* k_idx, const uint8_t* k_sf, const void* w, float* scores,
@@ -463,6 +615,21 @@ dsa_status_t run_mfma(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_
 }
 
 template <int WDT>
+dsa_status_t run_stream(const dsa_shape_t& s, const void* q_idx, const void* k_idx, const void* w,
+                        float* scores, hipStream_t stream) {
+  const int nkb = (s.S + kStKeysPerBlock - 1) / kStKeysPerBlock;
+  const int64_t blocks = static_cast<int64_t>(s.B) * s.T * nkb;
+  if (blocks > 0x7fffffff)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: %lld key blocks", static_cast<long long>(blocks));
+  LaunchTimer timer;
+  hipExtLaunchKernelGGL(indexer_stream<WDT>, dim3(static_cast<unsigned>(blocks)), dim3(kStWaves * 64),
+                        0, stream, timer.start(), timer.stop(), 0, s.T, s.S, nkb, s.idx_scale,
+                        static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), w,
+                        scores);
+  return timer.done("indexer_stream");
+}
+
+template <int WDT>
 dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_idx,
                          const void* w, float* scores, hipStream_t stream) {
   const int n_qblk = (s.T + kPfWaves - 1) / kPfWaves;
@@ -487,6 +654,9 @@ dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8
   if (v32 && s.idx_dtype == DSA_BF16 && s.T >= kPfMinQueries)
     return wbf ? run_prefill<DSA_BF16>(s, q_idx, k_idx, w, scores, stream)
                : run_prefill<DSA_F32>(s, q_idx, k_idx, w, scores, stream);
+  if (v32 && s.idx_dtype == DSA_BF16)
+    return wbf ? run_stream<DSA_BF16>(s, q_idx, k_idx, w, scores, stream)
+               : run_stream<DSA_F32>(s, q_idx, k_idx, w, scores, stream);
   // the per-query kernels put the query row on grid.y
   if (static_cast<int64_t>(s.B) * s.T > 65535)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: B*T = %lld exceeds 65535 query rows",
