@@ -6,17 +6,17 @@
 // causal mask M added to it).  The head sum accumulates in fp32 and the
 // prefactor multiplies it once, after the sum.
 //
-// Two kernels:
-//  * indexer_mfma: 64 heads x 128 dims (the V3.2 indexer), bf16 or e4m3.
-//    One wave scores 16 keys at a time as a [64 heads] x [16 keys] MFMA tile
-//    (heads on the M side, keys on the N side, the 128 dims as the reduction),
-//    loading each key row straight from global memory into the MFMA operand
-//    registers: every key byte is read once, with no LDS round trip.  The
-//    query tile sits in registers for the wave's whole key range.  ReLU, the
-//    head weights and the head sum run on the accumulator registers: each
-//    lane holds 16 heads of one key, sums them, and two cross-lane adds finish
-//    the 64-head reduction.
+// Three kernels:
+//  * indexer_stream (few queries per sequence, 64 heads x 128 dims, bf16 or
+//    e4m3): each wave streams a run of key rows through its own LDS ring with
+//    whole-line direct copies and scores them on MFMAs against the query tile
+//    it keeps in registers.
+//  * indexer_prefill (8 or more queries per sequence, bf16): 8 queries per
+//    workgroup share every key chunk through LDS.
 //  * indexer_generic: any HI x DI, f32 / bf16 / e4m3, plain fp32 VALU loops.
+// ReLU, the head weights and the head sum run on the MFMA accumulator
+// registers: each lane holds 16 heads of one key and sums them, and lane
+// swaps finish the 64-head reduction.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -90,7 +90,7 @@ indexer_generic(int T, int S, int HI, int DI, float idx_scale, const void* __res
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel, HI = 64, DI = 128.
+// MFMA kernels, HI = 64, DI = 128.
 //
 // MFMA 16x16x32 operand layouts (lane l, g = l / 16, n = l % 16):
 //   A (16 x 32): lane holds row n, reduction elements 8g .. 8g+7
@@ -99,164 +99,13 @@ indexer_generic(int T, int S, int HI, int DI, float idx_scale, const void* __res
 // Rows are heads (4 blocks of 16), columns are keys.  The 128-wide reduction
 // is split in 4 steps; the dims of step ks in lane group g are chosen so that
 // a lane's 4 steps cover one contiguous run of the key row: bf16 uses dims
-// 32*ks + 8*g + e (each step is one 16-byte load per lane, a 64-byte run per
-// key), fp8 uses dims 32*g + 8*ks + e (each lane loads 32 contiguous bytes).
+// 32*ks + 8*g + e (each step one 16-byte read per lane, a 64-byte run per
+// key), fp8 uses dims 32*g + 8*ks + e (32 contiguous bytes per lane).
 // ---------------------------------------------------------------------------
 constexpr int kIdxHeads = 64;
 constexpr int kIdxDim = 128;
-constexpr int kIdxWaves = 4;
-constexpr int kKeysPerWave = 128;   // 8 tiles of 16 keys
-constexpr int kTilesPerGroup = 4;    // tiles whose loads are issued together
 constexpr int kQStrideBf16 = kIdxDim + 8;   // padded LDS row (elements)
 constexpr int kQStrideFp8 = kIdxDim + 16;   // padded LDS row (bytes)
-
-template <bool FP8, int WDT>
-__global__ void __launch_bounds__(kIdxWaves * 64)
-indexer_mfma(int T, int S, float idx_scale, const void* __restrict__ q_idx,
-             const uint8_t* __restrict__ q_sf, const void* __restrict__ k_idx,
-             const uint8_t* __restrict__ k_sf, const void* __restrict__ w,
-             float* __restrict__ scores) {
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kIdxHeads * kQStrideBf16 * 2];
-  __shared__ float w_lds[kIdxHeads];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;
-  const int n = lane & 15;
-  const int64_t row = blockIdx.y;  // b * T + t
-  const int b = static_cast<int>(row / T);
-  const int t = static_cast<int>(row % T);
-  const int q_pos = S - T + t;
-  const int s_lim = min(S, q_pos + 1);  // keys [0, s_lim) are visible
-
-  const int s_begin = (blockIdx.x * kIdxWaves + wave) * kKeysPerWave;
-  const int s_end = min(S, s_begin + kKeysPerWave);
-  const bool active = s_begin < S && s_begin < s_lim;  // this wave has visible keys
-  const int64_t kbase = static_cast<int64_t>(b) * S;
-  // Key rows of a group of kTilesPerGroup 16-key tiles (keys past the visible
-  // range load row s_lim - 1, so every address stays in bounds).
-  auto load_group = [&](int s0, u32x4_t (&kb)[kTilesPerGroup][4], float (&ksc)[kTilesPerGroup]) {
-#pragma unroll
-    for (int j = 0; j < kTilesPerGroup; ++j) {
-      const int s = min(s0 + 16 * j + n, s_lim - 1);
-      if constexpr (!FP8) {
-        const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(
-            static_cast<const uint16_t*>(k_idx) + (kbase + s) * kIdxDim);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kb[j][ks] = __builtin_nontemporal_load(kr + 4 * ks + g);
-      } else {
-        const u32x4_t* kr = reinterpret_cast<const u32x4_t*>(
-            static_cast<const uint8_t*>(k_idx) + (kbase + s) * kIdxDim);
-        kb[j][0] = __builtin_nontemporal_load(kr + 2 * g);
-        kb[j][1] = __builtin_nontemporal_load(kr + 2 * g + 1);
-        ksc[j] = ue8m0_to_f32(k_sf[kbase + s]);
-      }
-    }
-  };
-  // the first key group goes out before the query is staged: both latencies overlap
-  u32x4_t kb0[kTilesPerGroup][4], kb1[kTilesPerGroup][4];
-  float ksc0[kTilesPerGroup] = {}, ksc1[kTilesPerGroup] = {};
-  if (active) load_group(s_begin, kb0, ksc0);
-
-  // ---- stage the query row (and w, times the query scales for fp8) ----
-  if constexpr (!FP8) {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
-        static_cast<const uint16_t*>(q_idx) + row * kIdxHeads * kIdxDim);
-    for (int i = threadIdx.x; i < kIdxHeads * kIdxDim / 8; i += blockDim.x) {
-      const int h = i / (kIdxDim / 8), c = i % (kIdxDim / 8);
-      *reinterpret_cast<u32x4_t*>(q_lds + (h * kQStrideBf16 + c * 8) * 2) = src[i];
-    }
-  } else {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
-        static_cast<const uint8_t*>(q_idx) + row * kIdxHeads * kIdxDim);
-    for (int i = threadIdx.x; i < kIdxHeads * kIdxDim / 16; i += blockDim.x) {
-      const int h = i / (kIdxDim / 16), c = i % (kIdxDim / 16);
-      *reinterpret_cast<u32x4_t*>(q_lds + h * kQStrideFp8 + c * 16) = src[i];
-    }
-  }
-  for (int h = threadIdx.x; h < kIdxHeads; h += blockDim.x) {
-    float wv = load_w<WDT>(w, row * kIdxHeads + h);
-    if constexpr (FP8) wv *= ue8m0_to_f32(q_sf[row * kIdxHeads + h]);
-    w_lds[h] = wv;
-  }
-  __syncthreads();
-
-  if (s_begin >= S) return;
-  float* out_row = scores + row * S;
-
-  if (s_begin >= s_lim) {  // every key of this wave is in the future
-    for (int s = s_begin + lane; s < s_end; s += 64) out_row[s] = -__builtin_inff();
-    return;
-  }
-
-  // ---- query operand (A) and head weights in registers ----
-  bf16x8_t qa[4][4];
-  long qa8[4][4];
-  float wreg[4][4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int h = mb * 16 + n;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if constexpr (!FP8)
-        qa[mb][ks] = *reinterpret_cast<const bf16x8_t*>(q_lds + (h * kQStrideBf16 + 32 * ks + 8 * g) * 2);
-      else
-        qa8[mb][ks] = *reinterpret_cast<const long*>(q_lds + h * kQStrideFp8 + 32 * g + 8 * ks);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wreg[mb][i] = w_lds[mb * 16 + 4 * g + i];
-  }
-
-  auto score_group = [&](int s0, const u32x4_t (&kb)[kTilesPerGroup][4],
-                         const float (&ksc)[kTilesPerGroup]) {
-#pragma unroll
-    for (int j = 0; j < kTilesPerGroup; ++j) {
-      f32x4_t acc[4];
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          if constexpr (!FP8) {
-            acc[mb] = mfma16x16x32_bf16(qa[mb][ks], __builtin_bit_cast(bf16x8_t, kb[j][ks]), acc[mb]);
-          } else {
-            // 32 contiguous bytes per lane: step ks takes bytes 8ks .. 8ks+7
-            const u32x4_t half = kb[j][ks >> 1];
-            const long kv = (ks & 1) ? (static_cast<long>(half[3]) << 32 | half[2])
-                                     : (static_cast<long>(half[1]) << 32 | half[0]);
-            acc[mb] = mfma16x16x32_fp8(qa8[mb][ks], kv, acc[mb]);
-          }
-        }
-      }
-      float part = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part = fmaf(wreg[mb][i], fmaxf(acc[mb][i], 0.f), part);
-      part = xor16_sum(part);
-      part = xor32_sum(part);
-      const int s = s0 + 16 * j + n;
-      if (g == 0 && s < s_end) {
-        float v;
-        if constexpr (FP8) v = idx_scale * (part * ksc[j]);
-        else v = idx_scale * part;
-        out_row[s] = (s < s_lim) ? v : -__builtin_inff();
-      }
-    }
-  };
-
-  // two-stage pipeline: the next group's key rows load while this group scores
-  constexpr int kGroupKeys = 16 * kTilesPerGroup;
-#pragma unroll
-  for (int grp = 0; grp < kKeysPerWave / kGroupKeys; grp += 2) {
-    const int s0 = s_begin + grp * kGroupKeys;
-    const int s1 = s0 + kGroupKeys;
-    if (s1 < s_end) load_group(s1, kb1, ksc1);
-    if (s0 < s_end) score_group(s0, kb0, ksc0);
-    if (s1 + kGroupKeys < s_end) load_group(s1 + kGroupKeys, kb0, ksc0);
-    if (s1 < s_end) score_group(s1, kb1, ksc1);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Query-blocked MFMA kernel for many queries per sequence (prefill), bf16,
@@ -434,36 +283,57 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
-// Streaming MFMA kernel for few queries per sequence (decode), bf16, HI = 64,
-// DI = 128.
+// Streaming MFMA kernel for few queries per sequence (decode), HI = 64,
+// DI = 128, bf16 or e4m3.
 //
 // Decode reads every key row of the sequence once per query: the kernel is a
-// stream of k^I from HBM.  Each wave owns 256 consecutive keys and moves them
-// through a private ring of four 8 KB LDS buffers with whole-line direct
+// stream of k^I from HBM.  Each wave owns a run of consecutive keys and moves
+// them through a private ring of four 8 KB LDS buffers with whole-line direct
 // copies (global_load_lds_dwordx4: 1 KB of contiguous key rows per
-// instruction), three 32-key chunks in flight while one is scored; per-lane
-// operand loads, whose 16 lanes per key row touch 64-byte pieces, stream
-// slower.  No barrier is needed after the query is staged (each wave reads
-// only what it copied).  The operands are read as in the prefill kernel (row
-// r's piece c in slot c ^ ((r & 7) << 1)), and every two chunks (4 tiles)
-// finish with the same reduce-scatter, so each wave keeps its 256 scores in 4
-// registers and stores them at the end, after its last load.
+// instruction), three chunks in flight while one is scored; per-lane operand
+// loads, whose 16 lanes per key row touch 64-byte pieces, stream slower.  No
+// barrier is needed after the query is staged (each wave reads only what it
+// copied).
+//  * bf16: a key row is 256 bytes, a chunk 32 keys (two 16-key tiles); row
+//    r's 16-byte piece c sits in slot c ^ ((r & 7) << 1) and operand step ks
+//    of lane (g, n) reads piece 4 ks + g of row n, as in the prefill kernel.
+//  * e4m3: a key row is 128 bytes, a chunk 64 keys (four tiles); piece c of
+//    row r sits in slot c ^ ((r >> 1) & 7), and lane (g, n) reads pieces 2g
+//    and 2g + 1 of row n (its 32 contiguous bytes, the dims of the four
+//    fp8 MFMA steps).  Every 16 lanes of a 16-byte read then cover the 64
+//    banks once.  The key block scales (one byte per key row) multiply the
+//    head sums at the end; the query block scales are folded into w.
+// Every 4 tiles finish with a reduce-scatter of the head sums (3 lane swaps,
+// 3 adds) that leaves one key's score per lane, so each wave keeps its scores
+// in a few registers and stores them at the end, after its last copy.
 // ---------------------------------------------------------------------------
 constexpr int kStWaves = 4;
-constexpr int kStChunkKeys = 32;                              // keys per chunk
-constexpr int kStChunkBytes = kStChunkKeys * kIdxDim * 2;     // 8 KB
+constexpr int kStChunkBytes = 8192;                           // per chunk
 constexpr int kStBuffers = 4;                                 // per wave
 constexpr int kStChunks = 8;                                  // chunks per wave
-constexpr int kStKeysPerBlock = kStWaves * kStChunks * kStChunkKeys;  // 1024
 constexpr int kStCopies = kStChunkBytes / 1024;               // 8 copies per chunk
 
-template <int WDT>
+template <bool FP8>
+struct StreamShape {
+  static constexpr int kRowBytes = FP8 ? kIdxDim : 2 * kIdxDim;
+  static constexpr int kChunkKeys = kStChunkBytes / kRowBytes;  // 64 / 32
+  static constexpr int kTiles = kChunkKeys / 16;                // per chunk
+  static constexpr int kWaveKeys = kStChunks * kChunkKeys;      // 512 / 256
+  static constexpr int kBlockKeys = kStWaves * kWaveKeys;       // 2048 / 1024
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;         // 8 / 4
+  static constexpr int kResults = kWaveKeys / 64;               // scores per lane
+};
+
+template <bool FP8, int WDT>
 __global__ void __launch_bounds__(kStWaves * 64)
-indexer_stream(int T, int S, int nkb, float idx_scale, const uint16_t* __restrict__ q_idx,
-               const uint16_t* __restrict__ k_idx, const void* __restrict__ w,
+indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict__ q_idx,
+               const uint8_t* __restrict__ q_sf, const uint8_t* __restrict__ k_idx,
+               const uint8_t* __restrict__ k_sf, const void* __restrict__ w,
                float* __restrict__ scores) {
+  using Sh = StreamShape<FP8>;
+  constexpr int kQRow = FP8 ? kQStrideFp8 : kQStrideBf16 * 2;  // staged query row, bytes
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kStWaves * kStBuffers * kStChunkBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kIdxHeads * kQStrideBf16 * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kIdxHeads * kQRow];
   __shared__ float w_lds[kIdxHeads];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -474,37 +344,58 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint16_t* __restric
   const int b = static_cast<int>(row / T);
   const int t = static_cast<int>(row % T);
   const int s_lim = min(S, S - T + t + 1);  // keys [0, s_lim) are visible
-  const int s_begin = (kb * kStWaves + wave) * (kStChunks * kStChunkKeys);
-  const int s_end = min(S, s_begin + kStChunks * kStChunkKeys);
+  const int s_begin = (kb * kStWaves + wave) * Sh::kWaveKeys;
+  const int s_end = min(S, s_begin + Sh::kWaveKeys);
   const int s_vis = min(s_end, s_lim);  // this wave scores [s_begin, s_vis)
-  const int nch = s_vis > s_begin ? (s_vis - s_begin + kStChunkKeys - 1) / kStChunkKeys : 0;
+  const int nch = s_vis > s_begin ? (s_vis - s_begin + Sh::kChunkKeys - 1) / Sh::kChunkKeys : 0;
   const int64_t kbase = static_cast<int64_t>(b) * S;
   const uint32_t wlds = lds_addr(kbuf) + wave * kStBuffers * kStChunkBytes;
 
-  // chunk c -> buffer c % 4; copy i covers chunk rows 4i .. 4i+3 (keys past
-  // the visible range load row s_vis - 1: every address stays in bounds)
+  // e4m3 key scale bytes, one per score this lane ends with (issued first:
+  // they retire before every copy, so the copy waits below cover them;
+  // s_vis >= 1, so the clamped key is a valid row)
+  uint8_t ksb[Sh::kResults];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < Sh::kResults; ++j) ksb[j] = k_sf[kbase + min(s_begin + 64 * j + lane, s_vis - 1)];
+  }
+
+  // chunk c -> buffer c % 4; copy i covers chunk rows kRowsPerCopy * i ..
+  // (keys past the visible range load row s_vis - 1: every address stays in
+  // bounds)
   auto issue_chunk = [&](int c) {
     const uint32_t dst = wlds + (c % kStBuffers) * kStChunkBytes;
 #pragma unroll
     for (int i = 0; i < kStCopies; ++i) {
-      const int r = 4 * i + (lane >> 4);
-      const int piece = (lane & 15) ^ ((r & 7) << 1);
-      const int key = min(s_begin + c * kStChunkKeys + r, s_vis - 1);
-      lds_dma_16_nt(k_idx + (kbase + key) * kIdxDim + piece * 8, dst + 1024 * i);
+      int r, piece;
+      if constexpr (FP8) {
+        r = 8 * i + (lane >> 3);
+        piece = (lane & 7) ^ ((r >> 1) & 7);
+      } else {
+        r = 4 * i + (lane >> 4);
+        piece = (lane & 15) ^ ((r & 7) << 1);
+      }
+      const int key = min(s_begin + c * Sh::kChunkKeys + r, s_vis - 1);
+      lds_dma_16_nt(k_idx + (kbase + key) * Sh::kRowBytes + piece * 16, dst + 1024 * i);
     }
   };
 #pragma unroll
   for (int c = 0; c < kStBuffers - 1; ++c)
     if (c < nch) issue_chunk(c);
 
-  // ---- stage the query row and the head weights ----
+  // ---- stage the query row and the head weights (times the query scales) ----
   {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(q_idx + row * kIdxHeads * kIdxDim);
-    for (int i = threadIdx.x; i < kIdxHeads * kIdxDim / 8; i += blockDim.x) {
-      const int h = i / (kIdxDim / 8), c = i % (kIdxDim / 8);
-      *reinterpret_cast<u32x4_t*>(q_lds + (h * kQStrideBf16 + c * 8) * 2) = src[i];
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(q_idx + row * kIdxHeads * Sh::kRowBytes);
+    constexpr int kPieces = Sh::kRowBytes / 16;
+    for (int i = threadIdx.x; i < kIdxHeads * kPieces; i += blockDim.x) {
+      const int h = i / kPieces, c = i % kPieces;
+      *reinterpret_cast<u32x4_t*>(q_lds + h * kQRow + c * 16) = src[i];
     }
-    for (int h = threadIdx.x; h < kIdxHeads; h += blockDim.x) w_lds[h] = load_w<WDT>(w, row * kIdxHeads + h);
+    for (int h = threadIdx.x; h < kIdxHeads; h += blockDim.x) {
+      float wv = load_w<WDT>(w, row * kIdxHeads + h);
+      if constexpr (FP8) wv *= ue8m0_to_f32(q_sf[row * kIdxHeads + h]);
+      w_lds[h] = wv;
+    }
   }
   __syncthreads();
 
@@ -514,24 +405,31 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint16_t* __restric
     return;
   }
   bf16x8_t qa[4][4];
+  long qa8[4][4];
   float wreg[4][4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int h = mb * 16 + n;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qa[mb][ks] = *reinterpret_cast<const bf16x8_t*>(q_lds + (h * kQStrideBf16 + 32 * ks + 8 * g) * 2);
+    for (int ks = 0; ks < 4; ++ks) {
+      if constexpr (FP8)
+        qa8[mb][ks] = *reinterpret_cast<const long*>(q_lds + h * kQRow + 32 * g + 8 * ks);
+      else
+        qa[mb][ks] = *reinterpret_cast<const bf16x8_t*>(q_lds + h * kQRow + (32 * ks + 8 * g) * 2);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) wreg[mb][i] = w_lds[mb * 16 + 4 * g + i];
   }
 
-  float res[kStChunks / 2];  // chunks 2j, 2j+1: 64 scores, key s_begin + 64 j + lane
+  float res[Sh::kResults];  // lane l: key s_begin + 64 j + l
   float part[4];
 #pragma unroll
   for (int c = 0; c < kStChunks; ++c) {
+    constexpr int kT = Sh::kTiles;
+    const int p0 = (c * kT) & 3;  // first part slot of this chunk
     if (c < nch) {  // wave-uniform
       // chunk c has landed; chunks up to c + 3 go out behind it
-      const int ahead = min(kStBuffers - 2, nch - 1 - c);  // copies issued after chunk c
+      const int ahead = min(kStBuffers - 2, nch - 1 - c);  // chunks issued after chunk c
       if (ahead >= 2)
         asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
       else if (ahead == 1)
@@ -541,47 +439,66 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint16_t* __restric
       if (c + kStBuffers - 1 < nch) issue_chunk(c + kStBuffers - 1);
       const uint8_t* buf = kbuf + (wave * kStBuffers + (c % kStBuffers)) * kStChunkBytes;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8_t kv[4];
-        const uint8_t* rp = buf + (16 * u + n) * (kIdxDim * 2);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kv[ks] = *reinterpret_cast<const bf16x8_t*>(rp + 16 * ((4 * ks + g) ^ ((n & 7) << 1)));
+      for (int u = 0; u < kT; ++u) {
+        const uint8_t* rp = buf + (16 * u + n) * Sh::kRowBytes;
         f32x4_t acc[4];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (FP8) {
+          const int f = (n >> 1) & 7;  // (row >> 1) & 7 of row 16 u + n
+          u32x4_t kv[2];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+          for (int j = 0; j < 2; ++j)
+            kv[j] = *reinterpret_cast<const u32x4_t*>(rp + 16 * ((2 * g + j) ^ f));
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x16x32_bf16(qa[mb][ks], kv[ks], acc[mb]);
-        float p0 = 0.f, p1 = 0.f;
+          for (int ks = 0; ks < 4; ++ks) {
+            const u32x4_t half = kv[ks >> 1];
+            const long kk = (ks & 1) ? (static_cast<long>(half[3]) << 32 | half[2])
+                                     : (static_cast<long>(half[1]) << 32 | half[0]);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x16x32_fp8(qa8[mb][ks], kk, acc[mb]);
+          }
+        } else {
+          bf16x8_t kv[4];
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            kv[ks] = *reinterpret_cast<const bf16x8_t*>(rp + 16 * ((4 * ks + g) ^ ((n & 7) << 1)));
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x16x32_bf16(qa[mb][ks], kv[ks], acc[mb]);
+        }
+        float h0 = 0.f, h1 = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-          p0 = fmaf(wreg[mb][0], fmaxf(acc[mb][0], 0.f), p0);
-          p1 = fmaf(wreg[mb][1], fmaxf(acc[mb][1], 0.f), p1);
-          p0 = fmaf(wreg[mb][2], fmaxf(acc[mb][2], 0.f), p0);
-          p1 = fmaf(wreg[mb][3], fmaxf(acc[mb][3], 0.f), p1);
+          h0 = fmaf(wreg[mb][0], fmaxf(acc[mb][0], 0.f), h0);
+          h1 = fmaf(wreg[mb][1], fmaxf(acc[mb][1], 0.f), h1);
+          h0 = fmaf(wreg[mb][2], fmaxf(acc[mb][2], 0.f), h0);
+          h1 = fmaf(wreg[mb][3], fmaxf(acc[mb][3], 0.f), h1);
         }
-        part[2 * (c & 1) + u] = p0 + p1;
+        part[p0 + u] = h0 + h1;
       }
     } else {
-      part[2 * (c & 1)] = 0.f;
-      part[2 * (c & 1) + 1] = 0.f;
+#pragma unroll
+      for (int u = 0; u < kT; ++u) part[p0 + u] = 0.f;
     }
-    if (c & 1) {  // cross-lane head sum of 4 tiles: lane l ends with key 64 (c / 2) + l
+    if (((c + 1) * kT) % 4 == 0) {  // cross-lane head sum of 4 tiles: lane l ends with key 64 j + l
       const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
       const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
-      const float h0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
-      const float h1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-      const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(h0), __float_as_uint(h1), false, false);
-      res[c >> 1] = idx_scale * (__uint_as_float(z[0]) + __uint_as_float(z[1]));
+      const float e0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+      const float e1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(e0), __float_as_uint(e1), false, false);
+      res[(c * kT) / 4] = __uint_as_float(z[0]) + __uint_as_float(z[1]);
     }
   }
-  // ---- the wave's scores: one 256-byte run per two chunks; future keys -inf ----
+  // ---- the wave's scores: one 256-byte run per 64 keys; future keys -inf ----
 #pragma unroll
-  for (int j = 0; j < kStChunks / 2; ++j) {
+  for (int j = 0; j < Sh::kResults; ++j) {
     const int s = s_begin + 64 * j + lane;
-    if (s < s_end) __builtin_nontemporal_store(s < s_lim ? res[j] : -__builtin_inff(), out_row + s);
+    float v;
+    if constexpr (FP8) v = idx_scale * (res[j] * ue8m0_to_f32(ksb[j]));
+    else v = idx_scale * res[j];
+    if (s < s_end) __builtin_nontemporal_store(s < s_lim ? v : -__builtin_inff(), out_row + s);
   }
 }
 
@@ -602,30 +519,19 @@ dsa_status_t run_generic(const dsa_shape_t& s, const void* q_idx, const uint8_t*
 }
 
 template <bool FP8, int WDT>
-dsa_status_t run_mfma(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
-                      const void* k_idx, const uint8_t* k_sf, const void* w, float* scores,
-                      hipStream_t stream) {
-  const int keys_per_block = kIdxWaves * kKeysPerWave;
-  dim3 grid((s.S + keys_per_block - 1) / keys_per_block, s.B * s.T);
-  LaunchTimer timer;
-  hipExtLaunchKernelGGL(indexer_mfma<FP8, WDT>, grid, dim3(kIdxWaves * 64), 0, stream,
-                        timer.start(), timer.stop(), 0, s.T, s.S, s.idx_scale, q_idx, q_sf, k_idx,
-                        k_sf, w, scores);
-  return timer.done("indexer_mfma");
-}
-
-template <int WDT>
-dsa_status_t run_stream(const dsa_shape_t& s, const void* q_idx, const void* k_idx, const void* w,
-                        float* scores, hipStream_t stream) {
-  const int nkb = (s.S + kStKeysPerBlock - 1) / kStKeysPerBlock;
+dsa_status_t run_stream(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
+                        const void* k_idx, const uint8_t* k_sf, const void* w, float* scores,
+                        hipStream_t stream) {
+  constexpr int kBlockKeys = StreamShape<FP8>::kBlockKeys;
+  const int nkb = (s.S + kBlockKeys - 1) / kBlockKeys;
   const int64_t blocks = static_cast<int64_t>(s.B) * s.T * nkb;
   if (blocks > 0x7fffffff)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: %lld key blocks", static_cast<long long>(blocks));
   LaunchTimer timer;
-  hipExtLaunchKernelGGL(indexer_stream<WDT>, dim3(static_cast<unsigned>(blocks)), dim3(kStWaves * 64),
-                        0, stream, timer.start(), timer.stop(), 0, s.T, s.S, nkb, s.idx_scale,
-                        static_cast<const uint16_t*>(q_idx), static_cast<const uint16_t*>(k_idx), w,
-                        scores);
+  hipExtLaunchKernelGGL(indexer_stream<FP8, WDT>, dim3(static_cast<unsigned>(blocks)),
+                        dim3(kStWaves * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
+                        nkb, s.idx_scale, static_cast<const uint8_t*>(q_idx), q_sf,
+                        static_cast<const uint8_t*>(k_idx), k_sf, w, scores);
   return timer.done("indexer_stream");
 }
 
@@ -655,18 +561,15 @@ dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8
     return wbf ? run_prefill<DSA_BF16>(s, q_idx, k_idx, w, scores, stream)
                : run_prefill<DSA_F32>(s, q_idx, k_idx, w, scores, stream);
   if (v32 && s.idx_dtype == DSA_BF16)
-    return wbf ? run_stream<DSA_BF16>(s, q_idx, k_idx, w, scores, stream)
-               : run_stream<DSA_F32>(s, q_idx, k_idx, w, scores, stream);
-  // the per-query kernels put the query row on grid.y
+    return wbf ? run_stream<false, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
+               : run_stream<false, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
+  if (v32 && s.idx_dtype == DSA_FP8_E4M3)
+    return wbf ? run_stream<true, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
+               : run_stream<true, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
+  // the generic kernel puts the query row on grid.y
   if (static_cast<int64_t>(s.B) * s.T > 65535)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: B*T = %lld exceeds 65535 query rows",
                 static_cast<long long>(s.B) * s.T);
-  if (v32 && s.idx_dtype == DSA_BF16)
-    return wbf ? run_mfma<false, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
-               : run_mfma<false, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
-  if (v32 && s.idx_dtype == DSA_FP8_E4M3)
-    return wbf ? run_mfma<true, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
-               : run_mfma<true, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
   switch (s.idx_dtype) {
     case DSA_F32:
       return wbf ? run_generic<DSA_F32, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)

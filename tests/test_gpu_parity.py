@@ -97,6 +97,12 @@ SCORE_CASES = {
     "prefill_real": g.CONFIGS["prefill_16k"].replace(B=2, T=203, S=203),
     # MFMA e4m3 kernel, integer twin (scale byte 127): bit-exact
     "fp8_int": g.CONFIGS["decode_64k_fp8"].replace(B=2, S=4200, integer=True),
+    # e4m3, three queries per sequence (causal tail), fp32 head weights, the
+    # second key block holding one partial chunk
+    "fp8_int_t3": g.CONFIGS["decode_64k_fp8"].replace(B=2, T=3, S=2100, w_dtype="f32",
+                                                      integer=True),
+    # e4m3, fewer keys than one chunk
+    "fp8_int_short": g.CONFIGS["decode_64k_fp8"].replace(B=3, S=40, integer=True),
     # real-valued: within 1e-4 of the row max
     "decode_real": g.CONFIGS["decode_8k"].replace(B=2, S=3000),
     "fp8_real": g.CONFIGS["decode_64k_fp8"].replace(B=2, S=5000),
