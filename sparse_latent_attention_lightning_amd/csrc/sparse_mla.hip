@@ -257,9 +257,6 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   __shared__ __attribute__((aligned(1024))) MlaTile tiles[kBuffers];
   // a window of the split's index entries as key rows (-1: skipped entry)
   __shared__ __attribute__((aligned(16))) int32_t idxw[kIdxWin];
-  // validity of each tile's rows (bit r: tile row r holds a valid key), written
-  // when the tile's copies are issued, two iterations before its use
-  __shared__ uint32_t vmask[kBuffers + 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -359,21 +356,16 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   struct TileCopies {
     const int32_t* wrow;  // the tile's 32 index entries in the window
     uint32_t lds;
-    int t;
   };
-  // the tile's validity mask, published by wave 0 (`entry`: its index entry
-  // lane & 31, read earlier so that the read's latency stays hidden)
-  auto publish_mask = [&](int t, int entry) {
-    if (wave == 0) {
-      const uint32_t vm = static_cast<uint32_t>(__ballot(entry >= 0));
-      if (lane == 0) vmask[t % (kBuffers + 1)] = vm;
-    }
-  };
+  // the tile's validity mask (bit r: tile row r holds a valid key), formed by
+  // every wave for itself from the index entries when the tile's copies go
+  // out (`entry`: entry lane & 31, read earlier so that its latency stays
+  // hidden); kept in scalar registers until the tile's logits
+  auto tile_mask = [&](int entry) { return static_cast<uint32_t>(__ballot(entry >= 0)); };
   auto prep_tile = [&](int t) {
     TileCopies c;
     c.wrow = &idxw[(t % kWinTiles) * kTileKeys];
     c.lds = lds_addr(tiles[(t + 2) % kBuffers].bytes);
-    c.t = t;
     return c;
   };
   // key row of copy k (0..7: tile row 8w + k, all lanes; 8: row 8w + lane/8),
@@ -397,9 +389,10 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     int keys[kCopiesPerTile];
 #pragma unroll
     for (int k = 0; k < kCopiesPerTile; ++k) keys[k] = copy_key(c, k);
-    publish_mask(t, c.wrow[lane & 31]);
+    const uint32_t vm = tile_mask(c.wrow[lane & 31]);
 #pragma unroll
     for (int k = 0; k < kCopiesPerTile; ++k) copy_row(c, k, keys[k]);
+    return vm;
   };
   // wait until at most `pending` later tiles' copies of this wave are in flight
   auto wait_tiles = [&](int pending) {
@@ -430,7 +423,10 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   // start-up: every wave has its query in registers, the ring is free; tiles
   // 0 and 1 go out
   __syncthreads();
-  for (int t = 0; t < 2 && t < ntiles; ++t) issue_tile(t);
+  // masks of the tile of the next logits and of the one after it
+  uint32_t vm_a = 0u, vm_b = 0u;
+  if (ntiles > 0) vm_a = issue_tile(0);
+  if (ntiles > 1) vm_b = issue_tile(1);
 
   // Online softmax with a fixed reference max per head: the first tile with a
   // valid key sets it, and p = 2^(x - ref) stays below 2^kRefSlack as long as
@@ -454,8 +450,10 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       store_window();
       __syncthreads();
     }
-    if (pass == 1)
-      for (int t = 0; t < 2 && t < ntiles; ++t) issue_tile(t);
+    if (pass == 1) {
+      if (ntiles > 0) vm_a = issue_tile(0);
+      if (ntiles > 1) vm_b = issue_tile(1);
+    }
 
     f32x16_t sacc;   // logits^T of the current tile (raw dot products)
     bf16x8_t pb[2];  // P^T of the previous tile, key steps 0 and 1
@@ -463,7 +461,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
 
     // ---- logits^T of tile it, with the copies of tile it + 2 ----
     // COPIES: with the copies of the tile two ahead (all but the last two tiles)
-    auto logits = [&](auto copies_tag, lds_char_t* cur, const TileCopies& nxt) {
+    auto logits = [&](auto copies_tag, lds_char_t* cur, const TileCopies& nxt, uint32_t& vm_nxt) {
       constexpr bool copies = decltype(copies_tag)::value;
       auto aload = [&](int ks) {
         const int off = ks < kLatSteps ? aoff[ks & 1] + 64 * (ks >> 1) : roff[ks - kLatSteps];
@@ -473,7 +471,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
 #pragma unroll
       for (int ks = 0; ks < kReadAhead; ++ks) ka[ks] = aload(ks);
       int key = copies ? copy_key(nxt, 0) : 0;
-      const int entry = copies && wave == 0 ? nxt.wrow[lane & 31] : 0;
+      const int entry = copies ? nxt.wrow[lane & 31] : 0;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         if (ks == 0)
@@ -485,7 +483,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
         // is read with step 4k - 1
         if (ks % 4 == 3 && ks / 4 + 1 < kCopiesPerTile && copies) key = copy_key(nxt, ks / 4 + 1);
         if (ks % 4 == 1 && ks / 4 < kCopiesPerTile && copies) copy_row(nxt, ks / 4, key);
-        if (ks == 6 && copies) publish_mask(nxt.t, entry);
+        if (ks == 6 && copies) vm_nxt = tile_mask(entry);
         __builtin_amdgcn_sched_barrier(0);
       }
       mfma32_drain(sacc);
@@ -595,11 +593,14 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
         nxt = prep_tile(t);
       }
       lds_char_t* cur = (lds_char_t*)(tiles[(it + 2) % kBuffers].bytes);
-      const uint32_t vm = __builtin_amdgcn_readfirstlane(vmask[it % (kBuffers + 1)]);
+      const uint32_t vm = vm_a;  // tile it
+      uint32_t vm_nxt = 0u;      // tile it + 2
       if (copies)
-        logits(std::true_type{}, cur, nxt);
+        logits(std::true_type{}, cur, nxt, vm_nxt);
       else
-        logits(std::false_type{}, cur, nxt);
+        logits(std::false_type{}, cur, nxt, vm_nxt);
+      vm_a = vm_b;
+      vm_b = vm_nxt;
       if (vm != 0xffffffffu) {  // skipped rows in this tile: their logits are -inf
         const uint32_t bits = (vm >> (4 * hl)) & 0x0f0f0f0fu;  // bit 8(i/4) + i%4: key of register i
 #pragma unroll
