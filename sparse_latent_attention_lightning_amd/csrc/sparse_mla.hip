@@ -380,7 +380,9 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     asm volatile("" : "+v"(s));
     s = max(s, 0);
     const int lo = k < 8 ? lat_lo[k >> 2] : rope_lo;
-    const uint32_t dst = k < 8 ? c.lds + kLatStride * (8 * wave + k) : c.lds + kRopeBase + 1024 * wave;
+    // (wave-uniform; readfirstlane keeps it in a scalar register for m0)
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(
+        k < 8 ? c.lds + kLatStride * (8 * wave + k) : c.lds + kRopeBase + 1024 * wave);
     lds_dma_16_sbase(kvb, static_cast<uint32_t>(s) * static_cast<uint32_t>(kD * 2) + lo, dst);
   };
   // all of a tile's copies at once (start-up): the key reads go out together
