@@ -72,14 +72,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// inclusive prefix sum over the 64 lanes of a wave
+// inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves (no
+// LDS round trips): shifts by 1, 2, 4 and 8 lanes within each 16-lane row
+// (lanes shifted in from outside the row add 0), then the row totals are
+// broadcast forward (lane 15 of rows 0 and 2 into rows 1 and 3, lane 31 into
+// rows 2 and 3; rows outside the row mask keep `old` = 0 and add nothing)
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
+  constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowShr + 1, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowShr + 2, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowShr + 4, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowShr + 8, 0xf, 0xf, true);
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowBcast15, 0xa, 0xf, false);
+  v += __builtin_amdgcn_update_dpp(0u, v, kRowBcast31, 0xc, 0xf, false);
   return v;
 }
 

@@ -35,9 +35,9 @@ constexpr int kPass1Bins = 4096;                 // 12 bits
 constexpr int kPassBins = 1024;                  // 10 bits (passes 2 and 3)
 constexpr int kSmallCand = 16;                   // boundary bins this small are ranked by one wave
 
-struct TopkLds {
+struct alignas(16) TopkLds {
   uint32_t hist[2][kPass1Bins];     // ping-pong: pass p counts into hist[p & 1]
-  uint32_t wave_tot[2][kTopkWaves];  // ping-pong scan scratch
+  uint32_t wave_tot[2][kTopkWaves];  // ping-pong scan scratch (16-byte aligned rows)
   uint32_t sel[3][2];                // per pass: boundary bin, count above it
   uint32_t cand_key[kSmallCand];
   int32_t cand_idx[kSmallCand];
@@ -55,36 +55,52 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
   const uint32_t inc = wave_inclusive_scan(v);
   if (lane == 63) wave_tot[wave] = inc;
   __syncthreads();
+  static_assert(kTopkWaves % 4 == 0, "wave totals read 4 at a time");
   uint32_t before = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kTopkWaves; ++i) {
-    const uint32_t t = wave_tot[i];
-    before += (i < wave) ? t : 0u;
-    tot += t;
+  for (int q = 0; q < kTopkWaves / 4; ++q) {
+    const uint4 t4 = reinterpret_cast<const uint4*>(wave_tot)[q];
+    const uint32_t t[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      before += (4 * q + e < wave) ? t[e] : 0u;
+      tot += t[e];
+    }
   }
   *total = tot;
   return before + inc - v;
 }
 
-// Bins [nb - (t+1)*per, nb - t*per) belong to thread t (scanned from the top):
+// Bins [NB - (t+1)*per, NB - t*per) belong to thread t (scanned from the top):
 // find the bin where the running count from the top reaches k_rem; the owner
 // thread records it and the count above it in sel.  Returns the histogram's
-// total (no bin is recorded when it is below k_rem).
-__device__ __forceinline__ uint32_t find_boundary(const uint32_t* hist, int nb, uint32_t k_rem,
+// total (no bin is recorded when it is below k_rem).  A thread's bins are
+// read once, with one 16-byte read when it owns four.
+template <int NB>
+__device__ __forceinline__ uint32_t find_boundary(const uint32_t* hist, uint32_t k_rem,
                                                   uint32_t* wave_tot, uint32_t* sel) {
-  const int per = nb / kTopkThreads;
-  const int hi_bin = nb - static_cast<int>(threadIdx.x) * per;  // exclusive
+  constexpr int per = NB / kTopkThreads;
+  static_assert(per == 1 || per == 4, "bins per thread");
+  const int hi_bin = NB - static_cast<int>(threadIdx.x) * per;  // exclusive
+  uint32_t c[per];  // c[k]: bin hi_bin - 1 - k
+  if constexpr (per == 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hist + hi_bin - 4);
+    c[0] = v.w; c[1] = v.z; c[2] = v.y; c[3] = v.x;
+  } else {
+    c[0] = hist[hi_bin - 1];
+  }
   uint32_t local = 0;
-  for (int k = 1; k <= per; ++k) local += hist[hi_bin - k];
+#pragma unroll
+  for (int k = 0; k < per; ++k) local += c[k];
   uint32_t tot;
   uint32_t acc = block_exclusive_scan(local, wave_tot, &tot);
-  for (int k = 1; k <= per; ++k) {
-    const uint32_t c = hist[hi_bin - k];
-    if (acc < k_rem && k_rem <= acc + c) {
-      sel[0] = static_cast<uint32_t>(hi_bin - k);
+#pragma unroll
+  for (int k = 0; k < per; ++k) {
+    if (acc < k_rem && k_rem <= acc + c[k]) {
+      sel[0] = static_cast<uint32_t>(hi_bin - 1 - k);
       sel[1] = acc;
     }
-    acc += c;
+    acc += c[k];
   }
   return tot;
 }
@@ -159,7 +175,7 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
   // the boundary bin of the K-th largest key; the total is the count of
   // selectable keys
   const uint32_t nvalid =
-      find_boundary(lds.hist[0], kPass1Bins, static_cast<uint32_t>(K_out), lds.wave_tot[0], lds.sel[0]);
+      find_boundary<kPass1Bins>(lds.hist[0], static_cast<uint32_t>(K_out), lds.wave_tot[0], lds.sel[0]);
   __syncthreads();
   const uint32_t ksel = min(static_cast<uint32_t>(K_out), nvalid);
 
@@ -186,7 +202,7 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
       for (int j = 0; j < E; ++j)
         if (key[j] != 0u && (key[j] & mask) == prefix) atomicAdd(&h[(key[j] >> kShift[p]) & (kPassBins - 1)], 1u);
       __syncthreads();
-      (void)find_boundary(h, kPassBins, k_rem, lds.wave_tot[(p + 1) & 1], lds.sel[p + 1]);
+      (void)find_boundary<kPassBins>(h, k_rem, lds.wave_tot[(p + 1) & 1], lds.sel[p + 1]);
       __syncthreads();
       const uint32_t bin = lds.sel[p + 1][0];
       prefix |= bin << kShift[p];
