@@ -315,11 +315,22 @@ struct TopkPlan {
   int chunk_elems;
 };
 
+// Rows longer than one workgroup's capacity: the smaller chunk (16 K
+// elements) when its candidate lists still fit one merge workgroup, since it
+// spreads stage 1 over twice the workgroups; else 32 K.
 TopkPlan plan(const dsa_shape_t& s) {
   TopkPlan p{1, s.S};
   if (s.S > kChunkElems) {
+    const int64_t K = k_eff(s);
     p.chunk_elems = kChunkElems;
-    p.chunks = (s.S + kChunkElems - 1) / kChunkElems;
+    for (int ce = kChunkElems / 2; ce <= kChunkElems; ce *= 2) {
+      const int64_t chunks = (s.S + ce - 1) / ce;
+      if (chunks * K <= kChunkElems && K < ce) {
+        p.chunk_elems = ce;
+        break;
+      }
+    }
+    p.chunks = (s.S + p.chunk_elems - 1) / p.chunk_elems;
   }
   return p;
 }

@@ -64,7 +64,9 @@ def test_workspace_sizes(dsa):
     assert mla == 32 * splits * 128 * 512 * 2 + 32 * splits * 128 * 4  # bf16 o and fp32 lse partials
     assert fwd >= 32 * 8192 * 4 + 32 * 2048 * 4 + mla
     long = _v32(dsa, B=8, S=131072)
-    assert dsa.workspace_bytes(long, dsa.ENTRY_TOPK) == 8 * 4 * 2048 * 8  # 4 chunks of candidates
+    assert dsa.workspace_bytes(long, dsa.ENTRY_TOPK) == 8 * 8 * 2048 * 8  # 8 chunks of 16 K keys
+    longer = _v32(dsa, B=1, S=300000)  # 19 chunks of 16 K would overflow one merge: 10 of 32 K
+    assert dsa.workspace_bytes(longer, dsa.ENTRY_TOPK) == 10 * 2048 * 8
     prefill = _v32(dsa, B=1, T=16384, S=16384)
     assert dsa.workspace_bytes(prefill, dsa.ENTRY_SPARSE_MLA) == 0         # no splits
     with pytest.raises(dsa.DsaError):

@@ -148,8 +148,12 @@ def _special_rows(S, K, rng):
     return np.stack(rows)
 
 
+# rows up to 32768 keys: one workgroup; longer rows: 16 K-key chunks (40000,
+# 131072), or 32 K-key chunks when the candidates of the 16 K chunks would not
+# fit one merge workgroup (300000: 19 chunks x 2048 > 32768)
 @pytest.mark.parametrize("S,K", [(256, 32), (1000, 64), (3000, 2048), (8192, 2048),
-                                 (16384, 2048), (40000, 2048), (131072, 2048), (100, 300)])
+                                 (16384, 2048), (40000, 2048), (131072, 2048), (300000, 2048),
+                                 (100, 300)])
 def test_topk_bit_exact(dsa, S, K):
     print(f"[topk] S={S} K={K}", flush=True)
     torch = U.torch()
