@@ -104,8 +104,6 @@ indexer_generic(int T, int S, int HI, int DI, float idx_scale, const void* __res
 // ---------------------------------------------------------------------------
 constexpr int kIdxHeads = 64;
 constexpr int kIdxDim = 128;
-constexpr int kQStrideBf16 = kIdxDim + 8;   // padded LDS row (elements)
-constexpr int kQStrideFp8 = kIdxDim + 16;   // padded LDS row (bytes)
 
 // ---------------------------------------------------------------------------
 // Query-blocked MFMA kernel for many queries per sequence (prefill), bf16,
@@ -331,10 +329,11 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
                const uint8_t* __restrict__ k_sf, const void* __restrict__ w,
                float* __restrict__ scores) {
   using Sh = StreamShape<FP8>;
-  constexpr int kQRow = FP8 ? kQStrideFp8 : kQStrideBf16 * 2;  // staged query row, bytes
+  constexpr int kWBytes = kIdxHeads * (WDT == DSA_BF16 ? 2 : 4);
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kStWaves * kStBuffers * kStChunkBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kIdxHeads * kQRow];
-  __shared__ float w_lds[kIdxHeads];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kIdxHeads * Sh::kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t w_lds[kWBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t qsf_lds[kIdxHeads];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -360,21 +359,46 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
     for (int j = 0; j < Sh::kResults; ++j) ksb[j] = k_sf[kbase + min(s_begin + 64 * j + lane, s_vis - 1)];
   }
 
-  // chunk c -> buffer c % 4; copy i covers chunk rows kRowsPerCopy * i ..
-  // (keys past the visible range load row s_vis - 1: every address stays in
-  // bounds)
+  // Key rows and query rows share one LDS layout: copy i of a 1 KB block
+  // covers rows kRowsPerCopy * i ..; lane l writes slot l % (row / 16) of row
+  // kRowsPerCopy * i + l / (row / 16), which holds the piece
+  // swizzled into it (bf16: slot ^ ((r & 7) << 1), e4m3: slot ^ ((r >> 1) & 7)).
+  auto copy_piece = [&](int i, int& r, int& piece) {
+    if constexpr (FP8) {
+      r = 8 * i + (lane >> 3);
+      piece = (lane & 7) ^ ((r >> 1) & 7);
+    } else {
+      r = 4 * i + (lane >> 4);
+      piece = (lane & 15) ^ ((r & 7) << 1);
+    }
+  };
+  // ---- the query row, the head weights (and the query scales) go out first,
+  // as whole-line copies into LDS; the compiler sees no load it must wait for ----
+  {
+    constexpr int kQCopies = kIdxHeads * Sh::kRowBytes / 1024 / kStWaves;  // per wave: 4 / 2
+    const uint8_t* qrow = q_idx + row * kIdxHeads * Sh::kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kQCopies; ++j) {
+      const int i = wave * kQCopies + j;
+      int r, piece;
+      copy_piece(i, r, piece);
+      lds_dma_16(qrow + r * Sh::kRowBytes + piece * 16, lds_addr(q_lds) + 1024 * i);
+    }
+    if (wave == 0 && lane < kWBytes / 16)
+      lds_dma_16(static_cast<const uint8_t*>(w) + row * kWBytes + 16 * lane, lds_addr(w_lds));
+    if constexpr (FP8)
+      if (wave == 1 && lane < kIdxHeads / 16)
+        lds_dma_16(q_sf + row * kIdxHeads + 16 * lane, lds_addr(qsf_lds));
+  }
+
+  // chunk c -> buffer c % 4 (keys past the visible range load row s_vis - 1:
+  // every address stays in bounds)
   auto issue_chunk = [&](int c) {
     const uint32_t dst = wlds + (c % kStBuffers) * kStChunkBytes;
 #pragma unroll
     for (int i = 0; i < kStCopies; ++i) {
       int r, piece;
-      if constexpr (FP8) {
-        r = 8 * i + (lane >> 3);
-        piece = (lane & 7) ^ ((r >> 1) & 7);
-      } else {
-        r = 4 * i + (lane >> 4);
-        piece = (lane & 15) ^ ((r & 7) << 1);
-      }
+      copy_piece(i, r, piece);
       const int key = min(s_begin + c * Sh::kChunkKeys + r, s_vis - 1);
       lds_dma_16_nt(k_idx + (kbase + key) * Sh::kRowBytes + piece * 16, dst + 1024 * i);
     }
@@ -382,22 +406,16 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
 #pragma unroll
   for (int c = 0; c < kStBuffers - 1; ++c)
     if (c < nch) issue_chunk(c);
-
-  // ---- stage the query row and the head weights (times the query scales) ----
-  {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(q_idx + row * kIdxHeads * Sh::kRowBytes);
-    constexpr int kPieces = Sh::kRowBytes / 16;
-    for (int i = threadIdx.x; i < kIdxHeads * kPieces; i += blockDim.x) {
-      const int h = i / kPieces, c = i % kPieces;
-      *reinterpret_cast<u32x4_t*>(q_lds + h * kQRow + c * 16) = src[i];
-    }
-    for (int h = threadIdx.x; h < kIdxHeads; h += blockDim.x) {
-      float wv = load_w<WDT>(w, row * kIdxHeads + h);
-      if constexpr (FP8) wv *= ue8m0_to_f32(q_sf[row * kIdxHeads + h]);
-      w_lds[h] = wv;
-    }
-  }
-  __syncthreads();
+  // the query copies are older than the chunks' 8 copies each
+  if (nch >= 3)
+    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (nch == 2)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (nch == 1)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave's query copies are in
 
   float* out_row = scores + row * S;
   if (nch == 0) {  // every key of this wave is in the future (or past S)
@@ -412,13 +430,22 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
     const int h = mb * 16 + n;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      // dims 32 g + 8 ks (e4m3) or 32 ks + 8 g (bf16) of head h: its piece,
+      // through the row's swizzle
       if constexpr (FP8)
-        qa8[mb][ks] = *reinterpret_cast<const long*>(q_lds + h * kQRow + 32 * g + 8 * ks);
+        qa8[mb][ks] = *reinterpret_cast<const long*>(
+            q_lds + h * Sh::kRowBytes + 16 * ((2 * g + (ks >> 1)) ^ ((h >> 1) & 7)) + 8 * (ks & 1));
       else
-        qa[mb][ks] = *reinterpret_cast<const bf16x8_t*>(q_lds + h * kQRow + (32 * ks + 8 * g) * 2);
+        qa[mb][ks] = *reinterpret_cast<const bf16x8_t*>(
+            q_lds + h * Sh::kRowBytes + 16 * ((4 * ks + g) ^ ((h & 7) << 1)));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wreg[mb][i] = w_lds[mb * 16 + 4 * g + i];
+    for (int i = 0; i < 4; ++i) {
+      const int hh = mb * 16 + 4 * g + i;
+      float wv = load_w<WDT>(w_lds, hh);
+      if constexpr (FP8) wv *= ue8m0_to_f32(qsf_lds[hh]);
+      wreg[mb][i] = wv;
+    }
   }
 
   float res[Sh::kResults];  // lane l: key s_begin + 64 j + l
