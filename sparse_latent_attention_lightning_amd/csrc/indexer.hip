@@ -11,7 +11,7 @@
 //    e4m3): each wave streams a run of key rows through its own LDS ring with
 //    whole-line direct copies and scores them on MFMAs against the query tile
 //    it keeps in registers.
-//  * indexer_prefill (8 or more queries per sequence, bf16): 8 queries per
+//  * indexer_prefill (8 or more queries per sequence, bf16): 4 queries per
 //    workgroup share every key chunk through LDS.
 //  * indexer_generic: any HI x DI, f32 / bf16 / e4m3, plain fp32 VALU loops.
 // ReLU, the head weights and the head sum run on the MFMA accumulator
@@ -113,10 +113,11 @@ constexpr int kIdxDim = 128;
 // 64 heads] x [128 dims] x [S keys], with the ReLU-weighted head sum applied
 // to every 64-head column.  Streaming the key rows once per query (as the
 // decode kernel does) would make the kernel bound by key traffic, so here a
-// block of 8 waves takes 8 consecutive queries of one sequence, one per wave,
-// and streams every key the 8 of them see through LDS once:
+// block of 4 waves takes 4 consecutive queries of one sequence, one per wave,
+// and streams every key the 4 of them see through LDS once (two such blocks
+// share a CU, so one block's MFMAs run while the other waits at a barrier):
 //  * keys move in 64-key chunks (16 KB) through a ring of 4 LDS buffers,
-//    copied global -> LDS by the DMA path, two 1 KB copies per wave per chunk;
+//    copied global -> LDS by the DMA path, four 1 KB copies per wave per chunk;
 //    a key row is 256 bytes = 16 pieces of 16 bytes, and piece c of row r sits
 //    in slot c ^ ((r & 7) << 1) of the row, so that the operand reads (lane
 //    (g, n): row n, piece 4 ks + g) touch all 64 banks in every cycle;
@@ -132,13 +133,14 @@ constexpr int kIdxDim = 128;
 // Blocks run longest first (the causal key range grows with the query index),
 // which balances the triangular work over the CUs.
 // ---------------------------------------------------------------------------
-constexpr int kPfWaves = 8;                                  // queries per block
+constexpr int kPfWaves = 4;                                  // queries per block
 constexpr int kPfChunkKeys = 64;
 constexpr int kPfRowBytes = kIdxDim * 2;                     // 256
 constexpr int kPfChunkBytes = kPfChunkKeys * kPfRowBytes;    // 16 KB
 constexpr int kPfBuffers = 4;
 constexpr int kPfMinQueries = 8;   // fewer queries per sequence use the per-query kernel
-static_assert(kPfChunkBytes == kPfWaves * 2 * 1024, "two 1 KB copies per wave per chunk");
+constexpr int kPfCopies = kPfChunkBytes / 1024 / kPfWaves;  // 1 KB copies per wave per chunk
+static_assert(kPfCopies * kPfWaves * 1024 == kPfChunkBytes, "whole copies per wave");
 
 template <int WDT>
 __global__ void __launch_bounds__(kPfWaves * 64)
@@ -163,13 +165,14 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
   const int64_t kbase = static_cast<int64_t>(b) * S;
   const uint32_t kb_lds = lds_addr(kbuf);
 
-  // chunk c -> buffer c % kPfBuffers; this wave copies rows 8 wave .. 8 wave + 7
+  // chunk c -> buffer c % kPfBuffers; this wave copies chunk rows
+  // 4 kPfCopies wave .. 4 kPfCopies (wave + 1) - 1
   // (keys past S - 1 load row S - 1: every address stays in bounds)
   auto issue_chunk = [&](int c) {
-    const uint32_t dst = kb_lds + (c % kPfBuffers) * kPfChunkBytes + wave * 2048;
+    const uint32_t dst = kb_lds + (c % kPfBuffers) * kPfChunkBytes + wave * kPfCopies * 1024;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = wave * 8 + i * 4 + (lane >> 4);
+    for (int i = 0; i < kPfCopies; ++i) {
+      const int r = (wave * kPfCopies + i) * 4 + (lane >> 4);
       const int piece = (lane & 15) ^ ((r & 7) << 1);
       const int key = min(c * kPfChunkKeys + r, S - 1);
       lds_dma_16(k_idx + (kbase + key) * kIdxDim + piece * 8, dst + i * 1024);
@@ -245,9 +248,9 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
     if (c == 0 || later <= 0)
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     else if (later == 1)
-      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPfCopies) : "memory");
     else
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPfCopies) : "memory");
     __syncthreads();   // every wave's copies of chunk c are in; chunk c - 1 is consumed
     if (c + kPfBuffers - 1 < nchunks) issue_chunk(c + kPfBuffers - 1);
     const uint8_t* buf = kbuf + (c % kPfBuffers) * kPfChunkBytes;
