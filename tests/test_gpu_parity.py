@@ -291,21 +291,41 @@ def test_forward_dense_when_k_covers_causal(dsa):
     np.testing.assert_allclose(lse.cpu().numpy().reshape(cfg.T, cfg.H), dl, rtol=1e-5, atol=1e-5)
 
 
-@pytest.mark.parametrize("case", ["decode_int", "decode_real"])
+FORWARD_CASES = {
+    "decode_int": g.CONFIGS["decode_8k"].replace(B=4, integer=True),
+    "decode_real": g.CONFIGS["decode_8k"].replace(B=4),
+    # two queries per sequence (the multi-token-prediction decode step): the
+    # second query also sees the first one's position
+    "decode_mtp": g.CONFIGS["decode_8k"].replace(B=2, T=2, S=3000),
+    # the YaRN-scaled softmax scale of the nnterp page (0.1352) instead of
+    # 1/sqrt(192)
+    "decode_yarn": g.CONFIGS["decode_8k"].replace(B=2, S=3000, sm_scale=0.1352),
+    # fewer keys than K: every key is selected, the sparse path is dense MLA
+    "decode_dense": g.CONFIGS["decode_8k"].replace(B=2, S=1500),
+    # the e4m3 indexer in front of the attention
+    "decode_fp8": g.CONFIGS["decode_64k_fp8"].replace(B=2, S=5000),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FORWARD_CASES))
 def test_forward_decode(dsa, case):
-    cfg = {"decode_int": g.CONFIGS["decode_8k"].replace(B=4, integer=True),
-           "decode_real": g.CONFIGS["decode_8k"].replace(B=4)}[case]
+    cfg = FORWARD_CASES[case]
+    print(f"[forward] {case}: {cfg}", flush=True)
     x = _inputs(cfg)
     o, lse, idx = _forward(dsa, cfg, x)
     rb, rt = _rows(cfg)
+    rows = cfg.B * cfg.T
     ref_sc = _oracle_scores(cfg, rb, rt)
     ref_idx = oracle.topk(cfg, ref_sc)
-    idx = idx.cpu().numpy().reshape(cfg.B, -1)
+    idx = idx.cpu().numpy().reshape(rows, -1)
     if cfg.integer:
         assert np.array_equal(idx, ref_idx)
     else:
         U.assert_selection_within_gap(idx, ref_idx, ref_sc)
-    ro, rl = oracle.sparse_mla(cfg, rb, g.full(cfg, "q").reshape(cfg.B, cfg.H, cfg.D),
+    if cfg.K >= cfg.S:
+        assert np.array_equal(idx, np.tile(np.arange(cfg.S, dtype=np.int32), (rows, 1)))
+    ro, rl = oracle.sparse_mla(cfg, rb, g.full(cfg, "q").reshape(rows, cfg.H, cfg.D),
                                g.full(cfg, "kv"), idx)
-    o = g.bf16_bits_to_f32(U.dev_to_np(o, "bf16")).reshape(cfg.B, cfg.H, cfg.Dc)
+    o = g.bf16_bits_to_f32(U.dev_to_np(o, "bf16")).reshape(rows, cfg.H, cfg.Dc)
     U.assert_rows_close(o, ro, U.RTOL["bf16"], f"{case} o")
+    np.testing.assert_allclose(lse.cpu().numpy().reshape(rows, cfg.H), rl, rtol=1e-4, atol=1e-4)
