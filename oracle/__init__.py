@@ -61,11 +61,12 @@ def load(path: Optional[str] = None):
             i32 = ctypes.c_int32
             sp = ctypes.POINTER(_Shape)
             lib.orc_indexer_scores.argtypes = [sp, i32, P, P, P, P, P, P, P, P]
+            lib.orc_indexer_scores_ragged.argtypes = [sp, i32, P, P, P, P, P, P, P, P, P]
             lib.orc_topk.argtypes = [sp, i32, P, P]
             lib.orc_sparse_mla.argtypes = [sp, i32, P, P, P, P, i32, P, P, P]
             lib.orc_dense_mla.argtypes = [sp, i32, P, P, P, P, P, P]
             lib.orc_explicit_mla.argtypes = [i32] * 6 + [ctypes.c_double] + [P] * 7
-            for f in ("orc_indexer_scores", "orc_topk", "orc_sparse_mla", "orc_dense_mla",
+            for f in ("orc_indexer_scores", "orc_indexer_scores_ragged", "orc_topk", "orc_sparse_mla", "orc_dense_mla",
                       "orc_explicit_mla"):
                 getattr(lib, f).restype = ctypes.c_int
             _libs[path] = lib
@@ -109,8 +110,9 @@ def _run_rows(fn, n, threads):
 
 
 def indexer_scores(cfg, row_b, row_t, q_idx_rows, w_rows, k_idx, q_sf_rows=None, k_sf=None,
-                   threads: Optional[int] = None, lib=None) -> np.ndarray:
-    """Index scores of the given query rows, [n, S] fp32 (future keys -inf)."""
+                   threads: Optional[int] = None, lib=None, seq_lens=None) -> np.ndarray:
+    """Index scores of the given query rows, [n, S] fp32 (future keys -inf).
+    seq_lens [B] (optional): per-sequence context lengths (ragged batch)."""
     lib = lib or load()
     sh = shape_of(cfg)
     row_b = _c(row_b, np.int32)
@@ -121,10 +123,11 @@ def indexer_scores(cfg, row_b, row_t, q_idx_rows, w_rows, k_idx, q_sf_rows=None,
     out = np.empty((n, cfg.S), np.float32)
     qrow = cfg.HI * cfg.DI
     nblk = cfg.DI // 128 if cfg.idx_dtype == "fp8" else 0
+    lens = _c(seq_lens, np.int32)
 
     def run(lo, hi):
-        rc = lib.orc_indexer_scores(
-            ctypes.byref(sh), hi - lo, row_b[lo:].ctypes.data, row_t[lo:].ctypes.data,
+        rc = lib.orc_indexer_scores_ragged(
+            ctypes.byref(sh), hi - lo, row_b[lo:].ctypes.data, row_t[lo:].ctypes.data, _ptr(lens),
             q_idx_rows.ctypes.data + lo * qrow * q_idx_rows.itemsize,
             None if q_sf_rows is None else q_sf_rows.ctypes.data + lo * cfg.HI * nblk,
             _ptr(k_idx), _ptr(k_sf),

@@ -74,18 +74,25 @@ static int check_shape(const orc_shape* sh) {
 /* Index score (MoE-block step list: S^I, then S~^I = S^I + M)               */
 /* ------------------------------------------------------------------------ */
 
-int orc_indexer_scores(const orc_shape* sh, int32_t n, const int32_t* row_b,
-                       const int32_t* row_t, const void* q_idx_rows,
-                       const uint8_t* q_sf_rows, const void* k_idx,
-                       const uint8_t* k_sf, const void* w_rows, float* scores) {
+/* Sequence b holds L_b valid keys at positions 0 .. L_b - 1 (L_b = S when
+ * seq_lens is NULL); its T queries are the last T positions, q_pos(t) =
+ * L_b - T + t, and key s is visible when s <= q_pos(t) (so never when
+ * s >= L_b).  A query with q_pos < 0 sees no key. */
+int orc_indexer_scores_ragged(const orc_shape* sh, int32_t n, const int32_t* row_b,
+                              const int32_t* row_t, const int32_t* seq_lens,
+                              const void* q_idx_rows, const uint8_t* q_sf_rows,
+                              const void* k_idx, const uint8_t* k_sf, const void* w_rows,
+                              float* scores) {
   if (check_shape(sh) || n < 0) return 1;
   const int32_t S = sh->S, HI = sh->HI, DI = sh->DI;
   for (int32_t r = 0; r < n; ++r) {
     const int32_t b = row_b[r], t = row_t[r];
     if (b < 0 || b >= sh->B || t < 0 || t >= sh->T) return 1;
-    const int32_t q_pos = S - sh->T + t;
+    const int32_t L = seq_lens ? seq_lens[b] : S;
+    if (L < 0 || L > S) return 1;
+    const int32_t q_pos = L - sh->T + t;
     for (int32_t s = 0; s < S; ++s) {
-      if (s > q_pos) { /* causal mask M: a future key */
+      if (s > q_pos) { /* causal mask M: a future key (or past the sequence) */
         scores[(int64_t)r * S + s] = -INFINITY;
         continue;
       }
@@ -109,6 +116,14 @@ int orc_indexer_scores(const orc_shape* sh, int32_t n, const int32_t* row_b,
     }
   }
   return 0;
+}
+
+int orc_indexer_scores(const orc_shape* sh, int32_t n, const int32_t* row_b,
+                       const int32_t* row_t, const void* q_idx_rows,
+                       const uint8_t* q_sf_rows, const void* k_idx,
+                       const uint8_t* k_sf, const void* w_rows, float* scores) {
+  return orc_indexer_scores_ragged(sh, n, row_b, row_t, NULL, q_idx_rows, q_sf_rows, k_idx,
+                                   k_sf, w_rows, scores);
 }
 
 /* ------------------------------------------------------------------------ */

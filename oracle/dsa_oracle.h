@@ -68,6 +68,15 @@ int orc_indexer_scores(const orc_shape* sh, int32_t n, const int32_t* row_b,
                        const uint8_t* q_sf_rows, const void* k_idx,
                        const uint8_t* k_sf, const void* w_rows, float* scores);
 
+/* The same with per-sequence context lengths (ragged batch; the padding mask
+ * of the nnterp page, section 02): sequence b has seq_lens[b] <= S valid keys
+ * and its queries sit at q_pos(t) = seq_lens[b] - T + t.  seq_lens NULL: all S. */
+int orc_indexer_scores_ragged(const orc_shape* sh, int32_t n, const int32_t* row_b,
+                              const int32_t* row_t, const int32_t* seq_lens,
+                              const void* q_idx_rows, const uint8_t* q_sf_rows,
+                              const void* k_idx, const uint8_t* k_sf, const void* w_rows,
+                              float* scores);
+
 /* Top-K selection of n score rows of length S -> [n, min(K, S)] int32. */
 int orc_topk(const orc_shape* sh, int32_t n, const float* scores, int32_t* idx);
 

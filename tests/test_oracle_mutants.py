@@ -23,8 +23,10 @@ MUTANTS = {
     "head_weight_index": ("(int64_t)r * HI + h);\n        acc", "(int64_t)r * HI);\n        acc"),
     "index_scale_dropped": ("= sh->idx_scale * accf;", "= accf;"),
     "causal_off_by_one": ("if (s > q_pos) {", "if (s >= q_pos) {"),
-    "decode_alignment": ("const int32_t q_pos = S - sh->T + t;\n    for (int32_t s = 0; s < S; ++s) {\n      if",
+    "decode_alignment": ("const int32_t q_pos = L - sh->T + t;\n    for (int32_t s = 0; s < S; ++s) {\n      if",
                          "const int32_t q_pos = t;\n    for (int32_t s = 0; s < S; ++s) {\n      if"),
+    # a ragged sequence's queries placed at the end of the whole cache
+    "ragged_alignment": ("const int32_t q_pos = L - sh->T + t;", "const int32_t q_pos = S - sh->T + t;"),
     "fp8_scale_ignored": (" * ue8m0_value(sf[row * nblk + d / 128]);", ";"),
     "tie_break_reversed": ("return (a->index > b->index) - (a->index < b->index);",
                            "return (a->index < b->index) - (a->index > b->index);"),

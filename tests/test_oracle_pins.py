@@ -168,6 +168,33 @@ def test_scores_causal_boundary_and_decode_alignment(oracle_lib):
         assert np.all(s[np.isfinite(s)] > 0)
 
 
+def test_scores_ragged_lengths(oracle_lib):
+    """Per-sequence context lengths L_b: sequence b's queries sit at
+    L_b - T + t and see keys 0 .. L_b - T + t, never one at or past L_b; a
+    query whose position is negative sees nothing.  Checked against the int64
+    closed form on integer inputs (lengths S, inside, equal to T, below T, 0)."""
+    lens = [37, 20, 5, 3, 0]
+    cfg = _cfg(B=len(lens))
+    rng = np.random.default_rng(12)
+    x = _draw(cfg, rng, integer=True)
+    rb, rt = _rows(cfg)
+    s = oracle.indexer_scores(cfg, rb, rt, x["q_idx"], x["w"], x["k_idx"],
+                              seq_lens=np.array(lens, np.int32))
+    d = np.einsum("nhd,nsd->nhs", x["q_idx"].astype(np.int64),
+                  x["k_idx"][rb].astype(np.int64))
+    acc = np.einsum("nh,nhs->ns", x["w"].astype(np.int64), np.maximum(d, 0))
+    ref = np.float32(cfg.index_scale) * acc.astype(np.float32)
+    qpos = np.array(lens, np.int64)[rb] - cfg.T + rt
+    vis = np.arange(cfg.S)[None, :] <= qpos[:, None]
+    assert np.array_equal(np.isfinite(s), vis)
+    assert np.array_equal(s[vis], ref[vis])
+    assert np.all(s[~vis] == -np.inf)
+    # lengths of S everywhere are the unragged call
+    full = oracle.indexer_scores(cfg, rb, rt, x["q_idx"], x["w"], x["k_idx"],
+                                 seq_lens=np.full(cfg.B, cfg.S, np.int32))
+    assert np.array_equal(full, _scores(cfg, x))
+
+
 def test_scores_integer_mode_exact_against_int64(oracle_lib):
     """Integer inputs in [-3, 3]: the score equals the int64 closed form, scaled."""
     cfg = g.CONFIGS["tiny"]
