@@ -95,6 +95,23 @@ dsa_status_t dsa_indexer_scores(const dsa_shape_t* shape, const void* q_idx,
                                 void* stream);
 
 /*
+ * Index scores of a ragged batch: sequence b holds seq_lens[b] valid keys at
+ * positions 0 .. seq_lens[b] - 1 of its S-row cache, and its T queries are its
+ * last T positions, q_pos(t) = seq_lens[b] - T + t (the padding
+ * attention_mask of the nnterp deepseek_v32 page, section 02, read as
+ * per-sequence context lengths).  Key s is scored when s <= q_pos(t); every
+ * other entry of the row, including those of keys past seq_lens[b], is -inf.
+ *   seq_lens [B] int32, device memory, 4-byte aligned (NULL: every sequence
+ *            holds S keys, which is dsa_indexer_scores); values are clamped
+ *            to [0, S]; a query with q_pos(t) < 0 gets a row of -inf.
+ * Other arguments and errors as dsa_indexer_scores.
+ */
+dsa_status_t dsa_indexer_scores_ragged(const dsa_shape_t* shape, const int32_t* seq_lens,
+                                       const void* q_idx, const uint8_t* q_sf,
+                                       const void* k_idx, const uint8_t* k_sf, const void* w,
+                                       float* scores, void* stream);
+
+/*
  * Top-K selection per score row (the step list's M^sel; layout from the
  * nnterp deepseek_v32 page, section 03).
  *   scores [B, T, S] fp32 (as written by dsa_indexer_scores, or any values)
@@ -139,6 +156,19 @@ dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx,
                          const void* w, const void* q, const void* kv,
                          int32_t* idx_out, void* o, float* lse, void* ws,
                          size_t ws_bytes, void* stream);
+
+/*
+ * The whole hot path over a ragged batch: the index scores as
+ * dsa_indexer_scores_ragged (seq_lens as there), then top-K (rows of a short
+ * sequence are padded with -1 once its visible keys are exhausted) and the
+ * sparse latent attention over the selection.  Other arguments, workspace and
+ * errors as dsa_forward (same workspace size).
+ */
+dsa_status_t dsa_forward_ragged(const dsa_shape_t* shape, const int32_t* seq_lens,
+                                const void* q_idx, const uint8_t* q_sf, const void* k_idx,
+                                const uint8_t* k_sf, const void* w, const void* q, const void* kv,
+                                int32_t* idx_out, void* o, float* lse, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* Workspace bytes an entry point needs for `shape` on the current device
  * (0 if none).  Returns (size_t)-1 when the shape is invalid. */

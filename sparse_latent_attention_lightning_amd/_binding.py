@@ -71,10 +71,13 @@ def lib() -> ctypes.CDLL:
         P, sz = ctypes.c_void_p, ctypes.c_size_t
         sp = ctypes.POINTER(DsaShape)
         L.dsa_indexer_scores.argtypes = [sp, P, P, P, P, P, P, P]
+        L.dsa_indexer_scores_ragged.argtypes = [sp, P, P, P, P, P, P, P, P]
         L.dsa_topk.argtypes = [sp, P, P, P, sz, P]
         L.dsa_sparse_mla_fwd.argtypes = [sp, P, P, P, P, P, P, sz, P]
         L.dsa_forward.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, sz, P]
-        for f in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_fwd", "dsa_forward"):
+        L.dsa_forward_ragged.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        for f in ("dsa_indexer_scores", "dsa_indexer_scores_ragged", "dsa_topk",
+                  "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_bytes.argtypes = [sp, ctypes.c_int32]
         L.dsa_workspace_bytes.restype = ctypes.c_size_t
@@ -159,6 +162,11 @@ def _check_mla(shape, q, kv, idx):
     return dev
 
 
+def _seq_lens(shape: DsaShape, seq_lens, dev):
+    _req(seq_lens, "seq_lens", (shape.B,), (torch.int32,), dev)
+    return seq_lens
+
+
 def dsa_indexer_scores(shape: DsaShape, q_idx, k_idx, w, q_sf=None, k_sf=None,
                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Index scores [B, T, S] fp32 (future keys -inf)."""
@@ -168,6 +176,22 @@ def dsa_indexer_scores(shape: DsaShape, q_idx, k_idx, w, q_sf=None, k_sf=None,
     _req(out, "scores", (shape.B, shape.T, shape.S), (torch.float32,), dev)
     _check(lib().dsa_indexer_scores(ctypes.byref(shape), _ptr(q_idx), _ptr(q_sf), _ptr(k_idx),
                                     _ptr(k_sf), _ptr(w), _ptr(out), _stream(dev)))
+    return out
+
+
+def dsa_indexer_scores_ragged(shape: DsaShape, seq_lens, q_idx, k_idx, w, q_sf=None, k_sf=None,
+                              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Index scores [B, T, S] fp32 of a ragged batch: sequence b holds
+    seq_lens[b] keys (int32 [B] on the device) and its queries are its last T
+    positions."""
+    dev = _check_indexer(shape, q_idx, k_idx, w, q_sf, k_sf)
+    _seq_lens(shape, seq_lens, dev)
+    if out is None:
+        out = torch.empty((shape.B, shape.T, shape.S), dtype=torch.float32, device=dev)
+    _req(out, "scores", (shape.B, shape.T, shape.S), (torch.float32,), dev)
+    _check(lib().dsa_indexer_scores_ragged(ctypes.byref(shape), _ptr(seq_lens), _ptr(q_idx),
+                                           _ptr(q_sf), _ptr(k_idx), _ptr(k_sf), _ptr(w), _ptr(out),
+                                           _stream(dev)))
     return out
 
 
@@ -211,7 +235,19 @@ def dsa_forward(shape: DsaShape, q_idx, k_idx, w, q, kv, q_sf=None, k_sf=None,
                 out: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None):
     """The whole hot path: (o, lse or None, idx or None)."""
+    return dsa_forward_ragged(shape, None, q_idx, k_idx, w, q, kv, q_sf, k_sf, want_idx, want_lse,
+                              ws, out, idx_out, lse)
+
+
+def dsa_forward_ragged(shape: DsaShape, seq_lens, q_idx, k_idx, w, q, kv, q_sf=None, k_sf=None,
+                       want_idx: bool = True, want_lse: bool = True,
+                       ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       idx_out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """The whole hot path over a ragged batch (seq_lens int32 [B] on the
+    device, or None for full sequences): (o, lse or None, idx or None)."""
     dev = _check_indexer(shape, q_idx, k_idx, w, q_sf, k_sf)
+    if seq_lens is not None:
+        _seq_lens(shape, seq_lens, dev)
     _check_mla(shape, q, kv, None)
     if out is None:
         out = torch.empty((shape.B, shape.T, shape.H, shape.Dc), dtype=q.dtype, device=dev)
@@ -221,9 +257,16 @@ def dsa_forward(shape: DsaShape, q_idx, k_idx, w, q, kv, q_sf=None, k_sf=None,
         lse = torch.empty((shape.B, shape.T, shape.H), dtype=torch.float32, device=dev)
     if ws is None:
         ws = _workspace(shape, ENTRY_FORWARD, dev)
-    _check(lib().dsa_forward(ctypes.byref(shape), _ptr(q_idx), _ptr(q_sf), _ptr(k_idx), _ptr(k_sf),
-                             _ptr(w), _ptr(q), _ptr(kv), _ptr(idx_out), _ptr(out), _ptr(lse),
-                             _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev)))
+    if seq_lens is None:
+        _check(lib().dsa_forward(ctypes.byref(shape), _ptr(q_idx), _ptr(q_sf), _ptr(k_idx),
+                                 _ptr(k_sf), _ptr(w), _ptr(q), _ptr(kv), _ptr(idx_out), _ptr(out),
+                                 _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
+                                 _stream(dev)))
+    else:
+        _check(lib().dsa_forward_ragged(ctypes.byref(shape), _ptr(seq_lens), _ptr(q_idx),
+                                        _ptr(q_sf), _ptr(k_idx), _ptr(k_sf), _ptr(w), _ptr(q),
+                                        _ptr(kv), _ptr(idx_out), _ptr(out), _ptr(lse), _ptr(ws),
+                                        0 if ws is None else ws.numel(), _stream(dev)))
     return out, lse, idx_out
 
 

@@ -81,6 +81,13 @@ dsa_status_t check_indexer_args(const dsa_shape_t& s, const void* q_idx, const u
   return DSA_OK;
 }
 
+// context lengths of a ragged batch: nullable (all S); else 4-byte aligned
+dsa_status_t check_seq_lens(const int32_t* seq_lens) {
+  if (seq_lens != nullptr && (reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0)
+    return fail(DSA_ERR_INVALID_ARG, "seq_lens is not 4-byte aligned");
+  return DSA_OK;
+}
+
 dsa_status_t check_mla_args(const void* q, const void* kv, const int32_t* idx, const void* o) {
   dsa_status_t st;
   if ((st = need(q, "q")) || (st = need(kv, "kv")) || (st = need(idx, "idx")) ||
@@ -216,15 +223,23 @@ using namespace dsa;
 
 extern "C" {
 
-dsa_status_t dsa_indexer_scores(const dsa_shape_t* shape, const void* q_idx, const uint8_t* q_sf,
-                                const void* k_idx, const uint8_t* k_sf, const void* w,
-                                float* scores, void* stream) {
+dsa_status_t dsa_indexer_scores_ragged(const dsa_shape_t* shape, const int32_t* seq_lens,
+                                       const void* q_idx, const uint8_t* q_sf,
+                                       const void* k_idx, const uint8_t* k_sf, const void* w,
+                                       float* scores, void* stream) {
   g_last_error[0] = '\0';
   dsa_status_t st = check_shape(shape);
   if (st != DSA_OK) return st;
   if ((st = check_indexer_args(*shape, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
-  return launch_indexer(*shape, q_idx, q_sf, k_idx, k_sf, w, scores,
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
+  return launch_indexer(*shape, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores,
                         static_cast<hipStream_t>(stream));
+}
+
+dsa_status_t dsa_indexer_scores(const dsa_shape_t* shape, const void* q_idx, const uint8_t* q_sf,
+                                const void* k_idx, const uint8_t* k_sf, const void* w,
+                                float* scores, void* stream) {
+  return dsa_indexer_scores_ragged(shape, nullptr, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
 }
 
 dsa_status_t dsa_topk(const dsa_shape_t* shape, const float* scores, int32_t* idx, void* ws,
@@ -249,13 +264,15 @@ dsa_status_t dsa_sparse_mla_fwd(const dsa_shape_t* shape, const void* q, const v
                            static_cast<hipStream_t>(stream));
 }
 
-dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx, const uint8_t* q_sf,
-                         const void* k_idx, const uint8_t* k_sf, const void* w, const void* q,
-                         const void* kv, int32_t* idx_out, void* o, float* lse, void* ws,
-                         size_t ws_bytes, void* stream) {
+dsa_status_t dsa_forward_ragged(const dsa_shape_t* shape, const int32_t* seq_lens,
+                                const void* q_idx, const uint8_t* q_sf, const void* k_idx,
+                                const uint8_t* k_sf, const void* w, const void* q, const void* kv,
+                                int32_t* idx_out, void* o, float* lse, void* ws,
+                                size_t ws_bytes, void* stream) {
   g_last_error[0] = '\0';
   dsa_status_t st = check_shape(shape);
   if (st != DSA_OK) return st;
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
   const dsa_shape_t& s = *shape;
   const ForwardLayout L = forward_layout(s);
   if (ws == nullptr || ws_bytes < L.total)
@@ -268,10 +285,19 @@ dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx, const uint
   if ((st = check_indexer_args(s, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
   if ((st = check_mla_args(q, kv, idx, o)) != DSA_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if ((st = launch_indexer(s, q_idx, q_sf, k_idx, k_sf, w, scores, hs)) != DSA_OK) return st;
+  if ((st = launch_indexer(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, hs)) != DSA_OK)
+    return st;
   if ((st = launch_topk(s, scores, idx, base + L.topk_ws, L.mla_ws - L.topk_ws, hs)) != DSA_OK)
     return st;
   return launch_sparse_mla(s, q, kv, idx, o, lse, base + L.mla_ws, L.total - L.mla_ws, hs);
+}
+
+dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx, const uint8_t* q_sf,
+                         const void* k_idx, const uint8_t* k_sf, const void* w, const void* q,
+                         const void* kv, int32_t* idx_out, void* o, float* lse, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return dsa_forward_ragged(shape, nullptr, q_idx, q_sf, k_idx, k_sf, w, q, kv, idx_out, o, lse,
+                            ws, ws_bytes, stream);
 }
 
 size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry) {

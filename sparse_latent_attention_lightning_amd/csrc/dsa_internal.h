@@ -42,9 +42,10 @@ class LaunchTimer {
 inline int32_t k_eff(const dsa_shape_t& s) { return s.K < s.S ? s.K : s.S; }
 
 // ---- index scores -------------------------------------------------------
+// seq_lens: device int32 [B] context lengths of a ragged batch, or nullptr
 dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                             const void* k_idx, const uint8_t* k_sf, const void* w,
-                            float* scores, hipStream_t stream);
+                            const int32_t* seq_lens, float* scores, hipStream_t stream);
 
 // ---- top-k -------------------------------------------------------------
 size_t topk_workspace_bytes(const dsa_shape_t& s);

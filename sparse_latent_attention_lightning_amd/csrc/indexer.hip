@@ -31,6 +31,12 @@ __device__ __forceinline__ float load_w(const void* w, int64_t i) {
     return static_cast<const float*>(w)[i];
 }
 
+// Keys of sequence b: all S, or its own context length in a ragged batch
+// (clamped to [0, S]); its T queries are its last T positions.
+__device__ __forceinline__ int seq_len(const int32_t* seq_lens, int b, int S) {
+  return seq_lens == nullptr ? S : min(max(seq_lens[b], 0), S);
+}
+
 template <int IDT>
 __device__ __forceinline__ float load_idx(const void* p, int64_t i) {
   if constexpr (IDT == DSA_BF16)
@@ -50,14 +56,14 @@ __global__ void __launch_bounds__(256)
 indexer_generic(int T, int S, int HI, int DI, float idx_scale, const void* __restrict__ q_idx,
                 const uint8_t* __restrict__ q_sf, const void* __restrict__ k_idx,
                 const uint8_t* __restrict__ k_sf, const void* __restrict__ w,
-                float* __restrict__ scores) {
+                const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
   extern __shared__ float smem[];
   float* qs = smem;             // [HI * DI]
   float* ws = smem + HI * DI;   // [HI]
   const int64_t row = blockIdx.y;  // b * T + t
   const int b = static_cast<int>(row / T);
   const int t = static_cast<int>(row % T);
-  const int q_pos = S - T + t;
+  const int q_pos = seq_len(seq_lens, b, S) - T + t;
   const int nblk = DI / 128;
   for (int i = threadIdx.x; i < HI * DI; i += blockDim.x) {
     float v = load_idx<IDT>(q_idx, row * HI * DI + i);
@@ -146,7 +152,7 @@ template <int WDT>
 __global__ void __launch_bounds__(kPfWaves * 64)
 indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __restrict__ q_idx,
                 const uint16_t* __restrict__ k_idx, const void* __restrict__ w,
-                float* __restrict__ scores) {
+                const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPfBuffers * kPfChunkBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -159,8 +165,9 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
   const int t = t0 + wave;
   const bool has_q = t < T;
   const int tq = min(t, T - 1);
-  const int q_pos = S - T + tq;
-  const int kend = S - T + min(t0 + kPfWaves, T);    // keys [0, kend) are visible to some query
+  const int L = seq_len(seq_lens, b, S);
+  const int q_pos = L - T + tq;
+  const int kend = max(0, L - T + min(t0 + kPfWaves, T));  // keys [0, kend) are visible to some query
   const int nchunks = (kend + kPfChunkKeys - 1) / kPfChunkKeys;
   const int64_t kbase = static_cast<int64_t>(b) * S;
   const uint32_t kb_lds = lds_addr(kbuf);
@@ -330,7 +337,7 @@ __global__ void __launch_bounds__(kStWaves * 64)
 indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict__ q_idx,
                const uint8_t* __restrict__ q_sf, const uint8_t* __restrict__ k_idx,
                const uint8_t* __restrict__ k_sf, const void* __restrict__ w,
-               float* __restrict__ scores) {
+               const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
   using Sh = StreamShape<FP8>;
   constexpr int kWBytes = kIdxHeads * (WDT == DSA_BF16 ? 2 : 4);
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kStWaves * kStBuffers * kStChunkBytes];
@@ -345,7 +352,8 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
   const int kb = static_cast<int>(blockIdx.x % nkb);
   const int b = static_cast<int>(row / T);
   const int t = static_cast<int>(row % T);
-  const int s_lim = min(S, S - T + t + 1);  // keys [0, s_lim) are visible
+  const int L = seq_len(seq_lens, b, S);
+  const int s_lim = max(0, min(L, L - T + t + 1));  // keys [0, s_lim) are visible
   const int s_begin = (kb * kStWaves + wave) * Sh::kWaveKeys;
   const int s_end = min(S, s_begin + Sh::kWaveKeys);
   const int s_vis = min(s_end, s_lim);  // this wave scores [s_begin, s_vis)
@@ -354,12 +362,13 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
   const uint32_t wlds = lds_addr(kbuf) + wave * kStBuffers * kStChunkBytes;
 
   // e4m3 key scale bytes, one per score this lane ends with (issued first:
-  // they retire before every copy, so the copy waits below cover them;
-  // s_vis >= 1, so the clamped key is a valid row)
+  // they retire before every copy, so the copy waits below cover them; the
+  // key is clamped into [0, s_vis - 1], or is row 0 when nothing is visible)
   uint8_t ksb[Sh::kResults];
   if constexpr (FP8) {
 #pragma unroll
-    for (int j = 0; j < Sh::kResults; ++j) ksb[j] = k_sf[kbase + min(s_begin + 64 * j + lane, s_vis - 1)];
+    for (int j = 0; j < Sh::kResults; ++j)
+      ksb[j] = k_sf[kbase + max(0, min(s_begin + 64 * j + lane, s_vis - 1))];
   }
 
   // Key rows and query rows share one LDS layout: copy i of a 1 KB block
@@ -534,8 +543,8 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
 
 template <int IDT, int WDT>
 dsa_status_t run_generic(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
-                         const void* k_idx, const uint8_t* k_sf, const void* w, float* scores,
-                         hipStream_t stream) {
+                         const void* k_idx, const uint8_t* k_sf, const void* w,
+                         const int32_t* seq_lens, float* scores, hipStream_t stream) {
   const size_t lds = (static_cast<size_t>(s.HI) * s.DI + s.HI) * sizeof(float);
   if (lds > 64 * 1024)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: HI*DI = %d too large for the generic kernel",
@@ -544,14 +553,14 @@ dsa_status_t run_generic(const dsa_shape_t& s, const void* q_idx, const uint8_t*
   LaunchTimer timer;
   hipExtLaunchKernelGGL(indexer_generic<IDT, WDT>, grid, dim3(256), lds, stream, timer.start(),
                         timer.stop(), 0, s.T, s.S, s.HI, s.DI, s.idx_scale, q_idx, q_sf, k_idx,
-                        k_sf, w, scores);
+                        k_sf, w, seq_lens, scores);
   return timer.done("indexer_generic");
 }
 
 template <bool FP8, int WDT>
 dsa_status_t run_stream(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
-                        const void* k_idx, const uint8_t* k_sf, const void* w, float* scores,
-                        hipStream_t stream) {
+                        const void* k_idx, const uint8_t* k_sf, const void* w,
+                        const int32_t* seq_lens, float* scores, hipStream_t stream) {
   constexpr int kBlockKeys = StreamShape<FP8>::kBlockKeys;
   const int nkb = (s.S + kBlockKeys - 1) / kBlockKeys;
   const int64_t blocks = static_cast<int64_t>(s.B) * s.T * nkb;
@@ -561,13 +570,14 @@ dsa_status_t run_stream(const dsa_shape_t& s, const void* q_idx, const uint8_t* 
   hipExtLaunchKernelGGL(indexer_stream<FP8, WDT>, dim3(static_cast<unsigned>(blocks)),
                         dim3(kStWaves * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
                         nkb, s.idx_scale, static_cast<const uint8_t*>(q_idx), q_sf,
-                        static_cast<const uint8_t*>(k_idx), k_sf, w, scores);
+                        static_cast<const uint8_t*>(k_idx), k_sf, w, seq_lens, scores);
   return timer.done("indexer_stream");
 }
 
 template <int WDT>
 dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_idx,
-                         const void* w, float* scores, hipStream_t stream) {
+                         const void* w, const int32_t* seq_lens, float* scores,
+                         hipStream_t stream) {
   const int n_qblk = (s.T + kPfWaves - 1) / kPfWaves;
   const int64_t blocks = static_cast<int64_t>(n_qblk) * s.B;
   if (blocks > 0x7fffffff)
@@ -576,7 +586,7 @@ dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_
   hipExtLaunchKernelGGL(indexer_prefill<WDT>, dim3(static_cast<unsigned>(blocks)),
                         dim3(kPfWaves * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
                         n_qblk, s.idx_scale, static_cast<const uint16_t*>(q_idx),
-                        static_cast<const uint16_t*>(k_idx), w, scores);
+                        static_cast<const uint16_t*>(k_idx), w, seq_lens, scores);
   return timer.done("indexer_prefill");
 }
 
@@ -584,32 +594,32 @@ dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_
 
 dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                             const void* k_idx, const uint8_t* k_sf, const void* w,
-                            float* scores, hipStream_t stream) {
+                            const int32_t* seq_lens, float* scores, hipStream_t stream) {
   const bool v32 = s.HI == kIdxHeads && s.DI == kIdxDim;
   const bool wbf = s.w_dtype == DSA_BF16;
   if (v32 && s.idx_dtype == DSA_BF16 && s.T >= kPfMinQueries)
-    return wbf ? run_prefill<DSA_BF16>(s, q_idx, k_idx, w, scores, stream)
-               : run_prefill<DSA_F32>(s, q_idx, k_idx, w, scores, stream);
+    return wbf ? run_prefill<DSA_BF16>(s, q_idx, k_idx, w, seq_lens, scores, stream)
+               : run_prefill<DSA_F32>(s, q_idx, k_idx, w, seq_lens, scores, stream);
   if (v32 && s.idx_dtype == DSA_BF16)
-    return wbf ? run_stream<false, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
-               : run_stream<false, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
+    return wbf ? run_stream<false, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
+               : run_stream<false, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);
   if (v32 && s.idx_dtype == DSA_FP8_E4M3)
-    return wbf ? run_stream<true, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
-               : run_stream<true, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
+    return wbf ? run_stream<true, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
+               : run_stream<true, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);
   // the generic kernel puts the query row on grid.y
   if (static_cast<int64_t>(s.B) * s.T > 65535)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: B*T = %lld exceeds 65535 query rows",
                 static_cast<long long>(s.B) * s.T);
   switch (s.idx_dtype) {
     case DSA_F32:
-      return wbf ? run_generic<DSA_F32, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
-                 : run_generic<DSA_F32, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
+      return wbf ? run_generic<DSA_F32, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
+                 : run_generic<DSA_F32, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);
     case DSA_BF16:
-      return wbf ? run_generic<DSA_BF16, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
-                 : run_generic<DSA_BF16, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
+      return wbf ? run_generic<DSA_BF16, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
+                 : run_generic<DSA_BF16, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);
     case DSA_FP8_E4M3:
-      return wbf ? run_generic<DSA_FP8_E4M3, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream)
-                 : run_generic<DSA_FP8_E4M3, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, scores, stream);
+      return wbf ? run_generic<DSA_FP8_E4M3, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
+                 : run_generic<DSA_FP8_E4M3, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);
   }
   return fail(DSA_ERR_UNSUPPORTED, "indexer: unknown idx_dtype %d", s.idx_dtype);
 }

@@ -106,6 +106,20 @@ def test_null_and_misaligned_pointers_rejected(dsa):
     assert rc == 1 and "shape is NULL" in L.dsa_last_error().decode()
 
 
+def test_ragged_entry_points_check_seq_lens_on_host(dsa):
+    L = dsa.lib()
+    s = _v32(dsa)
+    P = ctypes.c_void_p(256)
+    odd = ctypes.c_void_p(258)
+    rc = L.dsa_indexer_scores_ragged(ctypes.byref(s), odd, P, None, P, None, P, P, None)
+    assert rc == 1 and "seq_lens is not 4-byte aligned" in L.dsa_last_error().decode()
+    rc = L.dsa_forward_ragged(ctypes.byref(s), odd, P, None, P, None, P, P, P, None, P, None,
+                              P, 1 << 40, None)
+    assert rc == 1 and "seq_lens is not 4-byte aligned" in L.dsa_last_error().decode()
+    rc = L.dsa_indexer_scores_ragged(None, None, P, None, P, None, P, P, None)
+    assert rc == 1 and "shape is NULL" in L.dsa_last_error().decode()
+
+
 def test_forward_workspace_too_small(dsa):
     L = dsa.lib()
     s = _v32(dsa)

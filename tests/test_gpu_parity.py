@@ -52,13 +52,13 @@ def _host_rows(cfg, tensor, rb, rt):
     return np.concatenate(parts)
 
 
-def _oracle_scores(cfg, rb, rt):
+def _oracle_scores(cfg, rb, rt, seq_lens=None):
     k = g.full(cfg, "k_idx")
     qi = _host_rows(cfg, "q_idx", rb, rt)
     w = _host_rows(cfg, "w", rb, rt)
     if cfg.idx_dtype == "fp8":
-        return oracle.indexer_scores(cfg, rb, rt, qi[0], w, k[0], qi[1], k[1])
-    return oracle.indexer_scores(cfg, rb, rt, qi, w, k)
+        return oracle.indexer_scores(cfg, rb, rt, qi[0], w, k[0], qi[1], k[1], seq_lens=seq_lens)
+    return oracle.indexer_scores(cfg, rb, rt, qi, w, k, seq_lens=seq_lens)
 
 
 def _inputs(cfg):
@@ -123,6 +123,40 @@ def test_indexer_scores(dsa, case):
     if cfg.integer:
         assert np.array_equal(got, ref), f"{case}: integer-valued scores must be bit-exact"
     else:
+        U.assert_scores_close(got, ref, what=case)
+
+
+# ragged batches: per-sequence context lengths, including one shorter than T
+# (its first queries see nothing) and one of 0 keys; integer inputs: bit-exact
+RAGGED_CASES = {
+    "stream_decode": (g.CONFIGS["decode_8k"].replace(B=4, S=3000, integer=True),
+                      [3000, 1700, 1, 0]),
+    "stream_t3": (g.CONFIGS["decode_8k"].replace(B=3, T=3, S=2100, integer=True),
+                  [2100, 1000, 2]),
+    "stream_fp8": (g.CONFIGS["decode_64k_fp8"].replace(B=3, S=4200, integer=True),
+                   [4200, 2049, 64]),
+    "prefill": (g.CONFIGS["prefill_16k"].replace(B=3, T=300, S=1000, integer=True),
+                [1000, 650, 100]),
+    "generic": (SCORE_CASES["generic_bf16"], [77, 30]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(RAGGED_CASES))
+def test_indexer_scores_ragged(dsa, case):
+    cfg, lens = RAGGED_CASES[case]
+    print(f"[indexer_scores_ragged] {case}: {cfg} lens={lens}", flush=True)
+    torch = U.torch()
+    x = _inputs(cfg)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    got = dsa.dsa_indexer_scores_ragged(U.shape_of(cfg), lens_dev, x["q_idx"], x["k_idx"], x["w"],
+                                        x["q_sf"], x["k_sf"])
+    got = got.cpu().numpy().reshape(cfg.B * cfg.T, cfg.S)
+    rb, rt = _rows(cfg)
+    ref = _oracle_scores(cfg, rb, rt, seq_lens=np.array(lens, np.int32))
+    if cfg.integer:
+        assert np.array_equal(got, ref), f"{case}: integer-valued scores must be bit-exact"
+    else:
+        assert np.array_equal(np.isfinite(got), np.isfinite(ref))
         U.assert_scores_close(got, ref, what=case)
 
 
@@ -289,6 +323,31 @@ def test_forward_dense_when_k_covers_causal(dsa):
     do, dl = oracle.dense_mla(cfg, rb, rt, g.full(cfg, "q")[0], g.full(cfg, "kv"))
     U.assert_rows_close(o.cpu().numpy().reshape(cfg.T, cfg.H, cfg.Dc), do, U.RTOL["f32"], "dense")
     np.testing.assert_allclose(lse.cpu().numpy().reshape(cfg.T, cfg.H), dl, rtol=1e-5, atol=1e-5)
+
+
+def test_forward_ragged(dsa):
+    """A ragged decode batch: short sequences select fewer than K keys (their
+    rows end in -1) and attend over their own keys only."""
+    cfg = g.CONFIGS["decode_8k"].replace(B=4, S=3000)
+    lens = [3000, 2500, 1000, 37]
+    torch = U.torch()
+    x = _inputs(cfg)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, lse, idx = dsa.dsa_forward_ragged(U.shape_of(cfg), lens_dev, x["q_idx"], x["k_idx"], x["w"],
+                                         x["q"], x["kv"], x["q_sf"], x["k_sf"])
+    rb, rt = _rows(cfg)
+    ref_sc = _oracle_scores(cfg, rb, rt, seq_lens=np.array(lens, np.int32))
+    ref_idx = oracle.topk(cfg, ref_sc)
+    idx = idx.cpu().numpy().reshape(cfg.B, -1)
+    U.assert_selection_within_gap(idx, ref_idx, ref_sc)
+    for b, L in enumerate(lens):
+        assert (idx[b] >= 0).sum() == min(L, cfg.K_eff)
+        assert idx[b][idx[b] >= 0].max() < L
+    ro, rl = oracle.sparse_mla(cfg, rb, g.full(cfg, "q").reshape(cfg.B, cfg.H, cfg.D),
+                               g.full(cfg, "kv"), idx)
+    o = g.bf16_bits_to_f32(U.dev_to_np(o, "bf16")).reshape(cfg.B, cfg.H, cfg.Dc)
+    U.assert_rows_close(o, ro, U.RTOL["bf16"], "ragged o")
+    np.testing.assert_allclose(lse.cpu().numpy().reshape(cfg.B, cfg.H), rl, rtol=1e-4, atol=1e-4)
 
 
 FORWARD_CASES = {
