@@ -66,8 +66,10 @@ def load(path: Optional[str] = None):
             lib.orc_sparse_mla.argtypes = [sp, i32, P, P, P, P, i32, P, P, P]
             lib.orc_dense_mla.argtypes = [sp, i32, P, P, P, P, P, P]
             lib.orc_explicit_mla.argtypes = [i32] * 6 + [ctypes.c_double] + [P] * 7
+            lib.orc_cache_fill.argtypes = [i32, i32] + [P] * 10
+            lib.orc_quantize_e4m3_block.argtypes = [P, i32, P, P]
             for f in ("orc_indexer_scores", "orc_indexer_scores_ragged", "orc_topk", "orc_sparse_mla", "orc_dense_mla",
-                      "orc_explicit_mla"):
+                      "orc_explicit_mla", "orc_cache_fill", "orc_quantize_e4m3_block"):
                 getattr(lib, f).restype = ctypes.c_int
             _libs[path] = lib
         return _libs[path]
@@ -220,3 +222,50 @@ def explicit_mla(qC, qR, c, r, W_UK, W_UV, sm_scale, lib=None) -> np.ndarray:
     if rc:
         raise ValueError("orc_explicit_mla rejected its arguments")
     return out
+
+
+FILL_COLS = 768  # 512 latent + 64 rotary + 128 indexer key + 64 head weights
+
+
+def cache_fill(x_bits, W_bits, kv_gamma, k_gamma, k_beta, rope_cos, rope_sin,
+               threads: Optional[int] = None, lib=None):
+    """Cache fill and indexer inputs of n tokens: (kv [n, 576], k^I [n, 128],
+    w [n, 64]) in fp64, before any rounding to a storage format.  x_bits
+    [n, D] and W_bits [768, D] are bf16 bit patterns (uint16)."""
+    lib = lib or load()
+    x_bits = _c(x_bits, np.uint16)
+    W_bits = _c(W_bits, np.uint16)
+    n, D = x_bits.shape
+    assert W_bits.shape == (FILL_COLS, D)
+    kv_gamma, k_gamma, k_beta = (_c(a, np.float32) for a in (kv_gamma, k_gamma, k_beta))
+    rope_cos, rope_sin = _c(rope_cos, np.float32), _c(rope_sin, np.float32)
+    assert rope_cos.shape == (n, 32) and rope_sin.shape == (n, 32)
+    kv = np.empty((n, 576), np.float64)
+    k = np.empty((n, 128), np.float64)
+    w = np.empty((n, 64), np.float64)
+
+    def run(lo, hi):
+        rc = lib.orc_cache_fill(hi - lo, D, x_bits[lo:].ctypes.data, W_bits.ctypes.data,
+                                kv_gamma.ctypes.data, k_gamma.ctypes.data, k_beta.ctypes.data,
+                                rope_cos[lo:].ctypes.data, rope_sin[lo:].ctypes.data,
+                                kv[lo:].ctypes.data, k[lo:].ctypes.data, w[lo:].ctypes.data)
+        if rc:
+            raise ValueError("orc_cache_fill rejected its arguments")
+
+    _run_rows(run, n, threads or default_threads())
+    return kv, k, w
+
+
+def quantize_e4m3(y, block: int = 128, lib=None):
+    """ue8m0 + E4M3 block quantisation of fp64 values [..., m * block]:
+    (codes uint8 [..., m * block], scale bytes uint8 [..., m])."""
+    lib = lib or load()
+    y = _c(y, np.float64)
+    flat = y.reshape(-1, block)
+    codes = np.empty(flat.shape, np.uint8)
+    sb = np.empty(flat.shape[0], np.uint8)
+    for i in range(flat.shape[0]):
+        if lib.orc_quantize_e4m3_block(flat[i].ctypes.data, block, codes[i].ctypes.data,
+                                       sb[i:].ctypes.data):
+            raise ValueError("orc_quantize_e4m3_block rejected its arguments")
+    return codes.reshape(y.shape), sb.reshape(y.shape[:-1] + (y.shape[-1] // block,))

@@ -317,3 +317,108 @@ int orc_explicit_mla(int32_t H, int32_t Dc, int32_t Dn, int32_t Dv, int32_t Dr,
   free(logit);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Cache fill and indexer inputs, the step before the path (MoE-block step   */
+/* list: c^KV = x W_DKV, c^KV normalised, k^pe = x W_KR rotated, w = x W_w;  */
+/* the indexer's key projection wk with k_norm, a LayerNorm with affine and  */
+/* bias, from the nnterp deepseek_v32 module tree; the joint down-projection */
+/* split [512, 64] from the model.py excerpt on the same page).              */
+/* ------------------------------------------------------------------------ */
+
+#define ORC_FILL_LAT 512
+#define ORC_FILL_ROPE 64
+#define ORC_FILL_IDX 128
+#define ORC_FILL_W 64
+#define ORC_FILL_COLS (ORC_FILL_LAT + ORC_FILL_ROPE + ORC_FILL_IDX + ORC_FILL_W)
+#define ORC_NORM_EPS 1e-6
+
+int orc_cache_fill(int32_t n, int32_t D, const uint16_t* x, const uint16_t* W,
+                   const float* kv_gamma, const float* k_gamma, const float* k_beta,
+                   const float* rope_cos, const float* rope_sin, double* kv_out,
+                   double* k_out, double* w_out) {
+  if (n < 0 || D <= 0 || !x || !W || !kv_gamma || !k_gamma || !k_beta || !rope_cos ||
+      !rope_sin || !kv_out || !k_out || !w_out)
+    return 1;
+  double p[ORC_FILL_COLS];
+  for (int32_t t = 0; t < n; ++t) {
+    /* the joint projection: p_j = sum_d x[d] W[j][d] */
+    for (int32_t j = 0; j < ORC_FILL_COLS; ++j) {
+      double acc = 0.0;
+      for (int32_t d = 0; d < D; ++d)
+        acc += bf16_value(x[(int64_t)t * D + d]) * bf16_value(W[(int64_t)j * D + d]);
+      p[j] = acc;
+    }
+    double* kv = kv_out + (int64_t)t * (ORC_FILL_LAT + ORC_FILL_ROPE);
+    /* c^KV: RMSNorm over the 512 latent dims, then the gain */
+    double ms = 0.0;
+    for (int32_t i = 0; i < ORC_FILL_LAT; ++i) ms += p[i] * p[i];
+    ms /= ORC_FILL_LAT;
+    const double inv_rms = 1.0 / sqrt(ms + ORC_NORM_EPS);
+    for (int32_t i = 0; i < ORC_FILL_LAT; ++i) kv[i] = p[i] * inv_rms * kv_gamma[i];
+    /* k^pe: pair (2i, 2i + 1) is turned by angle i of this token and lands in
+     * dims i and i + 32 of the rotary part */
+    const double* kpe = p + ORC_FILL_LAT;
+    for (int32_t i = 0; i < ORC_FILL_ROPE / 2; ++i) {
+      const double c = rope_cos[(int64_t)t * (ORC_FILL_ROPE / 2) + i];
+      const double s = rope_sin[(int64_t)t * (ORC_FILL_ROPE / 2) + i];
+      const double a = kpe[2 * i], b = kpe[2 * i + 1];
+      kv[ORC_FILL_LAT + i] = a * c - b * s;
+      kv[ORC_FILL_LAT + ORC_FILL_ROPE / 2 + i] = a * s + b * c;
+    }
+    /* k^I: LayerNorm over its 128 dims (population variance), gain and bias */
+    const double* y = p + ORC_FILL_LAT + ORC_FILL_ROPE;
+    double mean = 0.0;
+    for (int32_t i = 0; i < ORC_FILL_IDX; ++i) mean += y[i];
+    mean /= ORC_FILL_IDX;
+    double var = 0.0;
+    for (int32_t i = 0; i < ORC_FILL_IDX; ++i) var += (y[i] - mean) * (y[i] - mean);
+    var /= ORC_FILL_IDX;
+    const double inv_std = 1.0 / sqrt(var + ORC_NORM_EPS);
+    for (int32_t i = 0; i < ORC_FILL_IDX; ++i)
+      k_out[(int64_t)t * ORC_FILL_IDX + i] = (y[i] - mean) * inv_std * k_gamma[i] + k_beta[i];
+    /* w: the head weights, as projected */
+    for (int32_t i = 0; i < ORC_FILL_W; ++i)
+      w_out[(int64_t)t * ORC_FILL_W + i] = p[ORC_FILL_LAT + ORC_FILL_ROPE + ORC_FILL_IDX + i];
+  }
+  return 0;
+}
+
+/* OCP E4M3FN code of |v| <= 448, round to nearest, ties to the even code */
+static uint8_t e4m3_code_of(double v) {
+  const uint8_t sign = (v < 0 || (v == 0 && signbit(v))) ? 0x80 : 0x00;
+  double a = fabs(v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a < ldexp(1.0, -6)) { /* subnormal: steps of 2^-9 */
+    const double q = a * 512.0;
+    double r = floor(q);
+    const double f = q - r;
+    if (f > 0.5 || (f == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    return sign | (uint8_t)r; /* r == 8 is the smallest normal, code 0x08 */
+  }
+  int e;
+  const double m = frexp(a, &e); /* a = m 2^e, m in [0.5, 1) */
+  int E = e - 1;                 /* a = (2m) 2^E, 2m in [1, 2) */
+  const double q = (2.0 * m - 1.0) * 8.0;
+  double r = floor(q);
+  const double f = q - r;
+  if (f > 0.5 || (f == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  if (r == 8.0) { r = 0.0; ++E; }
+  if (E + 7 > 15 || (E + 7 == 15 && r == 7.0)) return sign | 0x7E;
+  return sign | (uint8_t)(((E + 7) << 3) | (int)r);
+}
+
+int orc_quantize_e4m3_block(const double* y, int32_t len, uint8_t* codes, uint8_t* scale_byte) {
+  if (!y || !codes || !scale_byte || len <= 0) return 1;
+  double amax = 0.0;
+  for (int32_t i = 0; i < len; ++i) amax = fmax(amax, fabs(y[i]));
+  int e = 0; /* the smallest e with 448 2^e >= amax (0 for an all-zero block) */
+  if (amax > 0.0) {
+    e = (int)ceil(log2(amax / 448.0));
+    while (e > -127 && ldexp(448.0, e - 1) >= amax) --e;
+    while (e < 127 && ldexp(448.0, e) < amax) ++e;
+  }
+  *scale_byte = (uint8_t)(e + 127);
+  for (int32_t i = 0; i < len; ++i) codes[i] = e4m3_code_of(ldexp(y[i], -e));
+  return 0;
+}

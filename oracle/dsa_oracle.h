@@ -101,6 +101,28 @@ int orc_explicit_mla(int32_t H, int32_t Dc, int32_t Dn, int32_t Dv, int32_t Dr,
                      const double* qR, const double* c, const double* r,
                      const double* W_UK, const double* W_UV, double* out);
 
+/* Cache fill and indexer inputs for n tokens (the step before the path).
+ * x [n, D] bf16 hidden states; W [768, D] bf16 joint projection in Linear
+ * layout, rows 0-511 the latent down-projection W_DKV, 512-575 the rotary key
+ * W_KR, 576-703 the indexer key wk, 704-767 the head-weight projection W_w.
+ * With p = W x (fp64 sums of exact products) and eps = 1e-6:
+ *   kv_out [n, 576] = [ RMSNorm(p[0:512]) * kv_gamma ;
+ *                       rotary part: pair (2i, 2i+1) of p[512:576] turned by
+ *                       (rope_cos[t, i], rope_sin[t, i]) into dims i, i + 32 ]
+ *   k_out [n, 128]  = LayerNorm(p[576:704]) * k_gamma + k_beta
+ *   w_out [n, 64]   = p[704:768]
+ * The rotation angles are the caller's (rope_cos / rope_sin [n, 32]). */
+int orc_cache_fill(int32_t n, int32_t D, const uint16_t* x, const uint16_t* W,
+                   const float* kv_gamma, const float* k_gamma, const float* k_beta,
+                   const float* rope_cos, const float* rope_sin, double* kv_out,
+                   double* k_out, double* w_out);
+
+/* ue8m0 + OCP E4M3FN quantisation of one block of len values: the scale is
+ * 2^e with e the smallest integer such that 448 2^e >= max |y| (byte e + 127;
+ * an all-zero block gets byte 127), and each code is y / 2^e rounded to the
+ * nearest E4M3 value, ties to the even code. */
+int orc_quantize_e4m3_block(const double* y, int32_t len, uint8_t* codes, uint8_t* scale_byte);
+
 #ifdef __cplusplus
 }
 #endif

@@ -491,3 +491,104 @@ def test_page_constants_fix_the_shapes():
         m = (0.1 * d["mscale"] * math.log(d["rope_factor"]) + 1.0) ** 2
         assert round(m, 2) == f
         assert round(m * (dn + dr) ** -0.5, 4) == v[f"softmax_scale_yarn_{ver}"]
+
+
+# ---------------------------------------------------------------------------
+# cache fill and indexer inputs (the step before the path)
+# ---------------------------------------------------------------------------
+
+def _fill_inputs(n=4, D=96, seed=21):
+    rng = np.random.default_rng(seed)
+    x = g.f32_to_bf16_bits(rng.standard_normal((n, D)).astype(np.float32))
+    W = g.f32_to_bf16_bits((rng.standard_normal((oracle.FILL_COLS, D)) / 8).astype(np.float32))
+    ang = rng.uniform(-math.pi, math.pi, (n, 32))
+    return x, W, np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def _proj(x, W):
+    """The joint projection by numpy's matmul on the exact bf16 values."""
+    return g.bf16_bits_to_f32(x).astype(np.float64) @ g.bf16_bits_to_f32(W).astype(np.float64).T
+
+
+def test_fill_projection_is_the_matmul(oracle_lib):
+    """w is the raw projection; the other three blocks are functions of theirs."""
+    x, W, c, s = _fill_inputs()
+    _, _, w = oracle.cache_fill(x, W, np.ones(512), np.ones(128), np.zeros(128), c, s)
+    np.testing.assert_allclose(w, _proj(x, W)[:, 704:768], rtol=1e-12, atol=1e-12)
+
+
+def test_fill_latent_rmsnorm(oracle_lib):
+    """gain 1: unit root-mean-square; scale invariant (x doubled, exact in
+    bf16); the gain multiplies elementwise."""
+    x, W, c, s = _fill_inputs()
+    ones, zeros = np.ones(128), np.zeros(128)
+    kv, _, _ = oracle.cache_fill(x, W, np.ones(512), ones, zeros, c, s)
+    rms = np.sqrt((kv[:, :512] ** 2).mean(axis=1))
+    assert np.all(np.abs(rms - 1) < 1e-5)
+    x2 = g.f32_to_bf16_bits(2 * g.bf16_bits_to_f32(x))
+    kv2, _, _ = oracle.cache_fill(x2, W, np.ones(512), ones, zeros, c, s)
+    np.testing.assert_allclose(kv2[:, :512], kv[:, :512], rtol=1e-5, atol=1e-6)
+    gain = np.linspace(-2, 3, 512).astype(np.float32)
+    kvg, _, _ = oracle.cache_fill(x, W, gain, ones, zeros, c, s)
+    np.testing.assert_allclose(kvg[:, :512], kv[:, :512] * gain, rtol=1e-12, atol=1e-12)
+    # direction: the normalised latent is parallel to the raw one
+    raw = _proj(x, W)[:, :512]
+    cos = (kv[:, :512] * raw).sum(1) / np.linalg.norm(kv[:, :512], axis=1) / np.linalg.norm(raw, axis=1)
+    assert np.all(cos > 1 - 1e-12)
+
+
+def test_fill_rotary_layout_and_rotation(oracle_lib):
+    """Angle 0: the rotary part is the projection's even dims, then its odd
+    ones (the nnterp deepseek_v32 page, section 02); a quarter turn maps
+    (a, b) to (-b, a); every rotation keeps each pair's length."""
+    x, W, c, s = _fill_inputs()
+    n = x.shape[0]
+    ones, zeros = np.ones(128), np.zeros(128)
+    kpe = _proj(x, W)[:, 512:576]
+    kv, _, _ = oracle.cache_fill(x, W, np.ones(512), ones, zeros, np.ones((n, 32)), np.zeros((n, 32)))
+    np.testing.assert_allclose(kv[:, 512:544], kpe[:, 0::2], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(kv[:, 544:576], kpe[:, 1::2], rtol=1e-12, atol=1e-12)
+    kv, _, _ = oracle.cache_fill(x, W, np.ones(512), ones, zeros, np.zeros((n, 32)), np.ones((n, 32)))
+    np.testing.assert_allclose(kv[:, 512:544], -kpe[:, 1::2], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(kv[:, 544:576], kpe[:, 0::2], rtol=1e-12, atol=1e-12)
+    kv, _, _ = oracle.cache_fill(x, W, np.ones(512), ones, zeros, c, s)
+    np.testing.assert_allclose(kv[:, 512:544] ** 2 + kv[:, 544:576] ** 2,
+                               kpe[:, 0::2] ** 2 + kpe[:, 1::2] ** 2, rtol=1e-6)
+
+
+def test_fill_indexer_key_layernorm(oracle_lib):
+    """gain 1, bias 0: zero mean and unit variance; gain and bias are affine."""
+    x, W, c, s = _fill_inputs()
+    _, k, _ = oracle.cache_fill(x, W, np.ones(512), np.ones(128), np.zeros(128), c, s)
+    assert np.all(np.abs(k.mean(axis=1)) < 1e-12)
+    assert np.all(np.abs(k.var(axis=1) - 1) < 1e-5)
+    gam = np.linspace(0.5, 2, 128).astype(np.float32)
+    bet = np.linspace(-1, 1, 128).astype(np.float32)
+    _, k2, _ = oracle.cache_fill(x, W, np.ones(512), gam, bet, c, s)
+    np.testing.assert_allclose(k2, k * gam + bet, rtol=1e-12, atol=1e-12)
+    # the raw projection's own centring and scale
+    raw = _proj(x, W)[:, 576:704]
+    z = (raw - raw.mean(1, keepdims=True)) / np.sqrt(raw.var(1, keepdims=True) + 1e-6)
+    np.testing.assert_allclose(k, z, rtol=1e-9, atol=1e-9)
+
+
+def test_quantize_e4m3_blocks(oracle_lib):
+    """The block quantiser against the input generator's numpy version, and
+    hand-worked cases: exact codes, ties to even, scale at and above a power of
+    two, the all-zero block, the subnormal range."""
+    rng = np.random.default_rng(22)
+    y = rng.standard_normal((6, 256)) * np.array([1e-3, 1, 7, 300, 2e4, 0.02])[:, None]
+    y[2, :128] = 0.0
+    codes, sb = oracle.quantize_e4m3(y)
+    c2, s2 = g.quantize_e4m3_blocks(y.astype(np.float32))
+    assert np.array_equal(codes, c2) and np.array_equal(sb, s2)
+    blk = np.zeros(128)
+    blk[:6] = [448.0, 1.0625, 1.1875, -2.5, 2.0 ** -9 * 1.5, 2.0 ** -9 * 0.5]
+    codes, sb = oracle.quantize_e4m3(blk)
+    assert sb.tolist() == [127]                               # 448 fits exactly: scale 1
+    assert codes[:6].tolist() == [0x7E, 0x38, 0x3A, 0xC2, 0x02, 0x00]
+    blk[0] = 448.0 * 1.0001                                   # just above: next power of two
+    _, sb = oracle.quantize_e4m3(blk)
+    assert sb.tolist() == [128]
+    _, sb = oracle.quantize_e4m3(np.zeros(128))
+    assert sb.tolist() == [127]
