@@ -170,6 +170,50 @@ dsa_status_t dsa_forward_ragged(const dsa_shape_t* shape, const int32_t* seq_len
                                 int32_t* idx_out, void* o, float* lse, void* ws,
                                 size_t ws_bytes, void* stream);
 
+/*
+ * Cache fill and indexer inputs for N new tokens, the step before the path
+ * (atlas.klimoza.dev, DeepSeek-V3.2-Exp MoE block, "All 43 steps": c^KV =
+ * x W_DKV and its RMSNorm, k^pe = x W_KR rotated, w = x W_w; the indexer key
+ * wk with k_norm, a LayerNorm with gain and bias, from the nnterp
+ * deepseek_v32 module tree; the [512, 64] split of the joint down-projection
+ * from the model.py excerpt there).  With p = W x (fp32 accumulation):
+ *   x         [N, D] bf16   the tokens' attention inputs; D % 64 == 0
+ *   W         [768, D] bf16 joint projection in Linear layout (row j holds
+ *             output j's weights): rows 0-511 W_DKV, 512-575 W_KR,
+ *             576-703 wk, 704-767 W_w
+ *   kv_gamma  [512] fp32    gain of the latent RMSNorm (eps 1e-6)
+ *   k_gamma, k_beta [128] fp32  gain and bias of the indexer key LayerNorm
+ *             (eps 1e-6, population variance)
+ *   rope_cos, rope_sin [N, 32] fp32  the rotation of pair i for token n (the
+ *             frequencies, YaRN or not, are the caller's)
+ *   slots     [N] int64     the cache row each token fills (b * S + position
+ *             for caches laid out [B, S, ...]); a negative slot skips the
+ *             cache writes of that token.  Slots must be rows of the caches.
+ *   kv_cache  [rows, 576] kv_dtype (BF16 or F32): row slots[n] receives
+ *             [RMSNorm(p[0:512]) * kv_gamma ; p[512:576] with pair (2i, 2i+1)
+ *             turned into dims i and i + 32, the layout the nnterp page
+ *             states for this model]
+ *   k_cache   [rows, 128] k_dtype (BF16, F32, or FP8_E4M3 codes):
+ *             LayerNorm(p[576:704]) * k_gamma + k_beta; for FP8 the row's
+ *             ue8m0 scale byte goes to k_sf[slots[n]] (2^e with e the smallest
+ *             integer such that 448 2^e >= max |value|; codes round to
+ *             nearest, ties to even)
+ *   w_out     [N, 64] w_dtype (BF16 or F32): p[704:768], the head weights of
+ *             the token's query
+ * Every pointer is device memory, 16-byte aligned.  ws: at least
+ * dsa_cache_fill_workspace_bytes(N, D) bytes (fp32 partial projections).
+ * Errors as the other entry points (checked on the host before any launch).
+ */
+dsa_status_t dsa_cache_fill(int32_t N, int32_t D, const void* x, const void* W,
+                            const float* kv_gamma, const float* k_gamma, const float* k_beta,
+                            const float* rope_cos, const float* rope_sin, const int64_t* slots,
+                            int32_t kv_dtype, void* kv_cache, int32_t k_dtype, void* k_cache,
+                            uint8_t* k_sf, int32_t w_dtype, void* w_out, void* ws,
+                            size_t ws_bytes, void* stream);
+/* Workspace bytes of dsa_cache_fill on the current device ((size_t)-1 for
+ * invalid sizes). */
+size_t dsa_cache_fill_workspace_bytes(int32_t N, int32_t D);
+
 /* Workspace bytes an entry point needs for `shape` on the current device
  * (0 if none).  Returns (size_t)-1 when the shape is invalid. */
 size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry);

@@ -76,6 +76,11 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_mla_fwd.argtypes = [sp, P, P, P, P, P, P, sz, P]
         L.dsa_forward.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.dsa_forward_ragged.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        i32 = ctypes.c_int32
+        L.dsa_cache_fill.argtypes = [i32, i32] + [P] * 8 + [i32, P, i32, P, P, i32, P, P, sz, P]
+        L.dsa_cache_fill.restype = ctypes.c_int
+        L.dsa_cache_fill_workspace_bytes.argtypes = [i32, i32]
+        L.dsa_cache_fill_workspace_bytes.restype = sz
         for f in ("dsa_indexer_scores", "dsa_indexer_scores_ragged", "dsa_topk",
                   "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged"):
             getattr(L, f).restype = ctypes.c_int
@@ -288,3 +293,44 @@ def dsa_timing_end(max_kernels: int = 32) -> dict:
                                     min_ms=r.min_ms, max_ms=r.max_ms,
                                     avg_us=1e3 * r.total_ms / r.launches if r.launches else None)
     return out
+
+
+_DT_OF = {torch.bfloat16: DSA_BF16, torch.float32: DSA_F32, torch.uint8: DSA_FP8_E4M3}
+
+
+def dsa_cache_fill(x, W, kv_gamma, k_gamma, k_beta, rope_cos, rope_sin, slots, kv_cache, k_cache,
+                   k_sf=None, w_out: Optional[torch.Tensor] = None,
+                   w_dtype=torch.bfloat16, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Cache fill and indexer inputs of N tokens: writes rows slots[n] of
+    kv_cache [rows, 576] (bf16 / fp32) and k_cache [rows, 128] (bf16 / fp32,
+    or uint8 E4M3 codes with k_sf [rows] ue8m0 scales); returns the head
+    weights w [N, 64]."""
+    N, D = x.shape
+    dev = x.device
+    _req(x, "x", (N, D), (torch.bfloat16,), dev)
+    _req(W, "W", (768, D), (torch.bfloat16,), dev)
+    _req(kv_gamma, "kv_gamma", (512,), (torch.float32,), dev)
+    _req(k_gamma, "k_gamma", (128,), (torch.float32,), dev)
+    _req(k_beta, "k_beta", (128,), (torch.float32,), dev)
+    _req(rope_cos, "rope_cos", (N, 32), (torch.float32,), dev)
+    _req(rope_sin, "rope_sin", (N, 32), (torch.float32,), dev)
+    _req(slots, "slots", (N,), (torch.int64,), dev)
+    _req(kv_cache, "kv_cache", (kv_cache.shape[0], 576), (torch.bfloat16, torch.float32), dev)
+    _req(k_cache, "k_cache", (k_cache.shape[0], 128), (torch.bfloat16, torch.float32, torch.uint8),
+         dev)
+    if k_cache.dtype == torch.uint8:
+        _req(k_sf, "k_sf", (k_cache.shape[0],), (torch.uint8,), dev)
+    if w_out is None:
+        w_out = torch.empty((N, 64), dtype=w_dtype, device=dev)
+    _req(w_out, "w_out", (N, 64), (torch.bfloat16, torch.float32), dev)
+    if ws is None:
+        nb = lib().dsa_cache_fill_workspace_bytes(N, D)
+        if nb == ctypes.c_size_t(-1).value:
+            raise DsaError(1, f"cache fill: invalid sizes N={N}, D={D}")
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _check(lib().dsa_cache_fill(N, D, _ptr(x), _ptr(W), _ptr(kv_gamma), _ptr(k_gamma),
+                                _ptr(k_beta), _ptr(rope_cos), _ptr(rope_sin), _ptr(slots),
+                                _DT_OF[kv_cache.dtype], _ptr(kv_cache), _DT_OF[k_cache.dtype],
+                                _ptr(k_cache), _ptr(k_sf), _DT_OF[w_out.dtype], _ptr(w_out),
+                                _ptr(ws), ws.numel(), _stream(dev)))
+    return w_out

@@ -1,0 +1,304 @@
+// Cache fill and indexer inputs on gfx950: the step before the sparse path.
+//
+// For each new token with hidden state x (the attention input) the joint
+// projection p = W x covers four blocks (atlas.klimoza.dev, DeepSeek-V3.2-Exp
+// MoE block, "All 43 steps": c^KV = x W_DKV, k^pe = x W_KR, w = x W_w; the
+// indexer key projection wk and its k_norm from the nnterp deepseek_v32
+// module tree; the [512, 64] split of the joint down-projection from the
+// model.py excerpt on the same page):
+//   c^KV = p[0:512]     -> RMSNorm (eps 1e-6) times the gain       -> kv row 0..511
+//   k^pe = p[512:576]   -> pair (2i, 2i+1) turned by the token's
+//                          angle i into dims i and i + 32           -> kv row 512..575
+//   k^I  = p[576:704]   -> LayerNorm (eps 1e-6), gain and bias      -> indexer key row
+//                          (bf16, or E4M3 codes with one ue8m0 scale)
+//   w    = p[704:768]   -> the head weights of the token's query
+// The nnterp page states the rotary layout for this model: pair (2i, 2i+1)
+// of the projection lands in dims i and i + 32.
+//
+// Two kernels:
+//  * fill_gemm: p = x W^T for all tokens on 32x32x16 bf16 MFMAs, fp32
+//    partial sums over slices of the hidden dimension (few tokens: the
+//    weights stream through many workgroups at once).  Both operands are
+//    contiguous along the reduction (W in Linear layout, one output per row),
+//    so every lane loads 64 contiguous bytes of one row per 64-wide step.
+//  * fill_rows: one workgroup per token sums the partials in a fixed order
+//    (deterministic), then the norms, the rotation, the quantiser, and the
+//    scatter into the caches' rows.
+#include "dsa_device.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kFillLat = 512, kFillRope = 64, kFillIdx = 128, kFillW = 64;
+constexpr int kFillCols = kFillLat + kFillRope + kFillIdx + kFillW;  // 768
+constexpr int kGemmKStep = 64;                  // reduction width per iteration
+constexpr int kGemmRows = 32;                   // tokens per workgroup
+constexpr int kGemmWaveCols = 64;               // outputs per wave (two 32-wide tiles)
+constexpr int kGemmCols = 4 * kGemmWaveCols;    // outputs per workgroup (4 waves)
+static_assert(kFillCols % kGemmCols == 0, "whole column blocks");
+constexpr float kNormEps = 1e-6f;
+
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4v_t;
+
+__device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// grid: (column blocks, token blocks, slices of the hidden dimension).
+// Lane (h, m) of wave w: A = token row m0 + m, B = output rows c0 + 32 j + m;
+// step s of a 64-wide chunk takes hidden dims k + 32 h + 8 s .. + 8 on both
+// sides (any assignment shared by A and B gives the same sum).
+__global__ void __launch_bounds__(256)
+fill_gemm(int N, int D, int chunks_per_slice, const uint16_t* __restrict__ x,
+          const uint16_t* __restrict__ W, float* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hl = lane >> 5, m = lane & 31;
+  const int m0 = blockIdx.y * kGemmRows;
+  const int c0 = blockIdx.x * kGemmCols + wave * kGemmWaveCols;
+  const int nchunks = D / kGemmKStep;
+  const int ch0 = blockIdx.z * chunks_per_slice;
+  const int ch1 = min(nchunks, ch0 + chunks_per_slice);
+  const int row = min(m0 + m, N - 1);  // tail rows load a valid row, never stored
+  const u32x4v_t* ap = reinterpret_cast<const u32x4v_t*>(x + static_cast<int64_t>(row) * D + 32 * hl);
+  const u32x4v_t* bp0 = reinterpret_cast<const u32x4v_t*>(W + static_cast<int64_t>(c0 + m) * D + 32 * hl);
+  const u32x4v_t* bp1 = reinterpret_cast<const u32x4v_t*>(W + static_cast<int64_t>(c0 + 32 + m) * D + 32 * hl);
+  f32x16_t acc0, acc1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
+  // one chunk ahead in registers
+  u32x4v_t a[2][4], b0[2][4], b1[2][4];
+  auto load = [&](int ch, int buf) {
+    const int o = ch * (kGemmKStep / 8);  // in 16-byte units
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a[buf][s] = __builtin_nontemporal_load(ap + o + s);
+      b0[buf][s] = __builtin_nontemporal_load(bp0 + o + s);
+      b1[buf][s] = __builtin_nontemporal_load(bp1 + o + s);
+    }
+  };
+  if (ch0 < ch1) load(ch0, 0);
+  for (int ch = ch0; ch < ch1; ++ch) {
+    const int buf = (ch - ch0) & 1;
+    if (ch + 1 < ch1) load(ch + 1, buf ^ 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[buf][s]);
+      acc0 = mfma32(av, __builtin_bit_cast(bf16x8_t, b0[buf][s]), acc0);
+      acc1 = mfma32(av, __builtin_bit_cast(bf16x8_t, b1[buf][s]), acc1);
+    }
+  }
+  // register i of a tile: token m0 + 8 (i / 4) + 4 h + i % 4, output c0 + 32 j + m
+  float* out = part + static_cast<int64_t>(blockIdx.z) * N * kFillCols;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = m0 + 8 * (i >> 2) + 4 * hl + (i & 3);
+    if (t < N) {
+      out[static_cast<int64_t>(t) * kFillCols + c0 + m] = acc0[i];
+      out[static_cast<int64_t>(t) * kFillCols + c0 + 32 + m] = acc1[i];
+    }
+  }
+}
+
+// sum over a workgroup of 256 threads (4 waves); red: 4 floats of LDS
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();  // red may be reused
+  return r;
+}
+
+// fp32 -> OCP E4M3FN code, round to nearest with ties to the even code;
+// |v| <= 448 (the caller's scale guarantees it; larger saturates to 448)
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  if (a < 0.015625f) {  // below 2^-6: subnormal steps of 2^-9, rint ties to even
+    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));  // 8 = smallest normal
+  }
+  // keep 3 mantissa bits: add half an ulp of the 3-bit mantissa (minus one
+  // when the kept lsb is 0, so exact halves go to the even code), then cut
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  const int e = static_cast<int>(r >> 23) - 127;  // -6 .. 8
+  uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | ((r >> 20) & 7u);
+  if (code > 0x7Eu) code = 0x7Eu;  // 448 is the largest finite code
+  return sign | code;
+}
+
+// One workgroup of 256 threads per token.
+template <int KVDT, int KDT, int WDT>
+__global__ void __launch_bounds__(256)
+fill_rows(int N, int slices, const float* __restrict__ part, const float* __restrict__ kv_gamma,
+          const float* __restrict__ k_gamma, const float* __restrict__ k_beta,
+          const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
+          const int64_t* __restrict__ slots, void* __restrict__ kv_cache,
+          void* __restrict__ k_cache, uint8_t* __restrict__ k_sf, void* __restrict__ w_out) {
+  __shared__ float p[kFillCols];
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int n = blockIdx.x;
+  const int64_t slot = slots[n];
+  // the projection: partial sums in slice order
+  for (int c = tid; c < kFillCols; c += 256) {
+    float acc = 0.f;
+    for (int sl = 0; sl < slices; ++sl) acc += part[(static_cast<int64_t>(sl) * N + n) * kFillCols + c];
+    p[c] = acc;
+  }
+  __syncthreads();
+
+  // c^KV: RMSNorm over 512 dims (two per thread)
+  const float c0v = p[tid], c1v = p[tid + 256];
+  const float ms = block_sum(c0v * c0v + c1v * c1v, red) * (1.0f / kFillLat);
+  const float inv_rms = 1.0f / sqrtf(ms + kNormEps);
+  // k^I: LayerNorm over 128 dims (threads 0..127), mean then squared deviations
+  const float y = tid < kFillIdx ? p[kFillLat + kFillRope + tid] : 0.f;
+  const float mean = block_sum(y, red) * (1.0f / kFillIdx);
+  const float dev = tid < kFillIdx ? y - mean : 0.f;
+  const float var = block_sum(dev * dev, red) * (1.0f / kFillIdx);
+  const float z = tid < kFillIdx ? dev * (1.0f / sqrtf(var + kNormEps)) * k_gamma[tid] + k_beta[tid] : 0.f;
+
+  if (slot >= 0) {
+    // kv row: [normalised latent ; rotated key]
+    auto put_kv = [&](int i, float v) {
+      if constexpr (KVDT == DSA_BF16)
+        static_cast<uint16_t*>(kv_cache)[slot * (kFillLat + kFillRope) + i] = f32_to_bf16(v);
+      else
+        static_cast<float*>(kv_cache)[slot * (kFillLat + kFillRope) + i] = v;
+    };
+    put_kv(tid, c0v * inv_rms * kv_gamma[tid]);
+    put_kv(tid + 256, c1v * inv_rms * kv_gamma[tid + 256]);
+    if (tid < kFillRope / 2) {
+      const float cs = rope_cos[static_cast<int64_t>(n) * (kFillRope / 2) + tid];
+      const float sn = rope_sin[static_cast<int64_t>(n) * (kFillRope / 2) + tid];
+      const float a = p[kFillLat + 2 * tid], b = p[kFillLat + 2 * tid + 1];
+      put_kv(kFillLat + tid, a * cs - b * sn);
+      put_kv(kFillLat + kFillRope / 2 + tid, a * sn + b * cs);
+    }
+  }
+  // indexer key row
+  if constexpr (KDT == DSA_FP8_E4M3) {
+    // the scale 2^e: the smallest e with 448 2^e >= max |z| (an all-zero row: e = 0)
+    float amax = tid < kFillIdx ? fabsf(z) : 0.f;
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(red[0], red[1]);
+    int e = 0;
+    if (amax > 0.f) {
+      e = ilogbf(amax) - 8;  // 448 = 1.75 2^8
+      while (e > -127 && ldexpf(448.0f, e - 1) >= amax) --e;
+      while (e < 127 && ldexpf(448.0f, e) < amax) ++e;
+    }
+    if (slot >= 0 && tid < kFillIdx) {
+      static_cast<uint8_t*>(k_cache)[slot * kFillIdx + tid] =
+          static_cast<uint8_t>(e4m3_code(ldexpf(z, -e)));
+      if (tid == 0) k_sf[slot] = static_cast<uint8_t>(e + 127);
+    }
+  } else {
+    if (slot >= 0 && tid < kFillIdx) {
+      if constexpr (KDT == DSA_BF16)
+        static_cast<uint16_t*>(k_cache)[slot * kFillIdx + tid] = f32_to_bf16(z);
+      else
+        static_cast<float*>(k_cache)[slot * kFillIdx + tid] = z;
+    }
+  }
+  // head weights of the token's query
+  if (tid < kFillW) {
+    const float v = p[kFillLat + kFillRope + kFillIdx + tid];
+    if constexpr (WDT == DSA_BF16)
+      static_cast<uint16_t*>(w_out)[static_cast<int64_t>(n) * kFillW + tid] = f32_to_bf16(v);
+    else
+      static_cast<float*>(w_out)[static_cast<int64_t>(n) * kFillW + tid] = v;
+  }
+}
+
+struct FillPlan {
+  int row_blocks, slices, chunks_per_slice;
+};
+
+FillPlan fill_plan(int N, int D) {
+  FillPlan p;
+  p.row_blocks = (N + kGemmRows - 1) / kGemmRows;
+  const int nchunks = D / kGemmKStep;
+  const int col_blocks = kFillCols / kGemmCols;
+  // enough workgroups to spread the weight stream over the chip, at most 32
+  // slices (the partials stay small next to the weights)
+  int slices = (2 * device_info().cu_count + col_blocks * p.row_blocks - 1) / (col_blocks * p.row_blocks);
+  slices = max(1, min(min(slices, 32), nchunks));
+  p.chunks_per_slice = (nchunks + slices - 1) / slices;
+  p.slices = (nchunks + p.chunks_per_slice - 1) / p.chunks_per_slice;
+  return p;
+}
+
+template <int KVDT, int KDT, int WDT>
+dsa_status_t run_rows(int N, int slices, const float* part, const float* kv_gamma,
+                      const float* k_gamma, const float* k_beta, const float* rope_cos,
+                      const float* rope_sin, const int64_t* slots, void* kv_cache, void* k_cache,
+                      uint8_t* k_sf, void* w_out, hipStream_t stream) {
+  LaunchTimer timer;
+  hipExtLaunchKernelGGL(fill_rows<KVDT, KDT, WDT>, dim3(N), dim3(256), 0, stream, timer.start(),
+                        timer.stop(), 0, N, slices, part, kv_gamma, k_gamma, k_beta, rope_cos,
+                        rope_sin, slots, kv_cache, k_cache, k_sf, w_out);
+  return timer.done("fill_rows");
+}
+
+template <int KVDT, int KDT>
+dsa_status_t run_rows_w(int wdt, int N, int slices, const float* part, const float* kv_gamma,
+                        const float* k_gamma, const float* k_beta, const float* rope_cos,
+                        const float* rope_sin, const int64_t* slots, void* kv_cache,
+                        void* k_cache, uint8_t* k_sf, void* w_out, hipStream_t stream) {
+  return wdt == DSA_BF16
+             ? run_rows<KVDT, KDT, DSA_BF16>(N, slices, part, kv_gamma, k_gamma, k_beta, rope_cos,
+                                             rope_sin, slots, kv_cache, k_cache, k_sf, w_out, stream)
+             : run_rows<KVDT, KDT, DSA_F32>(N, slices, part, kv_gamma, k_gamma, k_beta, rope_cos,
+                                            rope_sin, slots, kv_cache, k_cache, k_sf, w_out, stream);
+}
+
+}  // namespace
+
+size_t cache_fill_workspace_bytes(int N, int D) {
+  const FillPlan p = fill_plan(N, D);
+  return static_cast<size_t>(p.slices) * N * kFillCols * sizeof(float);
+}
+
+dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const float* kv_gamma,
+                               const float* k_gamma, const float* k_beta, const float* rope_cos,
+                               const float* rope_sin, const int64_t* slots, int kv_dtype,
+                               void* kv_cache, int k_dtype, void* k_cache, uint8_t* k_sf,
+                               int w_dtype, void* w_out, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (N == 0) return DSA_OK;
+  const FillPlan p = fill_plan(N, D);
+  const size_t need = cache_fill_workspace_bytes(N, D);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "cache fill: workspace of %zu bytes needed, %zu given", need,
+                ws_bytes);
+  float* part = static_cast<float*>(ws);
+  {
+    LaunchTimer timer;
+    hipExtLaunchKernelGGL(fill_gemm, dim3(kFillCols / kGemmCols, p.row_blocks, p.slices),
+                          dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D,
+                          p.chunks_per_slice, static_cast<const uint16_t*>(x),
+                          static_cast<const uint16_t*>(W), part);
+    const dsa_status_t st = timer.done("fill_gemm");
+    if (st != DSA_OK) return st;
+  }
+#define DSA_FILL_ROWS(KV, K)                                                                    \
+  run_rows_w<KV, K>(w_dtype, N, p.slices, part, kv_gamma, k_gamma, k_beta, rope_cos, rope_sin, \
+                    slots, kv_cache, k_cache, k_sf, w_out, stream)
+  if (kv_dtype == DSA_BF16) {
+    if (k_dtype == DSA_FP8_E4M3) return DSA_FILL_ROWS(DSA_BF16, DSA_FP8_E4M3);
+    if (k_dtype == DSA_BF16) return DSA_FILL_ROWS(DSA_BF16, DSA_BF16);
+    return DSA_FILL_ROWS(DSA_BF16, DSA_F32);
+  }
+  if (k_dtype == DSA_FP8_E4M3) return DSA_FILL_ROWS(DSA_F32, DSA_FP8_E4M3);
+  if (k_dtype == DSA_BF16) return DSA_FILL_ROWS(DSA_F32, DSA_BF16);
+  return DSA_FILL_ROWS(DSA_F32, DSA_F32);
+#undef DSA_FILL_ROWS
+}
+
+}  // namespace dsa

@@ -300,6 +300,43 @@ dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx, const uint
                             ws, ws_bytes, stream);
 }
 
+dsa_status_t dsa_cache_fill(int32_t N, int32_t D, const void* x, const void* W,
+                            const float* kv_gamma, const float* k_gamma, const float* k_beta,
+                            const float* rope_cos, const float* rope_sin, const int64_t* slots,
+                            int32_t kv_dtype, void* kv_cache, int32_t k_dtype, void* k_cache,
+                            uint8_t* k_sf, int32_t w_dtype, void* w_out, void* ws,
+                            size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || D <= 0 || D % 64 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "cache fill: N = %d, D = %d (D must be a positive multiple of 64)",
+                N, D);
+  if (kv_dtype != DSA_BF16 && kv_dtype != DSA_F32)
+    return fail(DSA_ERR_UNSUPPORTED, "cache fill: kv_dtype %d", kv_dtype);
+  if (k_dtype != DSA_BF16 && k_dtype != DSA_F32 && k_dtype != DSA_FP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "cache fill: k_dtype %d", k_dtype);
+  if (w_dtype != DSA_BF16 && w_dtype != DSA_F32)
+    return fail(DSA_ERR_UNSUPPORTED, "cache fill: w_dtype %d", w_dtype);
+  if (N == 0) return DSA_OK;
+  dsa_status_t st;
+  if ((st = need(x, "x")) || (st = need(W, "W")) || (st = need(kv_gamma, "kv_gamma")) ||
+      (st = need(k_gamma, "k_gamma")) || (st = need(k_beta, "k_beta")) ||
+      (st = need(rope_cos, "rope_cos")) || (st = need(rope_sin, "rope_sin")) ||
+      (st = need(slots, "slots")) || (st = need(kv_cache, "kv_cache")) ||
+      (st = need(k_cache, "k_cache")) || (st = need(w_out, "w_out")))
+    return st;
+  if (k_dtype == DSA_FP8_E4M3 && k_sf == nullptr)
+    return fail(DSA_ERR_INVALID_ARG, "cache fill: k_sf is NULL with an FP8 indexer key");
+  if (ws != nullptr && !aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  return launch_cache_fill(N, D, x, W, kv_gamma, k_gamma, k_beta, rope_cos, rope_sin, slots,
+                           kv_dtype, kv_cache, k_dtype, k_cache, k_sf, w_dtype, w_out, ws,
+                           ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t dsa_cache_fill_workspace_bytes(int32_t N, int32_t D) {
+  if (N < 0 || D <= 0 || D % 64 != 0) return static_cast<size_t>(-1);
+  return N == 0 ? 0 : cache_fill_workspace_bytes(N, D);
+}
+
 size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry) {
   if (check_shape(shape) != DSA_OK) return static_cast<size_t>(-1);
   switch (entry) {

@@ -52,6 +52,15 @@ size_t topk_workspace_bytes(const dsa_shape_t& s);
 dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
                          size_t ws_bytes, hipStream_t stream);
 
+// ---- cache fill and indexer inputs ---------------------------------------
+size_t cache_fill_workspace_bytes(int N, int D);
+dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const float* kv_gamma,
+                               const float* k_gamma, const float* k_beta, const float* rope_cos,
+                               const float* rope_sin, const int64_t* slots, int kv_dtype,
+                               void* kv_cache, int k_dtype, void* k_cache, uint8_t* k_sf,
+                               int w_dtype, void* w_out, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 // ---- sparse latent attention ------------------------------------------
 size_t mla_workspace_bytes(const dsa_shape_t& s);
 dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* kv,

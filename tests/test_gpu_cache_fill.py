@@ -1,0 +1,142 @@
+"""GPU parity of the cache fill and indexer inputs (dsa_cache_fill) against
+the oracle (fp64).  Inputs are seeded draws: hidden states N(0, 1), the
+joint projection N(0, 1/D) (so projections are O(1)), gains around 1, biases
+around 0, rotation angles uniform.  bf16 outputs are compared row by row to
+the oracle rounded once; E4M3 keys by their codes (equal except where the
+oracle's fp64 value sits on a rounding tie of the GPU's fp32 one) and their
+scale bytes."""
+import math
+
+import numpy as np
+import pytest
+
+import dsa_inputs as g
+import oracle
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_latent_attention_lightning_amd as m
+    m.lib()
+    oracle.build(force=False)
+    return m
+
+
+def _draw(N, D, seed):
+    rng = np.random.default_rng(seed)
+    x = g.f32_to_bf16_bits(rng.standard_normal((N, D)).astype(np.float32))
+    W = g.f32_to_bf16_bits((rng.standard_normal((768, D)) / math.sqrt(D)).astype(np.float32))
+    kv_gamma = (1 + 0.1 * rng.standard_normal(512)).astype(np.float32)
+    k_gamma = (1 + 0.1 * rng.standard_normal(128)).astype(np.float32)
+    k_beta = (0.1 * rng.standard_normal(128)).astype(np.float32)
+    ang = rng.uniform(-math.pi, math.pi, (N, 32))
+    return dict(x=x, W=W, kv_gamma=kv_gamma, k_gamma=k_gamma, k_beta=k_beta,
+                cos=np.cos(ang).astype(np.float32), sin=np.sin(ang).astype(np.float32))
+
+
+def _run(dsa, d, slots, rows, kv_dt, k_dt, w_dt):
+    torch = U.torch()
+    dev = "cuda"
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x = t(d["x"].view(np.int16)).view(torch.bfloat16)
+    W = t(d["W"].view(np.int16)).view(torch.bfloat16)
+    kv_cache = torch.full((rows, 576), 7.0, dtype=kv_dt, device=dev)
+    if k_dt == "fp8":
+        k_cache = torch.full((rows, 128), 0x55, dtype=torch.uint8, device=dev)
+        k_sf = torch.full((rows,), 0xAA, dtype=torch.uint8, device=dev)
+    else:
+        k_cache = torch.full((rows, 128), 7.0, dtype=k_dt, device=dev)
+        k_sf = None
+    w = dsa.dsa_cache_fill(x, W, t(d["kv_gamma"]), t(d["k_gamma"]), t(d["k_beta"]), t(d["cos"]),
+                           t(d["sin"]), t(np.asarray(slots, np.int64)), kv_cache, k_cache, k_sf,
+                           w_dtype=w_dt)
+    torch.cuda.synchronize()
+    return kv_cache, k_cache, k_sf, w
+
+
+def _host(tensor):
+    torch = U.torch()
+    if tensor.dtype == torch.bfloat16:
+        return g.bf16_bits_to_f32(tensor.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return tensor.cpu().numpy().astype(np.float64)
+
+
+def _rows_close(got, ref, rtol, what):
+    err = np.abs(got - ref).max(axis=1)
+    lim = rtol * np.abs(ref).max(axis=1)
+    bad = np.nonzero(err > lim)[0]
+    assert bad.size == 0, f"{what}: rows {bad[:5]} off by {err[bad[:5]]} (allowed {lim[bad[:5]]})"
+
+
+def _check_fp8(codes, sb, ref):
+    """GPU E4M3 rows vs the oracle's fp64 rows: the scale byte is the
+    oracle's unless the row maximum is within 1e-5 of a scale boundary; codes
+    equal the oracle's quantisation except on a near-tie (2e-3 of a step: the
+    fp32 accumulation moves values by about 1e-5 of their size)."""
+    ref_codes, ref_sb = oracle.quantize_e4m3(ref)
+    ref_sb = ref_sb[:, 0]
+    amax = np.abs(ref).max(axis=1)
+    ratio = np.log2(amax / 448.0)
+    near_edge = np.abs(ratio - np.round(ratio)) < 1e-5
+    assert np.all((sb == ref_sb) | near_edge), "scale bytes differ away from a boundary"
+    ok = sb == ref_sb
+    scaled = ref[ok] / np.exp2(ref_sb[ok].astype(np.float64) - 127)[:, None]
+    deq_ref = g.e4m3_to_f32(ref_codes[ok]).astype(np.float64)
+    diff = codes[ok] != ref_codes[ok]
+    if diff.any():
+        # a code may differ only where the value is (almost) half-way between two codes
+        nxt = g.e4m3_to_f32(codes[ok]).astype(np.float64)
+        mid = 0.5 * (nxt + deq_ref)
+        step = np.abs(nxt - deq_ref)
+        assert np.all(np.abs(scaled[diff] - mid[diff]) <= 2e-3 * step[diff] + 1e-12), \
+            "E4M3 codes differ away from a rounding tie"
+    assert diff.mean() < 1e-3
+
+
+CASES = {
+    # decode step: one token per sequence of a 32-sequence batch, V3.2 width
+    "decode_bf16": (32, 7168, "bf16", "bf16", "bf16", 1),
+    "decode_fp8_key": (32, 7168, "bf16", "fp8", "bf16", 2),
+    # ragged token counts (partial 32-token blocks), fp32 outputs
+    "tokens_70_f32": (70, 7168, "f32", "f32", "f32", 3),
+    "tokens_5_fp8_small_width": (5, 256, "bf16", "fp8", "f32", 4),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_cache_fill(dsa, case):
+    N, D, kv_s, k_s, w_s, seed = CASES[case]
+    print(f"[cache_fill] {case}: N={N} D={D} kv={kv_s} k={k_s} w={w_s}", flush=True)
+    torch = U.torch()
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": "fp8"}
+    d = _draw(N, D, seed)
+    rows = 3 * N + 5
+    rng = np.random.default_rng(seed + 100)
+    slots = rng.permutation(rows)[:N].astype(np.int64)
+    slots[N // 2] = -1                             # this token's cache writes are skipped
+    kv_c, k_c, k_sf, w = _run(dsa, d, slots, rows, dt[kv_s], dt[k_s], dt[w_s])
+    rkv, rk, rw = oracle.cache_fill(d["x"], d["W"], d["kv_gamma"], d["k_gamma"], d["k_beta"],
+                                    d["cos"], d["sin"])
+    live = slots >= 0
+    rtol = 1e-2 if kv_s == "bf16" else 1e-4
+    kv_h = _host(kv_c)
+    _rows_close(kv_h[slots[live], :512], rkv[live, :512], rtol, "normalised latent")
+    _rows_close(kv_h[slots[live], 512:], rkv[live, 512:], rtol, "rotated key")
+    untouched = np.setdiff1d(np.arange(rows), slots[live])
+    assert np.all(kv_h[untouched] == 7.0), "rows outside the slots must stay untouched"
+    if k_s == "fp8":
+        codes = k_c.cpu().numpy()
+        sb = k_sf.cpu().numpy()
+        _check_fp8(codes[slots[live]], sb[slots[live]], rk[live])
+        assert np.all(codes[untouched] == 0x55) and np.all(sb[untouched] == 0xAA)
+    else:
+        k_h = _host(k_c)
+        _rows_close(k_h[slots[live]], rk[live], 1e-2 if k_s == "bf16" else 1e-4, "indexer key")
+        assert np.all(k_h[untouched] == 7.0)
+    _rows_close(_host(w), rw, 1e-2 if w_s == "bf16" else 1e-4, "head weights")
