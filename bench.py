@@ -210,6 +210,104 @@ def cpu_baseline(cfg, rows):
                        f"(scores, top-{cfg.K_eff}, sparse MLA) in fp64, {dt:.1f} s wall")
 
 
+# The cache fill and indexer inputs of new tokens (the step before the
+# path): the joint projection of the V3.2 width (D = 7168 -> 768 outputs)
+# plus norms, rotation, E4M3 keys and the scatter into the caches.
+FILL_WORKLOADS = {"cache_fill_decode": 32, "cache_fill_prefill": 16384}
+FILL_D = 7168
+
+
+def bench_cache_fill(args):
+    import numpy as np
+    import torch
+
+    import sparse_latent_attention_lightning_amd as dsa
+
+    N, D = FILL_WORKLOADS[args.workload], FILL_D
+    decode = N <= 256
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    w_bytes = 768 * D * 2
+    # rotate over enough weight copies that the 256 MB last-level cache cannot serve them
+    reps = args.replicas or (max(2, -(-600_000_000 // (w_bytes + N * D * 2))) if decode else 2)
+    xs = [torch.randn((N, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(reps)]
+    Ws = [(torch.randn((768, D), generator=gen, device=dev) / D ** 0.5).to(torch.bfloat16)
+          for _ in range(reps)]
+    ones512 = torch.ones(512, device=dev)
+    ones128 = torch.ones(128, device=dev)
+    zeros128 = torch.zeros(128, device=dev)
+    ang = torch.rand((N, 32), generator=gen, device=dev) * 6.283
+    cos, sin = torch.cos(ang), torch.sin(ang)
+    rows = N
+    slots = torch.arange(N, dtype=torch.int64, device=dev)
+    kv_cache = torch.empty((rows, 576), dtype=torch.bfloat16, device=dev)
+    k_cache = torch.empty((rows, 128), dtype=torch.uint8, device=dev)
+    k_sf = torch.empty((rows,), dtype=torch.uint8, device=dev)
+    w_out = torch.empty((N, 64), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, dsa.lib().dsa_cache_fill_workspace_bytes(N, D)), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        dsa.dsa_cache_fill(xs[i % reps], Ws[i % reps], ones512, ones128, zeros128, cos, sin, slots,
+                           kv_cache, k_cache, k_sf, w_out=w_out, ws=ws)
+
+    def timed(n, warm):
+        for i in range(warm):
+            step(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            step(warm + i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(args.steps, args.warmup)
+    dsa.dsa_timing_begin()
+    timed(args.steps, 0)
+    kt = dsa.dsa_timing_end()
+    for k, r in kt.items():
+        print(f"[bench] {k}: {r['avg_us']:.2f} us per launch ({r['launches']} launches)",
+              file=sys.stderr, flush=True)
+    # algorithmic: the weights and hidden states once, the cache rows, keys,
+    # scales and head weights written once
+    nbytes = w_bytes + N * D * 2 + N * (576 * 2 + 128 + 1 + 64 * 2)
+    nflops = 2.0 * N * 768 * D
+    t_gemm = kt["fill_gemm"]["avg_us"] / 1e6
+    roof = roofline(decode, nbytes if decode else 0, nflops, t_gemm)
+    roof["kernel"] = "fill_gemm"
+    roof["launch_us"] = round(t_gemm * 1e6, 2)
+    roof["algorithmic_per_launch"] = round(nbytes if decode else nflops)
+    roof["traffic"] = None
+    result = {
+        "metric": "cache-fill tokens/sec", "value": round(N / (ms / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": N, "hidden": D, "outputs": 768,
+                   "k_dtype": "fp8", "kv_dtype": "bf16"},
+        "kernel_us": {k: round(r["avg_us"], 2) for k, r in kt.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n_cpu = min(N, 32)
+        xb = xs[0][:n_cpu].view(torch.int16).cpu().numpy().view(np.uint16)
+        Wb = Ws[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        threads = oracle.default_threads()
+        t0 = time.perf_counter()
+        oracle.cache_fill(xb, Wb, np.ones(512), np.ones(128), np.zeros(128),
+                          cos[:n_cpu].cpu().numpy(), sin[:n_cpu].cpu().numpy(), threads=threads)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(n_cpu / dt, 2), "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"{n_cpu} tokens of the workload, fp64, {dt:.1f} s wall"}
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -219,6 +317,9 @@ def main():
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+    if args.workload in FILL_WORKLOADS:
+        bench_cache_fill(args)
+        return
     import torch
 
     import dsa_inputs as g

@@ -15,12 +15,13 @@
 // The nnterp page states the rotary layout for this model: pair (2i, 2i+1)
 // of the projection lands in dims i and i + 32.
 //
-// Two kernels:
-//  * fill_gemm: p = x W^T for all tokens on 32x32x16 bf16 MFMAs, fp32
-//    partial sums over slices of the hidden dimension (few tokens: the
-//    weights stream through many workgroups at once).  Both operands are
-//    contiguous along the reduction (W in Linear layout, one output per row),
-//    so every lane loads 64 contiguous bytes of one row per 64-wide step.
+// Kernels:
+//  * fill_gemm_skinny (few tokens, a decode step) / fill_gemm (many): p =
+//    x W^T on 32x32x16 bf16 MFMAs with fp32 partial sums over slices of the
+//    hidden dimension, so that the weights stream through many workgroups at
+//    once.  Both operands are contiguous along the reduction (W in Linear
+//    layout, one output per row), so every lane loads 64 contiguous bytes of
+//    one row per 64-wide step.
 //  * fill_rows: one workgroup per token sums the partials in a fixed order
 //    (deterministic), then the norms, the rotation, the quantiser, and the
 //    scatter into the caches' rows.
@@ -101,6 +102,65 @@ fill_gemm(int N, int D, int chunks_per_slice, const uint16_t* __restrict__ x,
   }
 }
 
+// Few tokens (a decode step): the weights are the traffic, and they should
+// be in flight all at once.  Workgroup = one 32-output tile of one slice of
+// the hidden dimension; its 4 waves take consecutive runs of kSkinnyChunks
+// 64-wide chunks each, issue every load of their run before the first MFMA,
+// and add their accumulators through LDS, so one partial per workgroup
+// reaches memory.  grid: (24 output tiles, token blocks, slices).
+constexpr int kSkinnyChunks = 4;
+constexpr int kSkinnyWaves = 4;
+
+__global__ void __launch_bounds__(kSkinnyWaves * 64)
+fill_gemm_skinny(int N, int D, const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
+                 float* __restrict__ part) {
+  __shared__ float red[kSkinnyWaves - 1][16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hl = lane >> 5, m = lane & 31;
+  const int m0 = blockIdx.y * kGemmRows;
+  const int c0 = blockIdx.x * 32;
+  const int nchunks = D / kGemmKStep;
+  const int ch0 = (blockIdx.z * kSkinnyWaves + wave) * kSkinnyChunks;
+  const int row = min(m0 + m, N - 1);
+  const u32x4v_t* ap = reinterpret_cast<const u32x4v_t*>(x + static_cast<int64_t>(row) * D + 32 * hl);
+  const u32x4v_t* bp = reinterpret_cast<const u32x4v_t*>(W + static_cast<int64_t>(c0 + m) * D + 32 * hl);
+  u32x4v_t a[kSkinnyChunks][4], b[kSkinnyChunks][4];
+#pragma unroll
+  for (int j = 0; j < kSkinnyChunks; ++j) {
+    const int ch = min(ch0 + j, nchunks - 1);  // past the end: a valid chunk, not used
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a[j][s] = ap[ch * (kGemmKStep / 8) + s];
+      b[j][s] = __builtin_nontemporal_load(bp + ch * (kGemmKStep / 8) + s);
+    }
+  }
+  f32x16_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kSkinnyChunks; ++j)
+    if (ch0 + j < nchunks)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = mfma32(__builtin_bit_cast(bf16x8_t, a[j][s]), __builtin_bit_cast(bf16x8_t, b[j][s]), acc);
+  if (wave > 0)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[wave - 1][i][lane] = acc[i];
+  __syncthreads();
+  if (wave == 0) {
+    float* out = part + static_cast<int64_t>(blockIdx.z) * N * kFillCols;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = acc[i];
+#pragma unroll
+      for (int u = 0; u < kSkinnyWaves - 1; ++u) v += red[u][i][lane];
+      const int t = m0 + 8 * (i >> 2) + 4 * hl + (i & 3);
+      if (t < N) out[static_cast<int64_t>(t) * kFillCols + c0 + m] = v;
+    }
+  }
+}
+
 // sum over a workgroup of 256 threads (4 waves); red: 4 floats of LDS
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -143,10 +203,29 @@ fill_rows(int N, int slices, const float* __restrict__ part, const float* __rest
   const int n = blockIdx.x;
   const int64_t slot = slots[n];
   // the projection: partial sums in slice order
-  for (int c = tid; c < kFillCols; c += 256) {
-    float acc = 0.f;
-    for (int sl = 0; sl < slices; ++sl) acc += part[(static_cast<int64_t>(sl) * N + n) * kFillCols + c];
-    p[c] = acc;
+  // (three outputs per thread, four slices per step: the loads of a step are
+  // independent; the sum runs in slice order)
+  {
+    const float* src = part + static_cast<int64_t>(n) * kFillCols + tid;
+    const int64_t stride = static_cast<int64_t>(N) * kFillCols;
+    float acc[3] = {0.f, 0.f, 0.f};
+    int sl = 0;
+    for (; sl + 4 <= slices; sl += 4) {
+      float v[4][3];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) v[u][q] = src[(sl + u) * stride + 256 * q];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) acc[q] += v[u][q];
+    }
+    for (; sl < slices; ++sl)
+#pragma unroll
+      for (int q = 0; q < 3; ++q) acc[q] += src[sl * stride + 256 * q];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) p[tid + 256 * q] = acc[q];
   }
   __syncthreads();
 
@@ -218,12 +297,20 @@ fill_rows(int N, int slices, const float* __restrict__ part, const float* __rest
 
 struct FillPlan {
   int row_blocks, slices, chunks_per_slice;
+  bool skinny;
 };
 
 FillPlan fill_plan(int N, int D) {
   FillPlan p;
   p.row_blocks = (N + kGemmRows - 1) / kGemmRows;
   const int nchunks = D / kGemmKStep;
+  // few tokens: 32-output tiles, each workgroup a 4 x kSkinnyChunks-chunk slice
+  p.skinny = p.row_blocks * (kFillCols / kGemmCols) < device_info().cu_count;
+  if (p.skinny) {
+    p.chunks_per_slice = kSkinnyWaves * kSkinnyChunks;
+    p.slices = (nchunks + p.chunks_per_slice - 1) / p.chunks_per_slice;
+    return p;
+  }
   const int col_blocks = kFillCols / kGemmCols;
   // enough workgroups to spread the weight stream over the chip, at most 32
   // slices (the partials stay small next to the weights)
@@ -278,7 +365,14 @@ dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const
     return fail(DSA_ERR_WORKSPACE, "cache fill: workspace of %zu bytes needed, %zu given", need,
                 ws_bytes);
   float* part = static_cast<float*>(ws);
-  {
+  if (p.skinny) {
+    LaunchTimer timer;
+    hipExtLaunchKernelGGL(fill_gemm_skinny, dim3(kFillCols / 32, p.row_blocks, p.slices),
+                          dim3(kSkinnyWaves * 64), 0, stream, timer.start(), timer.stop(), 0, N, D,
+                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), part);
+    const dsa_status_t st = timer.done("fill_gemm");
+    if (st != DSA_OK) return st;
+  } else {
     LaunchTimer timer;
     hipExtLaunchKernelGGL(fill_gemm, dim3(kFillCols / kGemmCols, p.row_blocks, p.slices),
                           dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D,
