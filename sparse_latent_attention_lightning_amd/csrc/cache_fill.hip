@@ -16,12 +16,12 @@
 // of the projection lands in dims i and i + 32.
 //
 // Kernels:
-//  * fill_gemm_skinny (few tokens, a decode step) / fill_gemm (many): p =
-//    x W^T on 32x32x16 bf16 MFMAs with fp32 partial sums over slices of the
-//    hidden dimension, so that the weights stream through many workgroups at
-//    once.  Both operands are contiguous along the reduction (W in Linear
-//    layout, one output per row), so every lane loads 64 contiguous bytes of
-//    one row per 64-wide step.
+//  * fill_gemm_skinny (few tokens, a decode step): p = x W^T on 32x32x16
+//    bf16 MFMAs with fp32 partial sums over slices of the hidden dimension,
+//    so that the weights stream through many workgroups at once;
+//    fill_gemm_tiled (many tokens): 128 x 128 tiles through an LDS ring.
+//    Both operands are contiguous along the reduction (W in Linear layout,
+//    one output per row).
 //  * fill_rows: one workgroup per token sums the partials in a fixed order
 //    (deterministic), then the norms, the rotation, the quantiser, and the
 //    scatter into the caches' rows.
@@ -34,72 +34,13 @@ namespace {
 constexpr int kFillLat = 512, kFillRope = 64, kFillIdx = 128, kFillW = 64;
 constexpr int kFillCols = kFillLat + kFillRope + kFillIdx + kFillW;  // 768
 constexpr int kGemmKStep = 64;                  // reduction width per iteration
-constexpr int kGemmRows = 32;                   // tokens per workgroup
-constexpr int kGemmWaveCols = 64;               // outputs per wave (two 32-wide tiles)
-constexpr int kGemmCols = 4 * kGemmWaveCols;    // outputs per workgroup (4 waves)
-static_assert(kFillCols % kGemmCols == 0, "whole column blocks");
+constexpr int kGemmRows = 32;                   // tokens per workgroup of the few-token kernel
 constexpr float kNormEps = 1e-6f;
 
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4v_t;
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// grid: (column blocks, token blocks, slices of the hidden dimension).
-// Lane (h, m) of wave w: A = token row m0 + m, B = output rows c0 + 32 j + m;
-// step s of a 64-wide chunk takes hidden dims k + 32 h + 8 s .. + 8 on both
-// sides (any assignment shared by A and B gives the same sum).
-__global__ void __launch_bounds__(256)
-fill_gemm(int N, int D, int chunks_per_slice, const uint16_t* __restrict__ x,
-          const uint16_t* __restrict__ W, float* __restrict__ part) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int hl = lane >> 5, m = lane & 31;
-  const int m0 = blockIdx.y * kGemmRows;
-  const int c0 = blockIdx.x * kGemmCols + wave * kGemmWaveCols;
-  const int nchunks = D / kGemmKStep;
-  const int ch0 = blockIdx.z * chunks_per_slice;
-  const int ch1 = min(nchunks, ch0 + chunks_per_slice);
-  const int row = min(m0 + m, N - 1);  // tail rows load a valid row, never stored
-  const u32x4v_t* ap = reinterpret_cast<const u32x4v_t*>(x + static_cast<int64_t>(row) * D + 32 * hl);
-  const u32x4v_t* bp0 = reinterpret_cast<const u32x4v_t*>(W + static_cast<int64_t>(c0 + m) * D + 32 * hl);
-  const u32x4v_t* bp1 = reinterpret_cast<const u32x4v_t*>(W + static_cast<int64_t>(c0 + 32 + m) * D + 32 * hl);
-  f32x16_t acc0, acc1;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc0[i] = acc1[i] = 0.f;
-  // one chunk ahead in registers
-  u32x4v_t a[2][4], b0[2][4], b1[2][4];
-  auto load = [&](int ch, int buf) {
-    const int o = ch * (kGemmKStep / 8);  // in 16-byte units
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      a[buf][s] = __builtin_nontemporal_load(ap + o + s);
-      b0[buf][s] = __builtin_nontemporal_load(bp0 + o + s);
-      b1[buf][s] = __builtin_nontemporal_load(bp1 + o + s);
-    }
-  };
-  if (ch0 < ch1) load(ch0, 0);
-  for (int ch = ch0; ch < ch1; ++ch) {
-    const int buf = (ch - ch0) & 1;
-    if (ch + 1 < ch1) load(ch + 1, buf ^ 1);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a[buf][s]);
-      acc0 = mfma32(av, __builtin_bit_cast(bf16x8_t, b0[buf][s]), acc0);
-      acc1 = mfma32(av, __builtin_bit_cast(bf16x8_t, b1[buf][s]), acc1);
-    }
-  }
-  // register i of a tile: token m0 + 8 (i / 4) + 4 h + i % 4, output c0 + 32 j + m
-  float* out = part + static_cast<int64_t>(blockIdx.z) * N * kFillCols;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int t = m0 + 8 * (i >> 2) + 4 * hl + (i & 3);
-    if (t < N) {
-      out[static_cast<int64_t>(t) * kFillCols + c0 + m] = acc0[i];
-      out[static_cast<int64_t>(t) * kFillCols + c0 + 32 + m] = acc1[i];
-    }
-  }
 }
 
 // Few tokens (a decode step): the weights are the traffic, and they should
@@ -159,6 +100,99 @@ fill_gemm_skinny(int N, int D, const uint16_t* __restrict__ x, const uint16_t* _
       if (t < N) out[static_cast<int64_t>(t) * kFillCols + c0 + m] = v;
     }
   }
+}
+
+// Many tokens (prefill): a tiled product.  Workgroup = 128 tokens x 128
+// outputs, wave w = a 64 x 64 quarter (2 x 2 tiles of 32 x 32); the
+// reduction moves in 64-wide chunks through a ring of kTStages LDS stages
+// (per stage an A tile of 128 token rows and a B tile of 128 weight rows,
+// 128 bytes each), filled by direct global -> LDS copies that run
+// kTStages - 1 chunks ahead.  A row's 16-byte piece c sits in slot
+// c ^ (r & 7) ^ ((r >> 3) & 1), so that the operand reads (32 rows, one piece
+// each) touch every bank once per cycle.
+constexpr int kTM = 128, kTN = 128, kTStages = 4;
+constexpr int kTTile = kTM * kGemmKStep * 2;  // 16 KB per operand tile
+constexpr int kTCopies = kTTile / 1024 / 4;   // copies per wave per operand tile
+
+__device__ __forceinline__ int tile_slot(int r, int piece) { return piece ^ (r & 7) ^ ((r >> 3) & 1); }
+
+__global__ void __launch_bounds__(256, 1)
+fill_gemm_tiled(int N, int D, const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
+                float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kTStages][2][kTTile];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane >> 5, m = lane & 31;
+  const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int nk = D / kGemmKStep;
+  // copy j of an operand tile covers its rows 8j .. 8j+7; lane l writes slot
+  // l & 7 of row 8j + l / 8 (rows past the last token load the last token)
+  auto issue = [&](int c) {
+    const int st = c % kTStages;
+#pragma unroll
+    for (int i = 0; i < kTCopies; ++i) {
+      const int j = wave * kTCopies + i;
+      const int r = 8 * j + (lane >> 3);
+      const int piece = tile_slot(r, lane & 7);
+      const int64_t k = static_cast<int64_t>(c) * kGemmKStep + piece * 8;
+      lds_dma_16(x + static_cast<int64_t>(min(m0 + r, N - 1)) * D + k, lds_addr(ring[st][0]) + 1024 * j);
+      lds_dma_16(W + static_cast<int64_t>(n0 + r) * D + k, lds_addr(ring[st][1]) + 1024 * j);
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < kTStages - 1; ++c)
+    if (c < nk) issue(c);
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+  for (int c = 0; c < nk; ++c) {
+    // chunk c has landed: the copies issued after it are those of the next
+    // min(kTStages - 2, nk - 1 - c) chunks, 2 kTCopies each
+    const int later = min(kTStages - 2, nk - 1 - c);
+    static_assert(kTStages == 4 && kTCopies == 4, "vmcnt immediates");
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's copies of chunk c are in; chunk c - 1 is consumed
+    if (c + kTStages - 1 < nk) issue(c + kTStages - 1);
+    const uint8_t* At = ring[c % kTStages][0];
+    const uint8_t* Bt = ring[c % kTStages][1];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int piece = 2 * s4 + hl;
+      bf16x8_t a[2], b[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int ra = wm + 32 * t + m, rb = wn + 32 * t + m;
+        a[t] = *reinterpret_cast<const bf16x8_t*>(At + ra * 128 + 16 * tile_slot(ra, piece));
+        b[t] = *reinterpret_cast<const bf16x8_t*>(Bt + rb * 128 + 16 * tile_slot(rb, piece));
+      }
+#pragma unroll
+      for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) acc[ta][tb] = mfma32(a[ta], b[tb], acc[ta][tb]);
+    }
+  }
+  // register i of tile (ta, tb): token m0 + wm + 32 ta + 8 (i / 4) + 4 h + i % 4,
+  // output n0 + wn + 32 tb + m
+#pragma unroll
+  for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int t = m0 + wm + 32 * ta + 8 * (i >> 2) + 4 * hl + (i & 3);
+      if (t < N)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+          part[static_cast<int64_t>(t) * kFillCols + n0 + wn + 32 * tb + m] = acc[ta][tb][i];
+    }
 }
 
 // sum over a workgroup of 256 threads (4 waves); red: 4 floats of LDS
@@ -304,20 +338,17 @@ FillPlan fill_plan(int N, int D) {
   FillPlan p;
   p.row_blocks = (N + kGemmRows - 1) / kGemmRows;
   const int nchunks = D / kGemmKStep;
-  // few tokens: 32-output tiles, each workgroup a 4 x kSkinnyChunks-chunk slice
-  p.skinny = p.row_blocks * (kFillCols / kGemmCols) < device_info().cu_count;
+  // few tokens (fewer 128 x 128 tiles than CUs): 32-output tiles, each
+  // workgroup a kSkinnyWaves x kSkinnyChunks-chunk slice
+  p.skinny = ((N + kTM - 1) / kTM) * (kFillCols / kTN) < device_info().cu_count;
   if (p.skinny) {
     p.chunks_per_slice = kSkinnyWaves * kSkinnyChunks;
     p.slices = (nchunks + p.chunks_per_slice - 1) / p.chunks_per_slice;
     return p;
   }
-  const int col_blocks = kFillCols / kGemmCols;
-  // enough workgroups to spread the weight stream over the chip, at most 32
-  // slices (the partials stay small next to the weights)
-  int slices = (2 * device_info().cu_count + col_blocks * p.row_blocks - 1) / (col_blocks * p.row_blocks);
-  slices = max(1, min(min(slices, 32), nchunks));
-  p.chunks_per_slice = (nchunks + slices - 1) / slices;
-  p.slices = (nchunks + p.chunks_per_slice - 1) / p.chunks_per_slice;
+  // otherwise 128 x 128 tiles over the whole hidden dimension
+  p.chunks_per_slice = nchunks;
+  p.slices = 1;
   return p;
 }
 
@@ -374,10 +405,9 @@ dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const
     if (st != DSA_OK) return st;
   } else {
     LaunchTimer timer;
-    hipExtLaunchKernelGGL(fill_gemm, dim3(kFillCols / kGemmCols, p.row_blocks, p.slices),
+    hipExtLaunchKernelGGL(fill_gemm_tiled, dim3(kFillCols / kTN, (N + kTM - 1) / kTM),
                           dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D,
-                          p.chunks_per_slice, static_cast<const uint16_t*>(x),
-                          static_cast<const uint16_t*>(W), part);
+                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), part);
     const dsa_status_t st = timer.done("fill_gemm");
     if (st != DSA_OK) return st;
   }
