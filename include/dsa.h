@@ -214,6 +214,24 @@ dsa_status_t dsa_cache_fill(int32_t N, int32_t D, const void* x, const void* W,
  * invalid sizes). */
 size_t dsa_cache_fill_workspace_bytes(int32_t N, int32_t D);
 
+/*
+ * The indexer query of N tokens: Q^I = c^Q wq_b (the nnterp deepseek_v32
+ * module tree: the indexer's wq_b maps the 1536-wide normalised query latent
+ * to 64 heads x 128; the bar over Q^I in the score is read as this query).
+ *   cq     [N, Dq] bf16      normalised query latents; Dq % 64 == 0 (1536)
+ *   wq_b   [8192, Dq] bf16   Linear layout: row 128 h + d is head h, dim d
+ *   q_out  [N, 64, 128] q_dtype (BF16, F32, or FP8_E4M3 codes), fp32
+ *          accumulation; for FP8 each (token, head) row gets its ue8m0 scale in
+ *          q_sf [N, 64] (the quantiser of dsa_cache_fill's keys)
+ * Every pointer is device memory, 16-byte aligned.  ws: at least
+ * dsa_indexer_query_workspace_bytes(N, Dq) bytes (fp32 partial projections).
+ */
+dsa_status_t dsa_indexer_query(int32_t N, int32_t Dq, const void* cq, const void* wq_b,
+                               int32_t q_dtype, void* q_out, uint8_t* q_sf, void* ws,
+                               size_t ws_bytes, void* stream);
+/* Workspace bytes of dsa_indexer_query ((size_t)-1 for invalid sizes). */
+size_t dsa_indexer_query_workspace_bytes(int32_t N, int32_t Dq);
+
 /* Workspace bytes an entry point needs for `shape` on the current device
  * (0 if none).  Returns (size_t)-1 when the shape is invalid. */
 size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry);

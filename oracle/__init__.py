@@ -68,8 +68,10 @@ def load(path: Optional[str] = None):
             lib.orc_explicit_mla.argtypes = [i32] * 6 + [ctypes.c_double] + [P] * 7
             lib.orc_cache_fill.argtypes = [i32, i32] + [P] * 10
             lib.orc_quantize_e4m3_block.argtypes = [P, i32, P, P]
+            lib.orc_indexer_query.argtypes = [i32, i32, P, P, i32, P]
             for f in ("orc_indexer_scores", "orc_indexer_scores_ragged", "orc_topk", "orc_sparse_mla", "orc_dense_mla",
-                      "orc_explicit_mla", "orc_cache_fill", "orc_quantize_e4m3_block"):
+                      "orc_explicit_mla", "orc_cache_fill", "orc_quantize_e4m3_block",
+                      "orc_indexer_query"):
                 getattr(lib, f).restype = ctypes.c_int
             _libs[path] = lib
         return _libs[path]
@@ -269,3 +271,22 @@ def quantize_e4m3(y, block: int = 128, lib=None):
                                        sb[i:].ctypes.data):
             raise ValueError("orc_quantize_e4m3_block rejected its arguments")
     return codes.reshape(y.shape), sb.reshape(y.shape[:-1] + (y.shape[-1] // block,))
+
+
+def indexer_query(cq_bits, wqb_bits, threads: Optional[int] = None, lib=None):
+    """Indexer query Q^I = c^Q wq_b of n tokens: [n, out_dim] fp64 (cq_bits
+    [n, Dq], wqb_bits [out_dim, Dq] bf16 bit patterns)."""
+    lib = lib or load()
+    cq_bits = _c(cq_bits, np.uint16)
+    wqb_bits = _c(wqb_bits, np.uint16)
+    n, Dq = cq_bits.shape
+    out_dim = wqb_bits.shape[0]
+    q = np.empty((n, out_dim), np.float64)
+
+    def run(lo, hi):
+        if lib.orc_indexer_query(hi - lo, Dq, cq_bits[lo:].ctypes.data, wqb_bits.ctypes.data,
+                                 out_dim, q[lo:].ctypes.data):
+            raise ValueError("orc_indexer_query rejected its arguments")
+
+    _run_rows(run, n, threads or default_threads())
+    return q

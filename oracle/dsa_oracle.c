@@ -422,3 +422,18 @@ int orc_quantize_e4m3_block(const double* y, int32_t len, uint8_t* codes, uint8_
   for (int32_t i = 0; i < len; ++i) codes[i] = e4m3_code_of(ldexp(y[i], -e));
   return 0;
 }
+
+/* The indexer query: Q^I = c^Q wq_b (the indexer's wq_b in the nnterp
+ * deepseek_v32 module tree), per token, fp64 sums of exact products. */
+int orc_indexer_query(int32_t n, int32_t Dq, const uint16_t* cq, const uint16_t* wq_b,
+                      int32_t out_dim, double* q) {
+  if (n < 0 || Dq <= 0 || out_dim <= 0 || !cq || !wq_b || !q) return 1;
+  for (int32_t t = 0; t < n; ++t)
+    for (int32_t j = 0; j < out_dim; ++j) {
+      double acc = 0.0;
+      for (int32_t d = 0; d < Dq; ++d)
+        acc += bf16_value(cq[(int64_t)t * Dq + d]) * bf16_value(wq_b[(int64_t)j * Dq + d]);
+      q[(int64_t)t * out_dim + j] = acc;
+    }
+  return 0;
+}

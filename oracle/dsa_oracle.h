@@ -123,6 +123,12 @@ int orc_cache_fill(int32_t n, int32_t D, const uint16_t* x, const uint16_t* W,
  * nearest E4M3 value, ties to the even code. */
 int orc_quantize_e4m3_block(const double* y, int32_t len, uint8_t* codes, uint8_t* scale_byte);
 
+/* The indexer query Q^I = c^Q wq_b of n tokens: cq [n, Dq] and wq_b
+ * [out_dim, Dq] bf16 (Linear layout; out_dim = 64 heads x 128, row 128 h + d
+ * is head h, dim d), q [n, out_dim] fp64. */
+int orc_indexer_query(int32_t n, int32_t Dq, const uint16_t* cq, const uint16_t* wq_b,
+                      int32_t out_dim, double* q);
+
 #ifdef __cplusplus
 }
 #endif

@@ -81,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.dsa_cache_fill.restype = ctypes.c_int
         L.dsa_cache_fill_workspace_bytes.argtypes = [i32, i32]
         L.dsa_cache_fill_workspace_bytes.restype = sz
+        L.dsa_indexer_query.argtypes = [i32, i32, P, P, i32, P, P, P, sz, P]
+        L.dsa_indexer_query.restype = ctypes.c_int
+        L.dsa_indexer_query_workspace_bytes.argtypes = [i32, i32]
+        L.dsa_indexer_query_workspace_bytes.restype = sz
         for f in ("dsa_indexer_scores", "dsa_indexer_scores_ragged", "dsa_topk",
                   "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged"):
             getattr(L, f).restype = ctypes.c_int
@@ -334,3 +338,29 @@ def dsa_cache_fill(x, W, kv_gamma, k_gamma, k_beta, rope_cos, rope_sin, slots, k
                                 _ptr(k_cache), _ptr(k_sf), _DT_OF[w_out.dtype], _ptr(w_out),
                                 _ptr(ws), ws.numel(), _stream(dev)))
     return w_out
+
+
+def dsa_indexer_query(cq, wq_b, q_dtype=torch.bfloat16, q_out: Optional[torch.Tensor] = None,
+                      q_sf: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Indexer query Q^I = c^Q wq_b of N tokens: q [N, 64, 128] (bf16 / fp32, or
+    uint8 E4M3 codes) and, for E4M3, q_sf [N, 64] ue8m0 scales (else None)."""
+    N, Dq = cq.shape
+    dev = cq.device
+    _req(cq, "cq", (N, Dq), (torch.bfloat16,), dev)
+    _req(wq_b, "wq_b", (8192, Dq), (torch.bfloat16,), dev)
+    fp8 = q_dtype == torch.uint8
+    if q_out is None:
+        q_out = torch.empty((N, 64, 128), dtype=q_dtype, device=dev)
+    _req(q_out, "q_out", (N, 64, 128), (torch.bfloat16, torch.float32, torch.uint8), dev)
+    if fp8 and q_sf is None:
+        q_sf = torch.empty((N, 64), dtype=torch.uint8, device=dev)
+    if q_sf is not None:
+        _req(q_sf, "q_sf", (N, 64), (torch.uint8,), dev)
+    if ws is None:
+        nb = lib().dsa_indexer_query_workspace_bytes(N, Dq)
+        if nb == ctypes.c_size_t(-1).value:
+            raise DsaError(1, f"indexer query: invalid sizes N={N}, Dq={Dq}")
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _check(lib().dsa_indexer_query(N, Dq, _ptr(cq), _ptr(wq_b), _DT_OF[q_out.dtype], _ptr(q_out),
+                                   _ptr(q_sf), _ptr(ws), ws.numel(), _stream(dev)))
+    return q_out, (q_sf if fp8 else None)

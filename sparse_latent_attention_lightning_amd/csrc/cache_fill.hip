@@ -53,8 +53,8 @@ constexpr int kSkinnyChunks = 4;
 constexpr int kSkinnyWaves = 4;
 
 __global__ void __launch_bounds__(kSkinnyWaves * 64)
-fill_gemm_skinny(int N, int D, const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
-                 float* __restrict__ part) {
+fill_gemm_skinny(int N, int D, int ncols, const uint16_t* __restrict__ x,
+                 const uint16_t* __restrict__ W, float* __restrict__ part) {
   __shared__ float red[kSkinnyWaves - 1][16][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -90,14 +90,14 @@ fill_gemm_skinny(int N, int D, const uint16_t* __restrict__ x, const uint16_t* _
     for (int i = 0; i < 16; ++i) red[wave - 1][i][lane] = acc[i];
   __syncthreads();
   if (wave == 0) {
-    float* out = part + static_cast<int64_t>(blockIdx.z) * N * kFillCols;
+    float* out = part + static_cast<int64_t>(blockIdx.z) * N * ncols;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float v = acc[i];
 #pragma unroll
       for (int u = 0; u < kSkinnyWaves - 1; ++u) v += red[u][i][lane];
       const int t = m0 + 8 * (i >> 2) + 4 * hl + (i & 3);
-      if (t < N) out[static_cast<int64_t>(t) * kFillCols + c0 + m] = v;
+      if (t < N) out[static_cast<int64_t>(t) * ncols + c0 + m] = v;
     }
   }
 }
@@ -117,8 +117,8 @@ constexpr int kTCopies = kTTile / 1024 / 4;   // copies per wave per operand til
 __device__ __forceinline__ int tile_slot(int r, int piece) { return piece ^ (r & 7) ^ ((r >> 3) & 1); }
 
 __global__ void __launch_bounds__(256, 1)
-fill_gemm_tiled(int N, int D, const uint16_t* __restrict__ x, const uint16_t* __restrict__ W,
-                float* __restrict__ part) {
+fill_gemm_tiled(int N, int D, int ncols, const uint16_t* __restrict__ x,
+                const uint16_t* __restrict__ W, float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kTStages][2][kTTile];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -191,7 +191,7 @@ fill_gemm_tiled(int N, int D, const uint16_t* __restrict__ x, const uint16_t* __
       if (t < N)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
-          part[static_cast<int64_t>(t) * kFillCols + n0 + wn + 32 * tb + m] = acc[ta][tb][i];
+          part[static_cast<int64_t>(t) * ncols + n0 + wn + 32 * tb + m] = acc[ta][tb][i];
     }
 }
 
@@ -334,13 +334,14 @@ struct FillPlan {
   bool skinny;
 };
 
-FillPlan fill_plan(int N, int D) {
+// ncols: outputs of the projection (a multiple of 128)
+FillPlan fill_plan(int N, int D, int ncols) {
   FillPlan p;
   p.row_blocks = (N + kGemmRows - 1) / kGemmRows;
   const int nchunks = D / kGemmKStep;
   // few tokens (fewer 128 x 128 tiles than CUs): 32-output tiles, each
   // workgroup a kSkinnyWaves x kSkinnyChunks-chunk slice
-  p.skinny = ((N + kTM - 1) / kTM) * (kFillCols / kTN) < device_info().cu_count;
+  p.skinny = ((N + kTM - 1) / kTM) * (ncols / kTN) < device_info().cu_count;
   if (p.skinny) {
     p.chunks_per_slice = kSkinnyWaves * kSkinnyChunks;
     p.slices = (nchunks + p.chunks_per_slice - 1) / p.chunks_per_slice;
@@ -376,11 +377,75 @@ dsa_status_t run_rows_w(int wdt, int N, int slices, const float* part, const flo
                                             rope_sin, slots, kv_cache, k_cache, k_sf, w_out, stream);
 }
 
+// The indexer query of each token (Q^I = c^Q wq_b, the nnterp module
+// tree's wq_b, 1536 -> 64 heads x 128): one wave per (token, head) adds the
+// slices of its 128 outputs (two per lane) and writes them as bf16 / fp32,
+// or as E4M3 codes with the head's ue8m0 scale (the quantiser of the keys).
+constexpr int kQHeads = 64, kQDim = 128, kQCols = kQHeads * kQDim;  // 8192
+
+template <int QDT>
+__global__ void __launch_bounds__(256)
+q_rows(int N, int slices, const float* __restrict__ part, void* __restrict__ q_out,
+       uint8_t* __restrict__ q_sf) {
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int64_t col = static_cast<int64_t>(h) * kQDim + 2 * lane;
+  const float* src = part + static_cast<int64_t>(n) * kQCols + col;
+  const int64_t stride = static_cast<int64_t>(N) * kQCols;
+  float v0 = 0.f, v1 = 0.f;
+  for (int sl = 0; sl < slices; ++sl) {  // slice order: deterministic
+    v0 += src[sl * stride];
+    v1 += src[sl * stride + 1];
+  }
+  const int64_t o = static_cast<int64_t>(n) * kQCols + col;
+  if constexpr (QDT == DSA_FP8_E4M3) {
+    const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    int e = 0;
+    if (amax > 0.f) {
+      e = ilogbf(amax) - 8;
+      while (e > -127 && ldexpf(448.0f, e - 1) >= amax) --e;
+      while (e < 127 && ldexpf(448.0f, e) < amax) ++e;
+    }
+    uint8_t* q = static_cast<uint8_t*>(q_out);
+    q[o] = static_cast<uint8_t>(e4m3_code(ldexpf(v0, -e)));
+    q[o + 1] = static_cast<uint8_t>(e4m3_code(ldexpf(v1, -e)));
+    if (lane == 0) q_sf[static_cast<int64_t>(n) * kQHeads + h] = static_cast<uint8_t>(e + 127);
+  } else if constexpr (QDT == DSA_BF16) {
+    reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(q_out) + o)[0] = f32x2_to_bf16x2(v0, v1);
+  } else {
+    static_cast<float*>(q_out)[o] = v0;
+    static_cast<float*>(q_out)[o + 1] = v1;
+  }
+}
+
+size_t projection_workspace_bytes(int N, int D, int ncols) {
+  const FillPlan p = fill_plan(N, D, ncols);
+  return static_cast<size_t>(p.slices) * N * ncols * sizeof(float);
+}
+
+// p = x W^T into fp32 partials (p.slices of them, [N, ncols] each)
+dsa_status_t launch_projection(const FillPlan& p, int N, int D, int ncols, const void* x,
+                               const void* W, float* part, const char* name, hipStream_t stream) {
+  LaunchTimer timer;
+  if (p.skinny)
+    hipExtLaunchKernelGGL(fill_gemm_skinny, dim3(ncols / 32, p.row_blocks, p.slices),
+                          dim3(kSkinnyWaves * 64), 0, stream, timer.start(), timer.stop(), 0, N, D,
+                          ncols, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
+                          part);
+  else
+    hipExtLaunchKernelGGL(fill_gemm_tiled, dim3(ncols / kTN, (N + kTM - 1) / kTM), dim3(256), 0,
+                          stream, timer.start(), timer.stop(), 0, N, D, ncols,
+                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), part);
+  return timer.done(name);
+}
+
 }  // namespace
 
-size_t cache_fill_workspace_bytes(int N, int D) {
-  const FillPlan p = fill_plan(N, D);
-  return static_cast<size_t>(p.slices) * N * kFillCols * sizeof(float);
+size_t cache_fill_workspace_bytes(int N, int D) { return projection_workspace_bytes(N, D, kFillCols); }
+
+size_t indexer_query_workspace_bytes(int N, int Dq) {
+  return projection_workspace_bytes(N, Dq, kQCols);
 }
 
 dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const float* kv_gamma,
@@ -390,25 +455,14 @@ dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const
                                int w_dtype, void* w_out, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
   if (N == 0) return DSA_OK;
-  const FillPlan p = fill_plan(N, D);
-  const size_t need = cache_fill_workspace_bytes(N, D);
+  const FillPlan p = fill_plan(N, D, kFillCols);
+  const size_t need = projection_workspace_bytes(N, D, kFillCols);
   if (ws == nullptr || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "cache fill: workspace of %zu bytes needed, %zu given", need,
                 ws_bytes);
   float* part = static_cast<float*>(ws);
-  if (p.skinny) {
-    LaunchTimer timer;
-    hipExtLaunchKernelGGL(fill_gemm_skinny, dim3(kFillCols / 32, p.row_blocks, p.slices),
-                          dim3(kSkinnyWaves * 64), 0, stream, timer.start(), timer.stop(), 0, N, D,
-                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), part);
-    const dsa_status_t st = timer.done("fill_gemm");
-    if (st != DSA_OK) return st;
-  } else {
-    LaunchTimer timer;
-    hipExtLaunchKernelGGL(fill_gemm_tiled, dim3(kFillCols / kTN, (N + kTM - 1) / kTM),
-                          dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D,
-                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), part);
-    const dsa_status_t st = timer.done("fill_gemm");
+  {
+    const dsa_status_t st = launch_projection(p, N, D, kFillCols, x, W, part, "fill_gemm", stream);
     if (st != DSA_OK) return st;
   }
 #define DSA_FILL_ROWS(KV, K)                                                                    \
@@ -423,6 +477,32 @@ dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const
   if (k_dtype == DSA_BF16) return DSA_FILL_ROWS(DSA_F32, DSA_BF16);
   return DSA_FILL_ROWS(DSA_F32, DSA_F32);
 #undef DSA_FILL_ROWS
+}
+
+dsa_status_t launch_indexer_query(int N, int Dq, const void* cq, const void* wq_b, int q_dtype,
+                                  void* q_out, uint8_t* q_sf, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  if (N == 0) return DSA_OK;
+  const FillPlan p = fill_plan(N, Dq, kQCols);
+  const size_t need = projection_workspace_bytes(N, Dq, kQCols);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "indexer query: workspace of %zu bytes needed, %zu given",
+                need, ws_bytes);
+  float* part = static_cast<float*>(ws);
+  dsa_status_t st = launch_projection(p, N, Dq, kQCols, cq, wq_b, part, "q_gemm", stream);
+  if (st != DSA_OK) return st;
+  LaunchTimer timer;
+  const dim3 grid(N, kQHeads / 4);
+  if (q_dtype == DSA_FP8_E4M3)
+    hipExtLaunchKernelGGL(q_rows<DSA_FP8_E4M3>, grid, dim3(256), 0, stream, timer.start(),
+                          timer.stop(), 0, N, p.slices, part, q_out, q_sf);
+  else if (q_dtype == DSA_BF16)
+    hipExtLaunchKernelGGL(q_rows<DSA_BF16>, grid, dim3(256), 0, stream, timer.start(),
+                          timer.stop(), 0, N, p.slices, part, q_out, q_sf);
+  else
+    hipExtLaunchKernelGGL(q_rows<DSA_F32>, grid, dim3(256), 0, stream, timer.start(),
+                          timer.stop(), 0, N, p.slices, part, q_out, q_sf);
+  return timer.done("q_rows");
 }
 
 }  // namespace dsa

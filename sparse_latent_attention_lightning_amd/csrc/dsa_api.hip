@@ -337,6 +337,30 @@ size_t dsa_cache_fill_workspace_bytes(int32_t N, int32_t D) {
   return N == 0 ? 0 : cache_fill_workspace_bytes(N, D);
 }
 
+dsa_status_t dsa_indexer_query(int32_t N, int32_t Dq, const void* cq, const void* wq_b,
+                               int32_t q_dtype, void* q_out, uint8_t* q_sf, void* ws,
+                               size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || Dq <= 0 || Dq % 64 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "indexer query: N = %d, Dq = %d (Dq must be a positive multiple of 64)",
+                N, Dq);
+  if (q_dtype != DSA_BF16 && q_dtype != DSA_F32 && q_dtype != DSA_FP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer query: q_dtype %d", q_dtype);
+  if (N == 0) return DSA_OK;
+  dsa_status_t st;
+  if ((st = need(cq, "cq")) || (st = need(wq_b, "wq_b")) || (st = need(q_out, "q_out"))) return st;
+  if (q_dtype == DSA_FP8_E4M3 && q_sf == nullptr)
+    return fail(DSA_ERR_INVALID_ARG, "indexer query: q_sf is NULL with FP8 output");
+  if (ws != nullptr && !aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  return launch_indexer_query(N, Dq, cq, wq_b, q_dtype, q_out, q_sf, ws, ws_bytes,
+                              static_cast<hipStream_t>(stream));
+}
+
+size_t dsa_indexer_query_workspace_bytes(int32_t N, int32_t Dq) {
+  if (N < 0 || Dq <= 0 || Dq % 64 != 0) return static_cast<size_t>(-1);
+  return N == 0 ? 0 : indexer_query_workspace_bytes(N, Dq);
+}
+
 size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry) {
   if (check_shape(shape) != DSA_OK) return static_cast<size_t>(-1);
   switch (entry) {

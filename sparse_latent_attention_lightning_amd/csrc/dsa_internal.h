@@ -54,6 +54,10 @@ dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx
 
 // ---- cache fill and indexer inputs ---------------------------------------
 size_t cache_fill_workspace_bytes(int N, int D);
+size_t indexer_query_workspace_bytes(int N, int Dq);
+dsa_status_t launch_indexer_query(int N, int Dq, const void* cq, const void* wq_b, int q_dtype,
+                                  void* q_out, uint8_t* q_sf, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const float* kv_gamma,
                                const float* k_gamma, const float* k_beta, const float* rope_cos,
                                const float* rope_sin, const int64_t* slots, int kv_dtype,

@@ -151,3 +151,32 @@ def test_cache_fill(dsa, case):
         _rows_close(k_h[slots[live]], rk[live], 1e-2 if k_s == "bf16" else 1e-4, "indexer key")
         assert np.all(k_h[untouched] == 7.0)
     _rows_close(_host(w), rw, 1e-2 if w_s == "bf16" else 1e-4, "head weights")
+
+
+QUERY_CASES = {
+    # one query per sequence of the 32-sequence decode batch, V3.2 widths
+    "decode_bf16": (32, 1536, "bf16", 11),
+    "decode_fp8": (32, 1536, "fp8", 12),
+    # enough tokens for the tiled kernel, a partial last 128-token tile
+    "tokens_600_fp8": (600, 1536, "fp8", 13),
+    "tokens_7_f32": (7, 1536, "f32", 14),
+}
+
+
+@pytest.mark.parametrize("case", sorted(QUERY_CASES))
+def test_indexer_query(dsa, case):
+    N, Dq, q_s, seed = QUERY_CASES[case]
+    print(f"[indexer_query] {case}: N={N} Dq={Dq} q={q_s}", flush=True)
+    torch = U.torch()
+    rng = np.random.default_rng(seed)
+    cq = g.f32_to_bf16_bits(rng.standard_normal((N, Dq)).astype(np.float32))
+    wq = g.f32_to_bf16_bits((rng.standard_normal((8192, Dq)) / math.sqrt(Dq)).astype(np.float32))
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).cuda().view(torch.bfloat16)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}[q_s]
+    q, q_sf = dsa.dsa_indexer_query(t(cq), t(wq), q_dtype=dt)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_query(cq, wq).reshape(N * 64, 128)
+    if q_s == "fp8":
+        _check_fp8(q.cpu().numpy().reshape(N * 64, 128), q_sf.cpu().numpy().reshape(N * 64), ref)
+    else:
+        _rows_close(_host(q).reshape(N * 64, 128), ref, 1e-2 if q_s == "bf16" else 1e-4, "indexer query")

@@ -592,3 +592,15 @@ def test_quantize_e4m3_blocks(oracle_lib):
     assert sb.tolist() == [128]
     _, sb = oracle.quantize_e4m3(np.zeros(128))
     assert sb.tolist() == [127]
+
+
+def test_indexer_query_is_the_matmul(oracle_lib):
+    """Q^I = c^Q wq_b: numpy's matmul on the exact bf16 values, row 128 h + d
+    of wq_b giving head h, dim d."""
+    rng = np.random.default_rng(23)
+    cq = g.f32_to_bf16_bits(rng.standard_normal((3, 64)).astype(np.float32))
+    wq = g.f32_to_bf16_bits(rng.standard_normal((256, 64)).astype(np.float32))
+    q = oracle.indexer_query(cq, wq)
+    ref = g.bf16_bits_to_f32(cq).astype(np.float64) @ g.bf16_bits_to_f32(wq).astype(np.float64).T
+    np.testing.assert_allclose(q, ref, rtol=1e-12, atol=1e-12)
+    assert q.reshape(3, 2, 128)[1, 1, 5] == q[1, 128 + 5]
