@@ -213,8 +213,10 @@ def cpu_baseline(cfg, rows):
 # The cache fill and indexer inputs of new tokens (the step before the
 # path): the joint projection of the V3.2 width (D = 7168 -> 768 outputs)
 # plus norms, rotation, E4M3 keys and the scatter into the caches.
-FILL_WORKLOADS = {"cache_fill_decode": 32, "cache_fill_prefill": 16384}
+FILL_WORKLOADS = {"cache_fill_decode": 32, "cache_fill_prefill": 16384,
+                  "indexer_query_decode": 32, "indexer_query_prefill": 16384}
 FILL_D = 7168
+QUERY_D = 1536   # the query latent width (q_lora_rank)
 
 
 def bench_cache_fill(args):
@@ -223,17 +225,20 @@ def bench_cache_fill(args):
 
     import sparse_latent_attention_lightning_amd as dsa
 
-    N, D = FILL_WORKLOADS[args.workload], FILL_D
+    N = FILL_WORKLOADS[args.workload]
+    query = args.workload.startswith("indexer_query")
+    D = QUERY_D if query else FILL_D
+    ncols = 8192 if query else 768
     decode = N <= 256
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
-    w_bytes = 768 * D * 2
+    w_bytes = ncols * D * 2
     # rotate over enough weight copies that the 256 MB last-level cache cannot serve them
     reps = args.replicas or (max(2, -(-600_000_000 // (w_bytes + N * D * 2))) if decode else 2)
     xs = [torch.randn((N, D), generator=gen, device=dev).to(torch.bfloat16) for _ in range(reps)]
-    Ws = [(torch.randn((768, D), generator=gen, device=dev) / D ** 0.5).to(torch.bfloat16)
+    Ws = [(torch.randn((ncols, D), generator=gen, device=dev) / D ** 0.5).to(torch.bfloat16)
           for _ in range(reps)]
     ones512 = torch.ones(512, device=dev)
     ones128 = torch.ones(128, device=dev)
@@ -246,11 +251,22 @@ def bench_cache_fill(args):
     k_cache = torch.empty((rows, 128), dtype=torch.uint8, device=dev)
     k_sf = torch.empty((rows,), dtype=torch.uint8, device=dev)
     w_out = torch.empty((N, 64), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(1, dsa.lib().dsa_cache_fill_workspace_bytes(N, D)), dtype=torch.uint8, device=dev)
+    if query:
+        ws = torch.empty(max(1, dsa.lib().dsa_indexer_query_workspace_bytes(N, D)), dtype=torch.uint8,
+                         device=dev)
+        q_out = torch.empty((N, 64, 128), dtype=torch.uint8, device=dev)
+        q_sf = torch.empty((N, 64), dtype=torch.uint8, device=dev)
+    else:
+        ws = torch.empty(max(1, dsa.lib().dsa_cache_fill_workspace_bytes(N, D)), dtype=torch.uint8,
+                         device=dev)
 
     def step(i):
-        dsa.dsa_cache_fill(xs[i % reps], Ws[i % reps], ones512, ones128, zeros128, cos, sin, slots,
-                           kv_cache, k_cache, k_sf, w_out=w_out, ws=ws)
+        if query:
+            dsa.dsa_indexer_query(xs[i % reps], Ws[i % reps], q_dtype=torch.uint8, q_out=q_out, q_sf=q_sf,
+                                  ws=ws)
+        else:
+            dsa.dsa_cache_fill(xs[i % reps], Ws[i % reps], ones512, ones128, zeros128, cos, sin, slots,
+                               kv_cache, k_cache, k_sf, w_out=w_out, ws=ws)
 
     def timed(n, warm):
         for i in range(warm):
@@ -274,25 +290,30 @@ def bench_cache_fill(args):
               file=sys.stderr, flush=True)
     # algorithmic: the weights and hidden states once, the cache rows, keys,
     # scales and head weights written once
-    nbytes = w_bytes + N * D * 2 + N * (576 * 2 + 128 + 1 + 64 * 2)
-    nflops = 2.0 * N * 768 * D
-    t_gemm = kt["fill_gemm"]["avg_us"] / 1e6
+    if query:
+        nbytes = w_bytes + N * D * 2 + N * 64 * (128 + 1)
+    else:
+        nbytes = w_bytes + N * D * 2 + N * (576 * 2 + 128 + 1 + 64 * 2)
+    nflops = 2.0 * N * ncols * D
+    gemm = "q_gemm" if query else "fill_gemm"
+    t_gemm = kt[gemm]["avg_us"] / 1e6
     roof = roofline(decode, nbytes if decode else 0, nflops, t_gemm)
-    roof["kernel"] = "fill_gemm"
+    roof["kernel"] = gemm
     roof["launch_us"] = round(t_gemm * 1e6, 2)
     roof["algorithmic_per_launch"] = round(nbytes if decode else nflops)
     roof["traffic"] = None
     result = {
-        "metric": "cache-fill tokens/sec", "value": round(N / (ms / 1e3), 1), "unit": "tokens/s",
+        "metric": ("indexer-query" if query else "cache-fill") + " tokens/sec",
+        "value": round(N / (ms / 1e3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": N, "hidden": D, "outputs": 768,
-                   "k_dtype": "fp8", "kv_dtype": "bf16"},
+        "config": {"workload": args.workload, "tokens": N, "hidden": D, "outputs": ncols,
+                   "out_dtype": "fp8" if query else "kv bf16, k fp8"},
         "kernel_us": {k: round(r["avg_us"], 2) for k, r in kt.items()},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not query:
         import oracle
         n_cpu = min(N, 32)
         xb = xs[0][:n_cpu].view(torch.int16).cpu().numpy().view(np.uint16)
