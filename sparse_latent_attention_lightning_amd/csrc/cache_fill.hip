@@ -39,6 +39,16 @@ constexpr float kNormEps = 1e-6f;
 
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4v_t;
 
+// Operands of a batch of products p_b = x_b W_b^T (one per head for the
+// absorption products, a batch of 1 otherwise): token n of batch b is the row
+// x + b sx + n ldx (D contiguous elements), output j of batch b the row
+// W + b sw + j D.  Partial sums go to part[(b slices + slice) N ncols].
+struct GemmOperands {
+  const uint16_t* x;
+  const uint16_t* W;
+  int64_t ldx, sx, sw;
+};
+
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -53,8 +63,7 @@ constexpr int kSkinnyChunks = 4;
 constexpr int kSkinnyWaves = 4;
 
 __global__ void __launch_bounds__(kSkinnyWaves * 64)
-fill_gemm_skinny(int N, int D, int ncols, const uint16_t* __restrict__ x,
-                 const uint16_t* __restrict__ W, float* __restrict__ part) {
+fill_gemm_skinny(int N, int D, int ncols, int slices, GemmOperands g, float* __restrict__ part) {
   __shared__ float red[kSkinnyWaves - 1][16][64];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -62,10 +71,11 @@ fill_gemm_skinny(int N, int D, int ncols, const uint16_t* __restrict__ x,
   const int m0 = blockIdx.y * kGemmRows;
   const int c0 = blockIdx.x * 32;
   const int nchunks = D / kGemmKStep;
-  const int ch0 = (blockIdx.z * kSkinnyWaves + wave) * kSkinnyChunks;
+  const int bt = blockIdx.z / slices, sl = blockIdx.z - bt * slices;
+  const int ch0 = (sl * kSkinnyWaves + wave) * kSkinnyChunks;
   const int row = min(m0 + m, N - 1);
-  const u32x4v_t* ap = reinterpret_cast<const u32x4v_t*>(x + static_cast<int64_t>(row) * D + 32 * hl);
-  const u32x4v_t* bp = reinterpret_cast<const u32x4v_t*>(W + static_cast<int64_t>(c0 + m) * D + 32 * hl);
+  const u32x4v_t* ap = reinterpret_cast<const u32x4v_t*>(g.x + bt * g.sx + row * g.ldx + 32 * hl);
+  const u32x4v_t* bp = reinterpret_cast<const u32x4v_t*>(g.W + bt * g.sw + static_cast<int64_t>(c0 + m) * D + 32 * hl);
   u32x4v_t a[kSkinnyChunks][4], b[kSkinnyChunks][4];
 #pragma unroll
   for (int j = 0; j < kSkinnyChunks; ++j) {
@@ -117,8 +127,7 @@ constexpr int kTCopies = kTTile / 1024 / 4;   // copies per wave per operand til
 __device__ __forceinline__ int tile_slot(int r, int piece) { return piece ^ (r & 7) ^ ((r >> 3) & 1); }
 
 __global__ void __launch_bounds__(256, 1)
-fill_gemm_tiled(int N, int D, int ncols, const uint16_t* __restrict__ x,
-                const uint16_t* __restrict__ W, float* __restrict__ part) {
+fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kTStages][2][kTTile];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -126,6 +135,9 @@ fill_gemm_tiled(int N, int D, int ncols, const uint16_t* __restrict__ x,
   const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int nk = D / kGemmKStep;
+  const uint16_t* x = g.x + blockIdx.z * g.sx;
+  const uint16_t* W = g.W + blockIdx.z * g.sw;
+  part += static_cast<int64_t>(blockIdx.z) * N * ncols;
   // copy j of an operand tile covers its rows 8j .. 8j+7; lane l writes slot
   // l & 7 of row 8j + l / 8 (rows past the last token load the last token)
   auto issue = [&](int c) {
@@ -136,7 +148,7 @@ fill_gemm_tiled(int N, int D, int ncols, const uint16_t* __restrict__ x,
       const int r = 8 * j + (lane >> 3);
       const int piece = tile_slot(r, lane & 7);
       const int64_t k = static_cast<int64_t>(c) * kGemmKStep + piece * 8;
-      lds_dma_16(x + static_cast<int64_t>(min(m0 + r, N - 1)) * D + k, lds_addr(ring[st][0]) + 1024 * j);
+      lds_dma_16(x + min(m0 + r, N - 1) * g.ldx + k, lds_addr(ring[st][0]) + 1024 * j);
       lds_dma_16(W + static_cast<int64_t>(n0 + r) * D + k, lds_addr(ring[st][1]) + 1024 * j);
     }
   };
@@ -419,25 +431,30 @@ q_rows(int N, int slices, const float* __restrict__ part, void* __restrict__ q_o
   }
 }
 
-size_t projection_workspace_bytes(int N, int D, int ncols) {
-  const FillPlan p = fill_plan(N, D, ncols);
-  return static_cast<size_t>(p.slices) * N * ncols * sizeof(float);
+size_t projection_workspace_bytes(int N, int D, int ncols, int batch = 1) {
+  const FillPlan p = fill_plan(N, D, ncols * batch);
+  return static_cast<size_t>(batch) * p.slices * N * ncols * sizeof(float);
 }
 
 // p = x W^T into fp32 partials (p.slices of them, [N, ncols] each)
-dsa_status_t launch_projection(const FillPlan& p, int N, int D, int ncols, const void* x,
-                               const void* W, float* part, const char* name, hipStream_t stream) {
+dsa_status_t launch_projection(const FillPlan& p, int N, int D, int ncols, int batch,
+                               const GemmOperands& g, float* part, const char* name,
+                               hipStream_t stream) {
   LaunchTimer timer;
   if (p.skinny)
-    hipExtLaunchKernelGGL(fill_gemm_skinny, dim3(ncols / 32, p.row_blocks, p.slices),
+    hipExtLaunchKernelGGL(fill_gemm_skinny, dim3(ncols / 32, p.row_blocks, batch * p.slices),
                           dim3(kSkinnyWaves * 64), 0, stream, timer.start(), timer.stop(), 0, N, D,
-                          ncols, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W),
-                          part);
+                          ncols, p.slices, g, part);
   else
-    hipExtLaunchKernelGGL(fill_gemm_tiled, dim3(ncols / kTN, (N + kTM - 1) / kTM), dim3(256), 0,
-                          stream, timer.start(), timer.stop(), 0, N, D, ncols,
-                          static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), part);
+    hipExtLaunchKernelGGL(fill_gemm_tiled, dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
+                          dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D, ncols, g,
+                          part);
   return timer.done(name);
+}
+
+// one projection of a batch of 1: x [N, D], W [ncols, D]
+GemmOperands plain(const void* x, const void* W, int D) {
+  return GemmOperands{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), D, 0, 0};
 }
 
 }  // namespace
@@ -462,7 +479,8 @@ dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const
                 ws_bytes);
   float* part = static_cast<float*>(ws);
   {
-    const dsa_status_t st = launch_projection(p, N, D, kFillCols, x, W, part, "fill_gemm", stream);
+    const dsa_status_t st =
+        launch_projection(p, N, D, kFillCols, 1, plain(x, W, D), part, "fill_gemm", stream);
     if (st != DSA_OK) return st;
   }
 #define DSA_FILL_ROWS(KV, K)                                                                    \
@@ -489,7 +507,7 @@ dsa_status_t launch_indexer_query(int N, int Dq, const void* cq, const void* wq_
     return fail(DSA_ERR_WORKSPACE, "indexer query: workspace of %zu bytes needed, %zu given",
                 need, ws_bytes);
   float* part = static_cast<float*>(ws);
-  dsa_status_t st = launch_projection(p, N, Dq, kQCols, cq, wq_b, part, "q_gemm", stream);
+  dsa_status_t st = launch_projection(p, N, Dq, kQCols, 1, plain(cq, wq_b, Dq), part, "q_gemm", stream);
   if (st != DSA_OK) return st;
   LaunchTimer timer;
   const dim3 grid(N, kQHeads / 4);
