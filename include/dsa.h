@@ -232,6 +232,65 @@ dsa_status_t dsa_indexer_query(int32_t N, int32_t Dq, const void* cq, const void
 /* Workspace bytes of dsa_indexer_query ((size_t)-1 for invalid sizes). */
 size_t dsa_indexer_query_workspace_bytes(int32_t N, int32_t Dq);
 
+/*
+ * Absorption products either side of the sparse attention (the step list of
+ * the atlas.klimoza.dev DeepSeek-V3.2-Exp page: k^C = c^KV W_UK and
+ * v = c^KV W_UV; the nnterp deepseek_v32 module tree: kv_b_proj 512 ->
+ * 32768 = 128 heads x (128 key dims + 128 value dims), q_b_proj's 192 per
+ * head = 128 + 64 rotary, o_proj 16384 -> 7168).  Absorbed, head h's query
+ * meets the latent rows through q_lat,h = W_UK,h q^C_h and its output
+ * leaves through W_UV,h o_lat,h, then wo.
+ *
+ * kv_b is kv_b_proj's weight in Linear layout, [H * 256, 512] bf16: rows
+ * 256 h .. 256 h + 127 are head h's key half, the next 128 its value half.
+ * H is the number of heads the caller holds (128 for the whole model).
+ */
+
+/* W_UK in the form dsa_absorb_query reads: w_uk_t [H, 512, 128] bf16 with
+ * w_uk_t[h][c][e] = kv_b[256 h + e][c] (a transpose, once per weight set).
+ * Device pointers, 16-byte aligned; w_uk_t must not overlap kv_b. */
+dsa_status_t dsa_absorb_prepare(int32_t H, const void* kv_b, void* w_uk_t, void* stream);
+
+/*
+ * The sparse attention's query of N tokens from q_b_proj's output:
+ *   qb   [N, H, 192] bf16: per head q^C (128) then q^pe (64, pairs (2i, 2i+1))
+ *   w_uk_t [H, 512, 128] bf16 from dsa_absorb_prepare
+ *   rope_cos, rope_sin [N, 32] fp32: the rotation of pair i for token n
+ *   q    [N, H, 576] q_dtype (BF16 or F32): q[n, h, c] = sum_e qb[n, h, e]
+ *        kv_b[256 h + e][c] for c < 512 (fp32 accumulation), then pair i of
+ *        q^pe turned into dims 512 + i and 544 + i (the cached key's layout)
+ * Device pointers, 16-byte aligned; no workspace.
+ */
+dsa_status_t dsa_absorb_query(int32_t N, int32_t H, const void* qb, const void* w_uk_t,
+                              const float* rope_cos, const float* rope_sin, int32_t q_dtype,
+                              void* q, void* stream);
+
+/*
+ * Head outputs from the latent contexts of N tokens:
+ *   o_lat [N, H, 512] bf16: dsa_sparse_mla_fwd's o
+ *   out   [N, H * 128] out_dtype (BF16 or F32): out[n, 128 h + d] =
+ *         sum_c o_lat[n, h, c] kv_b[256 h + 128 + d][c] (fp32 accumulation),
+ *         every head's output side by side, as o_proj / wo takes it
+ * Device pointers, 16-byte aligned; no workspace.
+ */
+dsa_status_t dsa_absorb_output(int32_t N, int32_t H, const void* o_lat, const void* kv_b,
+                               int32_t out_dtype, void* out, void* stream);
+
+/*
+ * The output projection wo (o_proj): out [N, Dout] = premix [N, Din] wo^T
+ * with wo [Dout, Din] bf16 in Linear layout (16384 -> 7168 for the model),
+ * fp32 accumulation, out_dtype BF16 or F32.  Din % 64 == 0, Dout % 128 == 0.
+ * ws: at least dsa_output_projection_workspace_bytes(N, Din, Dout) bytes
+ * (fp32 partial sums when few tokens split the reduction; 0 otherwise, and
+ * ws may then be NULL).  Device pointers, 16-byte aligned.
+ */
+dsa_status_t dsa_output_projection(int32_t N, int32_t Din, int32_t Dout, const void* premix,
+                                   const void* wo, int32_t out_dtype, void* out, void* ws,
+                                   size_t ws_bytes, void* stream);
+/* Workspace bytes of dsa_output_projection on the current device
+ * ((size_t)-1 for invalid sizes). */
+size_t dsa_output_projection_workspace_bytes(int32_t N, int32_t Din, int32_t Dout);
+
 /* Workspace bytes an entry point needs for `shape` on the current device
  * (0 if none).  Returns (size_t)-1 when the shape is invalid. */
 size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry);

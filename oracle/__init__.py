@@ -69,9 +69,13 @@ def load(path: Optional[str] = None):
             lib.orc_cache_fill.argtypes = [i32, i32] + [P] * 10
             lib.orc_quantize_e4m3_block.argtypes = [P, i32, P, P]
             lib.orc_indexer_query.argtypes = [i32, i32, P, P, i32, P]
+            lib.orc_absorb_query.argtypes = [i32] * 6 + [P] * 5
+            lib.orc_absorb_output.argtypes = [i32] * 5 + [P] * 3
+            lib.orc_linear_bf16.argtypes = [i32, i32, i32, P, P, P]
             for f in ("orc_indexer_scores", "orc_indexer_scores_ragged", "orc_topk", "orc_sparse_mla", "orc_dense_mla",
                       "orc_explicit_mla", "orc_cache_fill", "orc_quantize_e4m3_block",
-                      "orc_indexer_query"):
+                      "orc_indexer_query", "orc_absorb_query", "orc_absorb_output",
+                      "orc_linear_bf16"):
                 getattr(lib, f).restype = ctypes.c_int
             _libs[path] = lib
         return _libs[path]
@@ -290,3 +294,69 @@ def indexer_query(cq_bits, wqb_bits, threads: Optional[int] = None, lib=None):
 
     _run_rows(run, n, threads or default_threads())
     return q
+
+
+def absorb_query(qb, kv_b, rope_cos, rope_sin, Dn: int = 128, threads: Optional[int] = None,
+                 lib=None) -> np.ndarray:
+    """The sparse attention's query from q_b_proj's output, fp64: qb [n, H,
+    Dn + Dr], kv_b [H (Dn + Dv), Dc], rope_cos / rope_sin [n, Dr / 2] ->
+    q [n, H, Dc + Dr] (latent part absorbed through W_UK, rotary part turned)."""
+    lib = lib or load()
+    qb = _c(qb, np.float64)
+    kv_b = _c(kv_b, np.float64)
+    rope_cos, rope_sin = _c(rope_cos, np.float64), _c(rope_sin, np.float64)
+    n, H, in_w = qb.shape
+    Dr = in_w - Dn
+    Dc = kv_b.shape[1]
+    Dv = kv_b.shape[0] // H - Dn
+    assert kv_b.shape[0] == H * (Dn + Dv) and rope_cos.shape == (n, Dr // 2)
+    q = np.empty((n, H, Dc + Dr), np.float64)
+
+    def run(lo, hi):
+        if lib.orc_absorb_query(hi - lo, H, Dc, Dn, Dv, Dr, qb[lo:].ctypes.data, kv_b.ctypes.data,
+                                rope_cos[lo:].ctypes.data, rope_sin[lo:].ctypes.data,
+                                q[lo:].ctypes.data):
+            raise ValueError("orc_absorb_query rejected its arguments")
+
+    _run_rows(run, n, threads or default_threads())
+    return q
+
+
+def absorb_output(o, kv_b, Dn: int = 128, threads: Optional[int] = None, lib=None) -> np.ndarray:
+    """Head outputs from latent contexts, fp64: o [n, H, Dc], kv_b [H (Dn +
+    Dv), Dc] -> out [n, H Dv] (each head through its W_UV half)."""
+    lib = lib or load()
+    o = _c(o, np.float64)
+    kv_b = _c(kv_b, np.float64)
+    n, H, Dc = o.shape
+    Dv = kv_b.shape[0] // H - Dn
+    assert kv_b.shape == (H * (Dn + Dv), Dc)
+    out = np.empty((n, H * Dv), np.float64)
+
+    def run(lo, hi):
+        if lib.orc_absorb_output(hi - lo, H, Dc, Dn, Dv, o[lo:].ctypes.data, kv_b.ctypes.data,
+                                 out[lo:].ctypes.data):
+            raise ValueError("orc_absorb_output rejected its arguments")
+
+    _run_rows(run, n, threads or default_threads())
+    return out
+
+
+def linear_bf16(x_bits, W_bits, threads: Optional[int] = None, lib=None) -> np.ndarray:
+    """A Linear layer (o_proj / wo) on bf16 bit patterns: x [n, Din], W [Dout,
+    Din] -> x W^T [n, Dout] in fp64."""
+    lib = lib or load()
+    x_bits = _c(x_bits, np.uint16)
+    W_bits = _c(W_bits, np.uint16)
+    n, Din = x_bits.shape
+    Dout = W_bits.shape[0]
+    assert W_bits.shape == (Dout, Din)
+    out = np.empty((n, Dout), np.float64)
+
+    def run(lo, hi):
+        if lib.orc_linear_bf16(hi - lo, Din, Dout, x_bits[lo:].ctypes.data, W_bits.ctypes.data,
+                               out[lo:].ctypes.data):
+            raise ValueError("orc_linear_bf16 rejected its arguments")
+
+    _run_rows(run, n, threads or default_threads())
+    return out

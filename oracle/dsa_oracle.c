@@ -437,3 +437,66 @@ int orc_indexer_query(int32_t n, int32_t Dq, const uint16_t* cq, const uint16_t*
     }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Absorption either side of the sparse attention.                          */
+
+int orc_absorb_query(int32_t n, int32_t H, int32_t Dc, int32_t Dn, int32_t Dv, int32_t Dr,
+                     const double* qb, const double* kv_b, const double* rope_cos,
+                     const double* rope_sin, double* q) {
+  if (n < 0 || H <= 0 || Dc <= 0 || Dn <= 0 || Dv <= 0 || Dr < 0 || Dr % 2) return 1;
+  const int32_t in_w = Dn + Dr, out_w = Dc + Dr, head_rows = Dn + Dv;
+  for (int32_t t = 0; t < n; ++t)
+    for (int32_t h = 0; h < H; ++h) {
+      const double* qc = qb + ((int64_t)t * H + h) * in_w;
+      double* qo = q + ((int64_t)t * H + h) * out_w;
+      /* latent part: the head's q^C through its key half of kv_b */
+      for (int32_t c = 0; c < Dc; ++c) {
+        double acc = 0.0;
+        for (int32_t e = 0; e < Dn; ++e)
+          acc += qc[e] * kv_b[((int64_t)h * head_rows + e) * Dc + c];
+        qo[c] = acc;
+      }
+      /* rotary part: pair (2i, 2i+1) of q^pe turned by angle i */
+      const double* pe = qc + Dn;
+      for (int32_t i = 0; i < Dr / 2; ++i) {
+        const double cs = rope_cos[(int64_t)t * (Dr / 2) + i];
+        const double sn = rope_sin[(int64_t)t * (Dr / 2) + i];
+        const double a = pe[2 * i], b = pe[2 * i + 1];
+        qo[Dc + i] = a * cs - b * sn;
+        qo[Dc + Dr / 2 + i] = a * sn + b * cs;
+      }
+    }
+  return 0;
+}
+
+int orc_absorb_output(int32_t n, int32_t H, int32_t Dc, int32_t Dn, int32_t Dv,
+                      const double* o, const double* kv_b, double* out) {
+  if (n < 0 || H <= 0 || Dc <= 0 || Dn <= 0 || Dv <= 0) return 1;
+  const int32_t head_rows = Dn + Dv;
+  for (int32_t t = 0; t < n; ++t)
+    for (int32_t h = 0; h < H; ++h) {
+      const double* ol = o + ((int64_t)t * H + h) * Dc;
+      for (int32_t d = 0; d < Dv; ++d) {
+        /* the head's value half of kv_b: rows after its Dn key rows */
+        const double* wv = kv_b + ((int64_t)h * head_rows + Dn + d) * Dc;
+        double acc = 0.0;
+        for (int32_t c = 0; c < Dc; ++c) acc += ol[c] * wv[c];
+        out[((int64_t)t * H + h) * Dv + d] = acc;
+      }
+    }
+  return 0;
+}
+
+int orc_linear_bf16(int32_t n, int32_t Din, int32_t Dout, const uint16_t* x, const uint16_t* W,
+                    double* out) {
+  if (n < 0 || Din <= 0 || Dout <= 0 || !x || !W || !out) return 1;
+  for (int32_t t = 0; t < n; ++t)
+    for (int32_t j = 0; j < Dout; ++j) {
+      double acc = 0.0;
+      for (int32_t i = 0; i < Din; ++i)
+        acc += bf16_value(x[(int64_t)t * Din + i]) * bf16_value(W[(int64_t)j * Din + i]);
+      out[(int64_t)t * Dout + j] = acc;
+    }
+  return 0;
+}

@@ -129,6 +129,30 @@ int orc_quantize_e4m3_block(const double* y, int32_t len, uint8_t* codes, uint8_
 int orc_indexer_query(int32_t n, int32_t Dq, const uint16_t* cq, const uint16_t* wq_b,
                       int32_t out_dim, double* q);
 
+/* Absorption either side of the sparse attention (the MoE-block step list:
+ * k^C = c^KV W_UK and v = c^KV W_UV; the nnterp module tree's kv_b_proj
+ * 512 -> heads x (key dims + value dims)).  kv_b is kv_b_proj's Linear
+ * weight [H (Dn + Dv), Dc]: rows h (Dn + Dv) + e, e < Dn, are head h's key
+ * dims, the next Dv rows its value dims.  All values fp64.
+ *
+ * orc_absorb_query: qb [n, H, Dn + Dr] (q^C then q^pe per head), rope_cos and
+ * rope_sin [n, Dr / 2]; q [n, H, Dc + Dr]: q[t,h,c] = sum_e q^C[e] kv_b[h (Dn
+ * + Dv) + e][c], then pair (2i, 2i+1) of q^pe turned by angle i into dims
+ * Dc + i and Dc + Dr/2 + i (the cached rotary key's layout). */
+int orc_absorb_query(int32_t n, int32_t H, int32_t Dc, int32_t Dn, int32_t Dv, int32_t Dr,
+                     const double* qb, const double* kv_b, const double* rope_cos,
+                     const double* rope_sin, double* q);
+
+/* orc_absorb_output: o [n, H, Dc] latent contexts; out [n, H Dv] with
+ * out[t, h Dv + d] = sum_c o[t,h,c] kv_b[h (Dn + Dv) + Dn + d][c]. */
+int orc_absorb_output(int32_t n, int32_t H, int32_t Dc, int32_t Dn, int32_t Dv,
+                      const double* o, const double* kv_b, double* out);
+
+/* A Linear layer on bf16 operands (o_proj / wo): out [n, Dout] =
+ * x [n, Din] W^T with W [Dout, Din]; fp64 sums of exact products. */
+int orc_linear_bf16(int32_t n, int32_t Din, int32_t Dout, const uint16_t* x, const uint16_t* W,
+                    double* out);
+
 #ifdef __cplusplus
 }
 #endif

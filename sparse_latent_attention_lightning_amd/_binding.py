@@ -85,6 +85,15 @@ def lib() -> ctypes.CDLL:
         L.dsa_indexer_query.restype = ctypes.c_int
         L.dsa_indexer_query_workspace_bytes.argtypes = [i32, i32]
         L.dsa_indexer_query_workspace_bytes.restype = sz
+        L.dsa_absorb_prepare.argtypes = [i32, P, P, P]
+        L.dsa_absorb_query.argtypes = [i32, i32, P, P, P, P, i32, P, P]
+        L.dsa_absorb_output.argtypes = [i32, i32, P, P, i32, P, P]
+        L.dsa_output_projection.argtypes = [i32, i32, i32, P, P, i32, P, P, sz, P]
+        for f in ("dsa_absorb_prepare", "dsa_absorb_query", "dsa_absorb_output",
+                  "dsa_output_projection"):
+            getattr(L, f).restype = ctypes.c_int
+        L.dsa_output_projection_workspace_bytes.argtypes = [i32, i32, i32]
+        L.dsa_output_projection_workspace_bytes.restype = sz
         for f in ("dsa_indexer_scores", "dsa_indexer_scores_ragged", "dsa_topk",
                   "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged"):
             getattr(L, f).restype = ctypes.c_int
@@ -364,3 +373,74 @@ def dsa_indexer_query(cq, wq_b, q_dtype=torch.bfloat16, q_out: Optional[torch.Te
     _check(lib().dsa_indexer_query(N, Dq, _ptr(cq), _ptr(wq_b), _DT_OF[q_out.dtype], _ptr(q_out),
                                    _ptr(q_sf), _ptr(ws), ws.numel(), _stream(dev)))
     return q_out, (q_sf if fp8 else None)
+
+
+def dsa_absorb_prepare(kv_b, w_uk_t: Optional[torch.Tensor] = None):
+    """W_UK of kv_b_proj's weight kv_b [H * 256, 512] in the form
+    dsa_absorb_query reads: w_uk_t [H, 512, 128], w_uk_t[h, c, e] = kv_b[256 h + e, c]."""
+    R, C = kv_b.shape
+    if R % 256 or C != 512:
+        raise ValueError(f"kv_b has shape {tuple(kv_b.shape)}, expected [H * 256, 512]")
+    H = R // 256
+    dev = kv_b.device
+    _req(kv_b, "kv_b", (R, 512), (torch.bfloat16,), dev)
+    if w_uk_t is None:
+        w_uk_t = torch.empty((H, 512, 128), dtype=torch.bfloat16, device=dev)
+    _req(w_uk_t, "w_uk_t", (H, 512, 128), (torch.bfloat16,), dev)
+    _check(lib().dsa_absorb_prepare(H, _ptr(kv_b), _ptr(w_uk_t), _stream(dev)))
+    return w_uk_t
+
+
+def dsa_absorb_query(qb, w_uk_t, rope_cos, rope_sin, q_dtype=torch.bfloat16,
+                     q: Optional[torch.Tensor] = None):
+    """The sparse attention's query [N, H, 576] from q_b_proj's output qb
+    [N, H, 192]: the latent part q^C_h absorbed through W_UK,h, the rotary part
+    turned by the tokens' angles (rope_cos, rope_sin [N, 32])."""
+    N, H, _ = qb.shape
+    dev = qb.device
+    _req(qb, "qb", (N, H, 192), (torch.bfloat16,), dev)
+    _req(w_uk_t, "w_uk_t", (H, 512, 128), (torch.bfloat16,), dev)
+    _req(rope_cos, "rope_cos", (N, 32), (torch.float32,), dev)
+    _req(rope_sin, "rope_sin", (N, 32), (torch.float32,), dev)
+    if q is None:
+        q = torch.empty((N, H, 576), dtype=q_dtype, device=dev)
+    _req(q, "q", (N, H, 576), (torch.bfloat16, torch.float32), dev)
+    _check(lib().dsa_absorb_query(N, H, _ptr(qb), _ptr(w_uk_t), _ptr(rope_cos), _ptr(rope_sin),
+                                  _DT_OF[q.dtype], _ptr(q), _stream(dev)))
+    return q
+
+
+def dsa_absorb_output(o_lat, kv_b, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """Head outputs [N, H * 128] from the latent contexts o_lat [N, H, 512]
+    through each head's W_UV (the value half of kv_b [H * 256, 512])."""
+    N, H, _ = o_lat.shape
+    dev = o_lat.device
+    _req(o_lat, "o_lat", (N, H, 512), (torch.bfloat16,), dev)
+    _req(kv_b, "kv_b", (H * 256, 512), (torch.bfloat16,), dev)
+    if out is None:
+        out = torch.empty((N, H * 128), dtype=out_dtype, device=dev)
+    _req(out, "out", (N, H * 128), (torch.bfloat16, torch.float32), dev)
+    _check(lib().dsa_absorb_output(N, H, _ptr(o_lat), _ptr(kv_b), _DT_OF[out.dtype], _ptr(out),
+                                   _stream(dev)))
+    return out
+
+
+def dsa_output_projection(premix, wo, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None,
+                          ws: Optional[torch.Tensor] = None):
+    """out [N, Dout] = premix [N, Din] wo^T (wo [Dout, Din] in Linear layout)."""
+    N, Din = premix.shape
+    Dout = wo.shape[0]
+    dev = premix.device
+    _req(premix, "premix", (N, Din), (torch.bfloat16,), dev)
+    _req(wo, "wo", (Dout, Din), (torch.bfloat16,), dev)
+    if out is None:
+        out = torch.empty((N, Dout), dtype=out_dtype, device=dev)
+    _req(out, "out", (N, Dout), (torch.bfloat16, torch.float32), dev)
+    if ws is None:
+        nb = lib().dsa_output_projection_workspace_bytes(N, Din, Dout)
+        if nb == ctypes.c_size_t(-1).value:
+            raise DsaError(1, f"output projection: invalid sizes N={N}, Din={Din}, Dout={Dout}")
+        ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+    _check(lib().dsa_output_projection(N, Din, Dout, _ptr(premix), _ptr(wo), _DT_OF[out.dtype],
+                                       _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+    return out

@@ -42,12 +42,32 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4v_t
 // Operands of a batch of products p_b = x_b W_b^T (one per head for the
 // absorption products, a batch of 1 otherwise): token n of batch b is the row
 // x + b sx + n ldx (D contiguous elements), output j of batch b the row
-// W + b sw + j D.  Partial sums go to part[(b slices + slice) N ncols].
+// W + b sw + j D.  Partial sums go to part[(b slices + slice) N ncols]; a
+// product over one slice may instead write its result straight to
+// out + b so + n ldo + j (kernels instantiated with OUT = DSA_BF16 / DSA_F32).
 struct GemmOperands {
   const uint16_t* x;
   const uint16_t* W;
   int64_t ldx, sx, sw;
+  void* out;
+  int64_t ldo, so;
 };
+constexpr int kOutPartial = -1;
+
+// element (t, j) of batch b: a partial sum, or the finished value
+template <int OUT>
+__device__ __forceinline__ void gemm_store(const GemmOperands& g, float* part, int64_t pidx, int bt,
+                                           int t, int j, float v) {
+  if constexpr (OUT == kOutPartial) {
+    part[pidx] = v;
+  } else {
+    const int64_t o = bt * g.so + t * g.ldo + j;
+    if constexpr (OUT == DSA_BF16)
+      static_cast<uint16_t*>(g.out)[o] = f32_to_bf16(v);
+    else
+      static_cast<float*>(g.out)[o] = v;
+  }
+}
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -62,6 +82,7 @@ __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b,
 constexpr int kSkinnyChunks = 4;
 constexpr int kSkinnyWaves = 4;
 
+template <int OUT>
 __global__ void __launch_bounds__(kSkinnyWaves * 64)
 fill_gemm_skinny(int N, int D, int ncols, int slices, GemmOperands g, float* __restrict__ part) {
   __shared__ float red[kSkinnyWaves - 1][16][64];
@@ -100,14 +121,14 @@ fill_gemm_skinny(int N, int D, int ncols, int slices, GemmOperands g, float* __r
     for (int i = 0; i < 16; ++i) red[wave - 1][i][lane] = acc[i];
   __syncthreads();
   if (wave == 0) {
-    float* out = part + static_cast<int64_t>(blockIdx.z) * N * ncols;
+    const int64_t pbase = static_cast<int64_t>(blockIdx.z) * N * ncols;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float v = acc[i];
 #pragma unroll
       for (int u = 0; u < kSkinnyWaves - 1; ++u) v += red[u][i][lane];
       const int t = m0 + 8 * (i >> 2) + 4 * hl + (i & 3);
-      if (t < N) out[static_cast<int64_t>(t) * ncols + c0 + m] = v;
+      if (t < N) gemm_store<OUT>(g, part, pbase + static_cast<int64_t>(t) * ncols + c0 + m, bt, t, c0 + m, v);
     }
   }
 }
@@ -126,6 +147,7 @@ constexpr int kTCopies = kTTile / 1024 / 4;   // copies per wave per operand til
 
 __device__ __forceinline__ int tile_slot(int r, int piece) { return piece ^ (r & 7) ^ ((r >> 3) & 1); }
 
+template <int OUT>
 __global__ void __launch_bounds__(256, 1)
 fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kTStages][2][kTTile];
@@ -202,8 +224,10 @@ fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ par
       const int t = m0 + wm + 32 * ta + 8 * (i >> 2) + 4 * hl + (i & 3);
       if (t < N)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-          part[static_cast<int64_t>(t) * ncols + n0 + wn + 32 * tb + m] = acc[ta][tb][i];
+        for (int tb = 0; tb < 2; ++tb) {
+          const int j = n0 + wn + 32 * tb + m;
+          gemm_store<OUT>(g, part, static_cast<int64_t>(t) * ncols + j, blockIdx.z, t, j, acc[ta][tb][i]);
+        }
     }
 }
 
@@ -436,28 +460,227 @@ size_t projection_workspace_bytes(int N, int D, int ncols, int batch = 1) {
   return static_cast<size_t>(batch) * p.slices * N * ncols * sizeof(float);
 }
 
-// p = x W^T into fp32 partials (p.slices of them, [N, ncols] each)
-dsa_status_t launch_projection(const FillPlan& p, int N, int D, int ncols, int batch,
-                               const GemmOperands& g, float* part, const char* name,
-                               hipStream_t stream) {
+// p = x W^T into fp32 partials (p.slices of them, [N, ncols] each), or, for
+// out_dtype DSA_BF16 / DSA_F32 and one slice, straight into g.out
+template <int OUT>
+dsa_status_t launch_projection_as(const FillPlan& p, int N, int D, int ncols, int batch,
+                                  const GemmOperands& g, float* part, const char* name,
+                                  hipStream_t stream) {
   LaunchTimer timer;
   if (p.skinny)
-    hipExtLaunchKernelGGL(fill_gemm_skinny, dim3(ncols / 32, p.row_blocks, batch * p.slices),
+    hipExtLaunchKernelGGL(fill_gemm_skinny<OUT>, dim3(ncols / 32, p.row_blocks, batch * p.slices),
                           dim3(kSkinnyWaves * 64), 0, stream, timer.start(), timer.stop(), 0, N, D,
                           ncols, p.slices, g, part);
   else
-    hipExtLaunchKernelGGL(fill_gemm_tiled, dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
+    hipExtLaunchKernelGGL(fill_gemm_tiled<OUT>, dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
                           dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D, ncols, g,
                           part);
   return timer.done(name);
 }
 
+dsa_status_t launch_projection(const FillPlan& p, int N, int D, int ncols, int batch,
+                               const GemmOperands& g, float* part, const char* name,
+                               hipStream_t stream, int out_dtype = kOutPartial) {
+  if (out_dtype != kOutPartial && p.slices != 1)
+    return fail(DSA_ERR_INVALID_ARG, "%s: a direct output needs one slice, the plan has %d", name,
+                p.slices);
+  if (out_dtype == DSA_BF16)
+    return launch_projection_as<DSA_BF16>(p, N, D, ncols, batch, g, part, name, stream);
+  if (out_dtype == DSA_F32)
+    return launch_projection_as<DSA_F32>(p, N, D, ncols, batch, g, part, name, stream);
+  return launch_projection_as<kOutPartial>(p, N, D, ncols, batch, g, part, name, stream);
+}
+
 // one projection of a batch of 1: x [N, D], W [ncols, D]
 GemmOperands plain(const void* x, const void* W, int D) {
-  return GemmOperands{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), D, 0, 0};
+  return GemmOperands{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), D, 0, 0,
+                      nullptr, 0, 0};
+}
+
+// ---------------------------------------------------------------------------
+// Absorption products either side of the sparse attention (the step list of
+// the atlas.klimoza.dev DeepSeek-V3.2-Exp page: k^C = c^KV W_UK, v = c^KV
+// W_UV; kv_b_proj 512 -> 128 heads x (128 + 128) and o_proj 16384 -> 7168
+// in the nnterp module tree).  Absorbed, head h's query meets the latent
+// rows through q_lat,h = W_UK,h q^C_h and its output leaves through
+// W_UV,h o_lat,h, then wo.  kv_b_proj's Linear rows come per head: rows
+// 256 h .. 256 h + 127 are W_UK,h (key dims), the next 128 W_UV,h.
+constexpr int kLat = 512, kNope = 128, kVDim = 128, kQRope = 64;
+constexpr int kQbDim = kNope + kQRope;       // 192: q_b_proj's per-head output
+constexpr int kQDimOut = kLat + kQRope;      // 576: the sparse attention's query
+constexpr int kKvbRows = kNope + kVDim;      // 256 kv_b_proj rows per head
+
+// W_UK,h in reduction-contiguous form: wuk_t[h][c][e] = kv_b[256 h + e][c].
+// Workgroup = 64 latent columns of one head: the 128 x 64 block goes through
+// LDS (rows padded by 4 bytes), then out as 64 rows of 128 elements.
+__global__ void __launch_bounds__(256)
+uk_transpose(const uint16_t* __restrict__ kvb, uint16_t* __restrict__ wuk_t) {
+  __shared__ uint16_t tile[kNope][64 + 2];
+  const int h = blockIdx.y, c0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  const uint16_t* src = kvb + static_cast<int64_t>(h) * kKvbRows * kLat + c0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // 128 rows x 8 pieces of 8 elements
+    const int piece = tid + 256 * k;
+    const int e = piece >> 3, c = (piece & 7) * 8;
+    const u32x4v_t v = *reinterpret_cast<const u32x4v_t*>(src + static_cast<int64_t>(e) * kLat + c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      tile[e][c + 2 * u] = static_cast<uint16_t>(v[u]);
+      tile[e][c + 2 * u + 1] = static_cast<uint16_t>(v[u] >> 16);
+    }
+  }
+  __syncthreads();
+  uint16_t* dst = wuk_t + (static_cast<int64_t>(h) * kLat + c0) * kNope;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // 64 rows x 16 pieces
+    const int piece = tid + 256 * k;
+    const int c = piece >> 4, e = (piece & 15) * 8;
+    u32x4v_t v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = static_cast<uint32_t>(tile[e + 2 * u][c]) | (static_cast<uint32_t>(tile[e + 2 * u + 1][c]) << 16);
+    *reinterpret_cast<u32x4v_t*>(dst + static_cast<int64_t>(c) * kNope + e) = v;
+  }
+}
+
+// The rotary part of the absorbed query: pair (2i, 2i + 1) of the head's
+// q^pe turned by the token's angle i into dims 512 + i and 544 + i (the
+// layout of the cached rotary key, so that q and k share it).  One thread
+// per (token, head, pair).
+template <int ODT>
+__global__ void __launch_bounds__(256)
+q_rope(int N, int H, const uint16_t* __restrict__ qb, const float* __restrict__ rope_cos,
+       const float* __restrict__ rope_sin, void* __restrict__ q) {
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (id >= static_cast<int64_t>(N) * H * (kQRope / 2)) return;
+  const int i = static_cast<int>(id & 31);
+  const int64_t nh = id >> 5;
+  const int n = static_cast<int>(nh / H);
+  const uint32_t pr = *reinterpret_cast<const uint32_t*>(qb + nh * kQbDim + kNope + 2 * i);
+  const float a = bf16_to_f32(static_cast<uint16_t>(pr)), b = bf16_to_f32(static_cast<uint16_t>(pr >> 16));
+  const float c = rope_cos[static_cast<int64_t>(n) * 32 + i], sn = rope_sin[static_cast<int64_t>(n) * 32 + i];
+  const float r0 = a * c - b * sn, r1 = a * sn + b * c;
+  const int64_t o = nh * kQDimOut + kLat + i;
+  if constexpr (ODT == DSA_BF16) {
+    static_cast<uint16_t*>(q)[o] = f32_to_bf16(r0);
+    static_cast<uint16_t*>(q)[o + kQRope / 2] = f32_to_bf16(r1);
+  } else {
+    static_cast<float*>(q)[o] = r0;
+    static_cast<float*>(q)[o + kQRope / 2] = r1;
+  }
+}
+
+// out[t, j] = sum of the partials in slice order (deterministic); one thread
+// per 4 outputs
+template <int ODT>
+__global__ void __launch_bounds__(256)
+gemm_finish(int N, int ncols, int slices, const float* __restrict__ part, void* __restrict__ out) {
+  const int64_t id = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(N) * ncols;
+  if (4 * id >= total) return;
+  const float4* src = reinterpret_cast<const float4*>(part) + id;
+  const int64_t stride = total / 4;
+  float4 v = src[0];
+  for (int sl = 1; sl < slices; ++sl) {
+    const float4 u = src[sl * stride];
+    v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+  }
+  if constexpr (ODT == DSA_BF16) {
+    uint2 r;
+    r.x = f32x2_to_bf16x2(v.x, v.y);
+    r.y = f32x2_to_bf16x2(v.z, v.w);
+    reinterpret_cast<uint2*>(out)[id] = r;
+  } else {
+    reinterpret_cast<float4*>(out)[id] = v;
+  }
+}
+
+template <int ODT>
+dsa_status_t run_q_rope(int N, int H, const void* qb, const float* rope_cos, const float* rope_sin,
+                        void* q, hipStream_t stream) {
+  LaunchTimer timer;
+  const int64_t threads = static_cast<int64_t>(N) * H * (kQRope / 2);
+  hipExtLaunchKernelGGL(q_rope<ODT>, dim3(static_cast<uint32_t>((threads + 255) / 256)), dim3(256), 0,
+                        stream, timer.start(), timer.stop(), 0, N, H,
+                        static_cast<const uint16_t*>(qb), rope_cos, rope_sin, q);
+  return timer.done("q_rope");
 }
 
 }  // namespace
+
+dsa_status_t launch_absorb_prepare(int H, const void* kv_b, void* wuk_t, hipStream_t stream) {
+  if (H == 0) return DSA_OK;
+  LaunchTimer timer;
+  hipExtLaunchKernelGGL(uk_transpose, dim3(kLat / 64, H), dim3(256), 0, stream, timer.start(),
+                        timer.stop(), 0, static_cast<const uint16_t*>(kv_b),
+                        static_cast<uint16_t*>(wuk_t));
+  return timer.done("uk_transpose");
+}
+
+dsa_status_t launch_absorb_query(int N, int H, const void* qb, const void* wuk_t,
+                                 const float* rope_cos, const float* rope_sin, int q_dtype, void* q,
+                                 hipStream_t stream) {
+  if (N == 0 || H == 0) return DSA_OK;
+  // per head: [N, 128] x [128 -> 512], written into q[:, h, 0:512]
+  const GemmOperands g{static_cast<const uint16_t*>(qb), static_cast<const uint16_t*>(wuk_t),
+                       static_cast<int64_t>(H) * kQbDim, kQbDim,
+                       static_cast<int64_t>(kLat) * kNope, q,
+                       static_cast<int64_t>(H) * kQDimOut, kQDimOut};
+  const FillPlan p = fill_plan(N, kNope, kLat * H);
+  dsa_status_t st = launch_projection(p, N, kNope, kLat, H, g, nullptr, "absorb_q_gemm", stream, q_dtype);
+  if (st != DSA_OK) return st;
+  return q_dtype == DSA_BF16 ? run_q_rope<DSA_BF16>(N, H, qb, rope_cos, rope_sin, q, stream)
+                             : run_q_rope<DSA_F32>(N, H, qb, rope_cos, rope_sin, q, stream);
+}
+
+dsa_status_t launch_absorb_output(int N, int H, const void* o_lat, const void* kv_b, int out_dtype,
+                                  void* premix, hipStream_t stream) {
+  if (N == 0 || H == 0) return DSA_OK;
+  // per head: [N, 512] x [512 -> 128] with W_UV,h = kv_b rows 256 h + 128 ..
+  const GemmOperands g{static_cast<const uint16_t*>(o_lat),
+                       static_cast<const uint16_t*>(kv_b) + static_cast<int64_t>(kNope) * kLat,
+                       static_cast<int64_t>(H) * kLat, kLat,
+                       static_cast<int64_t>(kKvbRows) * kLat, premix,
+                       static_cast<int64_t>(H) * kVDim, kVDim};
+  const FillPlan p = fill_plan(N, kLat, kVDim * H);
+  return launch_projection(p, N, kLat, kVDim, H, g, nullptr, "absorb_o_gemm", stream, out_dtype);
+}
+
+size_t output_projection_workspace_bytes(int N, int Din, int Dout) {
+  const FillPlan p = fill_plan(N, Din, Dout);
+  return p.slices > 1 ? projection_workspace_bytes(N, Din, Dout) : 0;
+}
+
+dsa_status_t launch_output_projection(int N, int Din, int Dout, const void* premix, const void* wo,
+                                      int out_dtype, void* out, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+  if (N == 0) return DSA_OK;
+  const FillPlan p = fill_plan(N, Din, Dout);
+  GemmOperands g = plain(premix, wo, Din);
+  if (p.slices == 1) {
+    g.out = out;
+    g.ldo = Dout;
+    return launch_projection(p, N, Din, Dout, 1, g, nullptr, "wo_gemm", stream, out_dtype);
+  }
+  const size_t need = projection_workspace_bytes(N, Din, Dout);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "output projection: workspace of %zu bytes needed, %zu given",
+                need, ws_bytes);
+  float* part = static_cast<float*>(ws);
+  dsa_status_t st = launch_projection(p, N, Din, Dout, 1, g, part, "wo_gemm", stream);
+  if (st != DSA_OK) return st;
+  LaunchTimer timer;
+  const int64_t threads = static_cast<int64_t>(N) * Dout / 4;
+  const dim3 grid(static_cast<uint32_t>((threads + 255) / 256));
+  if (out_dtype == DSA_BF16)
+    hipExtLaunchKernelGGL(gemm_finish<DSA_BF16>, grid, dim3(256), 0, stream, timer.start(),
+                          timer.stop(), 0, N, Dout, p.slices, part, out);
+  else
+    hipExtLaunchKernelGGL(gemm_finish<DSA_F32>, grid, dim3(256), 0, stream, timer.start(),
+                          timer.stop(), 0, N, Dout, p.slices, part, out);
+  return timer.done("wo_finish");
+}
 
 size_t cache_fill_workspace_bytes(int N, int D) { return projection_workspace_bytes(N, D, kFillCols); }
 

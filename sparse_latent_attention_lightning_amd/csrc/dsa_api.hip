@@ -361,6 +361,70 @@ size_t dsa_indexer_query_workspace_bytes(int32_t N, int32_t Dq) {
   return N == 0 ? 0 : indexer_query_workspace_bytes(N, Dq);
 }
 
+dsa_status_t dsa_absorb_prepare(int32_t H, const void* kv_b, void* w_uk_t, void* stream) {
+  g_last_error[0] = '\0';
+  if (H < 0) return fail(DSA_ERR_INVALID_ARG, "absorb prepare: H = %d", H);
+  if (H == 0) return DSA_OK;
+  dsa_status_t st;
+  if ((st = need(kv_b, "kv_b")) || (st = need(w_uk_t, "w_uk_t"))) return st;
+  return launch_absorb_prepare(H, kv_b, w_uk_t, static_cast<hipStream_t>(stream));
+}
+
+dsa_status_t dsa_absorb_query(int32_t N, int32_t H, const void* qb, const void* w_uk_t,
+                              const float* rope_cos, const float* rope_sin, int32_t q_dtype,
+                              void* q, void* stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || H < 0) return fail(DSA_ERR_INVALID_ARG, "absorb query: N = %d, H = %d", N, H);
+  if (q_dtype != DSA_BF16 && q_dtype != DSA_F32)
+    return fail(DSA_ERR_UNSUPPORTED, "absorb query: q_dtype %d", q_dtype);
+  if (N == 0 || H == 0) return DSA_OK;
+  dsa_status_t st;
+  if ((st = need(qb, "qb")) || (st = need(w_uk_t, "w_uk_t")) || (st = need(rope_cos, "rope_cos")) ||
+      (st = need(rope_sin, "rope_sin")) || (st = need(q, "q")))
+    return st;
+  return launch_absorb_query(N, H, qb, w_uk_t, rope_cos, rope_sin, q_dtype, q,
+                             static_cast<hipStream_t>(stream));
+}
+
+dsa_status_t dsa_absorb_output(int32_t N, int32_t H, const void* o_lat, const void* kv_b,
+                               int32_t out_dtype, void* out, void* stream) {
+  g_last_error[0] = '\0';
+  if (N < 0 || H < 0) return fail(DSA_ERR_INVALID_ARG, "absorb output: N = %d, H = %d", N, H);
+  if (out_dtype != DSA_BF16 && out_dtype != DSA_F32)
+    return fail(DSA_ERR_UNSUPPORTED, "absorb output: out_dtype %d", out_dtype);
+  if (N == 0 || H == 0) return DSA_OK;
+  dsa_status_t st;
+  if ((st = need(o_lat, "o_lat")) || (st = need(kv_b, "kv_b")) || (st = need(out, "out"))) return st;
+  return launch_absorb_output(N, H, o_lat, kv_b, out_dtype, out, static_cast<hipStream_t>(stream));
+}
+
+static bool output_projection_dims_ok(int32_t N, int32_t Din, int32_t Dout) {
+  return N >= 0 && Din > 0 && Din % 64 == 0 && Dout > 0 && Dout % 128 == 0;
+}
+
+dsa_status_t dsa_output_projection(int32_t N, int32_t Din, int32_t Dout, const void* premix,
+                                   const void* wo, int32_t out_dtype, void* out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  if (!output_projection_dims_ok(N, Din, Dout))
+    return fail(DSA_ERR_INVALID_ARG,
+                "output projection: N = %d, Din = %d, Dout = %d (Din a positive multiple of 64, "
+                "Dout of 128)", N, Din, Dout);
+  if (out_dtype != DSA_BF16 && out_dtype != DSA_F32)
+    return fail(DSA_ERR_UNSUPPORTED, "output projection: out_dtype %d", out_dtype);
+  if (N == 0) return DSA_OK;
+  dsa_status_t st;
+  if ((st = need(premix, "premix")) || (st = need(wo, "wo")) || (st = need(out, "out"))) return st;
+  if (ws != nullptr && !aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  return launch_output_projection(N, Din, Dout, premix, wo, out_dtype, out, ws, ws_bytes,
+                                  static_cast<hipStream_t>(stream));
+}
+
+size_t dsa_output_projection_workspace_bytes(int32_t N, int32_t Din, int32_t Dout) {
+  if (!output_projection_dims_ok(N, Din, Dout)) return static_cast<size_t>(-1);
+  return N == 0 ? 0 : output_projection_workspace_bytes(N, Din, Dout);
+}
+
 size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry) {
   if (check_shape(shape) != DSA_OK) return static_cast<size_t>(-1);
   switch (entry) {

@@ -55,6 +55,17 @@ dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx
 // ---- cache fill and indexer inputs ---------------------------------------
 size_t cache_fill_workspace_bytes(int N, int D);
 size_t indexer_query_workspace_bytes(int N, int Dq);
+// ---- absorption products ---------------------------------------------------
+dsa_status_t launch_absorb_prepare(int H, const void* kv_b, void* wuk_t, hipStream_t stream);
+dsa_status_t launch_absorb_query(int N, int H, const void* qb, const void* wuk_t,
+                                 const float* rope_cos, const float* rope_sin, int q_dtype, void* q,
+                                 hipStream_t stream);
+dsa_status_t launch_absorb_output(int N, int H, const void* o_lat, const void* kv_b, int out_dtype,
+                                  void* premix, hipStream_t stream);
+size_t output_projection_workspace_bytes(int N, int Din, int Dout);
+dsa_status_t launch_output_projection(int N, int Din, int Dout, const void* premix, const void* wo,
+                                      int out_dtype, void* out, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
 dsa_status_t launch_indexer_query(int N, int Dq, const void* cq, const void* wq_b, int q_dtype,
                                   void* q_out, uint8_t* q_sf, void* ws, size_t ws_bytes,
                                   hipStream_t stream);

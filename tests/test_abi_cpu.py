@@ -149,3 +149,25 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(b, "_lib", None)
     with pytest.raises(ImportError):
         b.lib()
+
+
+def test_absorption_entry_points_check_arguments_on_host(dsa):
+    L = dsa.lib()
+    P = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert L.dsa_absorb_prepare(-1, P, P, None) == 1
+    assert L.dsa_absorb_prepare(4, None, P, None) == 1
+    assert L.dsa_absorb_prepare(0, None, None, None) == 0          # nothing to do
+    assert L.dsa_absorb_query(32, 128, P, P, P, P, 2, P, None) == 2  # no E4M3 query
+    assert L.dsa_absorb_query(-1, 128, P, P, P, P, 1, P, None) == 1
+    assert L.dsa_absorb_query(32, 128, P, P, None, P, 1, P, None) == 1
+    assert L.dsa_absorb_query(0, 128, None, None, None, None, 1, None, None) == 0
+    assert L.dsa_absorb_output(32, 128, P, P, 2, P, None) == 2
+    assert L.dsa_absorb_output(32, 128, P, None, 1, P, None) == 1
+    assert L.dsa_output_projection(32, 100, 7168, P, P, 1, P, None, 0, None) == 1  # Din % 64
+    assert "Din" in L.dsa_last_error().decode()
+    assert L.dsa_output_projection(32, 16384, 7000, P, P, 1, P, None, 0, None) == 1  # Dout % 128
+    assert L.dsa_output_projection(32, 16384, 7168, P, P, 2, P, None, 0, None) == 2
+    # few tokens split the 16384-wide reduction into 16 slices of fp32 partials
+    assert L.dsa_output_projection_workspace_bytes(32, 16384, 7168) == 16 * 32 * 7168 * 4
+    assert L.dsa_output_projection_workspace_bytes(16384, 16384, 7168) == 0  # tiled: none
+    assert L.dsa_output_projection_workspace_bytes(32, 100, 7168) == ctypes.c_size_t(-1).value

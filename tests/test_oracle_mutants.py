@@ -51,6 +51,15 @@ MUTANTS = {
     "softmax_unnormalised": ("double p = keys[j] >= 0 ? exp(logit[j] - m) / l : 0.0;",
                              "double p = keys[j] >= 0 ? exp(logit[j] - m) : 0.0;"),
     "lse_missing_max": ("*lse = m + log(l);", "*lse = log(l);"),
+    # absorption either side of the attention
+    "absorb_head_stride": ("acc += qc[e] * kv_b[((int64_t)h * head_rows + e) * Dc + c];",
+                           "acc += qc[e] * kv_b[((int64_t)h * Dn + e) * Dc + c];"),
+    "absorb_output_key_half": ("kv_b + ((int64_t)h * head_rows + Dn + d) * Dc;",
+                               "kv_b + ((int64_t)h * head_rows + d) * Dc;"),
+    "absorb_query_rope_sign": ("qo[Dc + i] = a * cs - b * sn;", "qo[Dc + i] = a * cs + b * sn;"),
+    "absorb_query_rope_interleaved": ("qo[Dc + i] = a * cs - b * sn;\n        qo[Dc + Dr / 2 + i] = a * sn + b * cs;",
+                                      "qo[Dc + 2 * i] = a * cs - b * sn;\n        qo[Dc + 2 * i + 1] = a * sn + b * cs;"),
+    "linear_transposed": ("bf16_value(W[(int64_t)j * Din + i]);", "bf16_value(W[(int64_t)i * Dout + j]);"),
     "invalid_index_as_key0": ("keys[j] = (s >= 0 && s < S) ? s : -1;", "keys[j] = (s >= 0 && s < S) ? s : 0;"),
 }
 

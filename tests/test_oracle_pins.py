@@ -604,3 +604,90 @@ def test_indexer_query_is_the_matmul(oracle_lib):
     ref = g.bf16_bits_to_f32(cq).astype(np.float64) @ g.bf16_bits_to_f32(wq).astype(np.float64).T
     np.testing.assert_allclose(q, ref, rtol=1e-12, atol=1e-12)
     assert q.reshape(3, 2, 128)[1, 1, 5] == q[1, 128 + 5]
+
+
+def _kvb_from_explicit(W_UK, W_UV, H, Dn, Dv):
+    """kv_b_proj's Linear weight [H (Dn + Dv), Dc] holding the step list's
+    W_UK [Dc, H Dn] and W_UV [Dc, H Dv]: per head its Dn key rows, then its Dv
+    value rows (heads x (key dims + value dims), the nnterp module tree)."""
+    Dc = W_UK.shape[0]
+    kvb = np.empty((H, Dn + Dv, Dc))
+    kvb[:, :Dn] = W_UK.T.reshape(H, Dn, Dc)
+    kvb[:, Dn:] = W_UV.T.reshape(H, Dv, Dc)
+    return kvb.reshape(H * (Dn + Dv), Dc)
+
+
+def test_absorption_routines_equal_explicit_form(oracle_lib):
+    """absorb_query -> sparse attention -> absorb_output equals the explicit
+    form with per-head keys c W_UK and values c W_UV (the oracle's explicit
+    routine).  Inputs are multiples of 1/4 in [-3/4, 3/4], so the absorbed
+    query and the fp32 storage the attention reads are exact: 1e-12."""
+    rng = np.random.default_rng(30)
+    H, Dc, Dn, Dv, Dr, S = 3, 16, 8, 6, 4, 11
+    sm = 0.31
+    q4 = lambda *shape: rng.integers(-3, 4, shape) / 4.0
+    qb = q4(1, H, Dn + Dr)
+    W_UK, W_UV = q4(Dc, H * Dn), q4(Dc, H * Dv)
+    kvb = _kvb_from_explicit(W_UK, W_UV, H, Dn, Dv)
+    kv = q4(S, Dc + Dr)
+    cos0, sin0 = np.ones((1, Dr // 2)), np.zeros((1, Dr // 2))
+    q = oracle.absorb_query(qb, kvb, cos0, sin0, Dn=Dn)
+    # latent part: numpy's product of the head's W_UK block with q^C
+    for h in range(H):
+        np.testing.assert_allclose(q[0, h, :Dc], W_UK[:, h * Dn:(h + 1) * Dn] @ qb[0, h, :Dn],
+                                   rtol=1e-12, atol=1e-12)
+    # angle 0: the rotary part is q^pe's even dims, then its odd ones
+    np.testing.assert_array_equal(q[0, :, Dc:Dc + Dr // 2], qb[0, :, Dn::2])
+    np.testing.assert_array_equal(q[0, :, Dc + Dr // 2:], qb[0, :, Dn + 1::2])
+    cfg = _cfg(B=1, T=1, S=S, H=H, Dc=Dc, Dr=Dr, K=S, sm_scale=sm)
+    o_lat, _ = oracle.sparse_mla(cfg, [0], q.astype(np.float32), kv[None].astype(np.float32),
+                                 np.arange(S, dtype=np.int32)[None])
+    out = oracle.absorb_output(o_lat, kvb, Dn=Dn)
+    explicit = oracle.explicit_mla(qb[0, :, :Dn], q[0, :, Dc:], kv[:, :Dc], kv[:, Dc:], W_UK, W_UV,
+                                   np.float64(np.float32(sm)))
+    np.testing.assert_allclose(out.reshape(H, Dv), explicit, rtol=1e-12, atol=1e-12)
+
+
+def test_absorbed_query_rotation_matches_cached_key(oracle_lib):
+    """The query's rotary part and the cached key's (cache_fill) turn alike:
+    their dot product depends on the two angles' difference only, so
+    q(a) . k(b) = q(a - b) . k(0) and q(a) . k(a) = q(0) . k(0)."""
+    rng = np.random.default_rng(31)
+    n, H = 4, 2
+    # keys: a projection that passes x straight into the rotary block
+    x = g.f32_to_bf16_bits(rng.standard_normal((n, 64)).astype(np.float32))
+    W = np.zeros((768, 64), np.float32)
+    W[512:576] = np.eye(64)
+    W = g.f32_to_bf16_bits(W)
+    a = rng.uniform(-math.pi, math.pi, (n, 32))
+    b = rng.uniform(-math.pi, math.pi, (n, 32))
+    f = lambda ang: (np.cos(ang), np.sin(ang))
+
+    def key(ang):
+        c, s = f(ang)
+        kv, _, _ = oracle.cache_fill(x, W, np.ones(512), np.ones(128), np.zeros(128),
+                                     c.astype(np.float32), s.astype(np.float32))
+        return kv[:, 512:]
+
+    qb = rng.standard_normal((n, H, 8 + 64))
+    kvb = rng.standard_normal((H * 16, 4))
+
+    def query(ang):
+        c, s = f(ang)
+        return oracle.absorb_query(qb, kvb, c, s, Dn=8)[:, :, 4:]
+
+    dot = lambda q, k: np.einsum("nhd,nd->nh", q, k)
+    np.testing.assert_allclose(dot(query(a), key(b)), dot(query(a - b), key(np.zeros_like(b))),
+                               rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(dot(query(a), key(a)), dot(query(0 * a), key(0 * a)),
+                               rtol=1e-6, atol=1e-6)
+
+
+def test_linear_bf16_is_the_matmul(oracle_lib):
+    """wo: numpy's matmul x W^T on the exact bf16 values (a non-square W)."""
+    rng = np.random.default_rng(32)
+    x = g.f32_to_bf16_bits(rng.standard_normal((3, 96)).astype(np.float32))
+    W = g.f32_to_bf16_bits(rng.standard_normal((40, 96)).astype(np.float32))
+    out = oracle.linear_bf16(x, W)
+    ref = g.bf16_bits_to_f32(x).astype(np.float64) @ g.bf16_bits_to_f32(W).astype(np.float64).T
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
