@@ -329,6 +329,122 @@ def bench_cache_fill(args):
     print(json.dumps(result))
 
 
+ABSORB_WORKLOADS = {"absorb_decode": 32, "absorb_prefill": 16384,
+                    "wo_decode": 32, "wo_prefill": 16384}
+HEADS, WO_IN, WO_OUT = 128, 16384, 7168
+
+
+def bench_absorb(args):
+    """The absorption products either side of the sparse attention: per-head
+    W_UK (query) and W_UV (output) products of the 128 heads (absorb_*), or
+    the output projection wo 16384 -> 7168 (wo_*), over N tokens."""
+    import numpy as np
+    import torch
+
+    import sparse_latent_attention_lightning_amd as dsa
+
+    N = ABSORB_WORKLOADS[args.workload]
+    wo = args.workload.startswith("wo")
+    decode = N <= 256
+    H = HEADS
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    rnd = lambda shape, sc=1.0: (torch.randn(shape, generator=gen, device=dev) * sc).to(torch.bfloat16)
+    w_bytes = WO_OUT * WO_IN * 2 if wo else H * 256 * 512 * 2 + H * 512 * 128 * 2
+    reps = args.replicas or (max(2, -(-600_000_000 // w_bytes)) if decode else 1)
+    if wo:
+        xs = [rnd((N, WO_IN))]
+        Ws = [rnd((WO_OUT, WO_IN), WO_IN ** -0.5) for _ in range(reps)]
+        out = torch.empty((N, WO_OUT), dtype=torch.bfloat16, device=dev)
+        nb = dsa.lib().dsa_output_projection_workspace_bytes(N, WO_IN, WO_OUT)
+        ws = torch.empty(max(1, nb), dtype=torch.uint8, device=dev)
+    else:
+        qb = rnd((N, H, 192))
+        o_lat = rnd((N, H, 512), 0.1)
+        kvbs = [rnd((H * 256, 512), 512 ** -0.5) for _ in range(reps)]
+        wuks = [dsa.dsa_absorb_prepare(k) for k in kvbs]
+        ang = torch.rand((N, 32), generator=gen, device=dev) * 6.283
+        cos, sin = torch.cos(ang), torch.sin(ang)
+        q = torch.empty((N, H, 576), dtype=torch.bfloat16, device=dev)
+        premix = torch.empty((N, H * 128), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        if wo:
+            dsa.dsa_output_projection(xs[0], Ws[i % reps], out=out, ws=ws)
+        else:
+            dsa.dsa_absorb_query(qb, wuks[i % reps], cos, sin, q=q)
+            dsa.dsa_absorb_output(o_lat, kvbs[i % reps], out=premix)
+
+    def timed(n, warm):
+        for i in range(warm):
+            step(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            step(warm + i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(args.steps, args.warmup)
+    dsa.dsa_timing_begin()
+    timed(args.steps, 0)
+    kt = dsa.dsa_timing_end()
+    for k, r in kt.items():
+        print(f"[bench] {k}: {r['avg_us']:.2f} us per launch ({r['launches']} launches)",
+              file=sys.stderr, flush=True)
+    # algorithmic per launch of the dominant product: its weights once, its
+    # inputs once, its outputs written once
+    if wo:
+        gemm = "wo_gemm"
+        nbytes = WO_OUT * WO_IN * 2 + N * WO_IN * 2 + N * WO_OUT * 2
+        nflops = 2.0 * N * WO_IN * WO_OUT
+    else:
+        gemm = "absorb_q_gemm"   # W_UK [128, 512] per head; q^C in, the 512 latent dims out
+        nbytes = H * 128 * 512 * 2 + N * H * 128 * 2 + N * H * 512 * 2
+        nflops = 2.0 * N * H * 128 * 512
+    t_gemm = kt[gemm]["avg_us"] / 1e6
+    roof = roofline(decode, nbytes if decode else 0, nflops, t_gemm)
+    roof["kernel"] = gemm
+    roof["launch_us"] = round(t_gemm * 1e6, 2)
+    roof["algorithmic_per_launch"] = round(nbytes if decode else nflops)
+    roof["traffic"] = None
+    result = {
+        "metric": ("output-projection" if wo else "absorption (query + output)") + " tokens/sec",
+        "value": round(N / (ms / 1e3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": ({"workload": args.workload, "tokens": N, "in": WO_IN, "out": WO_OUT} if wo else
+                   {"workload": args.workload, "tokens": N, "heads": H, "latent": 512,
+                    "key_dims": 128, "value_dims": 128}),
+        "kernel_us": {k: round(r["avg_us"], 2) for k, r in kt.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        n_cpu = min(N, 8 if wo else 32)
+        bits = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        if wo:
+            oracle.linear_bf16(bits(xs[0][:n_cpu]), bits(Ws[0]), threads=threads)
+        else:
+            kv = kvbs[0].float().cpu().numpy()
+            oracle.absorb_query(qb[:n_cpu].float().cpu().numpy(), kv, cos[:n_cpu].double().cpu().numpy(),
+                                sin[:n_cpu].double().cpu().numpy(), threads=threads)
+            oracle.absorb_output(o_lat[:n_cpu].float().cpu().numpy(), kv, threads=threads)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(n_cpu / dt, 2), "unit": "tokens/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"{n_cpu} tokens of the workload, fp64, {dt:.1f} s wall"}
+    print(json.dumps(result))
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -340,6 +456,9 @@ def main():
         sys.exit(2)
     if args.workload in FILL_WORKLOADS:
         bench_cache_fill(args)
+        return
+    if args.workload in ABSORB_WORKLOADS:
+        bench_absorb(args)
         return
     import torch
 
