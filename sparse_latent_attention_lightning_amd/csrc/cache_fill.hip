@@ -141,25 +141,41 @@ fill_gemm_skinny(int N, int D, int ncols, int slices, GemmOperands g, float* __r
 // kTStages - 1 chunks ahead.  A row's 16-byte piece c sits in slot
 // c ^ (r & 7) ^ ((r >> 3) & 1), so that the operand reads (32 rows, one piece
 // each) touch every bank once per cycle.
-constexpr int kTM = 128, kTN = 128, kTStages = 4;
+constexpr int kTM = 128, kTN = 128;
+constexpr int kXcds = 8;  // accelerator dies of the MI355X, one L2 each
 constexpr int kTTile = kTM * kGemmKStep * 2;  // 16 KB per operand tile
 constexpr int kTCopies = kTTile / 1024 / 4;   // copies per wave per operand tile
 
 __device__ __forceinline__ int tile_slot(int r, int piece) { return piece ^ (r & 7) ^ ((r >> 3) & 1); }
 
-template <int OUT>
-__global__ void __launch_bounds__(256, 1)
+// STAGES = 4 (the ring above, one workgroup per CU) or 2 for a reduction of
+// at most 4 chunks (half the LDS: two workgroups per CU hide each other's
+// load latency; each chunk then waits for its own copies)
+template <int OUT, int STAGES>
+__global__ void __launch_bounds__(256, 4 / STAGES)
 fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ part) {
+  static_assert(STAGES == 4 || STAGES == 2, "ring depth");
+  constexpr int kTStages = STAGES;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kTStages][2][kTTile];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane >> 5, m = lane & 31;
-  const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
+  // XCD-aware order: workgroup i is dispatched to XCD i % 8, each XCD with
+  // its own L2; give every XCD a contiguous run of tiles (output tile fastest)
+  // so that the tiles sharing a token block, and a batch's weights, meet in
+  // one L2 instead of being fetched by every XCD
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int total = gx * gy * gridDim.z;
+  const int lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int per_xcd = total / kXcds;
+  const int w_id = lin < per_xcd * kXcds ? (lin % kXcds) * per_xcd + lin / kXcds : lin;
+  const int bx = w_id % gx, by = (w_id / gx) % gy, bz = w_id / (gx * gy);
+  const int m0 = by * kTM, n0 = bx * kTN;
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   const int nk = D / kGemmKStep;
-  const uint16_t* x = g.x + blockIdx.z * g.sx;
-  const uint16_t* W = g.W + blockIdx.z * g.sw;
-  part += static_cast<int64_t>(blockIdx.z) * N * ncols;
+  const uint16_t* x = g.x + bz * g.sx;
+  const uint16_t* W = g.W + bz * g.sw;
+  part += static_cast<int64_t>(bz) * N * ncols;
   // copy j of an operand tile covers its rows 8j .. 8j+7; lane l writes slot
   // l & 7 of row 8j + l / 8 (rows past the last token load the last token)
   auto issue = [&](int c) {
@@ -188,7 +204,7 @@ fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ par
     // chunk c has landed: the copies issued after it are those of the next
     // min(kTStages - 2, nk - 1 - c) chunks, 2 kTCopies each
     const int later = min(kTStages - 2, nk - 1 - c);
-    static_assert(kTStages == 4 && kTCopies == 4, "vmcnt immediates");
+    static_assert(kTCopies == 4, "vmcnt immediates");
     if (later >= 2)
       asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else if (later == 1)
@@ -226,7 +242,7 @@ fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ par
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           const int j = n0 + wn + 32 * tb + m;
-          gemm_store<OUT>(g, part, static_cast<int64_t>(t) * ncols + j, blockIdx.z, t, j, acc[ta][tb][i]);
+          gemm_store<OUT>(g, part, static_cast<int64_t>(t) * ncols + j, bz, t, j, acc[ta][tb][i]);
         }
     }
 }
@@ -471,8 +487,12 @@ dsa_status_t launch_projection_as(const FillPlan& p, int N, int D, int ncols, in
     hipExtLaunchKernelGGL(fill_gemm_skinny<OUT>, dim3(ncols / 32, p.row_blocks, batch * p.slices),
                           dim3(kSkinnyWaves * 64), 0, stream, timer.start(), timer.stop(), 0, N, D,
                           ncols, p.slices, g, part);
+  else if (D <= 4 * kGemmKStep)
+    hipExtLaunchKernelGGL((fill_gemm_tiled<OUT, 2>), dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
+                          dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D, ncols, g,
+                          part);
   else
-    hipExtLaunchKernelGGL(fill_gemm_tiled<OUT>, dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
+    hipExtLaunchKernelGGL((fill_gemm_tiled<OUT, 4>), dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
                           dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D, ncols, g,
                           part);
   return timer.done(name);
