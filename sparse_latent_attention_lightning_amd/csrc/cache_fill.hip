@@ -78,14 +78,24 @@ __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b,
 // the hidden dimension; its 4 waves take consecutive runs of kSkinnyChunks
 // 64-wide chunks each, issue every load of their run before the first MFMA,
 // and add their accumulators through LDS, so one partial per workgroup
-// reaches memory.  grid: (24 output tiles, token blocks, slices).
+// reaches memory.  grid: (output tiles of 32, token blocks, batch x slices).
+//
+// Loads read whole rows: load s of a chunk gives lane l the 16-byte piece
+// l & 7 of row 8 s + l / 8 (8 rows x 128 contiguous bytes per instruction;
+// a lane per row of the MFMA layout would touch 32 rows, four times the
+// cache lines per instruction, and runs at about half the rate).  Each
+// chunk then goes through the wave's own 8 KB of LDS into the MFMA layout
+// (row r's piece c in slot tile_slot(r, c): conflict-free both ways).
 constexpr int kSkinnyChunks = 4;
 constexpr int kSkinnyWaves = 4;
+
+__device__ __forceinline__ int tile_slot(int r, int piece) { return piece ^ (r & 7) ^ ((r >> 3) & 1); }
 
 template <int OUT>
 __global__ void __launch_bounds__(kSkinnyWaves * 64)
 fill_gemm_skinny(int N, int D, int ncols, int slices, GemmOperands g, float* __restrict__ part) {
   __shared__ float red[kSkinnyWaves - 1][16][64];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kSkinnyWaves][2][kGemmRows * 128];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int hl = lane >> 5, m = lane & 31;
@@ -94,28 +104,46 @@ fill_gemm_skinny(int N, int D, int ncols, int slices, GemmOperands g, float* __r
   const int nchunks = D / kGemmKStep;
   const int bt = blockIdx.z / slices, sl = blockIdx.z - bt * slices;
   const int ch0 = (sl * kSkinnyWaves + wave) * kSkinnyChunks;
-  const int row = min(m0 + m, N - 1);
-  const u32x4v_t* ap = reinterpret_cast<const u32x4v_t*>(g.x + bt * g.sx + row * g.ldx + 32 * hl);
-  const u32x4v_t* bp = reinterpret_cast<const u32x4v_t*>(g.W + bt * g.sw + static_cast<int64_t>(c0 + m) * D + 32 * hl);
+  const int lr = lane >> 3, lp = lane & 7;  // this lane's row (within 8) and piece
   u32x4v_t a[kSkinnyChunks][4], b[kSkinnyChunks][4];
 #pragma unroll
-  for (int j = 0; j < kSkinnyChunks; ++j) {
-    const int ch = min(ch0 + j, nchunks - 1);  // past the end: a valid chunk, not used
+  for (int s = 0; s < 4; ++s) {
+    const u32x4v_t* ap = reinterpret_cast<const u32x4v_t*>(
+        g.x + bt * g.sx + static_cast<int64_t>(min(m0 + 8 * s + lr, N - 1)) * g.ldx + 8 * lp);
+    const u32x4v_t* bp = reinterpret_cast<const u32x4v_t*>(
+        g.W + bt * g.sw + static_cast<int64_t>(c0 + 8 * s + lr) * D + 8 * lp);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      a[j][s] = ap[ch * (kGemmKStep / 8) + s];
-      b[j][s] = __builtin_nontemporal_load(bp + ch * (kGemmKStep / 8) + s);
+    for (int j = 0; j < kSkinnyChunks; ++j) {
+      const int ch = min(ch0 + j, nchunks - 1);  // past the end: a valid chunk, not used
+      a[j][s] = ap[ch * (kGemmKStep / 8)];
+      b[j][s] = __builtin_nontemporal_load(bp + ch * (kGemmKStep / 8));
     }
   }
   f32x16_t acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  uint8_t* xs = stage[wave][0];
+  uint8_t* ws = stage[wave][1];
 #pragma unroll
-  for (int j = 0; j < kSkinnyChunks; ++j)
-    if (ch0 + j < nchunks)
+  for (int j = 0; j < kSkinnyChunks; ++j) {
+    if (ch0 + j < nchunks) {  // wave-uniform
+      // the wave's LDS is its own and the LDS runs one wave's operations in
+      // order: the previous chunk's reads are done before these writes land
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = mfma32(__builtin_bit_cast(bf16x8_t, a[j][s]), __builtin_bit_cast(bf16x8_t, b[j][s]), acc);
+      for (int s = 0; s < 4; ++s) {
+        const int r = 8 * s + lr;
+        *reinterpret_cast<u32x4v_t*>(xs + r * 128 + 16 * tile_slot(r, lp)) = a[j][s];
+        *reinterpret_cast<u32x4v_t*>(ws + r * 128 + 16 * tile_slot(r, lp)) = b[j][s];
+      }
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int piece = 2 * s4 + hl;
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xs + m * 128 + 16 * tile_slot(m, piece));
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(ws + m * 128 + 16 * tile_slot(m, piece));
+        acc = mfma32(av, bv, acc);
+      }
+    }
+  }
   if (wave > 0)
 #pragma unroll
     for (int i = 0; i < 16; ++i) red[wave - 1][i][lane] = acc[i];
@@ -145,8 +173,6 @@ constexpr int kTM = 128, kTN = 128;
 constexpr int kXcds = 8;  // accelerator dies of the MI355X, one L2 each
 constexpr int kTTile = kTM * kGemmKStep * 2;  // 16 KB per operand tile
 constexpr int kTCopies = kTTile / 1024 / 4;   // copies per wave per operand tile
-
-__device__ __forceinline__ int tile_slot(int r, int piece) { return piece ^ (r & 7) ^ ((r >> 3) & 1); }
 
 // STAGES = 4 (the ring above, one workgroup per CU) or 2 for a reduction of
 // at most 4 chunks (half the LDS: two workgroups per CU hide each other's
