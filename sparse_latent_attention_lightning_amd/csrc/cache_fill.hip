@@ -51,6 +51,7 @@ struct GemmOperands {
   int64_t ldx, sx, sw;
   void* out;
   int64_t ldo, so;
+  uint8_t* out_sf;  // E4M3 output: one ue8m0 scale byte per (row, 128-output tile)
 };
 constexpr int kOutPartial = -1;
 
@@ -67,6 +68,68 @@ __device__ __forceinline__ void gemm_store(const GemmOperands& g, float* part, i
     else
       static_cast<float*>(g.out)[o] = v;
   }
+}
+
+// fp32 -> OCP E4M3FN code, round to nearest with ties to the even code;
+// |v| <= 448 (the caller's scale guarantees it; larger saturates to 448)
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fminf(fabsf(v), 448.0f);
+  if (a < 0.015625f) {  // below 2^-6: subnormal steps of 2^-9, rint ties to even
+    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));  // 8 = smallest normal
+  }
+  // keep 3 mantissa bits: add half an ulp of the 3-bit mantissa (minus one
+  // when the kept lsb is 0, so exact halves go to the even code), then cut
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+  const int e = static_cast<int>(r >> 23) - 127;  // -6 .. 8
+  uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | ((r >> 20) & 7u);
+  if (code > 0x7Eu) code = 0x7Eu;  // 448 is the largest finite code
+  return sign | code;
+}
+
+// e of the ue8m0 scale 2^e of a block with largest magnitude amax: the
+// smallest integer with 448 2^e >= amax (0 for an all-zero block).  With
+// amax = M 2^E (1 <= M < 2) and 448 = 1.75 2^8: e = E - 8 when M <= 1.75,
+// else E - 7; subnormal maxima take the search.
+__device__ __forceinline__ int ue8m0_exponent(float amax) {
+  if (!(amax > 0.f)) return 0;
+  const uint32_t u = __float_as_uint(amax);
+  const int E = static_cast<int>(u >> 23) - 127;
+  if (E > -127) return E - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  int e = ilogbf(amax) - 8;
+  while (e > -127 && ldexpf(448.0f, e - 1) >= amax) --e;
+  while (e < 127 && ldexpf(448.0f, e) < amax) ++e;
+  return e;
+}
+
+// max over the wave's 64 lanes on lane moves (no LDS): xor 1 and 2 within
+// quads, the half-row and row mirrors (8 and 16 lanes), then the 16- and
+// 32-lane swaps of gfx950 (row r of the first operand trades places with row
+// r - 1 of the second: the two results hold both rows' maxima)
+__device__ __forceinline__ float wave_max_lanes(float v) {
+  auto dpp = [](float x, int ctrl) -> float {
+    switch (ctrl) {  // the control must be a constant
+      case 0xB1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+      case 0x4E: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+      case 0x141: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+      default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    }
+  };
+  v = fmaxf(v, dpp(v, 0xB1));   // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp(v, 0x4E));   // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp(v, 0x141));  // row_half_mirror
+  v = fmaxf(v, dpp(v, 0x140));  // row_mirror
+  const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+  const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
+}
+
+// v / 2^e (a multiplication by an exact power of two where 2^-e is a normal float)
+__device__ __forceinline__ float scale_down(float v, int e) {
+  return (e >= -126 && e <= 126) ? v * __uint_as_float(static_cast<uint32_t>(127 - e) << 23)
+                                 : ldexpf(v, -e);
 }
 
 __device__ __forceinline__ f32x16_t mfma32(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
@@ -259,18 +322,63 @@ fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ par
   }
   // register i of tile (ta, tb): token m0 + wm + 32 ta + 8 (i / 4) + 4 h + i % 4,
   // output n0 + wn + 32 tb + m
+  if constexpr (OUT == DSA_FP8_E4M3) {
+    // E4M3 codes with one ue8m0 scale per (token, 128-output tile), the
+    // quantiser of the indexer keys: the fp32 tile goes through the idle
+    // ring, then each wave finishes whole token rows (2 outputs per lane)
+    static_assert(kTM * kTN * 4 <= sizeof(ring), "fp32 tile in the ring");
+    __syncthreads();  // every wave is done with the ring
+    float* tile = reinterpret_cast<float*>(&ring[0][0][0]);
 #pragma unroll
-  for (int ta = 0; ta < 2; ++ta)
+    for (int ta = 0; ta < 2; ++ta)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int t = m0 + wm + 32 * ta + 8 * (i >> 2) + 4 * hl + (i & 3);
-      if (t < N)
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const int j = n0 + wn + 32 * tb + m;
-          gemm_store<OUT>(g, part, static_cast<int64_t>(t) * ncols + j, bz, t, j, acc[ta][tb][i]);
+        for (int i = 0; i < 16; ++i)
+          tile[(wm + 32 * ta + 8 * (i >> 2) + 4 * hl + (i & 3)) * kTN + wn + 32 * tb + m] = acc[ta][tb][i];
+    __syncthreads();
+    // wave w takes rows w + 4 k, eight independent rows at a time (one wave
+    // per SIMD here: the rows' dependent chains overlap only within a wave)
+    uint8_t* codes = static_cast<uint8_t*>(g.out) + bz * g.so;
+    constexpr int kRowsAtOnce = 8;
+#pragma unroll 1
+    for (int r0 = wave; r0 < kTM && m0 + r0 < N; r0 += 4 * kRowsAtOnce) {
+      float2 v[kRowsAtOnce];
+      float am[kRowsAtOnce];
+#pragma unroll
+      for (int u = 0; u < kRowsAtOnce; ++u)
+        v[u] = reinterpret_cast<const float2*>(tile + (r0 + 4 * u) * kTN)[lane];
+#pragma unroll
+      for (int u = 0; u < kRowsAtOnce; ++u) am[u] = fmaxf(fabsf(v[u].x), fabsf(v[u].y));
+#pragma unroll
+      for (int u = 0; u < kRowsAtOnce; ++u) am[u] = wave_max_lanes(am[u]);
+#pragma unroll
+      for (int u = 0; u < kRowsAtOnce; ++u) {
+        const int t = m0 + r0 + 4 * u;
+        const int e = ue8m0_exponent(am[u]);
+        const uint32_t c = e4m3_code(scale_down(v[u].x, e)) | (e4m3_code(scale_down(v[u].y, e)) << 8);
+        if (t < N) {
+          *reinterpret_cast<uint16_t*>(codes + static_cast<int64_t>(t) * g.ldo + n0 + 2 * lane) =
+              static_cast<uint16_t>(c);
+          if (lane == 0)
+            g.out_sf[(static_cast<int64_t>(bz) * N + t) * (ncols / kTN) + bx] = static_cast<uint8_t>(e + 127);
         }
+      }
     }
+  } else {
+#pragma unroll
+    for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = m0 + wm + 32 * ta + 8 * (i >> 2) + 4 * hl + (i & 3);
+        if (t < N)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            const int j = n0 + wn + 32 * tb + m;
+            gemm_store<OUT>(g, part, static_cast<int64_t>(t) * ncols + j, bz, t, j, acc[ta][tb][i]);
+          }
+      }
+  }
 }
 
 // sum over a workgroup of 256 threads (4 waves); red: 4 floats of LDS
@@ -281,24 +389,6 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   const float r = red[0] + red[1] + red[2] + red[3];
   __syncthreads();  // red may be reused
   return r;
-}
-
-// fp32 -> OCP E4M3FN code, round to nearest with ties to the even code;
-// |v| <= 448 (the caller's scale guarantees it; larger saturates to 448)
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fminf(fabsf(v), 448.0f);
-  if (a < 0.015625f) {  // below 2^-6: subnormal steps of 2^-9, rint ties to even
-    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));  // 8 = smallest normal
-  }
-  // keep 3 mantissa bits: add half an ulp of the 3-bit mantissa (minus one
-  // when the kept lsb is 0, so exact halves go to the even code), then cut
-  const uint32_t u = __float_as_uint(a);
-  const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
-  const int e = static_cast<int>(r >> 23) - 127;  // -6 .. 8
-  uint32_t code = (static_cast<uint32_t>(e + 7) << 3) | ((r >> 20) & 7u);
-  if (code > 0x7Eu) code = 0x7Eu;  // 448 is the largest finite code
-  return sign | code;
 }
 
 // One workgroup of 256 threads per token.
@@ -540,7 +630,7 @@ dsa_status_t launch_projection(const FillPlan& p, int N, int D, int ncols, int b
 // one projection of a batch of 1: x [N, D], W [ncols, D]
 GemmOperands plain(const void* x, const void* W, int D) {
   return GemmOperands{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), D, 0, 0,
-                      nullptr, 0, 0};
+                      nullptr, 0, 0, nullptr};
 }
 
 // ---------------------------------------------------------------------------
@@ -731,7 +821,8 @@ dsa_status_t launch_output_projection(int N, int Din, int Dout, const void* prem
 size_t cache_fill_workspace_bytes(int N, int D) { return projection_workspace_bytes(N, D, kFillCols); }
 
 size_t indexer_query_workspace_bytes(int N, int Dq) {
-  return projection_workspace_bytes(N, Dq, kQCols);
+  // many tokens: the tiled kernel writes the query itself (no partials)
+  return fill_plan(N, Dq, kQCols).skinny ? projection_workspace_bytes(N, Dq, kQCols) : 0;
 }
 
 dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const float* kv_gamma,
@@ -771,6 +862,25 @@ dsa_status_t launch_indexer_query(int N, int Dq, const void* cq, const void* wq_
                                   hipStream_t stream) {
   if (N == 0) return DSA_OK;
   const FillPlan p = fill_plan(N, Dq, kQCols);
+  if (!p.skinny) {
+    // one 128-output tile = one head: the tiled kernel writes the finished
+    // query (E4M3 codes and the head's scale, or bf16 / fp32) itself
+    GemmOperands g = plain(cq, wq_b, Dq);
+    g.out = q_out;
+    g.ldo = kQCols;
+    g.out_sf = q_sf;
+    if (q_dtype != DSA_FP8_E4M3)
+      return launch_projection(p, N, Dq, kQCols, 1, g, nullptr, "q_gemm", stream, q_dtype);
+    LaunchTimer timer;
+    const dim3 grid(kQCols / kTN, (N + kTM - 1) / kTM, 1);
+    if (Dq <= 4 * kGemmKStep)
+      hipExtLaunchKernelGGL((fill_gemm_tiled<DSA_FP8_E4M3, 2>), grid, dim3(256), 0, stream,
+                            timer.start(), timer.stop(), 0, N, Dq, kQCols, g, nullptr);
+    else
+      hipExtLaunchKernelGGL((fill_gemm_tiled<DSA_FP8_E4M3, 4>), grid, dim3(256), 0, stream,
+                            timer.start(), timer.stop(), 0, N, Dq, kQCols, g, nullptr);
+    return timer.done("q_gemm");
+  }
   const size_t need = projection_workspace_bytes(N, Dq, kQCols);
   if (ws == nullptr || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "indexer query: workspace of %zu bytes needed, %zu given",

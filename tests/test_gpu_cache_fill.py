@@ -157,8 +157,12 @@ QUERY_CASES = {
     # one query per sequence of the 32-sequence decode batch, V3.2 widths
     "decode_bf16": (32, 1536, "bf16", 11),
     "decode_fp8": (32, 1536, "fp8", 12),
-    # enough tokens for the tiled kernel, a partial last 128-token tile
+    # enough tokens for the tiled kernel (E4M3 codes and the head's scale
+    # written by its epilogue), a partial last 128-token tile
     "tokens_600_fp8": (600, 1536, "fp8", 13),
+    # the tiled kernel writing bf16 / fp32 rows itself
+    "tokens_600_bf16": (600, 1536, "bf16", 15),
+    "tokens_520_f32": (520, 1536, "f32", 16),
     "tokens_7_f32": (7, 1536, "f32", 14),
 }
 
