@@ -25,6 +25,8 @@
 //  * fill_rows: one workgroup per token sums the partials in a fixed order
 //    (deterministic), then the norms, the rotation, the quantiser, and the
 //    scatter into the caches' rows.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "dsa_internal.h"
 
@@ -364,6 +366,37 @@ fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ par
             g.out_sf[(static_cast<int64_t>(bz) * N + t) * (ncols / kTN) + bx] = static_cast<uint8_t>(e + 127);
         }
       }
+    }
+  } else if constexpr (OUT == DSA_BF16 || OUT == DSA_F32) {
+    // finished values: the tile goes through the idle ring so that each
+    // token's 128 outputs leave as whole 16-byte pieces of its row
+    using T = typename std::conditional<OUT == DSA_BF16, uint16_t, float>::type;
+    constexpr int kPer = 16 / sizeof(T);  // elements per 16-byte piece
+    static_assert(kTM * kTN * sizeof(T) <= sizeof(ring), "output tile in the ring");
+    __syncthreads();  // every wave is done with the ring
+    T* tile = reinterpret_cast<T*>(&ring[0][0][0]);
+#pragma unroll
+    for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float v = acc[ta][tb][i];
+          T* dst = tile + (wm + 32 * ta + 8 * (i >> 2) + 4 * hl + (i & 3)) * kTN + wn + 32 * tb + m;
+          if constexpr (OUT == DSA_BF16) *dst = f32_to_bf16(v);
+          else *dst = v;
+        }
+    __syncthreads();
+    T* out = static_cast<T*>(g.out) + bz * g.so;
+    constexpr int kPieces = kTM * kTN / kPer;  // of the whole tile
+#pragma unroll
+    for (int k = 0; k < kPieces / 256; ++k) {
+      const int piece = k * 256 + static_cast<int>(threadIdx.x);
+      const int r = piece / (kTN / kPer), cp = piece % (kTN / kPer);
+      const int t = m0 + r;
+      if (t < N)
+        *reinterpret_cast<u32x4v_t*>(out + static_cast<int64_t>(t) * g.ldo + n0 + kPer * cp) =
+            *reinterpret_cast<const u32x4v_t*>(tile + r * kTN + kPer * cp);
     }
   } else {
 #pragma unroll
