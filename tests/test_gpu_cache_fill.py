@@ -184,3 +184,67 @@ def test_indexer_query(dsa, case):
         _check_fp8(q.cpu().numpy().reshape(N * 64, 128), q_sf.cpu().numpy().reshape(N * 64), ref)
     else:
         _rows_close(_host(q).reshape(N * 64, 128), ref, 1e-2 if q_s == "bf16" else 1e-4, "indexer query")
+
+
+def _gpu_bf16(gen, shape, scale=1.0):
+    torch = U.torch()
+    return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * scale).to(torch.bfloat16)
+
+
+def _bits(t):
+    torch = U.torch()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _sampled(N, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 10)]))
+
+
+def test_cache_fill_prefill_16384_sampled(dsa):
+    """The prefill size bench.py times (16384 tokens, hidden 7168, fp8 keys):
+    inputs drawn on the GPU from a seeded generator, sampled tokens checked
+    against the oracle."""
+    torch = U.torch()
+    N, D = 16384, 7168
+    print(f"[cache_fill] prefill_16384_sampled: N={N} D={D}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(61)
+    x = _gpu_bf16(gen, (N, D))
+    W = _gpu_bf16(gen, (768, D), 1 / math.sqrt(D))
+    kv_gamma = 1 + 0.1 * torch.randn(512, generator=gen, device="cuda")
+    k_gamma = 1 + 0.1 * torch.randn(128, generator=gen, device="cuda")
+    k_beta = 0.1 * torch.randn(128, generator=gen, device="cuda")
+    ang = (torch.rand((N, 32), generator=gen, device="cuda") * 2 - 1) * math.pi
+    cos, sin = torch.cos(ang), torch.sin(ang)
+    slots = torch.arange(N, dtype=torch.int64, device="cuda")
+    kv_cache = torch.empty((N, 576), dtype=torch.bfloat16, device="cuda")
+    k_cache = torch.empty((N, 128), dtype=torch.uint8, device="cuda")
+    k_sf = torch.empty((N,), dtype=torch.uint8, device="cuda")
+    w = dsa.dsa_cache_fill(x, W, kv_gamma, k_gamma, k_beta, cos, sin, slots, kv_cache, k_cache, k_sf,
+                           w_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = torch.as_tensor(_sampled(N, 61), device="cuda")
+    rkv, rk, rw = oracle.cache_fill(_bits(x[rows]), _bits(W), kv_gamma.cpu().numpy(), k_gamma.cpu().numpy(),
+                                    k_beta.cpu().numpy(), cos[rows].cpu().numpy(), sin[rows].cpu().numpy())
+    kv_h = _host(kv_cache[rows])
+    _rows_close(kv_h[:, :512], rkv[:, :512], 1e-2, "normalised latent")
+    _rows_close(kv_h[:, 512:], rkv[:, 512:], 1e-2, "rotated key")
+    _check_fp8(k_cache[rows].cpu().numpy(), k_sf[rows].cpu().numpy(), rk)
+    _rows_close(_host(w[rows]), rw, 1e-2, "head weights")
+
+
+def test_indexer_query_prefill_16384_sampled(dsa):
+    """The prefill size bench.py times (16384 tokens, E4M3 output written by
+    the tiled kernel's epilogue): sampled tokens against the oracle."""
+    torch = U.torch()
+    N, Dq = 16384, 1536
+    print(f"[indexer_query] prefill_16384_sampled: N={N} Dq={Dq}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(62)
+    cq = _gpu_bf16(gen, (N, Dq))
+    wq = _gpu_bf16(gen, (8192, Dq), 1 / math.sqrt(Dq))
+    q, q_sf = dsa.dsa_indexer_query(cq, wq, q_dtype=torch.uint8)
+    torch.cuda.synchronize()
+    rows = torch.as_tensor(_sampled(N, 62), device="cuda")
+    n = rows.numel()
+    ref = oracle.indexer_query(_bits(cq[rows]), _bits(wq)).reshape(n * 64, 128)
+    _check_fp8(q[rows].cpu().numpy().reshape(n * 64, 128), q_sf[rows].cpu().numpy().reshape(n * 64), ref)
