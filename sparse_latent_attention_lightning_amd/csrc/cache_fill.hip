@@ -54,6 +54,13 @@ struct GemmOperands {
   void* out;
   int64_t ldo, so;
   uint8_t* out_sf;  // E4M3 output: one ue8m0 scale byte per (row, 128-output tile)
+  // the absorbed query's rotary part (tiled kernel, finished output, 4
+  // output tiles: tile b takes pairs 8b .. 8b+7): pair (2i, 2i+1) of x's
+  // elements rope_at .. rope_at + 63 turned by angle i into out elements
+  // rope_to + i and rope_to + 32 + i (null: none)
+  const float* rope_cos;
+  const float* rope_sin;
+  int rope_at, rope_to;
 };
 constexpr int kOutPartial = -1;
 
@@ -398,6 +405,36 @@ fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ par
         *reinterpret_cast<u32x4v_t*>(out + static_cast<int64_t>(t) * g.ldo + n0 + kPer * cp) =
             *reinterpret_cast<const u32x4v_t*>(tile + r * kTN + kPer * cp);
     }
+    if (g.rope_cos != nullptr) {
+      // the 32 pairs split over the 4 output tiles (8 each); a thread's 4
+      // (token, pair) items load everything before any arithmetic
+      constexpr int kPairs = 8, kItems = kTM * kPairs / 256;
+      uint32_t pr[kItems];
+      float cs[kItems], sn[kItems];
+#pragma unroll
+      for (int u = 0; u < kItems; ++u) {
+        const int it = static_cast<int>(threadIdx.x) + 256 * u;
+        const int t = min(m0 + it / kPairs, N - 1), i = bx * kPairs + it % kPairs;
+        pr[u] = *reinterpret_cast<const uint32_t*>(x + t * g.ldx + g.rope_at + 2 * i);
+        cs[u] = g.rope_cos[static_cast<int64_t>(t) * 32 + i];
+        sn[u] = g.rope_sin[static_cast<int64_t>(t) * 32 + i];
+      }
+#pragma unroll
+      for (int u = 0; u < kItems; ++u) {
+        const int it = static_cast<int>(threadIdx.x) + 256 * u;
+        const int t = m0 + it / kPairs, i = bx * kPairs + it % kPairs;
+        if (t >= N) continue;
+        const float a = bf16_to_f32(static_cast<uint16_t>(pr[u])), b = bf16_to_f32(static_cast<uint16_t>(pr[u] >> 16));
+        T* o = out + static_cast<int64_t>(t) * g.ldo + g.rope_to + i;
+        if constexpr (OUT == DSA_BF16) {
+          o[0] = f32_to_bf16(a * cs[u] - b * sn[u]);
+          o[32] = f32_to_bf16(a * sn[u] + b * cs[u]);
+        } else {
+          o[0] = a * cs[u] - b * sn[u];
+          o[32] = a * sn[u] + b * cs[u];
+        }
+      }
+    }
   } else {
 #pragma unroll
     for (int ta = 0; ta < 2; ++ta)
@@ -663,7 +700,7 @@ dsa_status_t launch_projection(const FillPlan& p, int N, int D, int ncols, int b
 // one projection of a batch of 1: x [N, D], W [ncols, D]
 GemmOperands plain(const void* x, const void* W, int D) {
   return GemmOperands{static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(W), D, 0, 0,
-                      nullptr, 0, 0, nullptr};
+                      nullptr, 0, 0, nullptr, nullptr, nullptr, 0, 0};
 }
 
 // ---------------------------------------------------------------------------
@@ -797,6 +834,20 @@ dsa_status_t launch_absorb_query(int N, int H, const void* qb, const void* wuk_t
                        static_cast<int64_t>(kLat) * kNope, q,
                        static_cast<int64_t>(H) * kQDimOut, kQDimOut};
   const FillPlan p = fill_plan(N, kNope, kLat * H);
+  static_assert(kLat / 128 * 8 == kQRope / 2, "the tiled kernel's 4 output tiles take 8 pairs each");
+  // few tokens: the tiled kernel turns the rotary part too (one launch less:
+  // 7.9 us against 7.7 + 4.4 for 32 tokens); for many tokens the extra loads
+  // in every workgroup's epilogue cost more than the separate pass (16384
+  // tokens: 1246 us against 858 + 190)
+  constexpr int kFuseRopeTokens = 1024;
+  if (!p.skinny && N <= kFuseRopeTokens) {
+    GemmOperands gr = g;
+    gr.rope_cos = rope_cos;
+    gr.rope_sin = rope_sin;
+    gr.rope_at = kNope;
+    gr.rope_to = kLat;
+    return launch_projection(p, N, kNope, kLat, H, gr, nullptr, "absorb_q_gemm", stream, q_dtype);
+  }
   dsa_status_t st = launch_projection(p, N, kNope, kLat, H, g, nullptr, "absorb_q_gemm", stream, q_dtype);
   if (st != DSA_OK) return st;
   return q_dtype == DSA_BF16 ? run_q_rope<DSA_BF16>(N, H, qb, rope_cos, rope_sin, q, stream)
