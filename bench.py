@@ -612,7 +612,9 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        rows = args.cpu_rows or (cfg.B * cfg.T if cfg.T == 1 else 16)
+        # a bounded sample: about as many query x key pairs as 32 queries over
+        # 8192 keys (decode: whole queries; prefill: 16 query rows)
+        rows = args.cpu_rows or (max(1, min(cfg.B * cfg.T, 32 * 8192 // cfg.S)) if cfg.T == 1 else 16)
         print(f"[bench] CPU oracle on {rows} queries ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, rows)
     print(json.dumps(result))
