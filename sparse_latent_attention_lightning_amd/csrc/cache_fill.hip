@@ -21,10 +21,19 @@
 //    so that the weights stream through many workgroups at once;
 //    fill_gemm_tiled (many tokens): 128 x 128 tiles through an LDS ring.
 //    Both operands are contiguous along the reduction (W in Linear layout,
-//    one output per row).
+//    one output per row); both take a batch of such products (one per head
+//    for the absorption products) and, when one slice covers the reduction,
+//    write the finished bf16 / fp32 values (the tiled kernel also E4M3 codes
+//    with one ue8m0 scale per 128-output tile, and the absorbed query's
+//    rotary part).
 //  * fill_rows: one workgroup per token sums the partials in a fixed order
 //    (deterministic), then the norms, the rotation, the quantiser, and the
-//    scatter into the caches' rows.
+//    scatter into the caches' rows; q_rows does the same for the indexer
+//    query's heads.
+//  * the absorption products either side of the sparse attention (see the
+//    section further down): uk_transpose (W_UK in reduction-contiguous
+//    form), q_rope (the query's rotary part), gemm_finish (slice sums of the
+//    output projection).
 #include <type_traits>
 
 #include "dsa_device.h"
