@@ -460,6 +460,142 @@ fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ par
   }
 }
 
+// Many tokens with a long reduction: 256 tokens x 128 outputs per workgroup,
+// wave w = 128 x 64 (4 x 2 MFMA tiles), so each operand read from LDS feeds
+// more MFMAs than the 128 x 128 kernel's 2 x 2 (6 reads per 8 MFMAs against
+// 4 per 4); a 3-stage ring of 48 KB stages (A 32 KB, B 16 KB), direct
+// copies two chunks ahead, the same swizzle.  Partial or finished bf16 /
+// fp32 output (the latter staged through the ring as 16-byte row pieces).
+constexpr int kWM = 256, kWStages = 3;
+constexpr int kWATile = kWM * kGemmKStep * 2;     // 32 KB
+constexpr int kWACopies = kWATile / 1024 / 4;     // 8 per wave
+constexpr int kWStage = kWATile + kTTile;         // 48 KB
+
+template <int OUT>
+__global__ void __launch_bounds__(256, 1)
+fill_gemm_wide(int N, int D, int ncols, GemmOperands g, float* __restrict__ part) {
+  static_assert(OUT != DSA_FP8_E4M3, "E4M3 output uses the 128-token kernel");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kWStages][kWStage];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hl = lane >> 5, m = lane & 31;
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int total = gx * gy * gridDim.z;
+  const int lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int per_xcd = total / kXcds;
+  const int w_id = lin < per_xcd * kXcds ? (lin % kXcds) * per_xcd + lin / kXcds : lin;
+  const int bx = w_id % gx, by = (w_id / gx) % gy, bz = w_id / (gx * gy);
+  const int m0 = by * kWM, n0 = bx * kTN;
+  const int wm = (wave >> 1) * 128, wn = (wave & 1) * 64;
+  const int nk = D / kGemmKStep;
+  const uint16_t* x = g.x + bz * g.sx;
+  const uint16_t* W = g.W + bz * g.sw;
+  part += static_cast<int64_t>(bz) * N * ncols;
+  auto issue = [&](int c) {
+    uint8_t* st = ring[c % kWStages];
+#pragma unroll
+    for (int i = 0; i < kWACopies; ++i) {  // A rows 8j .. 8j + 7, j < 32
+      const int j = wave * kWACopies + i;
+      const int r = 8 * j + (lane >> 3);
+      const int64_t k = static_cast<int64_t>(c) * kGemmKStep + tile_slot(r, lane & 7) * 8;
+      lds_dma_16(x + min(m0 + r, N - 1) * g.ldx + k, lds_addr(st) + 1024 * j);
+    }
+#pragma unroll
+    for (int i = 0; i < kTCopies; ++i) {  // B rows 8j .. 8j + 7, j < 16
+      const int j = wave * kTCopies + i;
+      const int r = 8 * j + (lane >> 3);
+      const int64_t k = static_cast<int64_t>(c) * kGemmKStep + tile_slot(r, lane & 7) * 8;
+      lds_dma_16(W + static_cast<int64_t>(n0 + r) * D + k, lds_addr(st + kWATile) + 1024 * j);
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < kWStages - 1; ++c)
+    if (c < nk) issue(c);
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+  static_assert(kWACopies + kTCopies == 12 && kWStages == 3, "vmcnt immediate: one chunk = 12 copies per wave");
+  for (int c = 0; c < nk; ++c) {
+    // chunk c has landed when at most the next chunk's 12 copies are out
+    if (c + 1 < nk)
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // every wave's copies of chunk c are in; chunk c - 1 is consumed
+    if (c + kWStages - 1 < nk) issue(c + kWStages - 1);
+    const uint8_t* At = ring[c % kWStages];
+    const uint8_t* Bt = At + kWATile;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int piece = 2 * s4 + hl;
+      bf16x8_t a[4], b[2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int ra = wm + 32 * t + m;
+        a[t] = *reinterpret_cast<const bf16x8_t*>(At + ra * 128 + 16 * tile_slot(ra, piece));
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int rb = wn + 32 * t + m;
+        b[t] = *reinterpret_cast<const bf16x8_t*>(Bt + rb * 128 + 16 * tile_slot(rb, piece));
+      }
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) acc[ta][tb] = mfma32(a[ta], b[tb], acc[ta][tb]);
+    }
+  }
+  // register i of tile (ta, tb): token m0 + wm + 32 ta + 8 (i / 4) + 4 h + i % 4,
+  // output n0 + wn + 32 tb + m
+  if constexpr (OUT == DSA_BF16 || OUT == DSA_F32) {
+    using T = typename std::conditional<OUT == DSA_BF16, uint16_t, float>::type;
+    constexpr int kPer = 16 / sizeof(T);
+    static_assert(kWM * kTN * sizeof(T) <= sizeof(ring), "output tile in the ring");
+    __syncthreads();  // every wave is done with the ring
+    T* tile = reinterpret_cast<T*>(&ring[0][0]);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float v = acc[ta][tb][i];
+          T* dst = tile + (wm + 32 * ta + 8 * (i >> 2) + 4 * hl + (i & 3)) * kTN + wn + 32 * tb + m;
+          if constexpr (OUT == DSA_BF16) *dst = f32_to_bf16(v);
+          else *dst = v;
+        }
+    __syncthreads();
+    T* out = static_cast<T*>(g.out) + bz * g.so;
+    constexpr int kPieces = kWM * kTN / kPer;
+#pragma unroll
+    for (int k = 0; k < kPieces / 256; ++k) {
+      const int piece = k * 256 + static_cast<int>(threadIdx.x);
+      const int r = piece / (kTN / kPer), cp = piece % (kTN / kPer);
+      const int t = m0 + r;
+      if (t < N)
+        *reinterpret_cast<u32x4v_t*>(out + static_cast<int64_t>(t) * g.ldo + n0 + kPer * cp) =
+            *reinterpret_cast<const u32x4v_t*>(tile + r * kTN + kPer * cp);
+    }
+  } else {
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = m0 + wm + 32 * ta + 8 * (i >> 2) + 4 * hl + (i & 3);
+        if (t < N)
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            const int j = n0 + wn + 32 * tb + m;
+            gemm_store<OUT>(g, part, static_cast<int64_t>(t) * ncols + j, bz, t, j, acc[ta][tb][i]);
+          }
+      }
+  }
+}
+
 // sum over a workgroup of 256 threads (4 waves); red: 4 floats of LDS
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -673,6 +809,17 @@ size_t projection_workspace_bytes(int N, int D, int ncols, int batch = 1) {
 
 // p = x W^T into fp32 partials (p.slices of them, [N, ncols] each), or, for
 // out_dtype DSA_BF16 / DSA_F32 and one slice, straight into g.out
+// 256-token tiles pay off with a long reduction (at least 16 chunks) and at
+// least two workgroups per CU (measured: the output projection of 16384
+// tokens 5047 -> 4146 us, the bf16 indexer query 660 -> 551 us; the cache
+// fill's 384 workgroups and the 8-chunk absorbed output got slower)
+template <int OUT>
+bool wide_tiles(int N, int D, int ncols, int batch, const GemmOperands& g) {
+  if (OUT == kOutPartial || g.rope_cos != nullptr || D < 16 * kGemmKStep) return false;
+  const int64_t wgs = static_cast<int64_t>(ncols / kTN) * ((N + kWM - 1) / kWM) * batch;
+  return wgs >= 2 * static_cast<int64_t>(device_info().cu_count);
+}
+
 template <int OUT>
 dsa_status_t launch_projection_as(const FillPlan& p, int N, int D, int ncols, int batch,
                                   const GemmOperands& g, float* part, const char* name,
@@ -682,6 +829,10 @@ dsa_status_t launch_projection_as(const FillPlan& p, int N, int D, int ncols, in
     hipExtLaunchKernelGGL(fill_gemm_skinny<OUT>, dim3(ncols / 32, p.row_blocks, batch * p.slices),
                           dim3(kSkinnyWaves * 64), 0, stream, timer.start(), timer.stop(), 0, N, D,
                           ncols, p.slices, g, part);
+  else if (wide_tiles<OUT>(N, D, ncols, batch, g))
+    hipExtLaunchKernelGGL(fill_gemm_wide<OUT>, dim3(ncols / kTN, (N + kWM - 1) / kWM, batch),
+                          dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D, ncols, g,
+                          part);
   else if (D <= 4 * kGemmKStep)
     hipExtLaunchKernelGGL((fill_gemm_tiled<OUT, 2>), dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
                           dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D, ncols, g,

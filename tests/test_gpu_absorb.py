@@ -131,6 +131,9 @@ WO_CASES = {
     "tokens_300_small": (300, 1024, 256, "f32", 53, False),
     # many tokens: the tiled kernel, a partial last tile
     "tokens_2100": (2100, 1024, 7168, "bf16", 54, False),
+    # 256-token tiles (long reduction, enough workgroups), a partial last tile
+    "tokens_2400_wide": (2400, 1024, 7168, "bf16", 56, False),
+    "tokens_2400_wide_f32": (2400, 1024, 7168, "f32", 57, False),
     # the prefill: 16384 tokens, sampled
     "prefill_16384": (16384, 16384, 7168, "bf16", 55, True),
 }
