@@ -474,7 +474,6 @@ constexpr int kWStage = kWATile + kTTile;         // 48 KB
 template <int OUT>
 __global__ void __launch_bounds__(256, 1)
 fill_gemm_wide(int N, int D, int ncols, GemmOperands g, float* __restrict__ part) {
-  static_assert(OUT != DSA_FP8_E4M3, "E4M3 output uses the 128-token kernel");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kWStages][kWStage];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -551,7 +550,50 @@ fill_gemm_wide(int N, int D, int ncols, GemmOperands g, float* __restrict__ part
   }
   // register i of tile (ta, tb): token m0 + wm + 32 ta + 8 (i / 4) + 4 h + i % 4,
   // output n0 + wn + 32 tb + m
-  if constexpr (OUT == DSA_BF16 || OUT == DSA_F32) {
+  if constexpr (OUT == DSA_FP8_E4M3) {
+    // E4M3 codes with one ue8m0 scale per (token, 128-output tile), the
+    // quantiser of the indexer keys: the fp32 tile goes through the idle
+    // ring, then each wave finishes whole token rows (2 outputs per lane)
+    static_assert(kWM * kTN * 4 <= sizeof(ring), "fp32 tile in the ring");
+    __syncthreads();  // every wave is done with the ring
+    float* tile = reinterpret_cast<float*>(&ring[0][0]);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          tile[(wm + 32 * ta + 8 * (i >> 2) + 4 * hl + (i & 3)) * kTN + wn + 32 * tb + m] = acc[ta][tb][i];
+    __syncthreads();
+    // wave w takes rows w + 4 k, eight independent rows at a time (one wave
+    // per SIMD here: the rows' dependent chains overlap only within a wave)
+    uint8_t* codes = static_cast<uint8_t*>(g.out) + bz * g.so;
+    constexpr int kRowsAtOnce = 8;
+#pragma unroll 1
+    for (int r0 = wave; r0 < kWM && m0 + r0 < N; r0 += 4 * kRowsAtOnce) {
+      float2 v[kRowsAtOnce];
+      float am[kRowsAtOnce];
+#pragma unroll
+      for (int u = 0; u < kRowsAtOnce; ++u)
+        v[u] = reinterpret_cast<const float2*>(tile + (r0 + 4 * u) * kTN)[lane];
+#pragma unroll
+      for (int u = 0; u < kRowsAtOnce; ++u) am[u] = fmaxf(fabsf(v[u].x), fabsf(v[u].y));
+#pragma unroll
+      for (int u = 0; u < kRowsAtOnce; ++u) am[u] = wave_max_lanes(am[u]);
+#pragma unroll
+      for (int u = 0; u < kRowsAtOnce; ++u) {
+        const int t = m0 + r0 + 4 * u;
+        const int e = ue8m0_exponent(am[u]);
+        const uint32_t c = e4m3_code(scale_down(v[u].x, e)) | (e4m3_code(scale_down(v[u].y, e)) << 8);
+        if (t < N) {
+          *reinterpret_cast<uint16_t*>(codes + static_cast<int64_t>(t) * g.ldo + n0 + 2 * lane) =
+              static_cast<uint16_t>(c);
+          if (lane == 0)
+            g.out_sf[(static_cast<int64_t>(bz) * N + t) * (ncols / kTN) + bx] = static_cast<uint8_t>(e + 127);
+        }
+      }
+    }
+  } else if constexpr (OUT == DSA_BF16 || OUT == DSA_F32) {
     using T = typename std::conditional<OUT == DSA_BF16, uint16_t, float>::type;
     constexpr int kPer = 16 / sizeof(T);
     static_assert(kWM * kTN * sizeof(T) <= sizeof(ring), "output tile in the ring");
@@ -1116,6 +1158,11 @@ dsa_status_t launch_indexer_query(int N, int Dq, const void* cq, const void* wq_
     if (q_dtype != DSA_FP8_E4M3)
       return launch_projection(p, N, Dq, kQCols, 1, g, nullptr, "q_gemm", stream, q_dtype);
     LaunchTimer timer;
+    if (wide_tiles<DSA_FP8_E4M3>(N, Dq, kQCols, 1, g)) {
+      hipExtLaunchKernelGGL(fill_gemm_wide<DSA_FP8_E4M3>, dim3(kQCols / kTN, (N + kWM - 1) / kWM, 1),
+                            dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, Dq, kQCols, g, nullptr);
+      return timer.done("q_gemm");
+    }
     const dim3 grid(kQCols / kTN, (N + kTM - 1) / kTM, 1);
     if (Dq <= 4 * kGemmKStep)
       hipExtLaunchKernelGGL((fill_gemm_tiled<DSA_FP8_E4M3, 2>), grid, dim3(256), 0, stream,
