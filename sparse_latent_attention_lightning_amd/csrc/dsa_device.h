@@ -153,6 +153,15 @@ __device__ __forceinline__ f32x4_t mfma16x16x32_bf16(const bf16x8_t& a, const bf
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// gfx950's 16x16x128 product of OCP e4m3 operands (format 0 for both, unit
+// E8M0 scales 127): lane (g, n) supplies 32 bytes of row n of each operand;
+// C as for every 16x16 product (lane (g, n): rows 4 g .. 4 g + 3, column n)
+__device__ __forceinline__ f32x4_t mfma16x16x128_e4m3(const i32x8_t& a, const i32x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 __device__ __forceinline__ f32x4_t mfma16x16x32_fp8(long a, long b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
 }

@@ -460,6 +460,17 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
     }
   }
 
+  // e4m3: the head block's 32 query bytes of this lane (dims 32 g .. 32 g + 31)
+  i32x8_t qa128[4];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        qa128[mb][2 * ks] = static_cast<int>(static_cast<uint64_t>(qa8[mb][ks]) & 0xffffffffu);
+        qa128[mb][2 * ks + 1] = static_cast<int>(static_cast<uint64_t>(qa8[mb][ks]) >> 32);
+      }
+  }
   float res[Sh::kResults];  // lane l: key s_begin + 64 j + l
   float part[4];
 #pragma unroll
@@ -484,19 +495,17 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if constexpr (FP8) {
+          // one 16x16x128 e4m3 product per head block: lane (g, n) holds
+          // dims 32 g .. 32 g + 31 of key n, in the byte order of the
+          // query's fragment (pieces 2 g and 2 g + 1 of the row)
           const int f = (n >> 1) & 7;  // (row >> 1) & 7 of row 16 u + n
-          u32x4_t kv[2];
+          const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(rp + 16 * ((2 * g) ^ f));
+          const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(rp + 16 * ((2 * g + 1) ^ f));
+          const i32x8_t kk = {static_cast<int>(k0[0]), static_cast<int>(k0[1]), static_cast<int>(k0[2]),
+                              static_cast<int>(k0[3]), static_cast<int>(k1[0]), static_cast<int>(k1[1]),
+                              static_cast<int>(k1[2]), static_cast<int>(k1[3])};
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            kv[j] = *reinterpret_cast<const u32x4_t*>(rp + 16 * ((2 * g + j) ^ f));
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const u32x4_t half = kv[ks >> 1];
-            const long kk = (ks & 1) ? (static_cast<long>(half[3]) << 32 | half[2])
-                                     : (static_cast<long>(half[1]) << 32 | half[0]);
-#pragma unroll
-            for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x16x32_fp8(qa8[mb][ks], kk, acc[mb]);
-          }
+          for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x16x128_e4m3(qa128[mb], kk, acc[mb]);
         } else {
           bf16x8_t kv[4];
 #pragma unroll
