@@ -158,3 +158,34 @@ def test_output_projection(dsa, case):
     rows = torch.as_tensor(_sample(N, full, seed), device="cuda")
     ref = oracle.linear_bf16(_bits(x[rows]), _bits(W))
     _rows_close(_val(out[rows]), ref, 1e-2 if dt == "bf16" else 1e-4, "output projection")
+
+
+def test_minimum_and_empty_sizes(dsa):
+    """One token and one head through every absorption entry point, the
+    smallest output projection (64 -> 128), and zero tokens (nothing launched,
+    empty outputs)."""
+    torch = U.torch()
+    print("[absorb] minimum and empty sizes", flush=True)
+    qb, kvb, cos, sin, o_lat = _inputs(1, 1, 71, False)
+    wuk = dsa.dsa_absorb_prepare(kvb)
+    q = dsa.dsa_absorb_query(qb, wuk, cos, sin, q_dtype=torch.float32)
+    out = dsa.dsa_absorb_output(o_lat, kvb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kv_np = _val(kvb)
+    rq = oracle.absorb_query(_val(qb), kv_np, cos.double().cpu().numpy(), sin.double().cpu().numpy())
+    _rows_close(_val(q)[..., :512], rq[..., :512], 1e-4, "absorbed latent query")
+    _rows_close(_val(q)[..., 512:], rq[..., 512:], 1e-4, "rotated query")
+    _rows_close(_val(out).reshape(1, 1, 128), oracle.absorb_output(_val(o_lat), kv_np).reshape(1, 1, 128),
+                1e-4, "head outputs")
+    rng = np.random.default_rng(72)
+    x = U.to_dev(g.f32_to_bf16_bits(rng.standard_normal((1, 64)).astype(np.float32)), "bf16")
+    W = U.to_dev(g.f32_to_bf16_bits(rng.standard_normal((128, 64)).astype(np.float32)), "bf16")
+    y = dsa.dsa_output_projection(x, W, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _rows_close(_val(y), oracle.linear_bf16(_bits(x), _bits(W)), 1e-4, "output projection")
+    # zero tokens: empty results, no launch
+    e_qb, e_o = qb[:0], o_lat[:0]
+    assert dsa.dsa_absorb_query(e_qb, wuk, cos[:0], sin[:0]).shape == (0, 1, 576)
+    assert dsa.dsa_absorb_output(e_o, kvb).shape == (0, 128)
+    assert dsa.dsa_output_projection(x[:0], W).shape == (0, 128)
+    torch.cuda.synchronize()
