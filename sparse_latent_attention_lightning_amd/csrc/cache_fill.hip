@@ -252,15 +252,14 @@ fill_gemm_skinny(int N, int D, int ncols, int slices, GemmOperands g, float* __r
 // each) touch every bank once per cycle.
 constexpr int kTM = 128, kTN = 128;
 constexpr int kXcds = 8;  // accelerator dies of the MI355X, one L2 each
-constexpr int kTwoStageMaxChunks = 8;
 constexpr int kTTile = kTM * kGemmKStep * 2;  // 16 KB per operand tile
 constexpr int kTCopies = kTTile / 1024 / 4;   // copies per wave per operand tile
 
-// STAGES = 4 (the ring above, one workgroup per CU) or 2 for a reduction of
-// at most kTwoStageMaxChunks chunks (half the LDS: two workgroups per CU
-// hide each other's load latency; each chunk then waits for its own
-// copies).  Measured at 8 chunks (the absorbed output, 512 wide, 16384
-// tokens): 700 us against 790 us with 4 stages.
+// STAGES = 4 (the ring above, one workgroup per CU) or 2 (half the LDS: two
+// workgroups per CU hide each other's load latency; each chunk then waits
+// for its own copies).  The launches use 2: measured faster for every
+// reduction tried (the 8-chunk absorbed output of 16384 tokens 700 us
+// against 790, the 112-chunk cache fill 250 us against 270).
 template <int OUT, int STAGES>
 __global__ void __launch_bounds__(256, 4 / STAGES)
 fill_gemm_tiled(int N, int D, int ncols, GemmOperands g, float* __restrict__ part) {
@@ -878,12 +877,8 @@ dsa_status_t launch_projection_as(const FillPlan& p, int N, int D, int ncols, in
     hipExtLaunchKernelGGL(fill_gemm_wide<OUT>, dim3(ncols / kTN, (N + kWM - 1) / kWM, batch),
                           dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D, ncols, g,
                           part);
-  else if (D <= kTwoStageMaxChunks * kGemmKStep)
-    hipExtLaunchKernelGGL((fill_gemm_tiled<OUT, 2>), dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
-                          dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D, ncols, g,
-                          part);
   else
-    hipExtLaunchKernelGGL((fill_gemm_tiled<OUT, 4>), dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
+    hipExtLaunchKernelGGL((fill_gemm_tiled<OUT, 2>), dim3(ncols / kTN, (N + kTM - 1) / kTM, batch),
                           dim3(256), 0, stream, timer.start(), timer.stop(), 0, N, D, ncols, g,
                           part);
   return timer.done(name);
@@ -1167,12 +1162,8 @@ dsa_status_t launch_indexer_query(int N, int Dq, const void* cq, const void* wq_
       return timer.done("q_gemm");
     }
     const dim3 grid(kQCols / kTN, (N + kTM - 1) / kTM, 1);
-    if (Dq <= kTwoStageMaxChunks * kGemmKStep)
-      hipExtLaunchKernelGGL((fill_gemm_tiled<DSA_FP8_E4M3, 2>), grid, dim3(256), 0, stream,
-                            timer.start(), timer.stop(), 0, N, Dq, kQCols, g, nullptr);
-    else
-      hipExtLaunchKernelGGL((fill_gemm_tiled<DSA_FP8_E4M3, 4>), grid, dim3(256), 0, stream,
-                            timer.start(), timer.stop(), 0, N, Dq, kQCols, g, nullptr);
+    hipExtLaunchKernelGGL((fill_gemm_tiled<DSA_FP8_E4M3, 2>), grid, dim3(256), 0, stream,
+                          timer.start(), timer.stop(), 0, N, Dq, kQCols, g, nullptr);
     return timer.done("q_gemm");
   }
   const size_t need = projection_workspace_bytes(N, Dq, kQCols);
