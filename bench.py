@@ -164,6 +164,18 @@ def summarize_pmc(fetch_dir, write_dir, mib, workload):
     print("\n".join(lines))
 
 
+def cpu_model():
+    """The host CPU's model name (first /proc/cpuinfo entry)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(cfg, rows):
     """The oracle (scores -> top-K -> sparse MLA) on `rows` queries of the
     workload, all host cores."""
@@ -205,7 +217,7 @@ def cpu_baseline(cfg, rows):
         oracle.sparse_mla(sub, zeros, q[sel], kv[b][None], idx, threads=threads)
         n += int(sel.sum())
     dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="queries/s", cores=threads, kind="oracle",
+    return dict(value=n / dt, unit="queries/s", cores=threads, cpu=cpu_model(), kind="oracle",
                 sample=f"{n} of {cfg.B * cfg.T} queries of the workload, full hot path "
                        f"(scores, top-{cfg.K_eff}, sparse MLA) in fp64, {dt:.1f} s wall")
 
@@ -324,7 +336,7 @@ def bench_cache_fill(args):
                           cos[:n_cpu].cpu().numpy(), sin[:n_cpu].cpu().numpy(), threads=threads)
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(n_cpu / dt, 2), "unit": "tokens/s", "cores": threads,
-                                  "kind": "oracle",
+                                  "cpu": cpu_model(), "kind": "oracle",
                                   "sample": f"{n_cpu} tokens of the workload, fp64, {dt:.1f} s wall"}
     print(json.dumps(result))
 
@@ -440,7 +452,7 @@ def bench_absorb(args):
             oracle.absorb_output(o_lat[:n_cpu].float().cpu().numpy(), kv, threads=threads)
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(n_cpu / dt, 2), "unit": "tokens/s", "cores": threads,
-                                  "kind": "oracle",
+                                  "cpu": cpu_model(), "kind": "oracle",
                                   "sample": f"{n_cpu} tokens of the workload, fp64, {dt:.1f} s wall"}
     print(json.dumps(result))
 
@@ -464,7 +476,7 @@ def main():
 
     import dsa_inputs as g
     import sparse_latent_attention_lightning_amd as dsa
-    from tests import gpu_util as U
+    from dsa_inputs import device as U
 
     cfg = g.CONFIGS[args.workload]
     dev = torch.device("cuda", 0)

@@ -175,8 +175,10 @@ dsa_status_t dsa_forward_ragged(const dsa_shape_t* shape, const int32_t* seq_len
  * (atlas.klimoza.dev, DeepSeek-V3.2-Exp MoE block, "All 43 steps": c^KV =
  * x W_DKV and its RMSNorm, k^pe = x W_KR rotated, w = x W_w; the indexer key
  * wk with k_norm, a LayerNorm with gain and bias, from the nnterp
- * deepseek_v32 module tree; the [512, 64] split of the joint down-projection
- * from the model.py excerpt there).  With p = W x (fp32 accumulation):
+ * deepseek_v32 module tree; the [512, 64] split of the joint down-projection,
+ * then the latent norm and the key rotation, from the mla-kv excerpt of the
+ * atlas "DeepSeek-V3.2-Exp · Attention input" page).  With p = W x (fp32
+ * accumulation):
  *   x         [N, D] bf16   the tokens' attention inputs; D % 64 == 0
  *   W         [768, D] bf16 joint projection in Linear layout (row j holds
  *             output j's weights): rows 0-511 W_DKV, 512-575 W_KR,

@@ -323,7 +323,8 @@ int orc_explicit_mla(int32_t H, int32_t Dc, int32_t Dn, int32_t Dv, int32_t Dr,
 /* list: c^KV = x W_DKV, c^KV normalised, k^pe = x W_KR rotated, w = x W_w;  */
 /* the indexer's key projection wk with k_norm, a LayerNorm with affine and  */
 /* bias, from the nnterp deepseek_v32 module tree; the joint down-projection */
-/* split [512, 64] from the model.py excerpt on the same page).              */
+/* split [512, 64], then the latent norm and the key rotation, from the     */
+/* mla-kv excerpt of the atlas "DeepSeek-V3.2-Exp . Attention input" page). */
 /* ------------------------------------------------------------------------ */
 
 #define ORC_FILL_LAT 512
@@ -412,11 +413,15 @@ int orc_quantize_e4m3_block(const double* y, int32_t len, uint8_t* codes, uint8_
   if (!y || !codes || !scale_byte || len <= 0) return 1;
   double amax = 0.0;
   for (int32_t i = 0; i < len; ++i) amax = fmax(amax, fabs(y[i]));
-  int e = 0; /* the smallest e with 448 2^e >= amax (0 for an all-zero block) */
+  /* the smallest e with 448 2^e >= amax (0 for an all-zero block), held    */
+  /* to the range of the scale byte e + 127: never below -127 (a block whose */
+  /* largest magnitude is under 448 2^-127 keeps the scale 2^-127)           */
+  int e = 0;
   if (amax > 0.0) {
     e = (int)ceil(log2(amax / 448.0));
-    while (e > -127 && ldexp(448.0, e - 1) >= amax) --e;
-    while (e < 127 && ldexp(448.0, e) < amax) ++e;
+    while (ldexp(448.0, e - 1) >= amax) --e;
+    while (ldexp(448.0, e) < amax) ++e;
+    if (e < -127) e = -127;
   }
   *scale_byte = (uint8_t)(e + 127);
   for (int32_t i = 0; i < len; ++i) codes[i] = e4m3_code_of(ldexp(y[i], -e));

@@ -140,6 +140,22 @@ def _req(t: torch.Tensor, name: str, shape: Tuple[int, ...], dtypes, device=None
         raise ValueError(f"{name} must be contiguous")
 
 
+def _ws_bytes(ws: Optional[torch.Tensor], device) -> int:
+    """Byte size of a caller workspace: a contiguous uint8 GPU tensor on
+    `device` (None: no workspace)."""
+    if ws is None:
+        return 0
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("ws must be a tensor")
+    if ws.device != device:
+        raise ValueError(f"ws is on {ws.device}, expected {device}")
+    if ws.dtype != torch.uint8:
+        raise ValueError(f"ws has dtype {ws.dtype}, expected torch.uint8")
+    if not ws.is_contiguous():
+        raise ValueError("ws must be contiguous")
+    return ws.numel()
+
+
 def _idx_dtypes(code):
     if code == DSA_FP8_E4M3:
         return (torch.uint8, torch.float8_e4m3fn)
@@ -224,7 +240,7 @@ def dsa_topk(shape: DsaShape, scores, out: Optional[torch.Tensor] = None,
     if ws is None:
         ws = _workspace(shape, ENTRY_TOPK, dev)
     _check(lib().dsa_topk(ctypes.byref(shape), _ptr(scores), _ptr(out), _ptr(ws),
-                          0 if ws is None else ws.numel(), _stream(dev)))
+                          _ws_bytes(ws, dev), _stream(dev)))
     return out
 
 
@@ -243,8 +259,7 @@ def dsa_sparse_mla_fwd(shape: DsaShape, q, kv, idx, out: Optional[torch.Tensor] 
     if ws is None:
         ws = _workspace(shape, ENTRY_SPARSE_MLA, dev)
     _check(lib().dsa_sparse_mla_fwd(ctypes.byref(shape), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out),
-                                    _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
-                                    _stream(dev)))
+                                    _ptr(lse), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)))
     return out, lse
 
 
@@ -269,22 +284,27 @@ def dsa_forward_ragged(shape: DsaShape, seq_lens, q_idx, k_idx, w, q, kv, q_sf=N
     _check_mla(shape, q, kv, None)
     if out is None:
         out = torch.empty((shape.B, shape.T, shape.H, shape.Dc), dtype=q.dtype, device=dev)
+    _req(out, "o", (shape.B, shape.T, shape.H, shape.Dc), (q.dtype,), dev)
     if idx_out is None and want_idx:
         idx_out = torch.empty((shape.B, shape.T, shape.K_eff), dtype=torch.int32, device=dev)
+    if idx_out is not None:
+        _req(idx_out, "idx_out", (shape.B, shape.T, shape.K_eff), (torch.int32,), dev)
     if lse is None and want_lse:
         lse = torch.empty((shape.B, shape.T, shape.H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _req(lse, "lse", (shape.B, shape.T, shape.H), (torch.float32,), dev)
     if ws is None:
         ws = _workspace(shape, ENTRY_FORWARD, dev)
+    nws = _ws_bytes(ws, dev)
     if seq_lens is None:
         _check(lib().dsa_forward(ctypes.byref(shape), _ptr(q_idx), _ptr(q_sf), _ptr(k_idx),
                                  _ptr(k_sf), _ptr(w), _ptr(q), _ptr(kv), _ptr(idx_out), _ptr(out),
-                                 _ptr(lse), _ptr(ws), 0 if ws is None else ws.numel(),
-                                 _stream(dev)))
+                                 _ptr(lse), _ptr(ws), nws, _stream(dev)))
     else:
         _check(lib().dsa_forward_ragged(ctypes.byref(shape), _ptr(seq_lens), _ptr(q_idx),
                                         _ptr(q_sf), _ptr(k_idx), _ptr(k_sf), _ptr(w), _ptr(q),
                                         _ptr(kv), _ptr(idx_out), _ptr(out), _ptr(lse), _ptr(ws),
-                                        0 if ws is None else ws.numel(), _stream(dev)))
+                                        nws, _stream(dev)))
     return out, lse, idx_out
 
 
@@ -345,7 +365,7 @@ def dsa_cache_fill(x, W, kv_gamma, k_gamma, k_beta, rope_cos, rope_sin, slots, k
                                 _ptr(k_beta), _ptr(rope_cos), _ptr(rope_sin), _ptr(slots),
                                 _DT_OF[kv_cache.dtype], _ptr(kv_cache), _DT_OF[k_cache.dtype],
                                 _ptr(k_cache), _ptr(k_sf), _DT_OF[w_out.dtype], _ptr(w_out),
-                                _ptr(ws), ws.numel(), _stream(dev)))
+                                _ptr(ws), _ws_bytes(ws, dev), _stream(dev)))
     return w_out
 
 
@@ -371,7 +391,7 @@ def dsa_indexer_query(cq, wq_b, q_dtype=torch.bfloat16, q_out: Optional[torch.Te
             raise DsaError(1, f"indexer query: invalid sizes N={N}, Dq={Dq}")
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     _check(lib().dsa_indexer_query(N, Dq, _ptr(cq), _ptr(wq_b), _DT_OF[q_out.dtype], _ptr(q_out),
-                                   _ptr(q_sf), _ptr(ws), ws.numel(), _stream(dev)))
+                                   _ptr(q_sf), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)))
     return q_out, (q_sf if fp8 else None)
 
 
@@ -442,5 +462,5 @@ def dsa_output_projection(premix, wo, out_dtype=torch.bfloat16, out: Optional[to
             raise DsaError(1, f"output projection: invalid sizes N={N}, Din={Din}, Dout={Dout}")
         ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
     _check(lib().dsa_output_projection(N, Din, Dout, _ptr(premix), _ptr(wo), _DT_OF[out.dtype],
-                                       _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+                                       _ptr(out), _ptr(ws), _ws_bytes(ws, dev), _stream(dev)))
     return out

@@ -4,8 +4,9 @@
 // projection p = W x covers four blocks (atlas.klimoza.dev, DeepSeek-V3.2-Exp
 // MoE block, "All 43 steps": c^KV = x W_DKV, k^pe = x W_KR, w = x W_w; the
 // indexer key projection wk and its k_norm from the nnterp deepseek_v32
-// module tree; the [512, 64] split of the joint down-projection from the
-// model.py excerpt on the same page):
+// module tree; the [512, 64] split of the joint down-projection, then the
+// latent norm and the key rotation, from the mla-kv excerpt of the atlas
+// "DeepSeek-V3.2-Exp · Attention input" page):
 //   c^KV = p[0:512]     -> RMSNorm (eps 1e-6) times the gain       -> kv row 0..511
 //   k^pe = p[512:576]   -> pair (2i, 2i+1) turned by the token's
 //                          angle i into dims i and i + 32           -> kv row 512..575
@@ -107,18 +108,17 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
 }
 
 // e of the ue8m0 scale 2^e of a block with largest magnitude amax: the
-// smallest integer with 448 2^e >= amax (0 for an all-zero block).  With
-// amax = M 2^E (1 <= M < 2) and 448 = 1.75 2^8: e = E - 8 when M <= 1.75,
-// else E - 7; subnormal maxima take the search.
+// smallest integer with 448 2^e >= amax (0 for an all-zero block), but not
+// below -127, the smallest scale the byte e + 127 can hold (a block whose
+// largest magnitude is under 448 2^-127 keeps that scale; its codes then
+// stay within range).  With amax = M 2^E (1 <= M < 2) and 448 = 1.75 2^8:
+// e = E - 8 when M <= 1.75, else E - 7.
 __device__ __forceinline__ int ue8m0_exponent(float amax) {
   if (!(amax > 0.f)) return 0;
   const uint32_t u = __float_as_uint(amax);
-  const int E = static_cast<int>(u >> 23) - 127;
-  if (E > -127) return E - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-  int e = ilogbf(amax) - 8;
-  while (e > -127 && ldexpf(448.0f, e - 1) >= amax) --e;
-  while (e < 127 && ldexpf(448.0f, e) < amax) ++e;
-  return e;
+  const int E = static_cast<int>(u >> 23) - 127;  // -127 for a subnormal amax
+  const int e = E - 8 + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : e;
 }
 
 // max over the wave's 64 lanes on lane moves (no LDS): xor 1 and 2 within
@@ -727,12 +727,7 @@ fill_rows(int N, int slices, const float* __restrict__ part, const float* __rest
     if ((tid & 63) == 0) red[tid >> 6] = amax;
     __syncthreads();
     amax = fmaxf(red[0], red[1]);
-    int e = 0;
-    if (amax > 0.f) {
-      e = ilogbf(amax) - 8;  // 448 = 1.75 2^8
-      while (e > -127 && ldexpf(448.0f, e - 1) >= amax) --e;
-      while (e < 127 && ldexpf(448.0f, e) < amax) ++e;
-    }
+    const int e = ue8m0_exponent(amax);
     if (slot >= 0 && tid < kFillIdx) {
       static_cast<uint8_t*>(k_cache)[slot * kFillIdx + tid] =
           static_cast<uint8_t>(e4m3_code(ldexpf(z, -e)));
@@ -828,12 +823,7 @@ q_rows(int N, int slices, const float* __restrict__ part, void* __restrict__ q_o
   const int64_t o = static_cast<int64_t>(n) * kQCols + col;
   if constexpr (QDT == DSA_FP8_E4M3) {
     const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-    int e = 0;
-    if (amax > 0.f) {
-      e = ilogbf(amax) - 8;
-      while (e > -127 && ldexpf(448.0f, e - 1) >= amax) --e;
-      while (e < 127 && ldexpf(448.0f, e) < amax) ++e;
-    }
+    const int e = ue8m0_exponent(amax);
     uint8_t* q = static_cast<uint8_t*>(q_out);
     q[o] = static_cast<uint8_t>(e4m3_code(ldexpf(v0, -e)));
     q[o + 1] = static_cast<uint8_t>(e4m3_code(ldexpf(v1, -e)));

@@ -11,16 +11,17 @@
 // selection, each row sums to one over it.)
 //
 // Kernels:
-//  * mla_mfma (H = 128, Dc = 512, Dr = 64, bf16): one workgroup of 8 waves
-//    takes one query row and one split of its index list.  All 128 heads share
-//    each gathered key tile: 32 selected rows are copied straight from global
-//    memory into LDS (row-major, swizzled) and read twice, directly for the
-//    logits and through transposing LDS reads for the value product.  Wave w
-//    owns heads 16w..16w+15: logits^T = K_tile . Q^T on MFMA (keys on M,
-//    heads on N), an online softmax in fp32 with exp2, and O^T += V^T . P^T on
-//    MFMA (latent dims on M, heads on N) with P^T taken straight from the
-//    logit accumulators.  A ring of 3 LDS tiles keeps the next tile's copies
-//    in flight during the current tile's MFMAs.
+//  * mla_mfma (H = 128, Dc = 512, Dr = 64, bf16): one workgroup of 4 waves
+//    (one per SIMD) takes one query row and one split of its index list.  All
+//    128 heads share each gathered tile of 32 selected key rows, copied
+//    straight from global memory into LDS (row-major, swizzled) and read
+//    twice: directly for the logits and through transposing LDS reads for the
+//    value product.  Wave w owns heads 32w..32w+31: logits^T = K_tile . Q^T on
+//    32x32x16 MFMAs (keys on M, heads on N), an online softmax in fp32 with
+//    exp2 against a fixed reference max, and O^T += V^T . P^T (latent dims on
+//    M, heads on N) with P^T taken straight from the logit accumulators.  A
+//    ring of 4 LDS tiles holds the tile of the value product, the tile of the
+//    logits and two tiles whose copies are in flight.
 //  * mla_combine: merges split partials (o_s, lse_s) with weights
 //    exp(lse_s - lse), deterministically (fixed split order, no atomics).
 //  * mla_generic: any shape, fp32 VALU loops, two passes over the index row.

@@ -248,3 +248,44 @@ def test_indexer_query_prefill_16384_sampled(dsa):
     n = rows.numel()
     ref = oracle.indexer_query(_bits(cq[rows]), _bits(wq)).reshape(n * 64, 128)
     _check_fp8(q[rows].cpu().numpy().reshape(n * 64, 128), q_sf[rows].cpu().numpy().reshape(n * 64), ref)
+
+
+@pytest.mark.parametrize("N", [32, 600])
+def test_e4m3_scale_floor(dsa, N):
+    """Rows whose largest magnitude lies below 448 2^-127: the ue8m0 scale byte
+    stops at 0 (2^-127, the smallest scale it holds) instead of wrapping, on
+    the GPU as in the oracle.  Cache fill: the indexer key's LayerNorm gain is
+    5e-37 (largest key values about 2e-36).  Indexer query: 8 nonzero hidden
+    dims per token holding small integers times 2^-62 and weights small
+    integers times 2^-62, so every product is a normal fp32 number and every
+    query value an exact multiple of 2^-124 below 448 2^-127.  N = 32 takes
+    the per-token quantisers, N = 600 the tiled projection's epilogue
+    (indexer query)."""
+    torch = U.torch()
+    print(f"[e4m3_scale_floor] N={N}", flush=True)
+    d = _draw(N, 256, 31 + N)
+    d["k_gamma"] = np.full(128, 5e-37, np.float32)
+    d["k_beta"] = np.zeros(128, np.float32)
+    slots = np.arange(N, dtype=np.int64)
+    _, k_c, k_sf, _ = _run(dsa, d, slots, N, torch.bfloat16, "fp8", torch.bfloat16)
+    _, rk, _ = oracle.cache_fill(d["x"], d["W"], d["kv_gamma"], d["k_gamma"], d["k_beta"],
+                                 d["cos"], d["sin"])
+    assert np.abs(rk).max() < 448.0 * 2.0 ** -127
+    sb = k_sf.cpu().numpy()
+    assert np.all(sb == 0), f"scale bytes {np.unique(sb)}"
+    _check_fp8(k_c.cpu().numpy(), sb, rk)
+    rng = np.random.default_rng(40 + N)
+    cqf = np.zeros((N, 1536), np.float32)
+    cqf[:, :8] = rng.integers(-2, 3, (N, 8)) * 2.0 ** -62
+    wqf = (rng.integers(-3, 4, (8192, 1536)) * 2.0 ** -62).astype(np.float32)
+    cq, wq = g.f32_to_bf16_bits(cqf), g.f32_to_bf16_bits(wqf)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.view(np.int16))).cuda().view(torch.bfloat16)
+    q, q_sf = dsa.dsa_indexer_query(t(cq), t(wq), q_dtype=torch.uint8)
+    torch.cuda.synchronize()
+    ref = oracle.indexer_query(cq, wq).reshape(N * 64, 128)
+    assert np.abs(ref).max() < 448.0 * 2.0 ** -127
+    qsf = q_sf.cpu().numpy().reshape(N * 64)
+    ref_codes, ref_sb = oracle.quantize_e4m3(ref)
+    nz = np.abs(ref).max(axis=1) > 0                     # all-zero rows keep scale byte 127
+    assert np.all(ref_sb[nz, 0] == 0) and np.array_equal(qsf, ref_sb[:, 0])
+    assert np.array_equal(q.cpu().numpy().reshape(N * 64, 128), ref_codes)

@@ -41,8 +41,9 @@ MUTANTS = {
                             "kv[ORC_FILL_LAT + ORC_FILL_ROPE / 2 + i] = b;"),
     "layernorm_bias_dropped": ("* k_gamma[i] + k_beta[i];", "* k_gamma[i];"),
     "layernorm_sample_variance": ("var /= ORC_FILL_IDX;", "var /= (ORC_FILL_IDX - 1);"),
-    "quant_scale_rounded_down": ("while (e > -127 && ldexp(448.0, e - 1) >= amax) --e;\n    while (e < 127 && ldexp(448.0, e) < amax) ++e;",
+    "quant_scale_rounded_down": ("while (ldexp(448.0, e - 1) >= amax) --e;\n    while (ldexp(448.0, e) < amax) ++e;",
                                  "e = (int)floor(log2(amax / 448.0));"),
+    "quant_scale_floor_dropped": ("if (e < -127) e = -127;", ""),
     "output_not_ascending": ("qsort(out, (size_t)take, sizeof(int32_t), by_value);", ""),
     "rotary_term_dropped": ("for (int32_t d = 0; d < D; ++d) /* latent part and rotary part together */",
                             "for (int32_t d = 0; d < sh->Dc; ++d)"),

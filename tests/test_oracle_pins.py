@@ -592,6 +592,22 @@ def test_quantize_e4m3_blocks(oracle_lib):
     assert sb.tolist() == [128]
     _, sb = oracle.quantize_e4m3(np.zeros(128))
     assert sb.tolist() == [127]
+    # the scale byte holds 2^(byte - 127) for bytes 0..254: a block whose
+    # largest magnitude lies below 448 2^-127 keeps the smallest scale, byte 0
+    # (the exponent would otherwise wrap the byte), and its codes stay finite
+    for amax in (1e-37, 3e-39, 1e-45, 448.0 * 2.0 ** -127):
+        blk = np.zeros(128)
+        blk[3] = -amax
+        blk[9] = amax / 3
+        codes, sb = oracle.quantize_e4m3(blk)
+        assert sb.tolist() == [0], (amax, sb)
+        c2, s2 = g.quantize_e4m3_blocks(blk.astype(np.float32))
+        assert np.array_equal(sb, s2) and np.array_equal(codes, c2)
+        assert codes[3] & 0x80 and (codes[3] & 0x7F) <= 0x7E
+    blk = np.zeros(128)
+    blk[0] = 448.0 * 2.0 ** -126                              # the largest scale-byte-1 block
+    _, sb = oracle.quantize_e4m3(blk)
+    assert sb.tolist() == [1]
 
 
 def test_indexer_query_is_the_matmul(oracle_lib):
