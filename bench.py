@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode_8k")
+    ap.add_argument("--workload", default="all",
+                    help="all (the four V3.2 workloads; decode_8k is the headline) or one workload")
     ap.add_argument("--replicas", type=int, default=0, help="input copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size (0 = auto)")
@@ -51,12 +52,15 @@ def parse():
 
 
 def algorithmic(cfg):
-    """Bytes each query must move and flops it must do (inputs read once,
-    outputs written once; scores and indices are intermediates)."""
+    """Bytes each query must move and flops it must do, averaged over the
+    workload's queries (inputs read once, outputs written once; scores and
+    indices are intermediates).  Query t of a sequence sees the keys
+    s <= q_pos(t) = S - T + t and attends over min(K, q_pos(t) + 1) of them."""
     e = {"bf16": 2, "f32": 4, "fp8": 1}
     ib, wb, mb = e[cfg.idx_dtype], e[cfg.w_dtype], e[cfg.mla_dtype]
-    causal_keys = cfg.S if cfg.T == 1 else (cfg.S - cfg.T) + (cfg.T + 1) / 2.0  # mean visible keys
-    sel = min(cfg.K_eff, causal_keys)
+    vis = [cfg.S - cfg.T + t + 1 for t in range(cfg.T)]
+    causal_keys = sum(vis) / cfg.T                          # mean visible keys
+    sel = sum(min(cfg.K_eff, v) for v in vis) / cfg.T       # mean selected keys
     nblk = cfg.DI // 128 if cfg.idx_dtype == "fp8" else 0
     idx_bytes = (cfg.S * cfg.DI * ib + cfg.S * nblk) / cfg.T + cfg.HI * cfg.DI * ib + cfg.HI * nblk + cfg.HI * wb
     mla_bytes = sel * cfg.D * mb + cfg.H * cfg.D * mb + cfg.H * cfg.Dc * mb
@@ -457,53 +461,36 @@ def bench_absorb(args):
     print(json.dumps(result))
 
 
-def main():
-    args = parse()
-    if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calibration_mib, args.workload)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
-    if args.workload in FILL_WORKLOADS:
-        bench_cache_fill(args)
-        return
-    if args.workload in ABSORB_WORKLOADS:
-        bench_absorb(args)
-        return
+PATH_WORKLOADS = ("decode_8k", "prefill_16k", "decode_128k", "decode_64k_fp8")
+
+
+def bench_path(cfg, args, steps, warmup, cpu):
+    """One workload of the hot path: `steps` timed dsa_forward calls after
+    `warmup` untimed ones, then the same steps with per-launch kernel timing,
+    and (cpu) the oracle on a bounded sample.  Returns the record."""
     import torch
 
-    import dsa_inputs as g
     import sparse_latent_attention_lightning_amd as dsa
     from dsa_inputs import device as U
 
-    cfg = g.CONFIGS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     shape = U.shape_of(cfg)
     print(f"[bench] workload {cfg.name}: {cfg}", file=sys.stderr, flush=True)
-
-    base = {n: U.upload(cfg, n, dev) for n in ("q_idx", "k_idx", "w", "q", "kv")}
-    if cfg.idx_dtype == "fp8":
-        base["q_idx"], base["q_sf"] = base["q_idx"]
-        base["k_idx"], base["k_sf"] = base["k_idx"]
-    else:
-        base["q_sf"] = base["k_sf"] = None
+    t_gen = time.perf_counter()
+    base = U.upload_all(cfg, dev)
     per_rep = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
     reps = args.replicas or max(2, min(8, int(1.0e9 // per_rep) + 1))
     replicas = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()}
                          for _ in range(reps - 1)]
-    print(f"[bench] {reps} input copies of {per_rep / 1e6:.0f} MB rotate through the timed loop",
-          file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    print(f"[bench] {reps} input copies of {per_rep / 1e6:.0f} MB rotate through the timed loop "
+          f"(drawn in {time.perf_counter() - t_gen:.1f} s)", file=sys.stderr, flush=True)
 
     ws = torch.zeros(dsa.workspace_bytes(shape, dsa.ENTRY_FORWARD), dtype=torch.uint8, device=dev)
     o = torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dc), dtype=base["q"].dtype, device=dev)
     lse = torch.empty((cfg.B, cfg.T, cfg.H), dtype=torch.float32, device=dev)
     idx = torch.empty((cfg.B, cfg.T, cfg.K_eff), dtype=torch.int32, device=dev)
-    scores = torch.empty((cfg.B, cfg.T, cfg.S), dtype=torch.float32, device=dev)
-    ws_topk = torch.zeros(max(1, dsa.workspace_bytes(shape, dsa.ENTRY_TOPK)), dtype=torch.uint8, device=dev)
-    ws_mla = torch.zeros(max(1, dsa.workspace_bytes(shape, dsa.ENTRY_SPARSE_MLA)), dtype=torch.uint8, device=dev)
 
     def step(i):
         x = replicas[i % reps]
@@ -512,14 +499,14 @@ def main():
 
     def run_indexer(i):
         x = replicas[i % reps]
-        dsa.dsa_indexer_scores(shape, x["q_idx"], x["k_idx"], x["w"], x["q_sf"], x["k_sf"], out=scores)
+        dsa.dsa_indexer_scores(shape, x["q_idx"], x["k_idx"], x["w"], x["q_sf"], x["k_sf"], out=run_indexer.scores)
 
     def run_topk(i):
-        dsa.dsa_topk(shape, scores, out=idx, ws=ws_topk)
+        dsa.dsa_topk(shape, run_indexer.scores, out=idx, ws=run_topk.ws)
 
     def run_mla(i):
         x = replicas[i % reps]
-        dsa.dsa_sparse_mla_fwd(shape, x["q"], x["kv"], idx, out=o, lse=lse, ws=ws_mla)
+        dsa.dsa_sparse_mla_fwd(shape, x["q"], x["kv"], idx, out=o, lse=lse, ws=run_mla.ws)
 
     def timed(fn, n, warm):
         for i in range(warm):
@@ -535,37 +522,30 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n  # ms
 
-    def copy_calibration():
-        if not args.copy_calibration:
-            return
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copied {args.copy_calibration} MiB 5 times", file=sys.stderr, flush=True)
-
     if args.only:
+        if args.only in ("indexer", "topk", "mla"):
+            run_indexer.scores = torch.empty((cfg.B, cfg.T, cfg.S), dtype=torch.float32, device=dev)
+            run_topk.ws = torch.zeros(max(1, dsa.workspace_bytes(shape, dsa.ENTRY_TOPK)), dtype=torch.uint8,
+                                      device=dev)
+            run_mla.ws = torch.zeros(max(1, dsa.workspace_bytes(shape, dsa.ENTRY_SPARSE_MLA)),
+                                     dtype=torch.uint8, device=dev)
         fn = {"forward": step, "indexer": run_indexer, "topk": run_topk, "mla": run_mla}[args.only]
         if args.only in ("topk", "mla"):
             run_indexer(0)
             run_topk(0)
-        ms = timed(fn, args.steps, args.warmup)
-        print(json.dumps({"only": args.only, "ms_per_call": ms}))
-        copy_calibration()
-        return
+        ms = timed(fn, steps, warmup)
+        return {"only": args.only, "workload": cfg.name, "ms_per_call": ms}
 
-    ms = timed(step, args.steps, args.warmup)
-    print(f"[bench] forward: {ms * 1e3:.1f} us per step", file=sys.stderr, flush=True)
+    ms = timed(step, steps, warmup)
+    print(f"[bench] {cfg.name} forward: {ms * 1e3:.1f} us per step", file=sys.stderr, flush=True)
 
-    # The same K steps once more with the library's kernel timing on: HIP
+    # The same steps once more with the library's kernel timing on: HIP
     # events around each kernel launch, recorded on the stream it runs on.
     dsa.dsa_timing_begin()
-    ms_timed = timed(step, args.steps, 0)
+    ms_timed = timed(step, steps, 0)
     kt = dsa.dsa_timing_end()
     for k, r in kt.items():
-        print(f"[bench] {k}: {r['avg_us']:.2f} us per launch ({r['launches']} launches)",
+        print(f"[bench] {cfg.name} {k}: {r['avg_us']:.2f} us per launch ({r['launches']} launches)",
               file=sys.stderr, flush=True)
 
     A = algorithmic(cfg)
@@ -588,7 +568,7 @@ def main():
     roof["algorithmic_per_launch"] = round(bytes_launch if decode else flops_launch)
     roof["traffic"] = counters_for(dom, cfg.name)
     # each stage of the path against its own bound (the attention stage is
-    # mla_mfma plus the split merge)
+    # every mla_* kernel of the step)
     stage_us = {"indexer": sum(r["avg_us"] for k, r in kt.items() if k.startswith("indexer")),
                 "topk": sum(r["avg_us"] for k, r in kt.items() if k.startswith("topk")),
                 "sparse_mla": sum(r["avg_us"] for k, r in kt.items() if k.startswith("mla"))}
@@ -599,37 +579,104 @@ def main():
     for k, v in stages.items():
         v["us"] = round(stage_us[k], 2)
     stages["topk"] = {"us": round(stage_us["topk"], 2), "bound": "alu"}
-
-    result = {
-        "metric": "indexer+sparse-MLA queries/sec",
+    rec = {
+        "workload": cfg.name,
         "value": round(value, 1),
         "unit": "queries/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if cfg.mla_dtype == "bf16" else "f32",
-        "data": "synthetic",
         "config": {"workload": cfg.name, "batch": cfg.B, "queries_per_seq": cfg.T, "keys": cfg.S,
                    "index_heads": cfg.HI, "index_dim": cfg.DI, "heads": cfg.H, "latent": cfg.Dc,
                    "rope": cfg.Dr, "topk": cfg.K, "idx_dtype": cfg.idx_dtype},
-        "step_hbm_frac": round(A["bytes"] * q / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "step_roofline": roofline(decode, A["bytes"] * q, A["flops"] * q, step_s),
         "step_tokens_per_s": round(value, 1),
         "kernel_us": {k: round(r["avg_us"], 2) for k, r in kt.items()},
         "ms_per_step_kernel_timing": round(ms_timed, 5),
         "stages": stages,
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    del replicas, base, ws
+    torch.cuda.empty_cache()
+    if cpu:
         # a bounded sample: about as many query x key pairs as 32 queries over
         # 8192 keys (decode: whole queries; prefill: 16 query rows)
         rows = args.cpu_rows or (max(1, min(cfg.B * cfg.T, 32 * 8192 // cfg.S)) if cfg.T == 1 else 16)
-        print(f"[bench] CPU oracle on {rows} queries ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, rows)
+        if cfg.idx_dtype == "fp8":
+            rows = args.cpu_rows or max(1, rows // 2)   # the oracle decodes e4m3 per element: slower
+        print(f"[bench] {cfg.name}: CPU oracle on {rows} queries ...", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, rows)
+    return rec
+
+
+def main():
+    args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calibration_mib, args.workload)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    if args.workload in FILL_WORKLOADS:
+        bench_cache_fill(args)
+        return
+    if args.workload in ABSORB_WORKLOADS:
+        bench_absorb(args)
+        return
+    import dsa_inputs as g
+
+    names = PATH_WORKLOADS if args.workload == "all" else (args.workload,)
+    recs = {}
+    for n in names:
+        cfg = g.CONFIGS[n]
+        # prefill steps take milliseconds: fewer of them keep the run short
+        steps = args.steps if cfg.T == 1 else max(3, min(args.steps, 10))
+        warmup = args.warmup if cfg.T == 1 else max(1, min(args.warmup, 3))
+        recs[n] = bench_path(cfg, args, steps, warmup, not args.no_cpu_baseline)
+        if args.only:
+            print(json.dumps(recs[n]))
+            if args.copy_calibration:
+                copy_calibration(args.copy_calibration)
+    if args.only:
+        return
+    head = recs[names[0]]
+    result = {
+        "metric": "indexer+sparse-MLA queries/sec",
+        "value": head["value"],
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": head["warmup"],
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": head["config"],
+    }
+    for k in ("step_roofline", "step_tokens_per_s", "kernel_us", "ms_per_step_kernel_timing", "stages",
+              "roofline", "cpu_baseline"):
+        if k in head:
+            result[k] = head[k]
+    if len(names) > 1:
+        result["workloads"] = {n: recs[n] for n in names[1:]}
     print(json.dumps(result))
+
+
+def copy_calibration(mib):
+    """Copy a `mib`-sized device buffer 5 times: the known-size kernel the
+    HBM counters are scaled by."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copied {mib} MiB 5 times", file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

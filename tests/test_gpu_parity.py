@@ -103,6 +103,13 @@ SCORE_CASES = {
                                                       integer=True),
     # e4m3, fewer keys than one chunk
     "fp8_int_short": g.CONFIGS["decode_64k_fp8"].replace(B=3, S=40, integer=True),
+    # e4m3 with many queries per sequence (a prefill chunk): 16 and 300
+    # queries over 1000 keys, every key chunk meeting the causal diagonal
+    "fp8_int_t16": g.CONFIGS["decode_64k_fp8"].replace(B=2, T=16, S=1000, integer=True),
+    "fp8_int_t300": g.CONFIGS["decode_64k_fp8"].replace(B=1, T=300, S=1000, integer=True),
+    # the same with fp32 head weights and a sequence length that is not a
+    # multiple of 4, real-valued
+    "fp8_real_t37": g.CONFIGS["decode_64k_fp8"].replace(B=2, T=37, S=517, w_dtype="f32"),
     # real-valued: within 1e-4 of the row max
     "decode_real": g.CONFIGS["decode_8k"].replace(B=2, S=3000),
     "fp8_real": g.CONFIGS["decode_64k_fp8"].replace(B=2, S=5000),
@@ -137,6 +144,8 @@ RAGGED_CASES = {
                    [4200, 2049, 64]),
     "prefill": (g.CONFIGS["prefill_16k"].replace(B=3, T=300, S=1000, integer=True),
                 [1000, 650, 100]),
+    "prefill_fp8": (g.CONFIGS["decode_64k_fp8"].replace(B=3, T=20, S=1000, integer=True),
+                    [1000, 500, 10]),
     "generic": (SCORE_CASES["generic_bf16"], [77, 30]),
 }
 
@@ -178,6 +187,13 @@ def _special_rows(S, K, rng):
     r[: S // 2] = -np.inf                                            # fewer than K selectable (for big K)
     rows.append(r)
     r = (rng.standard_normal(S) * 1e-30).astype(np.float32)          # subnormal-range values
+    rows.append(r)
+    r = rng.standard_normal(S).astype(np.float32)
+    r[rng.choice(S, size=min(S, 3), replace=False)] = np.inf        # a few +inf: always selected
+    rows.append(r)
+    r = rng.integers(-2, 3, S).astype(np.float32)
+    r[rng.random(S) < 0.5] = np.inf                                  # many tied +inf (lowest index wins)
+    r[rng.random(S) < 0.1] = np.nan
     rows.append(r)
     return np.stack(rows)
 
@@ -285,6 +301,78 @@ def test_mla_mfma_edge_indices(dsa):
     assert np.all(o[1] == 0) and np.all(np.isneginf(lse[1]))
 
 
+def _kv_log2_logit(cfg, q_row, kv_rows):
+    """sm_scale * q . kv_j in log2 units, fp64, for the keys kv_rows [n, D]."""
+    return cfg.softmax_scale * (kv_rows.astype(np.float64) @ q_row.astype(np.float64)) / math.log(2.0)
+
+
+def _plant_spikes(cfg, idx, q, kv, plants):
+    """Replace the key row selected at position j of query row r by 8 q[r, h]
+    (bf16): head h's logit for it then exceeds every other by far.  plants:
+    (query row, batch, position j, head, first position of j's split).
+    Returns the patched kv and, per plant, how far (log2 units) the spike's
+    logit lies above the largest logit, for its head, of the 32 positions that
+    open its split (the tile that sets the kernel's reference maximum)."""
+    kv = kv.copy()
+    for r, b, j, h, _ in plants:
+        s = int(idx[r, j])
+        kv[b, s] = g.f32_to_bf16_bits((8.0 * g.bf16_bits_to_f32(q[r, h])).astype(np.float32))
+    gaps = []
+    for r, b, j, h, first in plants:
+        qr = g.bf16_bits_to_f32(q[r, h])
+        keys = idx[r, first:first + 32]
+        keys = keys[keys >= 0]
+        ref = _kv_log2_logit(cfg, qr, g.bf16_bits_to_f32(kv[b, keys])).max()
+        spike = _kv_log2_logit(cfg, qr, g.bf16_bits_to_f32(kv[b, idx[r, j]][None]))[0]
+        gaps.append(spike - ref)
+    return kv, gaps
+
+
+@pytest.mark.parametrize("case", ["decode_split", "rows_window_reload"])
+def test_mla_softmax_restart(dsa, case):
+    """A selected key whose logit exceeds the largest logit of its split's
+    first tile by more than 2^32 (an attention-sink-like spike): the kernel's
+    fixed reference maximum no longer bounds the exponentials, so the split is
+    run again with its true maximum.  decode_split: the decode shape with 4
+    query rows (16 splits of 128 entries), spikes in late tiles of several
+    splits, one row without.  rows_window_reload: 256 query rows of 2048
+    selected keys each (no split; the index list passes through LDS in
+    windows of 1024 entries, so the second pass starts by reloading the
+    first window), spikes in the second window and in the first one.  The
+    definition is unchanged by the spike: softmax over the selection."""
+    torch = U.torch()
+    if case == "decode_split":
+        cfg = g.CONFIGS["decode_8k"].replace(B=4)
+        rows, split = cfg.B, 128
+        idx = _random_idx(cfg, np.random.default_rng(41))
+        # (row, batch, position, head); the first tile of each split starts at
+        # the split's first position
+        plants = [(0, 0, 70, 5), (1, 1, 5 * 128 + 100, 77), (2, 2, 2047, 127)]
+    else:
+        cfg = g.CONFIGS["prefill_16k"].replace(B=1, T=256, S=4096)
+        rows, split = cfg.T, cfg.K_eff
+        idx = _random_idx(cfg, np.random.default_rng(42))
+        plants = [(3, 0, 1500, 0), (200, 0, 40, 64), (255, 0, 2047, 100)]
+    print(f"[mla_softmax_restart] {case}: {cfg}", flush=True)
+    q = g.full(cfg, "q").reshape(rows, cfg.H, cfg.D)
+    kv = g.full(cfg, "kv")
+    kv, gaps = _plant_spikes(cfg, idx, q, kv, [p + (p[2] // split * split,) for p in plants])
+    assert min(gaps) > 32.0, f"spikes do not reach the restart condition: {gaps}"
+    dev_q = U.to_dev(q.reshape(cfg.B, cfg.T, cfg.H, cfg.D), "bf16")
+    dev_kv = U.to_dev(kv, "bf16")
+    o, lse = dsa.dsa_sparse_mla_fwd(U.shape_of(cfg), dev_q, dev_kv,
+                                    torch.from_numpy(idx.reshape(cfg.B, cfg.T, -1)).cuda())
+    o = g.bf16_bits_to_f32(U.dev_to_np(o, "bf16")).reshape(rows, cfg.H, cfg.Dc)
+    lse = lse.cpu().numpy().reshape(rows, cfg.H)
+    rb, _ = _rows(cfg)
+    ro, rl = oracle.sparse_mla(cfg, rb, q, kv, idx)
+    U.assert_rows_close(o, ro, U.RTOL["bf16"], what=f"{case} o")
+    assert np.all(np.abs(lse - rl) <= U.RTOL["bf16"] * np.maximum(1, np.abs(rl)))
+    for r, b, j, h in plants:  # the spike's head puts (almost) all its weight on the spike
+        spike = g.bf16_bits_to_f32(kv[b, idx[r, j], :cfg.Dc])
+        assert np.abs(o[r, h] - spike).max() <= U.RTOL["bf16"] * np.abs(spike).max()
+
+
 def test_mla_generic_bf16(dsa):
     cfg = SCORE_CASES["generic_bf16"]
     rb, _ = _rows(cfg)
@@ -388,3 +476,67 @@ def test_forward_decode(dsa, case):
     o = g.bf16_bits_to_f32(U.dev_to_np(o, "bf16")).reshape(rows, cfg.H, cfg.Dc)
     U.assert_rows_close(o, ro, U.RTOL["bf16"], f"{case} o")
     np.testing.assert_allclose(lse.cpu().numpy().reshape(rows, cfg.H), rl, rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("name", ["decode_8k", "decode_128k", "decode_64k_fp8"])
+def test_forward_bitwise_deterministic(dsa, name):
+    """dsa_forward at the full decode shapes, twice on the same inputs, the
+    second time with the workspace filled with random bytes: o, lse and the
+    selection are identical bit for bit (fixed reduction orders everywhere, no
+    atomics in the arithmetic, nothing read from the workspace before the call
+    writes it).  Inputs are drawn on the GPU from a seeded generator."""
+    torch = U.torch()
+    cfg = g.CONFIGS[name]
+    print(f"[forward_deterministic] {name}: {cfg}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(17)
+    bf = lambda *shape: torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16)
+    if cfg.idx_dtype == "fp8":
+        q_idx = torch.randint(0, 0x7F, (cfg.B, cfg.T, cfg.HI, cfg.DI), generator=gen, device="cuda",
+                              dtype=torch.uint8) | (torch.randint(0, 2, (cfg.B, cfg.T, cfg.HI, cfg.DI),
+                                                    generator=gen, device="cuda", dtype=torch.uint8) << 7)
+        k_idx = torch.randint(0, 0x7F, (cfg.B, cfg.S, cfg.DI), generator=gen, device="cuda",
+                              dtype=torch.uint8)
+        q_sf = torch.randint(120, 130, (cfg.B, cfg.T, cfg.HI, 1), generator=gen, device="cuda",
+                             dtype=torch.uint8)
+        k_sf = torch.randint(120, 130, (cfg.B, cfg.S, 1), generator=gen, device="cuda", dtype=torch.uint8)
+    else:
+        q_idx, k_idx = bf(cfg.B, cfg.T, cfg.HI, cfg.DI), bf(cfg.B, cfg.S, cfg.DI)
+        q_sf = k_sf = None
+    w = bf(cfg.B, cfg.T, cfg.HI)
+    q, kv = bf(cfg.B, cfg.T, cfg.H, cfg.D), bf(cfg.B, cfg.S, cfg.D)
+    shape = U.shape_of(cfg)
+    ws = torch.zeros(dsa.workspace_bytes(shape, dsa.ENTRY_FORWARD), dtype=torch.uint8, device="cuda")
+    o1, l1, i1 = dsa.dsa_forward(shape, q_idx, k_idx, w, q, kv, q_sf, k_sf, ws=ws)
+    o1, l1, i1 = o1.clone(), l1.clone(), i1.clone()
+    ws.copy_(torch.randint(0, 256, ws.shape, generator=gen, device="cuda", dtype=torch.uint8))
+    o2, l2, i2 = dsa.dsa_forward(shape, q_idx, k_idx, w, q, kv, q_sf, k_sf, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2), "selection differs between runs"
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "o differs between runs"
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), "lse differs between runs"
+    assert bool((i1 >= 0).all()), "every decode row selects K keys"
+
+
+def test_binding_rejects_bad_outputs(dsa):
+    """The binding checks caller-supplied outputs and workspaces of
+    dsa_forward before anything reaches the library (no launch happens)."""
+    torch = U.torch()
+    cfg = g.CONFIGS["decode_8k"].replace(B=2, S=3000)
+    x = _inputs(cfg)
+    shape = U.shape_of(cfg)
+    args = (shape, x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"])
+    bad = [
+        dict(out=torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dc - 1), dtype=torch.bfloat16, device="cuda")),
+        dict(out=torch.empty((cfg.B, cfg.T, cfg.H, cfg.Dc), dtype=torch.float32, device="cuda")),
+        dict(idx_out=torch.empty((cfg.B, cfg.T, cfg.K_eff - 1), dtype=torch.int32, device="cuda")),
+        dict(idx_out=torch.empty((cfg.B, cfg.T, cfg.K_eff), dtype=torch.int64, device="cuda")),
+        dict(lse=torch.empty((cfg.B, cfg.T, cfg.H), dtype=torch.bfloat16, device="cuda")),
+        dict(lse=torch.empty((cfg.B, cfg.T, cfg.H + 1), dtype=torch.float32, device="cuda")),
+        dict(ws=torch.empty(dsa.workspace_bytes(shape, dsa.ENTRY_FORWARD) // 4 + 1, dtype=torch.float32,
+                            device="cuda")),
+        dict(ws=torch.empty(2 * dsa.workspace_bytes(shape, dsa.ENTRY_FORWARD), dtype=torch.uint8,
+                            device="cuda")[::2]),
+    ]
+    for kw in bad:
+        with pytest.raises((ValueError, TypeError)):
+            dsa.dsa_forward(*args, **kw)
