@@ -171,6 +171,30 @@ dsa_status_t dsa_forward_ragged(const dsa_shape_t* shape, const int32_t* seq_len
                                 size_t ws_bytes, void* stream);
 
 /*
+ * dsa_forward for callers that cannot allocate device memory (code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation with no ws argument.  Its scratch (the
+ * scores, the selection when idx_out is NULL, the later steps' scratch) lives
+ * in a device array that the library itself holds on every GPU it runs on:
+ * 64 MiB (67108864 bytes), reserved when the library's code is loaded on that
+ * GPU and kept until the process ends.  The call allocates nothing.
+ *   - A shape whose dsa_workspace_bytes(shape, DSA_ENTRY_FORWARD) exceeds
+ *     64 MiB returns DSA_ERR_WORKSPACE before any launch (every decode
+ *     workload of the V3.2 shapes fits; a long prefill's [T, S] scores do not).
+ *   - All calls on one GPU share that GPU's array: calls that may overlap on
+ *     one GPU (several host threads, or several streams without an ordering
+ *     between them) race and give undefined results.  Calls ordered on one
+ *     stream are safe; nothing carries over from one call to the next.
+ *   - The first call on a GPU looks up the array's device address
+ *     (DSA_ERR_HIP if the runtime cannot give it).
+ * Other arguments, results and errors as dsa_forward.
+ */
+dsa_status_t dsa_forward_noalloc(const dsa_shape_t* shape, const void* q_idx,
+                                 const uint8_t* q_sf, const void* k_idx, const uint8_t* k_sf,
+                                 const void* w, const void* q, const void* kv,
+                                 int32_t* idx_out, void* o, float* lse, void* stream);
+
+/*
  * Cache fill and indexer inputs for N new tokens, the step before the path
  * (atlas.klimoza.dev, DeepSeek-V3.2-Exp MoE block, "All 43 steps": c^KV =
  * x W_DKV and its RMSNorm, k^pe = x W_KR rotated, w = x W_w; the indexer key

@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.dsa_sparse_mla_fwd.argtypes = [sp, P, P, P, P, P, P, sz, P]
         L.dsa_forward.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.dsa_forward_ragged.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.dsa_forward_noalloc.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P]
         i32 = ctypes.c_int32
         L.dsa_cache_fill.argtypes = [i32, i32] + [P] * 8 + [i32, P, i32, P, P, i32, P, P, sz, P]
         L.dsa_cache_fill.restype = ctypes.c_int
@@ -95,7 +96,7 @@ def lib() -> ctypes.CDLL:
         L.dsa_output_projection_workspace_bytes.argtypes = [i32, i32, i32]
         L.dsa_output_projection_workspace_bytes.restype = sz
         for f in ("dsa_indexer_scores", "dsa_indexer_scores_ragged", "dsa_topk",
-                  "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged"):
+                  "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged", "dsa_forward_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_bytes.argtypes = [sp, ctypes.c_int32]
         L.dsa_workspace_bytes.restype = ctypes.c_size_t
@@ -305,6 +306,32 @@ def dsa_forward_ragged(shape: DsaShape, seq_lens, q_idx, k_idx, w, q, kv, q_sf=N
                                         _ptr(q_sf), _ptr(k_idx), _ptr(k_sf), _ptr(w), _ptr(q),
                                         _ptr(kv), _ptr(idx_out), _ptr(out), _ptr(lse), _ptr(ws),
                                         nws, _stream(dev)))
+    return out, lse, idx_out
+
+
+def dsa_forward_noalloc(shape: DsaShape, q_idx, k_idx, w, q, kv, q_sf=None, k_sf=None,
+                        want_idx: bool = True, want_lse: bool = True,
+                        out: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None):
+    """The whole hot path on the library's own scratch (no workspace; the C
+    call allocates nothing): (o, lse or None, idx or None).  Outputs not
+    given are allocated here, before the call."""
+    dev = _check_indexer(shape, q_idx, k_idx, w, q_sf, k_sf)
+    _check_mla(shape, q, kv, None)
+    if out is None:
+        out = torch.empty((shape.B, shape.T, shape.H, shape.Dc), dtype=q.dtype, device=dev)
+    _req(out, "o", (shape.B, shape.T, shape.H, shape.Dc), (q.dtype,), dev)
+    if idx_out is None and want_idx:
+        idx_out = torch.empty((shape.B, shape.T, shape.K_eff), dtype=torch.int32, device=dev)
+    if idx_out is not None:
+        _req(idx_out, "idx_out", (shape.B, shape.T, shape.K_eff), (torch.int32,), dev)
+    if lse is None and want_lse:
+        lse = torch.empty((shape.B, shape.T, shape.H), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _req(lse, "lse", (shape.B, shape.T, shape.H), (torch.float32,), dev)
+    _check(lib().dsa_forward_noalloc(ctypes.byref(shape), _ptr(q_idx), _ptr(q_sf), _ptr(k_idx),
+                                     _ptr(k_sf), _ptr(w), _ptr(q), _ptr(kv), _ptr(idx_out),
+                                     _ptr(out), _ptr(lse), _stream(dev)))
     return out, lse, idx_out
 
 

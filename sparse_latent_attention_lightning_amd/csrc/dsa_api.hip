@@ -127,6 +127,65 @@ dsa_status_t check_launch(const char* what) {
   return DSA_OK;
 }
 
+size_t forward_workspace_bytes(const dsa_shape_t& s) { return forward_layout(s).total; }
+
+// The whole path on a workspace of forward_workspace_bytes(s) bytes at `base`
+// (the shape is checked, the workspace size is the caller's business).
+dsa_status_t forward_on(const dsa_shape_t& s, const int32_t* seq_lens, const void* q_idx,
+                        const uint8_t* q_sf, const void* k_idx, const uint8_t* k_sf, const void* w,
+                        const void* q, const void* kv, int32_t* idx_out, void* o, float* lse,
+                        char* base, hipStream_t hs) {
+  dsa_status_t st;
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
+  const ForwardLayout L = forward_layout(s);
+  float* scores = reinterpret_cast<float*>(base + L.scores);
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx);
+  if ((st = check_indexer_args(s, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
+  if ((st = check_mla_args(q, kv, idx, o)) != DSA_OK) return st;
+  if ((st = launch_indexer(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, hs)) != DSA_OK)
+    return st;
+  if ((st = launch_topk(s, scores, idx, base + L.topk_ws, L.mla_ws - L.topk_ws, hs)) != DSA_OK)
+    return st;
+  return launch_sparse_mla(s, q, kv, idx, o, lse, base + L.mla_ws, L.total - L.mla_ws, hs);
+}
+
+// ---- the library's own scratch memory (dsa_forward_noalloc) ---------------
+// A file-scope device array: every GPU the library runs on holds its own copy
+// (kNoallocScratchBytes) from the library's load until the process ends.  In
+// host code `noalloc_scratch` names only a host-side stand-in; the device
+// address of a GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address is handed to
+// kernels.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t noalloc_scratch[kNoallocScratchBytes];
+
+namespace {
+// the device address of `noalloc_scratch` on the current device (nullptr and
+// the error recorded when the runtime cannot give it)
+char* noalloc_scratch_ptr() {
+  static std::mutex mu;
+  static std::vector<char*> ptrs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    fail(DSA_ERR_HIP, "forward_noalloc: hipGetDevice failed");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<size_t>(dev) >= ptrs.size()) ptrs.resize(dev + 1, nullptr);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+    if (e != hipSuccess || p == nullptr) {
+      fail(DSA_ERR_HIP, "forward_noalloc: hipGetSymbolAddress of the scratch array: %s",
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    ptrs[dev] = static_cast<char*>(p);
+  }
+  return ptrs[dev];
+}
+}  // namespace
+
 // ---- kernel timing sessions ----------------------------------------------
 namespace {
 constexpr size_t kTimingCap = 65536;
@@ -272,24 +331,13 @@ dsa_status_t dsa_forward_ragged(const dsa_shape_t* shape, const int32_t* seq_len
   g_last_error[0] = '\0';
   dsa_status_t st = check_shape(shape);
   if (st != DSA_OK) return st;
-  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
-  const dsa_shape_t& s = *shape;
-  const ForwardLayout L = forward_layout(s);
+  const ForwardLayout L = forward_layout(*shape);
   if (ws == nullptr || ws_bytes < L.total)
     return fail(DSA_ERR_WORKSPACE, "forward: workspace of %zu bytes needed, %zu given", L.total,
                 ws_bytes);
   if (!aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
-  char* base = static_cast<char*>(ws);
-  float* scores = reinterpret_cast<float*>(base + L.scores);
-  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx);
-  if ((st = check_indexer_args(s, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
-  if ((st = check_mla_args(q, kv, idx, o)) != DSA_OK) return st;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if ((st = launch_indexer(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, hs)) != DSA_OK)
-    return st;
-  if ((st = launch_topk(s, scores, idx, base + L.topk_ws, L.mla_ws - L.topk_ws, hs)) != DSA_OK)
-    return st;
-  return launch_sparse_mla(s, q, kv, idx, o, lse, base + L.mla_ws, L.total - L.mla_ws, hs);
+  return forward_on(*shape, seq_lens, q_idx, q_sf, k_idx, k_sf, w, q, kv, idx_out, o, lse,
+                    static_cast<char*>(ws), static_cast<hipStream_t>(stream));
 }
 
 dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx, const uint8_t* q_sf,
@@ -298,6 +346,23 @@ dsa_status_t dsa_forward(const dsa_shape_t* shape, const void* q_idx, const uint
                          size_t ws_bytes, void* stream) {
   return dsa_forward_ragged(shape, nullptr, q_idx, q_sf, k_idx, k_sf, w, q, kv, idx_out, o, lse,
                             ws, ws_bytes, stream);
+}
+
+dsa_status_t dsa_forward_noalloc(const dsa_shape_t* shape, const void* q_idx, const uint8_t* q_sf,
+                                 const void* k_idx, const uint8_t* k_sf, const void* w, const void* q,
+                                 const void* kv, int32_t* idx_out, void* o, float* lse, void* stream) {
+  g_last_error[0] = '\0';
+  dsa_status_t st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  const size_t need = forward_workspace_bytes(*shape);
+  if (need > kNoallocScratchBytes)
+    return fail(DSA_ERR_WORKSPACE,
+                "forward_noalloc: this shape needs %zu bytes of scratch; the library's own scratch "
+                "holds %zu (use dsa_forward with a workspace)", need, kNoallocScratchBytes);
+  char* base = noalloc_scratch_ptr();
+  if (base == nullptr) return DSA_ERR_HIP;
+  return forward_on(*shape, nullptr, q_idx, q_sf, k_idx, k_sf, w, q, kv, idx_out, o, lse, base,
+                    static_cast<hipStream_t>(stream));
 }
 
 dsa_status_t dsa_cache_fill(int32_t N, int32_t D, const void* x, const void* W,

@@ -76,6 +76,15 @@ dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const
                                int w_dtype, void* w_out, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
+// ---- the whole path ------------------------------------------------------
+// Workspace bytes of dsa_forward, and the path on such a workspace at `base`
+// (shape already checked; pointers, alignment and seq_lens checked here).
+size_t forward_workspace_bytes(const dsa_shape_t& s);
+dsa_status_t forward_on(const dsa_shape_t& s, const int32_t* seq_lens, const void* q_idx,
+                        const uint8_t* q_sf, const void* k_idx, const uint8_t* k_sf, const void* w,
+                        const void* q, const void* kv, int32_t* idx_out, void* o, float* lse,
+                        char* base, hipStream_t stream);
+
 // ---- sparse latent attention ------------------------------------------
 size_t mla_workspace_bytes(const dsa_shape_t& s);
 dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* kv,
