@@ -597,6 +597,27 @@ def bench_path(cfg, args, steps, warmup, cpu):
         "stages": stages,
         "roofline": roof,
     }
+    if cfg.T < 8 and cfg.S <= 262144:
+        # the fused index scores -> top-K launch against the two launches
+        # dsa_forward uses, on the same inputs
+        scores = torch.empty((cfg.B, cfg.T, cfg.S), dtype=torch.float32, device=dev)
+        ws_tk = torch.zeros(max(1, dsa.workspace_bytes(shape, dsa.ENTRY_TOPK)), dtype=torch.uint8, device=dev)
+        ws_it = torch.zeros(dsa.workspace_bytes(shape, dsa.ENTRY_INDEXER_TOPK), dtype=torch.uint8, device=dev)
+
+        def fused(i):
+            x = replicas[i % reps]
+            dsa.dsa_indexer_topk(shape, x["q_idx"], x["k_idx"], x["w"], x["q_sf"], x["k_sf"], out=idx, ws=ws_it)
+
+        def separate(i):
+            x = replicas[i % reps]
+            dsa.dsa_indexer_scores(shape, x["q_idx"], x["k_idx"], x["w"], x["q_sf"], x["k_sf"], out=scores)
+            dsa.dsa_topk(shape, scores, out=idx, ws=ws_tk)
+
+        rec["indexer_topk_us"] = {"fused": round(1e3 * timed(fused, steps, warmup), 2),
+                                  "separate": round(1e3 * timed(separate, steps, warmup), 2)}
+        print(f"[bench] {cfg.name} index scores + top-K: fused {rec['indexer_topk_us']['fused']} us, "
+              f"separate {rec['indexer_topk_us']['separate']} us", file=sys.stderr, flush=True)
+        del scores, ws_tk, ws_it
     del replicas, base, ws
     torch.cuda.empty_cache()
     if cpu:
@@ -658,7 +679,7 @@ def main():
         "config": head["config"],
     }
     for k in ("step_roofline", "step_tokens_per_s", "kernel_us", "ms_per_step_kernel_timing", "stages",
-              "roofline", "cpu_baseline"):
+              "indexer_topk_us", "roofline", "cpu_baseline"):
         if k in head:
             result[k] = head[k]
     if len(names) > 1:

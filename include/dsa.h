@@ -74,7 +74,8 @@ typedef struct {
 typedef enum {
   DSA_ENTRY_TOPK = 0,
   DSA_ENTRY_SPARSE_MLA = 1,
-  DSA_ENTRY_FORWARD = 2
+  DSA_ENTRY_FORWARD = 2,
+  DSA_ENTRY_INDEXER_TOPK = 3
 } dsa_entry_t;
 
 /*
@@ -125,6 +126,30 @@ dsa_status_t dsa_indexer_scores_ragged(const dsa_shape_t* shape, const int32_t* 
  */
 dsa_status_t dsa_topk(const dsa_shape_t* shape, const float* scores, int32_t* idx,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Index scores and top-K selection in one launch, for decode (the fused
+ * streaming indexer -> top-K; the steps S^I + M and M^sel of the atlas
+ * DeepSeek-V3.2-Exp MoE-block step list, layout from the nnterp deepseek_v32
+ * page, section 03).  Covers the V3.2 indexer (HI = 64, DI = 128, BF16 or
+ * FP8_E4M3 keys) with fewer than 8 queries per sequence and S <= 262144;
+ * other shapes return DSA_ERR_UNSUPPORTED before any launch.
+ *   q_idx, q_sf, k_idx, k_sf, w: as dsa_indexer_scores
+ *   seq_lens: as dsa_indexer_scores_ragged (NULL: every sequence holds S keys)
+ *   idx [B, T, K_eff] int32 output: exactly dsa_topk of the scores
+ *       dsa_indexer_scores would give (same order, ties, padding)
+ * ws: at least dsa_workspace_bytes(shape, DSA_ENTRY_INDEXER_TOPK) bytes; the
+ * row scores ([B, T, S] fp32 at its start) stay there after the call, the
+ * rest holds per-row counters and histograms, valid whatever the workspace
+ * held before.  Calls sharing one workspace must not overlap.  Each key
+ * block's workgroup stores its scores and adds its block's histogram to its
+ * row's; the last one of the row selects (its row's scores are read back
+ * once more, from the caches).
+ */
+dsa_status_t dsa_indexer_topk(const dsa_shape_t* shape, const int32_t* seq_lens,
+                              const void* q_idx, const uint8_t* q_sf, const void* k_idx,
+                              const uint8_t* k_sf, const void* w, int32_t* idx, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /*
  * Sparse latent attention in absorbed form over the listed keys.

@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
-ENTRY_TOPK, ENTRY_SPARSE_MLA, ENTRY_FORWARD = 0, 1, 2
+ENTRY_TOPK, ENTRY_SPARSE_MLA, ENTRY_FORWARD, ENTRY_INDEXER_TOPK = 0, 1, 2, 3
 STATUS = {0: "DSA_OK", 1: "DSA_ERR_INVALID_ARG", 2: "DSA_ERR_UNSUPPORTED",
           3: "DSA_ERR_WORKSPACE", 4: "DSA_ERR_HIP"}
 
@@ -77,6 +77,7 @@ def lib() -> ctypes.CDLL:
         L.dsa_forward.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.dsa_forward_ragged.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.dsa_forward_noalloc.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P]
+        L.dsa_indexer_topk.argtypes = [sp, P, P, P, P, P, P, P, P, sz, P]
         i32 = ctypes.c_int32
         L.dsa_cache_fill.argtypes = [i32, i32] + [P] * 8 + [i32, P, i32, P, P, i32, P, P, sz, P]
         L.dsa_cache_fill.restype = ctypes.c_int
@@ -96,7 +97,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_output_projection_workspace_bytes.argtypes = [i32, i32, i32]
         L.dsa_output_projection_workspace_bytes.restype = sz
         for f in ("dsa_indexer_scores", "dsa_indexer_scores_ragged", "dsa_topk",
-                  "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged", "dsa_forward_noalloc"):
+                  "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged", "dsa_forward_noalloc",
+                  "dsa_indexer_topk"):
             getattr(L, f).restype = ctypes.c_int
         L.dsa_workspace_bytes.argtypes = [sp, ctypes.c_int32]
         L.dsa_workspace_bytes.restype = ctypes.c_size_t
@@ -227,6 +229,25 @@ def dsa_indexer_scores_ragged(shape: DsaShape, seq_lens, q_idx, k_idx, w, q_sf=N
     _check(lib().dsa_indexer_scores_ragged(ctypes.byref(shape), _ptr(seq_lens), _ptr(q_idx),
                                            _ptr(q_sf), _ptr(k_idx), _ptr(k_sf), _ptr(w), _ptr(out),
                                            _stream(dev)))
+    return out
+
+
+def dsa_indexer_topk(shape: DsaShape, q_idx, k_idx, w, q_sf=None, k_sf=None, seq_lens=None,
+                     out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Index scores and top-K in one launch (decode shapes): idx [B, T, K_eff]
+    int32, exactly dsa_topk of dsa_indexer_scores.  The row scores remain at
+    the start of ws ([B, T, S] fp32)."""
+    dev = _check_indexer(shape, q_idx, k_idx, w, q_sf, k_sf)
+    if seq_lens is not None:
+        _seq_lens(shape, seq_lens, dev)
+    if out is None:
+        out = torch.empty((shape.B, shape.T, shape.K_eff), dtype=torch.int32, device=dev)
+    _req(out, "idx", (shape.B, shape.T, shape.K_eff), (torch.int32,), dev)
+    if ws is None:
+        ws = _workspace(shape, ENTRY_INDEXER_TOPK, dev)
+    _check(lib().dsa_indexer_topk(ctypes.byref(shape), _ptr(seq_lens), _ptr(q_idx), _ptr(q_sf),
+                                  _ptr(k_idx), _ptr(k_sf), _ptr(w), _ptr(out), _ptr(ws),
+                                  _ws_bytes(ws, dev), _stream(dev)))
     return out
 
 

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <random>
 #include <utility>
 #include <vector>
 
@@ -96,6 +97,8 @@ dsa_status_t check_mla_args(const void* q, const void* kv, const int32_t* idx, c
   return DSA_OK;
 }
 
+// dsa_forward's workspace: the scores, the selection (when idx_out is NULL),
+// the top-K's scratch, then the attention's scratch
 struct ForwardLayout {
   size_t scores, idx, topk_ws, mla_ws, total;
 };
@@ -109,6 +112,25 @@ ForwardLayout forward_layout(const dsa_shape_t& s) {
   L.mla_ws = L.topk_ws + align_up(topk_workspace_bytes(s));
   L.total = L.mla_ws + align_up(mla_workspace_bytes(s));
   return L;
+}
+
+// dsa_indexer_topk's workspace: the scores, then the per-row state
+size_t indexer_topk_scores_bytes(const dsa_shape_t& s) {
+  return align_up(static_cast<size_t>(s.B) * s.T * s.S * sizeof(float));
+}
+size_t indexer_topk_total_bytes(const dsa_shape_t& s) {
+  return indexer_topk_scores_bytes(s) + align_up(indexer_select_workspace_bytes(s));
+}
+
+// A tag per call of the fused selection: distinct across calls of this
+// process (a random start plus a counter), 39 bits.
+uint64_t next_call_tag() {
+  static std::atomic<uint64_t> counter{0};
+  static const uint64_t salt = [] {
+    std::random_device rd;
+    return (static_cast<uint64_t>(rd()) << 32) ^ rd();
+  }();
+  return (salt + counter.fetch_add(1, std::memory_order_relaxed)) & ((uint64_t(1) << 39) - 1);
 }
 
 }  // namespace
@@ -311,6 +333,33 @@ dsa_status_t dsa_topk(const dsa_shape_t* shape, const float* scores, int32_t* id
   return launch_topk(*shape, scores, idx, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+dsa_status_t dsa_indexer_topk(const dsa_shape_t* shape, const int32_t* seq_lens,
+                              const void* q_idx, const uint8_t* q_sf, const void* k_idx,
+                              const uint8_t* k_sf, const void* w, int32_t* idx, void* ws,
+                              size_t ws_bytes, void* stream) {
+  g_last_error[0] = '\0';
+  dsa_status_t st = check_shape(shape);
+  if (st != DSA_OK) return st;
+  const dsa_shape_t& s = *shape;
+  if (!indexer_select_applies(s))
+    return fail(DSA_ERR_UNSUPPORTED,
+                "indexer_topk: covers HI = 64, DI = 128, BF16 or FP8 keys, T < 8 and S <= 262144 "
+                "(got HI = %d, DI = %d, T = %d, S = %d)", s.HI, s.DI, s.T, s.S);
+  const size_t ws_need = indexer_topk_total_bytes(s);
+  if (ws == nullptr || ws_bytes < ws_need)
+    return fail(DSA_ERR_WORKSPACE, "indexer_topk: workspace of %zu bytes needed, %zu given", ws_need,
+                ws_bytes);
+  if (!aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
+  if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base);
+  if ((st = check_indexer_args(s, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
+  if ((st = need(idx, "idx")) != DSA_OK) return st;
+  return launch_indexer_select(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, idx,
+                               base + indexer_topk_scores_bytes(s), next_call_tag(),
+                               static_cast<hipStream_t>(stream));
+}
+
 dsa_status_t dsa_sparse_mla_fwd(const dsa_shape_t* shape, const void* q, const void* kv,
                                 const int32_t* idx, void* o, float* lse, void* ws,
                                 size_t ws_bytes, void* stream) {
@@ -496,6 +545,12 @@ size_t dsa_workspace_bytes(const dsa_shape_t* shape, int32_t entry) {
     case DSA_ENTRY_TOPK: return topk_workspace_bytes(*shape);
     case DSA_ENTRY_SPARSE_MLA: return mla_workspace_bytes(*shape);
     case DSA_ENTRY_FORWARD: return forward_layout(*shape).total;
+    case DSA_ENTRY_INDEXER_TOPK:
+      if (!indexer_select_applies(*shape)) {
+        fail(DSA_ERR_UNSUPPORTED, "indexer_topk does not cover this shape");
+        return static_cast<size_t>(-1);
+      }
+      return indexer_topk_total_bytes(*shape);
   }
   fail(DSA_ERR_INVALID_ARG, "unknown entry %d", entry);
   return static_cast<size_t>(-1);

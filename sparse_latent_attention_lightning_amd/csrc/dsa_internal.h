@@ -47,6 +47,17 @@ dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8
                             const void* k_idx, const uint8_t* k_sf, const void* w,
                             const int32_t* seq_lens, float* scores, hipStream_t stream);
 
+// The index scores with the top-K selection fused in (decode: fewer than 8
+// queries per sequence, V3.2 indexer shapes): scores go to `scores` (scratch),
+// the selection to idx [rows, K_eff]; sel_ws holds the per-row meeting state
+// and histograms (indexer_select_workspace_bytes), tag is the call's own.
+bool indexer_select_applies(const dsa_shape_t& s);
+size_t indexer_select_workspace_bytes(const dsa_shape_t& s);
+dsa_status_t launch_indexer_select(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
+                                   const void* k_idx, const uint8_t* k_sf, const void* w,
+                                   const int32_t* seq_lens, float* scores, int32_t* idx,
+                                   void* sel_ws, uint64_t tag, hipStream_t stream);
+
 // ---- top-k -------------------------------------------------------------
 size_t topk_workspace_bytes(const dsa_shape_t& s);
 dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,

@@ -19,6 +19,7 @@
 // swaps finish the 64-head reduction.
 #include "dsa_device.h"
 #include "dsa_internal.h"
+#include "select_row.h"
 
 namespace dsa {
 namespace {
@@ -332,13 +333,42 @@ struct StreamShape {
   static constexpr int kResults = kWaveKeys / 64;               // scores per lane
 };
 
-template <bool FP8, int WDT>
+// The fused selection (SELECT): the key-block workgroups of a query row meet
+// through two per-row words of the caller's workspace and a 12-bit histogram
+// of the row.
+//   state[0] = tag (40 bits) << 24 | arrivals (12 bits) << 12 | flushes (12 bits)
+//   state[1] = the tag once the row's histogram has been zeroed for this call
+// The tag is the call's own (bit 39 clear); a state with another tag is
+// stale (an earlier call, or whatever the workspace held) and counts as
+// zero.  A workgroup, once its scores are stored (device-scope stores) and
+// its block's histogram is built in LDS, arrives: the first arrival of the
+// call zeroes the row's histogram and then publishes the tag in state[1];
+// every later arrival waits for that (the first arrival is already running,
+// so the wait ends), then adds its block histogram to the row's with device
+// atomics and counts a flush.  The workgroup whose flush completes the count
+// has the whole row: it selects the row's top-K (select_row.h) and writes
+// idx, then marks both words stale (tag with bit 39 set), so that a replay
+// of the same call starts afresh.  The scores never leave the workspace.
+constexpr uint64_t kTagStale = uint64_t(1) << 39;
+constexpr int kSelWaitSpins = 1 << 20;  // rounds of about 256 cycles
+
+struct SelectArgs {
+  int32_t* idx;       // [rows, K]
+  int K;
+  uint64_t* state;    // [rows, 2]
+  uint32_t* hist;     // [rows, 4096]
+  uint64_t tag;
+};
+
+template <bool FP8, int WDT, bool SELECT>
 __global__ void __launch_bounds__(kStWaves * 64)
 indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict__ q_idx,
                const uint8_t* __restrict__ q_sf, const uint8_t* __restrict__ k_idx,
                const uint8_t* __restrict__ k_sf, const void* __restrict__ w,
-               const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
+               const int32_t* __restrict__ seq_lens, float* __restrict__ scores, SelectArgs sa) {
   using Sh = StreamShape<FP8>;
+  static_assert(!SELECT || sizeof(sel::Lds) <= kStWaves * kStBuffers * kStChunkBytes,
+                "the selection's scratch fits the idle key ring");
   constexpr int kWBytes = kIdxHeads * (WDT == DSA_BF16 ? 2 : 4);
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kStWaves * kStBuffers * kStChunkBytes];
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kIdxHeads * Sh::kRowBytes];
@@ -430,7 +460,7 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
   __syncthreads();  // every wave's query copies are in
 
   float* out_row = scores + row * S;
-  if (nch == 0) {  // every key of this wave is in the future (or past S)
+  if (!SELECT && nch == 0) {  // every key of this wave is in the future (or past S)
     for (int s = s_begin + lane; s < s_end; s += 64) out_row[s] = -__builtin_inff();
     return;
   }
@@ -540,13 +570,89 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
     }
   }
   // ---- the wave's scores: one 256-byte run per 64 keys; future keys -inf ----
+  float sv[Sh::kResults];
 #pragma unroll
   for (int j = 0; j < Sh::kResults; ++j) {
     const int s = s_begin + 64 * j + lane;
     float v;
     if constexpr (FP8) v = idx_scale * (res[j] * ue8m0_to_f32(ksb[j]));
     else v = idx_scale * res[j];
-    if (s < s_end) __builtin_nontemporal_store(s < s_lim ? v : -__builtin_inff(), out_row + s);
+    sv[j] = s < s_lim ? v : -__builtin_inff();
+    if constexpr (SELECT) {
+      if (s < s_end) __hip_atomic_store(out_row + s, sv[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      if (s < s_end) __builtin_nontemporal_store(sv[j], out_row + s);
+    }
+  }
+  if constexpr (SELECT) {
+    // ---- the block's histogram, the row's meeting, the last one selects ----
+    __shared__ uint32_t sel_flag;
+    const int tid = threadIdx.x;
+    uint32_t* lh = reinterpret_cast<uint32_t*>(kbuf);  // every wave is past its last chunk
+    __syncthreads();
+    for (int i = tid; i < sel::kBins1; i += kStWaves * 64) lh[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < Sh::kResults; ++j) {
+      const uint32_t key = score_key(sv[j]);
+      if (s_begin + 64 * j + lane < s_end && key != 0u) atomicAdd(&lh[key >> 20], 1u);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's score stores are complete
+    __syncthreads();
+    uint64_t* st = sa.state + 2 * row;
+    uint32_t* gh = sa.hist + row * sel::kBins1;
+    if (tid == 0) {
+      // once the call's tag is in the word, arrivals only add; a compare and
+      // swap installs the tag (the first arrival) and is retried only while
+      // the word is stale
+      uint64_t old = __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool first = false;
+      for (;;) {
+        if ((old >> 24) == sa.tag) {
+          __hip_atomic_fetch_add(st, uint64_t(1) << 12, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        if (__hip_atomic_compare_exchange_strong(st, &old, (sa.tag << 24) | (uint64_t(1) << 12),
+                                                 __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+          first = true;
+          break;
+        }
+      }
+      sel_flag = first ? 1u : 0u;
+    }
+    __syncthreads();
+    if (sel_flag) {  // the first arrival: a zeroed row histogram, then the tag
+      for (int i = tid; i < sel::kBins1; i += kStWaves * 64)
+        __hip_atomic_store(gh + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(st + 1, sa.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (tid == 0) {  // wait for the first arrival's zeroing (it is running)
+      for (int spin = 0; spin < kSelWaitSpins &&
+                         __hip_atomic_load(st + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != sa.tag;
+           ++spin)
+        __builtin_amdgcn_s_sleep(4);
+    }
+    __syncthreads();
+    for (int i = tid; i < sel::kBins1; i += kStWaves * 64) {
+      const uint32_t c = lh[i];
+      if (c != 0u) __hip_atomic_fetch_add(gh + i, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's histogram adds are complete
+    __syncthreads();
+    if (tid == 0) {
+      const uint64_t old = __hip_atomic_fetch_add(st, uint64_t(1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sel_flag = (static_cast<int>(old & 0xfffu) + 1 == nkb) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!sel_flag) return;
+    sel::Lds& L = *reinterpret_cast<sel::Lds*>(kbuf);
+    sel::select_row(L, out_row, S, gh, sa.K, sa.idx + row * sa.K);
+    if (tid == 0) {
+      __hip_atomic_store(st, (sa.tag | kTagStale) << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(st + 1, sa.tag | kTagStale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -566,21 +672,22 @@ dsa_status_t run_generic(const dsa_shape_t& s, const void* q_idx, const uint8_t*
   return timer.done("indexer_generic");
 }
 
-template <bool FP8, int WDT>
+template <bool FP8, int WDT, bool SELECT = false>
 dsa_status_t run_stream(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                         const void* k_idx, const uint8_t* k_sf, const void* w,
-                        const int32_t* seq_lens, float* scores, hipStream_t stream) {
+                        const int32_t* seq_lens, float* scores, hipStream_t stream,
+                        SelectArgs sa = SelectArgs{}) {
   constexpr int kBlockKeys = StreamShape<FP8>::kBlockKeys;
   const int nkb = (s.S + kBlockKeys - 1) / kBlockKeys;
   const int64_t blocks = static_cast<int64_t>(s.B) * s.T * nkb;
   if (blocks > 0x7fffffff)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: %lld key blocks", static_cast<long long>(blocks));
   LaunchTimer timer;
-  hipExtLaunchKernelGGL(indexer_stream<FP8, WDT>, dim3(static_cast<unsigned>(blocks)),
+  hipExtLaunchKernelGGL((indexer_stream<FP8, WDT, SELECT>), dim3(static_cast<unsigned>(blocks)),
                         dim3(kStWaves * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
                         nkb, s.idx_scale, static_cast<const uint8_t*>(q_idx), q_sf,
-                        static_cast<const uint8_t*>(k_idx), k_sf, w, seq_lens, scores);
-  return timer.done("indexer_stream");
+                        static_cast<const uint8_t*>(k_idx), k_sf, w, seq_lens, scores, sa);
+  return timer.done(SELECT ? "indexer_select" : "indexer_stream");
 }
 
 template <int WDT>
@@ -600,6 +707,38 @@ dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_
 }
 
 }  // namespace
+
+bool indexer_select_applies(const dsa_shape_t& s) {
+  return s.HI == kIdxHeads && s.DI == kIdxDim && s.T < kPfMinQueries && s.S <= sel::kMaxRow &&
+         (s.idx_dtype == DSA_BF16 || s.idx_dtype == DSA_FP8_E4M3) &&
+         static_cast<int64_t>(s.B) * s.T <= 65535;
+}
+
+size_t indexer_select_workspace_bytes(const dsa_shape_t& s) {
+  const size_t rows = static_cast<size_t>(s.B) * s.T;
+  return rows * (2 * sizeof(uint64_t) + sel::kBins1 * sizeof(uint32_t));
+}
+
+dsa_status_t launch_indexer_select(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
+                                   const void* k_idx, const uint8_t* k_sf, const void* w,
+                                   const int32_t* seq_lens, float* scores, int32_t* idx,
+                                   void* sel_ws, uint64_t tag, hipStream_t stream) {
+  if (!indexer_select_applies(s))
+    return fail(DSA_ERR_UNSUPPORTED, "indexer_select: shape not covered by the fused selection");
+  const size_t rows = static_cast<size_t>(s.B) * s.T;
+  SelectArgs sa;
+  sa.idx = idx;
+  sa.K = k_eff(s);
+  sa.state = static_cast<uint64_t*>(sel_ws);
+  sa.hist = reinterpret_cast<uint32_t*>(static_cast<char*>(sel_ws) + rows * 2 * sizeof(uint64_t));
+  sa.tag = tag & (kTagStale - 1);
+  const bool wbf = s.w_dtype == DSA_BF16;
+  if (s.idx_dtype == DSA_BF16)
+    return wbf ? run_stream<false, DSA_BF16, true>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream, sa)
+               : run_stream<false, DSA_F32, true>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream, sa);
+  return wbf ? run_stream<true, DSA_BF16, true>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream, sa)
+             : run_stream<true, DSA_F32, true>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream, sa);
+}
 
 dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                             const void* k_idx, const uint8_t* k_sf, const void* w,

@@ -73,6 +73,23 @@ def test_workspace_sizes(dsa):
         dsa.workspace_bytes(_v32(dsa, K=0), dsa.ENTRY_TOPK)
     with pytest.raises(dsa.DsaError):
         dsa.workspace_bytes(s, 7)
+    # the fused index scores -> top-K: the scores, then per row two state
+    # words and a 4096-bin histogram
+    it = dsa.workspace_bytes(s, dsa.ENTRY_INDEXER_TOPK)
+    assert it == 32 * 8192 * 4 + 32 * (16 + 4096 * 4)
+    with pytest.raises(dsa.DsaError):            # prefill: not covered by the fused launch
+        dsa.workspace_bytes(prefill, dsa.ENTRY_INDEXER_TOPK)
+
+
+def test_indexer_topk_rejects_uncovered_shapes_on_host(dsa):
+    L = dsa.lib()
+    P = ctypes.c_void_p(256)   # never dereferenced: refused on the host
+    for bad in (dict(T=8, S=4096), dict(S=300000), dict(HI=32), dict(idx_dtype=0)):
+        s = _v32(dsa, **bad)
+        rc = L.dsa_indexer_topk(ctypes.byref(s), None, P, None, P, None, P, P, P, 1 << 40, None)
+        assert rc == 2, bad
+    rc = L.dsa_indexer_topk(ctypes.byref(_v32(dsa)), None, P, None, P, None, P, P, P, 1024, None)
+    assert rc == 3 and "workspace" in L.dsa_last_error().decode()
 
 
 @pytest.mark.parametrize("bad,msg", [

@@ -540,3 +540,77 @@ def test_binding_rejects_bad_outputs(dsa):
     for kw in bad:
         with pytest.raises((ValueError, TypeError)):
             dsa.dsa_forward(*args, **kw)
+
+
+# ---------------------------------------------------------------------------
+# the fused index scores -> top-K of dsa_forward (decode shapes)
+# ---------------------------------------------------------------------------
+
+FUSED_CASES = {
+    "decode_real": g.CONFIGS["decode_8k"].replace(B=8),
+    # integer inputs: many equal scores, the boundary key exact with ties
+    "decode_int": g.CONFIGS["decode_8k"].replace(B=8, integer=True),
+    "mtp_t2": g.CONFIGS["decode_8k"].replace(B=2, T=2, S=3000),
+    # a row length that is not a multiple of 4 (scalar reads of the row)
+    "odd_keys": g.CONFIGS["decode_8k"].replace(B=3, S=3001),
+    # fewer keys than K: every selectable key is taken
+    "short_rows": g.CONFIGS["decode_8k"].replace(B=2, S=1500),
+    "fp8_int": g.CONFIGS["decode_64k_fp8"].replace(B=3, S=20000, integer=True),
+    "fp8_real": g.CONFIGS["decode_64k_fp8"].replace(B=3, S=20000),
+    # 128 key blocks meeting per row, integer ties (no planted cluster: its
+    # offsets are not integers)
+    "long_int": g.CONFIGS["decode_128k"].replace(B=2, integer=True, cluster=0),
+    # the planted cluster
+    "long_real": g.CONFIGS["decode_128k"].replace(B=2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FUSED_CASES))
+def test_fused_selection_exact(dsa, case):
+    """dsa_indexer_topk selects inside the indexer launch: its selection
+    equals the oracle's top-K of the very scores the launch left in the
+    workspace, bit for bit, and those scores are the oracle's (exactly on
+    integer inputs, within the score bar otherwise).  The workspace starts
+    out holding arbitrary bytes, and the call runs twice on it."""
+    torch = U.torch()
+    cfg = FUSED_CASES[case]
+    print(f"[fused_selection] {case}: {cfg}", flush=True)
+    x = _inputs(cfg)
+    shape = U.shape_of(cfg)
+    ws = torch.empty(dsa.workspace_bytes(shape, dsa.ENTRY_INDEXER_TOPK), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)                                       # whatever the workspace held before
+    rows = cfg.B * cfg.T
+    rb, rt = _rows(cfg)
+    ref = _oracle_scores(cfg, rb, rt)
+    first = None
+    for rep in range(2):
+        idx = dsa.dsa_indexer_topk(shape, x["q_idx"], x["k_idx"], x["w"], x["q_sf"], x["k_sf"], ws=ws)
+        torch.cuda.synchronize()
+        sc = ws[: rows * cfg.S * 4].view(torch.float32).cpu().numpy().reshape(rows, cfg.S)
+        got = idx.cpu().numpy().reshape(rows, -1)
+        assert np.array_equal(got, oracle.topk(cfg, sc)), f"{case}: selection differs from the oracle's"
+        if cfg.integer:
+            assert np.array_equal(sc, ref)
+        else:
+            U.assert_scores_close(sc, ref, what=case)
+        if first is None:
+            first = got
+        else:
+            assert np.array_equal(first, got), f"{case}: the second call selects differently"
+
+
+def test_fused_selection_ragged(dsa):
+    """dsa_indexer_topk over a ragged batch (a sequence shorter than K, one
+    with a single key, one with none): the oracle's selection of the scores
+    it computed."""
+    torch = U.torch()
+    cfg = g.CONFIGS["decode_8k"].replace(B=4, S=3000, integer=True)
+    lens = [3000, 1700, 1, 0]
+    x = _inputs(cfg)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    shape = U.shape_of(cfg)
+    ws = torch.empty(dsa.workspace_bytes(shape, dsa.ENTRY_INDEXER_TOPK), dtype=torch.uint8, device="cuda")
+    idx = dsa.dsa_indexer_topk(shape, x["q_idx"], x["k_idx"], x["w"], seq_lens=lens_dev, ws=ws)
+    rb, rt = _rows(cfg)
+    ref_sc = _oracle_scores(cfg, rb, rt, seq_lens=np.array(lens, np.int32))
+    assert np.array_equal(idx.cpu().numpy().reshape(cfg.B, -1), oracle.topk(cfg, ref_sc))
