@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8
 
 
 def parse():
@@ -72,14 +73,16 @@ def algorithmic(cfg):
                 indexer_flops=idx_flops, mla_flops=mla_flops, flops=idx_flops + mla_flops)
 
 
-def roofline(decode, nbytes, nflops, seconds):
+def roofline(decode, nbytes, nflops, seconds, peak_tflops=MFMA_BF16_PEAK_TFLOPS):
+    """HBM roofline (decode) or MFMA roofline (prefill) against the peak of
+    the contraction's dtype."""
     if decode:
         achieved = nbytes / seconds / 1e9
         return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     achieved = nflops / seconds / 1e12
-    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tflops,
+            "unit": "TFLOP/s", "frac": round(achieved / peak_tflops, 4)}
 
 
 def source_hash():
@@ -461,7 +464,7 @@ def bench_absorb(args):
     print(json.dumps(result))
 
 
-PATH_WORKLOADS = ("decode_8k", "prefill_16k", "decode_128k", "decode_64k_fp8")
+PATH_WORKLOADS = ("decode_8k", "prefill_16k", "decode_128k", "decode_64k_fp8", "prefill_16k_fp8")
 
 
 def bench_path(cfg, args, steps, warmup, cpu):
@@ -556,13 +559,15 @@ def bench_path(cfg, args, steps, warmup, cpu):
     # the dominant kernel: the longest average launch of the step
     dom = max(kt, key=lambda k: kt[k]["avg_us"])
     t_dom = kt[dom]["avg_us"] / 1e6
+    peak = MFMA_BF16_PEAK_TFLOPS
     if dom.startswith("indexer"):
         bytes_launch, flops_launch = A["indexer_bytes"] * q, A["indexer_flops"] * q
+        peak = MFMA_FP8_PEAK_TFLOPS if cfg.idx_dtype == "fp8" else MFMA_BF16_PEAK_TFLOPS
     elif dom.startswith("mla") and dom != "mla_combine":
         bytes_launch, flops_launch = A["mla_bytes"] * q, A["mla_flops"] * q
     else:
         raise SystemExit(f"bench: no algorithmic model for dominant kernel {dom}")
-    roof = roofline(decode, bytes_launch, flops_launch, t_dom)
+    roof = roofline(decode, bytes_launch, flops_launch, t_dom, peak)
     roof["kernel"] = dom
     roof["launch_us"] = round(t_dom * 1e6, 2)
     roof["algorithmic_per_launch"] = round(bytes_launch if decode else flops_launch)
@@ -572,8 +577,10 @@ def bench_path(cfg, args, steps, warmup, cpu):
     stage_us = {"indexer": sum(r["avg_us"] for k, r in kt.items() if k.startswith("indexer")),
                 "topk": sum(r["avg_us"] for k, r in kt.items() if k.startswith("topk")),
                 "sparse_mla": sum(r["avg_us"] for k, r in kt.items() if k.startswith("mla"))}
+    idx_peak = MFMA_FP8_PEAK_TFLOPS if cfg.idx_dtype == "fp8" else MFMA_BF16_PEAK_TFLOPS
     stages = {
-        "indexer": roofline(decode, A["indexer_bytes"] * q, A["indexer_flops"] * q, stage_us["indexer"] / 1e6),
+        "indexer": roofline(decode, A["indexer_bytes"] * q, A["indexer_flops"] * q, stage_us["indexer"] / 1e6,
+                            idx_peak),
         "sparse_mla": roofline(decode, A["mla_bytes"] * q, A["mla_flops"] * q, stage_us["sparse_mla"] / 1e6),
     }
     for k, v in stages.items():

@@ -110,6 +110,10 @@ CONFIGS: Dict[str, Config] = {
                           w_dtype=BF16, mla_dtype=BF16, seed=3, cluster=4096, **_V32),
     "decode_64k_fp8": Config("decode_64k_fp8", B=64, T=1, S=65536, idx_dtype=FP8,
                              w_dtype=BF16, mla_dtype=BF16, seed=4, **_V32),
+    # the prefill with the checkpoint's indexer format (e4m3 codes, ue8m0
+    # block scales): prefill_16k's shapes and draws, quantised like decode_64k_fp8
+    "prefill_16k_fp8": Config("prefill_16k_fp8", B=1, T=16384, S=16384, idx_dtype=FP8,
+                              w_dtype=BF16, mla_dtype=BF16, seed=5, **_V32),
 }
 
 

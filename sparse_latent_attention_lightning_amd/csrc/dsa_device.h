@@ -138,6 +138,15 @@ __device__ __forceinline__ void lds_dma_16_nt(const void* src, uint32_t lds) {
                : "v"(src), "s"(lds)
                : "memory", "m0");
 }
+// 4-byte global -> LDS copy per lane: lane l writes LDS [lds + 4 l] (the
+// source 4-byte aligned; lanes outside exec copy nothing).  Counted like the
+// 16-byte copies.
+__device__ __forceinline__ void lds_dma_4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "memory", "m0");
+}
 // The same copy from a wave-uniform 64-bit base plus a 32-bit per-lane byte
 // offset (the saddr form: no 64-bit address arithmetic per lane).
 __device__ __forceinline__ void lds_dma_16_sbase(const void* base, uint32_t off, uint32_t lds) {

@@ -292,6 +292,173 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// Query-blocked e4m3 kernel for many queries per sequence (prefill): the
+// design of indexer_prefill on gfx950's 16x16x128 f8f6f4 product.
+//  * keys move in 128-key chunks (128 bytes per key: 16 KB) through a ring of
+//    4 LDS buffers, four 1 KB copies per wave per chunk; piece c of row r in
+//    slot c ^ ((r >> 1) & 7), lane (g, n) reads pieces 2g and 2g + 1 of row n
+//    (its 32 bytes of the key for the one product per 16 keys and head
+//    block), every bank once per cycle;
+//  * the chunk's 128 ue8m0 key scales follow it into the buffer (each wave
+//    copies 32 of them as 4-byte pieces, so every wave counts the same
+//    copies);
+//  * each wave keeps its query's 64 x 128 codes as four A operands (32
+//    VGPRs) and its head weights times the query scales of the heads;
+//  * per 16-key tile: 4 products (one per head block), then ReLU, weight and
+//    the in-lane head sum; the products of tile u + 1 are issued before the
+//    VALU work of tile u;
+//  * per 64 keys one reduce-scatter leaves one key's sum per lane, which is
+//    multiplied by that key's scale (a power of two: it commutes exactly
+//    with the ReLU and the head sum) and by the prefactor.
+// The key scale bytes are copied as 4-byte pieces, so the launcher sends only
+// sequence lengths that are multiples of 4 here (others: indexer_stream).
+// ---------------------------------------------------------------------------
+constexpr int kPf8ChunkKeys = 128;
+constexpr int kPf8RowBytes = kIdxDim;                           // 128
+constexpr int kPf8KeyBytes = kPf8ChunkKeys * kPf8RowBytes;      // 16 KB
+constexpr int kPf8Stride = kPf8KeyBytes + kPf8ChunkKeys;        // keys, then their scales
+constexpr int kPf8Copies = kPf8KeyBytes / 1024 / kPfWaves;      // 4: 1 KB copies per wave
+constexpr int kPf8Ops = kPf8Copies + 1;                         // memory ops per wave per chunk
+static_assert(kPf8Copies * kPfWaves * 1024 == kPf8KeyBytes, "whole copies per wave");
+
+template <int WDT>
+__global__ void __launch_bounds__(kPfWaves * 64)
+indexer_prefill_fp8(int T, int S, int n_qblk, float idx_scale, const uint8_t* __restrict__ q_idx,
+                    const uint8_t* __restrict__ q_sf, const uint8_t* __restrict__ k_idx,
+                    const uint8_t* __restrict__ k_sf, const void* __restrict__ w,
+                    const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPfBuffers * kPf8Stride];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const int nb = gridDim.x / n_qblk;                                // sequences
+  const int qb = n_qblk - 1 - static_cast<int>(blockIdx.x) / nb;    // longest first
+  const int b = static_cast<int>(blockIdx.x) % nb;
+  const int t0 = qb * kPfWaves;
+  const int t = t0 + wave;
+  const bool has_q = t < T;
+  const int tq = min(t, T - 1);
+  const int L = seq_len(seq_lens, b, S);
+  const int q_pos = L - T + tq;
+  const int kend = max(0, L - T + min(t0 + kPfWaves, T));  // keys [0, kend) are visible to some query
+  const int nchunks = (kend + kPf8ChunkKeys - 1) / kPf8ChunkKeys;
+  const int64_t kbase = static_cast<int64_t>(b) * S;
+  const uint32_t kb_lds = lds_addr(kbuf);
+
+  // chunk c -> buffer c % kPfBuffers; this wave copies rows 32 wave .. 32
+  // wave + 31 (8 rows per 1 KB copy) and the scales of the same 32 keys
+  // (keys past S - 1 load row S - 1, scale pieces stay inside the row)
+  auto issue_chunk = [&](int c) {
+    const uint32_t dst = kb_lds + (c % kPfBuffers) * kPf8Stride;
+#pragma unroll
+    for (int i = 0; i < kPf8Copies; ++i) {
+      const int r = (wave * kPf8Copies + i) * 8 + (lane >> 3);
+      const int piece = (lane & 7) ^ ((r >> 1) & 7);
+      const int key = min(c * kPf8ChunkKeys + r, S - 1);
+      lds_dma_16(k_idx + (kbase + key) * kPf8RowBytes + piece * 16, dst + (wave * kPf8Copies + i) * 1024);
+    }
+    const int key4 = min(c * kPf8ChunkKeys + 32 * wave + 4 * (lane & 7), S - 4);
+    if (lane < 8) lds_dma_4(k_sf + kbase + key4, dst + kPf8KeyBytes + 32 * wave);
+  };
+#pragma unroll
+  for (int c = 0; c < kPfBuffers - 1; ++c)
+    if (c < nchunks) issue_chunk(c);
+
+  // ---- the query's codes (A operands) and head weights, in registers ----
+  const int64_t row = static_cast<int64_t>(b) * T + tq;
+  i32x8_t qa[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const u32x4_t* hp = reinterpret_cast<const u32x4_t*>(q_idx + (row * kIdxHeads + 16 * mb + n) * kIdxDim + 32 * g);
+    const u32x4_t lo = __builtin_nontemporal_load(hp);
+    const u32x4_t hi = __builtin_nontemporal_load(hp + 1);
+    qa[mb] = i32x8_t{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                     static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                     static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+  }
+  float wreg[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t hh = row * kIdxHeads + 16 * mb + 4 * g + i;
+      wreg[mb][i] = load_w<WDT>(w, hh) * ue8m0_to_f32(q_sf[hh]);
+    }
+
+  float* out_row = scores + row * S;
+
+  // one 16-key tile: 4 products into acc (key operands read from LDS)
+  auto tile_mfma = [&](const uint8_t* buf, int u, f32x4_t (&acc)[4]) {
+    const uint8_t* rp = buf + (16 * u + n) * kPf8RowBytes;
+    const int f = (n >> 1) & 7;  // (row >> 1) & 7 of row 16 u + n
+    const u32x4_t k0 = *reinterpret_cast<const u32x4_t*>(rp + 16 * ((2 * g) ^ f));
+    const u32x4_t k1 = *reinterpret_cast<const u32x4_t*>(rp + 16 * ((2 * g + 1) ^ f));
+    const i32x8_t kk = {static_cast<int>(k0[0]), static_cast<int>(k0[1]), static_cast<int>(k0[2]),
+                        static_cast<int>(k0[3]), static_cast<int>(k1[0]), static_cast<int>(k1[1]),
+                        static_cast<int>(k1[2]), static_cast<int>(k1[3])};
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16x16x128_e4m3(qa[mb], kk, f32x4_t{0.f, 0.f, 0.f, 0.f});
+  };
+  // ReLU, head weights and the in-lane part of the head sum
+  auto tile_part = [&](const f32x4_t (&acc)[4]) -> float {
+    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      p0 = fmaf(wreg[mb][0], fmaxf(acc[mb][0], 0.f), p0);
+      p1 = fmaf(wreg[mb][1], fmaxf(acc[mb][1], 0.f), p1);
+      p0 = fmaf(wreg[mb][2], fmaxf(acc[mb][2], 0.f), p0);
+      p1 = fmaf(wreg[mb][3], fmaxf(acc[mb][3], 0.f), p1);
+    }
+    return p0 + p1;
+  };
+  // cross-lane head sum of 4 tiles: lane l ends with key 64 h + l of chunk c
+  auto half_store = [&](const uint8_t* buf, int c, int h, const float (&part)[4]) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+    const auto d = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+    const float h0 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const float h1 = __uint_as_float(d[0]) + __uint_as_float(d[1]);
+    const auto e = __builtin_amdgcn_permlane16_swap(__float_as_uint(h0), __float_as_uint(h1), false, false);
+    const float ks = ue8m0_to_f32(buf[kPf8KeyBytes + 64 * h + lane]);
+    const float v = idx_scale * ((__uint_as_float(e[0]) + __uint_as_float(e[1])) * ks);
+    const int key = c * kPf8ChunkKeys + 64 * h + lane;
+    if (has_q && key < S) __builtin_nontemporal_store(key <= q_pos ? v : -__builtin_inff(), out_row + key);
+  };
+
+  f32x4_t acc0[4], acc1[4];
+  float part[4];
+  for (int c = 0; c < nchunks; ++c) {
+    // chunk c has landed: the copies issued after it are those of chunks
+    // c + 1 .. min(c + kPfBuffers - 2, nchunks - 1), kPf8Ops per chunk (the
+    // first chunk also waits for the query loads, issued after the copies)
+    const int later = min(kPfBuffers - 2, nchunks - 1 - c);
+    if (c == 0 || later <= 0)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPf8Ops) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPf8Ops) : "memory");
+    __syncthreads();   // every wave's copies of chunk c are in; chunk c - 1 is consumed
+    if (c + kPfBuffers - 1 < nchunks) issue_chunk(c + kPfBuffers - 1);
+    const uint8_t* buf = kbuf + (c % kPfBuffers) * kPf8Stride;
+    tile_mfma(buf, 0, acc0);
+#pragma unroll
+    for (int u = 1; u < 8; ++u) {
+      if (u & 1) tile_mfma(buf, u, acc1); else tile_mfma(buf, u, acc0);
+      part[(u - 1) & 3] = (u & 1) ? tile_part(acc0) : tile_part(acc1);
+      if (u == 4) half_store(buf, c, 0, part);
+    }
+    part[3] = tile_part(acc1);
+    half_store(buf, c, 1, part);
+  }
+  // keys past the block's last chunk are in every query's future
+  if (has_q) {
+    const int k0 = nchunks * kPf8ChunkKeys;
+    for (int k = k0 + lane; k < S; k += 64) __builtin_nontemporal_store(-__builtin_inff(), out_row + k);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Streaming MFMA kernel for few queries per sequence (decode), HI = 64,
 // DI = 128, bf16 or e4m3.
 //
@@ -691,6 +858,22 @@ dsa_status_t run_stream(const dsa_shape_t& s, const void* q_idx, const uint8_t* 
 }
 
 template <int WDT>
+dsa_status_t run_prefill_fp8(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
+                             const void* k_idx, const uint8_t* k_sf, const void* w,
+                             const int32_t* seq_lens, float* scores, hipStream_t stream) {
+  const int n_qblk = (s.T + kPfWaves - 1) / kPfWaves;
+  const int64_t blocks = static_cast<int64_t>(n_qblk) * s.B;
+  if (blocks > 0x7fffffff)
+    return fail(DSA_ERR_UNSUPPORTED, "indexer: %lld query blocks", static_cast<long long>(blocks));
+  LaunchTimer timer;
+  hipExtLaunchKernelGGL(indexer_prefill_fp8<WDT>, dim3(static_cast<unsigned>(blocks)),
+                        dim3(kPfWaves * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
+                        n_qblk, s.idx_scale, static_cast<const uint8_t*>(q_idx), q_sf,
+                        static_cast<const uint8_t*>(k_idx), k_sf, w, seq_lens, scores);
+  return timer.done("indexer_prefill_fp8");
+}
+
+template <int WDT>
 dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_idx,
                          const void* w, const int32_t* seq_lens, float* scores,
                          hipStream_t stream) {
@@ -751,6 +934,9 @@ dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8
   if (v32 && s.idx_dtype == DSA_BF16)
     return wbf ? run_stream<false, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
                : run_stream<false, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);
+  if (v32 && s.idx_dtype == DSA_FP8_E4M3 && s.T >= kPfMinQueries && s.S % 4 == 0)
+    return wbf ? run_prefill_fp8<DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
+               : run_prefill_fp8<DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);
   if (v32 && s.idx_dtype == DSA_FP8_E4M3)
     return wbf ? run_stream<true, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
                : run_stream<true, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);

@@ -108,8 +108,12 @@ SCORE_CASES = {
     "fp8_int_t16": g.CONFIGS["decode_64k_fp8"].replace(B=2, T=16, S=1000, integer=True),
     "fp8_int_t300": g.CONFIGS["decode_64k_fp8"].replace(B=1, T=300, S=1000, integer=True),
     # the same with fp32 head weights and a sequence length that is not a
-    # multiple of 4, real-valued
+    # multiple of 4 (the per-query kernel), real-valued
     "fp8_real_t37": g.CONFIGS["decode_64k_fp8"].replace(B=2, T=37, S=517, w_dtype="f32"),
+    # query-blocked e4m3 kernel, real-valued: the last 512 queries of 2048 keys,
+    # and fp32 head weights with a ragged last query block and key chunk
+    "fp8_real_t512": g.CONFIGS["decode_64k_fp8"].replace(B=1, T=512, S=2048),
+    "fp8_real_w32_t70": g.CONFIGS["decode_64k_fp8"].replace(B=2, T=70, S=1300, w_dtype="f32"),
     # real-valued: within 1e-4 of the row max
     "decode_real": g.CONFIGS["decode_8k"].replace(B=2, S=3000),
     "fp8_real": g.CONFIGS["decode_64k_fp8"].replace(B=2, S=5000),
