@@ -42,7 +42,16 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* The enumerations cross the ABI as 32-bit integers.  Compiled as C++ they
+ * have a fixed int32_t underlying type, so every int32 value a caller passes
+ * is a value of the type (an unknown one is rejected by the call). */
+#ifdef __cplusplus
+#define DSA_ENUM(tag) enum tag : int32_t
+#else
+#define DSA_ENUM(tag) enum tag
+#endif
+
+typedef DSA_ENUM(dsa_status_e) {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, misaligned pointer */
   DSA_ERR_UNSUPPORTED = 2, /* dtype or shape combination without a kernel */
@@ -50,7 +59,7 @@ typedef enum {
   DSA_ERR_HIP = 4          /* a HIP runtime call or launch failed */
 } dsa_status_t;
 
-typedef enum {
+typedef DSA_ENUM(dsa_dtype_e) {
   DSA_F32 = 0,
   DSA_BF16 = 1,
   DSA_FP8_E4M3 = 2 /* OCP E4M3FN bytes with one ue8m0 scale byte per 128 elements */
@@ -71,7 +80,7 @@ typedef struct {
   int32_t mla_dtype; /* dsa_dtype_t of q, kv and o: F32 or BF16 */
 } dsa_shape_t;
 
-typedef enum {
+typedef DSA_ENUM(dsa_entry_e) {
   DSA_ENTRY_TOPK = 0,
   DSA_ENTRY_SPARSE_MLA = 1,
   DSA_ENTRY_FORWARD = 2,

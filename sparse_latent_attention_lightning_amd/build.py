@@ -37,8 +37,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+def _compile(src: str, extra, build_dir: str) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -49,18 +49,28 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra=(), jobs: int = 8) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for a CPU check of
+# the library's host code (argument checks, workspace sizing, error paths).
+# Each -fsanitize= applies to the host pass only; device code is unchanged.
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=undefined",
+                       "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def build(extra=(), jobs: int = 8, out: str = LIB, build_dir: str = BUILD_DIR) -> str:
+    """Compile every csrc/*.hip and link them into `out` (default: the
+    in-tree libdsa.so the binding loads)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, list(extra), build_dir), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -673,11 +673,16 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
 // planner uses) unrolls everything: the NS partial loads and the wave's NS
 // contiguous lse values (scalar loads) are all issued before the first wait.
 // Every split's partial is written (an empty split holds zeros with weight 0).
+// With xcd_map (rows a multiple of 8), workgroup L merges heads of row
+// 8 (L / 256) + L % 8: the XCD that wrote the row's partials (mla_mfma's
+// xcd_map) also merges them.
 template <int NS>
 __global__ void __launch_bounds__(256)
-mla_combine(int nsplit_rt, int64_t total_heads, const uint16_t* __restrict__ part_o,
+mla_combine(int nsplit_rt, int xcd_map, int64_t total_heads, const uint16_t* __restrict__ part_o,
             const float* __restrict__ part_lse, uint16_t* __restrict__ o, float* __restrict__ lse) {
-  const int64_t rh = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));  // row * H + head
+  const int64_t L = blockIdx.x;
+  const int64_t hq = xcd_map ? (L >> 8) * 256 + (L & 7) * 32 + ((L >> 3) & 31) : L;  // 4-head group
+  const int64_t rh = __builtin_amdgcn_readfirstlane(hq * 4 + (threadIdx.x >> 6));  // row * H + head
   if (rh >= total_heads) return;
   const int nsplit = NS > 0 ? NS : nsplit_rt;
   const int lane = threadIdx.x & 63;
@@ -793,7 +798,7 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
     const dim3 cgrid(static_cast<unsigned>((total_heads + 3) / 4));
     auto combine = [&](auto kernel) {
       hipExtLaunchKernelGGL(kernel, cgrid, dim3(256), 0, stream, ctimer.start(), ctimer.stop(), 0,
-                            p.splits, total_heads, static_cast<const uint16_t*>(part_o),
+                            p.splits, xcd_map, total_heads, static_cast<const uint16_t*>(part_o),
                             static_cast<const float*>(part_lse), static_cast<uint16_t*>(o), lse);
     };
     switch (p.splits) {
