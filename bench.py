@@ -49,6 +49,12 @@ def parse():
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
                          "`--only forward --copy-calibration MIB` into profiles/hbm_counters.json")
     ap.add_argument("--calibration-mib", type=int, default=256)
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("COUNTER_DIR", "UTIL_DIR"),
+                    help="no GPU: MFMA work per kernel from a rocprofv3 --pmc run of "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_VALU_MFMA_BUSY_CYCLES "
+                         "GRBM_GUI_ACTIVE and one of MfmaUtil")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="no GPU: the kernel table of a rocprofv3 --kernel-trace --stats run")
     return ap.parse_args()
 
 
@@ -113,6 +119,13 @@ def _kernel_short_name(name):
     return name.split("(")[0].split("<")[0].split("::")[-1].strip()
 
 
+def _kernel_template_name(name):
+    """Kernel name with its template arguments, without namespaces and the
+    parameter list (rocprofv3 without -T reports the full signature)."""
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "").replace("dsa::", "")
+    return name.split("(")[0].strip()
+
+
 def _pmc_rows(d, counter):
     """{kernel: {dispatch id: counter value summed over its instances}}."""
     import csv
@@ -169,6 +182,55 @@ def summarize_pmc(fetch_dir, write_dir, mib, workload):
     print(f"calibration: {ck} copying {mib} MiB (last 5 dispatches) reads FETCH_SIZE {cf:,.0f} KiB "
           f"and WRITE_SIZE {cw:,.0f} KiB: factors {f_fetch:.4f} (fetch), {f_write:.4f} (write)\n")
     print("\n".join(lines))
+
+
+def summarize_trace(d):
+    """Markdown table of a rocprofv3 --stats kernel summary (*kernel_stats.csv)."""
+    import csv
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    print("| kernel | calls | average us | min us | max us | share |")
+    print("|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print(f"| {_kernel_template_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} % |")
+
+
+def summarize_mfma(counter_dir, util_dir):
+    """Per kernel: MFMA flops per dispatch (MOPS x 512, bf16 and fp8), the
+    dispatch's duration under counter collection, the flop rate that gives,
+    and rocprofv3's MfmaUtil (MFMA busy cycles over GPU-active cycles of all
+    SIMDs) from a second run."""
+    import csv
+
+    def read(d):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        per = {}
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                k = per.setdefault(_kernel_template_name(r["Kernel_Name"]), {})
+                e = k.setdefault(int(r["Dispatch_Id"]), {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return per
+
+    cnt, util = read(counter_dir), read(util_dir)
+    print("| kernel | dispatches | bf16 MFMA flops | fp8 MFMA flops | us (counting) | MFMA TFLOP/s | MfmaUtil |")
+    print("|---|---|---|---|---|---|---|")
+    for k in sorted(cnt, key=lambda k: -sum(e["ns"] for e in cnt[k].values())):
+        ds = list(cnt[k].values())
+        n = len(ds)
+        bf = sum(e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for e in ds) / n * 512
+        f8 = sum(e.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0) for e in ds) / n * 512
+        us = sum(e["ns"] for e in ds) / n / 1e3
+        if bf + f8 == 0:
+            continue
+        u = [e.get("MfmaUtil") for e in util.get(k, {}).values() if "MfmaUtil" in e]
+        util_txt = f"{sum(u) / len(u):.1f} %" if u else "n/a"
+        print(f"| {k} | {n} | {bf:.4g} | {f8:.4g} | {us:.1f} | {(bf + f8) / us / 1e6:.1f} | {util_txt} |")
 
 
 def cpu_model():
@@ -646,6 +708,12 @@ def bench_path(cfg, args, steps, warmup, cpu):
 
 def main():
     args = parse()
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calibration_mib, args.workload)
         return

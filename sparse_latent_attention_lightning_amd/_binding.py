@@ -64,55 +64,61 @@ def lib() -> ctypes.CDLL:
     """The loaded libdsa (raises if it is not built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built; run "
-                              "`python -m sparse_latent_attention_lightning_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        P, sz = ctypes.c_void_p, ctypes.c_size_t
-        sp = ctypes.POINTER(DsaShape)
-        L.dsa_indexer_scores.argtypes = [sp, P, P, P, P, P, P, P]
-        L.dsa_indexer_scores_ragged.argtypes = [sp, P, P, P, P, P, P, P, P]
-        L.dsa_topk.argtypes = [sp, P, P, P, sz, P]
-        L.dsa_sparse_mla_fwd.argtypes = [sp, P, P, P, P, P, P, sz, P]
-        L.dsa_forward.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, sz, P]
-        L.dsa_forward_ragged.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
-        L.dsa_forward_noalloc.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P]
-        L.dsa_indexer_topk.argtypes = [sp, P, P, P, P, P, P, P, P, sz, P]
-        i32 = ctypes.c_int32
-        L.dsa_cache_fill.argtypes = [i32, i32] + [P] * 8 + [i32, P, i32, P, P, i32, P, P, sz, P]
-        L.dsa_cache_fill.restype = ctypes.c_int
-        L.dsa_cache_fill_workspace_bytes.argtypes = [i32, i32]
-        L.dsa_cache_fill_workspace_bytes.restype = sz
-        L.dsa_indexer_query.argtypes = [i32, i32, P, P, i32, P, P, P, sz, P]
-        L.dsa_indexer_query.restype = ctypes.c_int
-        L.dsa_indexer_query_workspace_bytes.argtypes = [i32, i32]
-        L.dsa_indexer_query_workspace_bytes.restype = sz
-        L.dsa_absorb_prepare.argtypes = [i32, P, P, P]
-        L.dsa_absorb_query.argtypes = [i32, i32, P, P, P, P, i32, P, P]
-        L.dsa_absorb_output.argtypes = [i32, i32, P, P, i32, P, P]
-        L.dsa_output_projection.argtypes = [i32, i32, i32, P, P, i32, P, P, sz, P]
-        for f in ("dsa_absorb_prepare", "dsa_absorb_query", "dsa_absorb_output",
-                  "dsa_output_projection"):
-            getattr(L, f).restype = ctypes.c_int
-        L.dsa_output_projection_workspace_bytes.argtypes = [i32, i32, i32]
-        L.dsa_output_projection_workspace_bytes.restype = sz
-        for f in ("dsa_indexer_scores", "dsa_indexer_scores_ragged", "dsa_topk",
-                  "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged", "dsa_forward_noalloc",
-                  "dsa_indexer_topk"):
-            getattr(L, f).restype = ctypes.c_int
-        L.dsa_workspace_bytes.argtypes = [sp, ctypes.c_int32]
-        L.dsa_workspace_bytes.restype = ctypes.c_size_t
-        L.dsa_timing_begin.argtypes = []
-        L.dsa_timing_begin.restype = ctypes.c_int
-        L.dsa_timing_end.argtypes = [ctypes.POINTER(DsaKernelTime), ctypes.c_int32,
-                                     ctypes.POINTER(ctypes.c_int32)]
-        L.dsa_timing_end.restype = ctypes.c_int
-        L.dsa_status_str.argtypes = [ctypes.c_int]
-        L.dsa_status_str.restype = ctypes.c_char_p
-        L.dsa_last_error.argtypes = []
-        L.dsa_last_error.restype = ctypes.c_char_p
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Loads a build of libdsa at `path` (the release build, or the
+    -DDSA_DEBUG one) and declares its entry points."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run "
+                          "`python -m sparse_latent_attention_lightning_amd.build`")
+    L = ctypes.CDLL(path)
+    P, sz = ctypes.c_void_p, ctypes.c_size_t
+    sp = ctypes.POINTER(DsaShape)
+    L.dsa_indexer_scores.argtypes = [sp, P, P, P, P, P, P, P]
+    L.dsa_indexer_scores_ragged.argtypes = [sp, P, P, P, P, P, P, P, P]
+    L.dsa_topk.argtypes = [sp, P, P, P, sz, P]
+    L.dsa_sparse_mla_fwd.argtypes = [sp, P, P, P, P, P, P, sz, P]
+    L.dsa_forward.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.dsa_forward_ragged.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.dsa_forward_noalloc.argtypes = [sp, P, P, P, P, P, P, P, P, P, P, P]
+    L.dsa_indexer_topk.argtypes = [sp, P, P, P, P, P, P, P, P, sz, P]
+    i32 = ctypes.c_int32
+    L.dsa_cache_fill.argtypes = [i32, i32] + [P] * 8 + [i32, P, i32, P, P, i32, P, P, sz, P]
+    L.dsa_cache_fill.restype = ctypes.c_int
+    L.dsa_cache_fill_workspace_bytes.argtypes = [i32, i32]
+    L.dsa_cache_fill_workspace_bytes.restype = sz
+    L.dsa_indexer_query.argtypes = [i32, i32, P, P, i32, P, P, P, sz, P]
+    L.dsa_indexer_query.restype = ctypes.c_int
+    L.dsa_indexer_query_workspace_bytes.argtypes = [i32, i32]
+    L.dsa_indexer_query_workspace_bytes.restype = sz
+    L.dsa_absorb_prepare.argtypes = [i32, P, P, P]
+    L.dsa_absorb_query.argtypes = [i32, i32, P, P, P, P, i32, P, P]
+    L.dsa_absorb_output.argtypes = [i32, i32, P, P, i32, P, P]
+    L.dsa_output_projection.argtypes = [i32, i32, i32, P, P, i32, P, P, sz, P]
+    for f in ("dsa_absorb_prepare", "dsa_absorb_query", "dsa_absorb_output",
+              "dsa_output_projection"):
+        getattr(L, f).restype = ctypes.c_int
+    L.dsa_output_projection_workspace_bytes.argtypes = [i32, i32, i32]
+    L.dsa_output_projection_workspace_bytes.restype = sz
+    for f in ("dsa_indexer_scores", "dsa_indexer_scores_ragged", "dsa_topk",
+              "dsa_sparse_mla_fwd", "dsa_forward", "dsa_forward_ragged", "dsa_forward_noalloc",
+              "dsa_indexer_topk"):
+        getattr(L, f).restype = ctypes.c_int
+    L.dsa_workspace_bytes.argtypes = [sp, ctypes.c_int32]
+    L.dsa_workspace_bytes.restype = ctypes.c_size_t
+    L.dsa_timing_begin.argtypes = []
+    L.dsa_timing_begin.restype = ctypes.c_int
+    L.dsa_timing_end.argtypes = [ctypes.POINTER(DsaKernelTime), ctypes.c_int32,
+                                 ctypes.POINTER(ctypes.c_int32)]
+    L.dsa_timing_end.restype = ctypes.c_int
+    L.dsa_status_str.argtypes = [ctypes.c_int]
+    L.dsa_status_str.restype = ctypes.c_char_p
+    L.dsa_last_error.argtypes = []
+    L.dsa_last_error.restype = ctypes.c_char_p
+    return L
 
 
 def _check(status: int):

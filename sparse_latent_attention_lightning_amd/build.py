@@ -73,5 +73,17 @@ def build(extra=(), jobs: int = 8, out: str = LIB, build_dir: str = BUILD_DIR) -
     return out
 
 
+DEBUG_LIB = os.path.join(PKG, "libdsa_debug.so")
+
+
+def build_debug(jobs: int = 8) -> str:
+    """libdsa_debug.so: the same sources with -DDSA_DEBUG (LDS filled with
+    0xff bytes before first use; index rows checked on the device, with a
+    synchronizing read-back, after top-K and before the attention)."""
+    return build(extra=["-DDSA_DEBUG"], jobs=jobs, out=DEBUG_LIB, build_dir=os.path.join(BUILD_DIR, "debug"))
+
+
 if __name__ == "__main__":
     print(build())
+    if "--debug" in sys.argv[1:]:
+        print(build_debug())

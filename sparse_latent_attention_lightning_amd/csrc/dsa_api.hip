@@ -355,9 +355,14 @@ dsa_status_t dsa_indexer_topk(const dsa_shape_t* shape, const int32_t* seq_lens,
   float* scores = reinterpret_cast<float*>(base);
   if ((st = check_indexer_args(s, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
   if ((st = need(idx, "idx")) != DSA_OK) return st;
-  return launch_indexer_select(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, idx,
-                               base + indexer_topk_scores_bytes(s), next_call_tag(),
-                               static_cast<hipStream_t>(stream));
+  st = launch_indexer_select(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, idx,
+                             base + indexer_topk_scores_bytes(s), next_call_tag(), static_cast<hipStream_t>(stream));
+#ifdef DSA_DEBUG
+  if (st == DSA_OK)
+    st = debug_check_idx(static_cast<int64_t>(s.B) * s.T, k_eff(s), s.S, true, idx,
+                         static_cast<hipStream_t>(stream), "fused top-K output");
+#endif
+  return st;
 }
 
 dsa_status_t dsa_sparse_mla_fwd(const dsa_shape_t* shape, const void* q, const void* kv,

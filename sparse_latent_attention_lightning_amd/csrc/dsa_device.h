@@ -108,6 +108,22 @@ __device__ __forceinline__ float xor32_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Debug builds (-DDSA_DEBUG): fill an LDS buffer with 0xff bytes before its
+// first use (NaN as bf16 or fp32, -1 as int32: a skipped key), so that a read
+// of LDS nothing wrote shows up in the results.  Every thread of the
+// workgroup calls it; it ends with a barrier.  Other builds: nothing.
+template <int BYTES>
+__device__ __forceinline__ void debug_poison_lds(void* p) {
+#ifdef DSA_DEBUG
+  static_assert(BYTES % 16 == 0, "whole 16-byte pieces");
+  u32x4_t* q = static_cast<u32x4_t*>(p);
+  for (int i = threadIdx.x; i < BYTES / 16; i += blockDim.x) q[i] = u32x4_t{~0u, ~0u, ~0u, ~0u};
+  __syncthreads();
+#else
+  (void)p;
+#endif
+}
+
 // LDS byte address of a __shared__ object
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(

@@ -87,6 +87,16 @@ dsa_status_t launch_cache_fill(int N, int D, const void* x, const void* W, const
                                int w_dtype, void* w_out, void* ws, size_t ws_bytes,
                                hipStream_t stream);
 
+// ---- debug builds (-DDSA_DEBUG) -------------------------------------------
+#ifdef DSA_DEBUG
+// Checks rows x W index entries on the device and waits for the result: every
+// entry in [-1, S), and with `sorted` the valid entries of each row strictly
+// ascending with the -1 padding after them.  Fails with DSA_ERR_INVALID_ARG
+// naming `what` otherwise.  Synchronizes `stream` (not for graph capture).
+dsa_status_t debug_check_idx(int64_t rows, int W, int S, bool sorted, const int32_t* idx,
+                             hipStream_t stream, const char* what);
+#endif
+
 // ---- the whole path ------------------------------------------------------
 // Workspace bytes of dsa_forward, and the path on such a workspace at `base`
 // (shape already checked; pointers, alignment and seq_lens checked here).

@@ -155,6 +155,7 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
                 const uint16_t* __restrict__ k_idx, const void* __restrict__ w,
                 const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPfBuffers * kPfChunkBytes];
+  debug_poison_lds<sizeof(kbuf)>(kbuf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -328,6 +329,7 @@ indexer_prefill_fp8(int T, int S, int n_qblk, float idx_scale, const uint8_t* __
                     const uint8_t* __restrict__ k_sf, const void* __restrict__ w,
                     const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPfBuffers * kPf8Stride];
+  debug_poison_lds<sizeof(kbuf)>(kbuf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
@@ -541,6 +543,8 @@ indexer_stream(int T, int S, int nkb, float idx_scale, const uint8_t* __restrict
   __shared__ __attribute__((aligned(16))) uint8_t q_lds[kIdxHeads * Sh::kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[kWBytes];
   __shared__ __attribute__((aligned(16))) uint8_t qsf_lds[kIdxHeads];
+  debug_poison_lds<sizeof(kbuf)>(kbuf);
+  debug_poison_lds<sizeof(q_lds)>(q_lds);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;

@@ -258,6 +258,9 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   __shared__ __attribute__((aligned(1024))) MlaTile tiles[kBuffers];
   // a window of the split's index entries as key rows (-1: skipped entry)
   __shared__ __attribute__((aligned(16))) int32_t idxw[kIdxWin];
+  __shared__ int32_t last_valid[kMlaWaves];  // per wave: the split's last valid entry it saw
+  debug_poison_lds<sizeof(tiles)>(tiles);
+  debug_poison_lds<sizeof(idxw)>(idxw);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -275,7 +278,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   const int b = static_cast<int>(row / T);
   const int j0 = sp * kps;
   const int nj = max(0, min(W, j0 + kps) - j0);
-  const int ntiles = (nj + kTileKeys - 1) / kTileKeys;
+  int ntiles;  // tiles up to the split's last valid entry (set with the first index window)
   const uint16_t* kv_seq = kv + static_cast<int64_t>(b) * S * kD;
 
   // The split's index entries go through LDS a window at a time: thread i
@@ -317,8 +320,32 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     }
   }
   load_window(0);
+  // The split ends after its last valid entry: the entries past it add
+  // nothing (top-K rows of queries with fewer than K visible keys end in -1
+  // padding, which this drops).  Entries beyond the first window are read
+  // here once more only for splits longer than the window.
+  {
+    int last = -1;
+#pragma unroll
+    for (int u = 0; u < kWinPerThread; ++u)
+      if (win[u] >= 0 && win[u] < S) last = j0 + tid + u * kMlaThreads;
+    for (int j = j0 + kIdxWin + tid; j < j_end; j += kMlaThreads) {
+      const int e = idx_row[j];
+      if (e >= 0 && e < S) last = j;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    if (lane == 0) last_valid[wave] = last;
+  }
   store_window();   // waits for the window's loads, and so for the query copies issued before them
-  __syncthreads();  // the first index window is published
+  __syncthreads();  // the first index window and the last valid entries are published
+  {
+    int last = last_valid[0];
+#pragma unroll
+    for (int w = 1; w < kMlaWaves; ++w) last = max(last, last_valid[w]);
+    const int nj_used = last >= j0 ? last - j0 + 1 : 0;
+    ntiles = __builtin_amdgcn_readfirstlane((nj_used + kTileKeys - 1) / kTileKeys);
+  }
   {
     lds_char_t* qst = (lds_char_t*)(tiles[wave].bytes) + m * (kD * 2);
 #pragma unroll
@@ -770,6 +797,12 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
     return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: B*T = %lld exceeds 65535 rows",
                 static_cast<long long>(rows));
   const int W = k_eff(s);
+#ifdef DSA_DEBUG
+  {
+    const dsa_status_t st = debug_check_idx(rows, W, s.S, false, idx, stream, "attention index rows");
+    if (st != DSA_OK) return st;
+  }
+#endif
   const MlaPlan p = plan(s);
   if (p.mfma) {
     if (static_cast<int64_t>(s.S) * kD * 2 > 0xffffffffLL)

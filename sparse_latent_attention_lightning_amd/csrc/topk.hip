@@ -115,6 +115,7 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
             const int32_t* __restrict__ cand_idx_in, int K_out, int32_t* __restrict__ idx_out,
             uint32_t* __restrict__ cand_key_out) {
   __shared__ TopkLds lds;
+  debug_poison_lds<sizeof(lds)>(&lds);
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.y;
   const int chunk = blockIdx.x;
@@ -344,8 +345,9 @@ size_t topk_workspace_bytes(const dsa_shape_t& s) {
   return rows * p.chunks * k_eff(s) * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
-dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
+namespace {
+dsa_status_t topk_launches(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(s.B) * s.T;
   if (rows > 65535)
     return fail(DSA_ERR_UNSUPPORTED, "topk: B*T = %lld exceeds 65535 rows",
@@ -371,6 +373,17 @@ dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx
   return run_select<true, false>(static_cast<int>(n2), n2 % 4 == 0, dim3(1, rows),
                                  static_cast<int>(n2), n2, static_cast<int>(n2), nullptr, cand_key,
                                  cand_idx, K, idx, nullptr, stream);
+}
+}  // namespace
+
+dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  dsa_status_t st = topk_launches(s, scores, idx, ws, ws_bytes, stream);
+#ifdef DSA_DEBUG
+  if (st == DSA_OK)
+    st = debug_check_idx(static_cast<int64_t>(s.B) * s.T, k_eff(s), s.S, true, idx, stream, "top-K output");
+#endif
+  return st;
 }
 
 }  // namespace dsa

@@ -55,6 +55,7 @@ CASES = {
     "decode_128k": (g.CONFIGS["decode_128k"], lambda c: _decode_rows(c, 8, 14)),
     "decode_64k_fp8": (g.CONFIGS["decode_64k_fp8"], lambda c: _decode_rows(c, 6, 15)),
     "decode_64k_fp8_int": (g.CONFIGS["decode_64k_fp8"].replace(integer=True), lambda c: _decode_rows(c, 4, 16)),
+    "prefill_16k_fp8": (g.CONFIGS["prefill_16k_fp8"], lambda c: _prefill_rows(c, 4, 17)),
 }
 
 
