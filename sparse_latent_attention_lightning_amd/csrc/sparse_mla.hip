@@ -181,8 +181,8 @@ constexpr int kKSteps = kD / 16;             // 36 logits reduction steps of 16 
 constexpr int kLatSteps = kDc / 16;          // 32 of them over the latent part
 constexpr int kDimBlocks = kDc / 32;         // 16 value blocks of 32 dims
 constexpr int kPvSteps = 2 * kDimBlocks;     // value MFMAs per tile (2 key steps)
-constexpr int kReadAhead = 3;                // logits A-operand reads issued ahead of their MFMAs
-constexpr int kVAhead = 3;                   // value A operands (2 reads each) issued ahead
+constexpr int kReadAhead = 4;                // logits A-operand reads issued ahead of their MFMAs
+constexpr int kVAhead = 4;                   // value A operands (2 reads each) issued ahead
 constexpr float kRefSlack = 32.0f;           // log2 units: p <= 2^32 against the reference max
 constexpr int kIdxWin = 1024;                // index entries staged in LDS at a time
 constexpr int kWinTiles = kIdxWin / kTileKeys;
