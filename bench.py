@@ -696,11 +696,16 @@ def bench_path(cfg, args, steps, warmup, cpu):
     del replicas, base, ws
     torch.cuda.empty_cache()
     if cpu:
-        # a bounded sample: about as many query x key pairs as 32 queries over
-        # 8192 keys (decode: whole queries; prefill: 16 query rows)
-        rows = args.cpu_rows or (max(1, min(cfg.B * cfg.T, 32 * 8192 // cfg.S)) if cfg.T == 1 else 16)
-        if cfg.idx_dtype == "fp8":
-            rows = args.cpu_rows or max(1, rows // 2)   # the oracle decodes e4m3 per element: slower
+        # a bounded sample of about 5-20 s of host work: decode, up to 4 x 32
+        # queries over 8192 keys worth of query x key pairs (whole queries);
+        # prefill, 64 query rows; the oracle decodes e4m3 per element, so the
+        # e4m3 workloads take an eighth (decode) or a quarter (prefill)
+        if cfg.T == 1:
+            rows = max(1, min(cfg.B * cfg.T, 4 * 32 * 8192 // cfg.S))
+            rows = max(1, rows // 8) if cfg.idx_dtype == "fp8" else rows
+        else:
+            rows = 16 if cfg.idx_dtype == "fp8" else 64
+        rows = args.cpu_rows or rows
         print(f"[bench] {cfg.name}: CPU oracle on {rows} queries ...", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(cfg, rows)
     return rec
