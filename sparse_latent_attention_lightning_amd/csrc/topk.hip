@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t find_boundary(const uint32_t* hist, uint32_t
 // scores.  OUT_CAND: the result is a candidate list (key and index written).
 // VEC: every thread's run of E inputs starts 16-byte aligned (16-byte loads).
 template <int E, bool SRC_CAND, bool OUT_CAND, bool VEC>
-__global__ void __launch_bounds__(kTopkThreads)
+__global__ void __launch_bounds__(kTopkThreads, (E <= 16 && !SRC_CAND && !OUT_CAND) ? 8 : 1)
 topk_select(int n_in, int64_t in_stride, int chunk_elems,
             const float* __restrict__ scores, const uint32_t* __restrict__ cand_key_in,
             const int32_t* __restrict__ cand_idx_in, int K_out, int32_t* __restrict__ idx_out,
@@ -127,7 +127,7 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
 
   // ---- thread t owns elements [E t, E t + E): keys in registers ----
   uint32_t key[E];
-  int32_t id[E];
+  int32_t id[SRC_CAND ? E : 1];  // candidate indices; a score's index is its position
   const int i0 = tid * E;
   if (VEC && i0 + E <= n) {
 #pragma unroll
@@ -141,8 +141,6 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
         const float4 f4 = *reinterpret_cast<const float4*>(scores + in_base + i0 + j);
         key[j] = score_key(f4.x); key[j + 1] = score_key(f4.y);
         key[j + 2] = score_key(f4.z); key[j + 3] = score_key(f4.w);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) id[j + e] = elem0 + i0 + j + e;
       }
     }
   } else {
@@ -155,14 +153,19 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
           id[j] = cand_idx_in[in_base + i];
         } else {
           key[j] = score_key(scores[in_base + i]);
-          id[j] = elem0 + i;
         }
       } else {
         key[j] = 0u;
-        id[j] = -1;
+        if constexpr (SRC_CAND) id[j] = -1;
       }
     }
   }
+  // the row index of element j of this thread (keys of elements past the
+  // input are 0, so they are never taken and their index is never used)
+  auto index_of = [&](int j) -> int32_t {
+    if constexpr (SRC_CAND) return id[j];
+    else return elem0 + i0 + j;
+  };
   // clear both histograms while the loads are in flight
   for (int i = tid; i < 2 * kPass1Bins; i += kTopkThreads) (&lds.hist[0][0])[i] = 0u;
   if (tid == 0) lds.ncand = 0u;
@@ -222,15 +225,20 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
     for (int j = 0; j < E; ++j) take |= static_cast<uint32_t>(key[j] != 0u) << j;
   } else if (cnt <= kSmallCand) {
     // rank the few boundary candidates directly
-    int slot[E];
+    // element j's list slot (< kSmallCand: 4 bits) in nibble j % 8 of slot4[j / 8]
+    static_assert(kSmallCand <= 16, "slots in 4 bits");
+    uint32_t is_cand = 0;  // bit j: element j is a boundary candidate
+    uint32_t slot4[(E + 7) / 8];
+#pragma unroll
+    for (int q = 0; q < (E + 7) / 8; ++q) slot4[q] = 0u;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      slot[j] = -1;
       if (key[j] != 0u && (key[j] & mask) == prefix) {
         const uint32_t s = atomicAdd(&lds.ncand, 1u);
         lds.cand_key[s] = key[j];
-        lds.cand_idx[s] = id[j];
-        slot[j] = static_cast<int>(s);
+        lds.cand_idx[s] = index_of(j);
+        is_cand |= 1u << j;
+        slot4[j / 8] |= s << (4 * (j % 8));
       }
     }
     __syncthreads();
@@ -250,7 +258,8 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
     const uint32_t thr_hi = prefix | ~mask;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      const bool t = key[j] > thr_hi || (slot[j] >= 0 && lds.cand_take[slot[j]] != 0u);
+      bool t = key[j] > thr_hi;
+      if ((is_cand >> j) & 1u) t = lds.cand_take[(slot4[j / 8] >> (4 * (j % 8))) & 15u] != 0u;
       take |= static_cast<uint32_t>(t) << j;
     }
   } else {
@@ -279,7 +288,7 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
 #pragma unroll
   for (int j = 0; j < E; ++j) {
     if (((take >> j) & 1u) && pos < static_cast<uint32_t>(K_out)) {  // pos < ksel <= K_out by construction
-      idx_out[out_base + pos] = id[j];
+      idx_out[out_base + pos] = index_of(j);
       if constexpr (OUT_CAND) cand_key_out[out_base + pos] = key[j];
       ++pos;
     }
