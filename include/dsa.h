@@ -173,6 +173,10 @@ dsa_status_t dsa_indexer_topk(const dsa_shape_t* shape, const int32_t* seq_lens,
  *   lse [B, T, H]        fp32 output (nullable): log sum_j exp(logit_j)
  * A row with no valid index gives o = 0 and lse = -inf.  Accumulation is in
  * fp32.  ws: at least dsa_workspace_bytes(shape, DSA_ENTRY_SPARSE_MLA) bytes.
+ * A build with -DDSA_DEBUG checks the rows on the device first and returns
+ * DSA_ERR_INVALID_ARG for entries outside [-1, S) (it synchronizes the
+ * stream to read the check back); its top-K entry points also check their
+ * own output (entries in [-1, S), valid entries ascending, -1 padding last).
  */
 dsa_status_t dsa_sparse_mla_fwd(const dsa_shape_t* shape, const void* q,
                                 const void* kv, const int32_t* idx, void* o,
