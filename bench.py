@@ -142,7 +142,7 @@ def _pmc_rows(d, counter):
     return per
 
 
-def summarize_pmc(fetch_dir, write_dir, mib, workload):
+def summarize_pmc(fetch_dir, write_dir, mib, workload, out_path=None):
     """HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each scaled by what the counter reads for the calibration copy
     (the last 5 device-copy dispatches of the run, `mib` MiB each)."""
@@ -171,7 +171,7 @@ def summarize_pmc(fetch_dir, write_dir, mib, workload):
         out[k] = {"fetch_kib": round(fv, 1), "write_kib": round(wv, 1),
                   "hbm_bytes_per_launch": round(hbm), "source_hash": source_hash()}
         lines.append(f"| {k} | {len(fetch[k])} | {fv:,.0f} | {wv:,.0f} | {hbm:,.0f} |")
-    p = os.path.join(ROOT, "profiles", "hbm_counters.json")
+    p = out_path or os.path.join(ROOT, "profiles", "hbm_counters.json")
     d = json.load(open(p)) if os.path.exists(p) else {}
     d[workload] = out
     d[workload]["_calibration"] = {"copy_kernel": ck, "copy_mib": mib, "fetch_kib": round(cf, 1),
