@@ -164,6 +164,8 @@ dsa_status_t forward_on(const dsa_shape_t& s, const int32_t* seq_lens, const voi
   int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(base + L.idx);
   if ((st = check_indexer_args(s, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
   if ((st = check_mla_args(q, kv, idx, o)) != DSA_OK) return st;
+  // every step's shape limits before the first launch: a failing call enqueues nothing
+  if ((st = topk_check(s)) != DSA_OK || (st = mla_check(s)) != DSA_OK) return st;
   if ((st = launch_indexer(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, hs)) != DSA_OK)
     return st;
   if ((st = launch_topk(s, scores, idx, base + L.topk_ws, L.mla_ws - L.topk_ws, hs)) != DSA_OK)

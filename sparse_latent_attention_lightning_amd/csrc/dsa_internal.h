@@ -59,6 +59,9 @@ dsa_status_t launch_indexer_select(const dsa_shape_t& s, const void* q_idx, cons
                                    void* sel_ws, uint64_t tag, hipStream_t stream);
 
 // ---- top-k -------------------------------------------------------------
+// DSA_OK when launch_topk has kernels for the shape, else the failure (set
+// with fail) it would return; launches nothing.
+dsa_status_t topk_check(const dsa_shape_t& s);
 size_t topk_workspace_bytes(const dsa_shape_t& s);
 dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
                          size_t ws_bytes, hipStream_t stream);
@@ -107,6 +110,8 @@ dsa_status_t forward_on(const dsa_shape_t& s, const int32_t* seq_lens, const voi
                         char* base, hipStream_t stream);
 
 // ---- sparse latent attention ------------------------------------------
+// As topk_check, for launch_sparse_mla.
+dsa_status_t mla_check(const dsa_shape_t& s);
 size_t mla_workspace_bytes(const dsa_shape_t& s);
 dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* kv,
                                const int32_t* idx, void* o, float* lse, void* ws,

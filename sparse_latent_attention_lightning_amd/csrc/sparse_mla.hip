@@ -789,13 +789,29 @@ size_t mla_workspace_bytes(const dsa_shape_t& s) {
   return (po + 255) / 256 * 256 + rows * p.splits * s.H * sizeof(float);
 }
 
-dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* kv,
-                               const int32_t* idx, void* o, float* lse, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
+dsa_status_t mla_check(const dsa_shape_t& s) {
   const int64_t rows = static_cast<int64_t>(s.B) * s.T;
   if (rows > 65535)
     return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: B*T = %lld exceeds 65535 rows",
                 static_cast<long long>(rows));
+  if (plan(s).mfma) {
+    if (static_cast<int64_t>(s.S) * kD * 2 > 0xffffffffLL)
+      return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: S = %d key rows exceed 4 GiB per sequence", s.S);
+  } else if ((static_cast<size_t>(s.Dc) + s.Dr + k_eff(s)) * sizeof(float) > 64 * 1024) {
+    return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: D + K = %d too large for the generic kernel",
+                s.Dc + s.Dr + k_eff(s));
+  }
+  return DSA_OK;
+}
+
+dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* kv,
+                               const int32_t* idx, void* o, float* lse, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  {
+    const dsa_status_t st = mla_check(s);
+    if (st != DSA_OK) return st;
+  }
+  const int64_t rows = static_cast<int64_t>(s.B) * s.T;
   const int W = k_eff(s);
 #ifdef DSA_DEBUG
   {
@@ -805,8 +821,6 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
 #endif
   const MlaPlan p = plan(s);
   if (p.mfma) {
-    if (static_cast<int64_t>(s.S) * kD * 2 > 0xffffffffLL)
-      return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: S = %d key rows exceed 4 GiB per sequence", s.S);
     uint16_t* part_o = nullptr;
     float* part_lse = nullptr;
     if (p.splits > 1) {
@@ -844,9 +858,6 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
     return ctimer.done("mla_combine");
   }
   const size_t lds = (static_cast<size_t>(s.Dc) + s.Dr + W) * sizeof(float);
-  if (lds > 64 * 1024)
-    return fail(DSA_ERR_UNSUPPORTED, "sparse_mla: D + K = %d too large for the generic kernel",
-                s.Dc + s.Dr + W);
   LaunchTimer timer;
   const dim3 grid(s.H, static_cast<unsigned>(rows));
   if (s.mla_dtype == DSA_BF16)

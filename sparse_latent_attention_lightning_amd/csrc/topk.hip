@@ -354,13 +354,24 @@ size_t topk_workspace_bytes(const dsa_shape_t& s) {
   return rows * p.chunks * k_eff(s) * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
-namespace {
-dsa_status_t topk_launches(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
-                           size_t ws_bytes, hipStream_t stream) {
+dsa_status_t topk_check(const dsa_shape_t& s) {
   const int64_t rows = static_cast<int64_t>(s.B) * s.T;
   if (rows > 65535)
     return fail(DSA_ERR_UNSUPPORTED, "topk: B*T = %lld exceeds 65535 rows",
                 static_cast<long long>(rows));
+  const TopkPlan p = plan(s);
+  const int K = k_eff(s);
+  if (p.chunks > 1 && (static_cast<int64_t>(p.chunks) * K > kChunkElems || K >= p.chunk_elems))
+    return fail(DSA_ERR_UNSUPPORTED, "topk: S = %d with K = %d needs more than two stages", s.S, K);
+  return DSA_OK;
+}
+
+namespace {
+dsa_status_t topk_launches(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  dsa_status_t st = topk_check(s);
+  if (st != DSA_OK) return st;
+  const int64_t rows = static_cast<int64_t>(s.B) * s.T;
   const int K = k_eff(s);
   const TopkPlan p = plan(s);
   if (p.chunks == 1) {
@@ -368,14 +379,12 @@ dsa_status_t topk_launches(const dsa_shape_t& s, const float* scores, int32_t* i
                                     nullptr, nullptr, K, idx, nullptr, stream);
   }
   const int64_t n2 = static_cast<int64_t>(p.chunks) * K;
-  if (n2 > kChunkElems || K >= p.chunk_elems)
-    return fail(DSA_ERR_UNSUPPORTED, "topk: S = %d with K = %d needs more than two stages", s.S, K);
   const size_t need = topk_workspace_bytes(s);
   if (ws == nullptr || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "topk: workspace of %zu bytes needed, %zu given", need, ws_bytes);
   int32_t* cand_idx = static_cast<int32_t*>(ws);
   uint32_t* cand_key = reinterpret_cast<uint32_t*>(cand_idx + rows * n2);
-  dsa_status_t st = run_select<false, true>(p.chunk_elems, s.S % 4 == 0, dim3(p.chunks, rows), s.S,
+  st = run_select<false, true>(p.chunk_elems, s.S % 4 == 0, dim3(p.chunks, rows), s.S,
                                             s.S, p.chunk_elems, scores, nullptr, nullptr, K,
                                             cand_idx, cand_key, stream);
   if (st != DSA_OK) return st;

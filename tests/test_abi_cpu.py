@@ -145,6 +145,21 @@ def test_forward_workspace_too_small(dsa):
     assert rc == 3 and "workspace" in L.dsa_last_error().decode()
 
 
+@pytest.mark.parametrize("over,msg", [
+    (dict(B=65536), "65535 rows"),                 # one grid row per query row in top-K and attention
+    (dict(B=1, S=600000), "two stages"),           # top-K candidates of more than 16 chunks of 32768
+])
+def test_forward_shape_limits_fail_before_any_launch(dsa, over, msg):
+    """dsa_forward checks every step's limits before its first launch: without a
+    GPU a launch would fail with DSA_ERR_HIP, so DSA_ERR_UNSUPPORTED here means
+    nothing was enqueued."""
+    L = dsa.lib()
+    s = _v32(dsa, **over)
+    P = ctypes.c_void_p(256)
+    rc = L.dsa_forward(ctypes.byref(s), P, None, P, None, P, P, P, None, P, None, P, 1 << 50, None)
+    assert rc == 2 and msg in L.dsa_last_error().decode()
+
+
 def test_timing_session_on_host(dsa):
     # no launches happen, so no event is created and no device is touched
     with pytest.raises(dsa.DsaError, match="no active session"):
