@@ -404,6 +404,24 @@ def test_forward_tiny_exact_selection(dsa):
     U.assert_rows_close(o.cpu().numpy().reshape(cfg.T, cfg.H, cfg.Dc), ro, U.RTOL["f32"], "tiny o")
 
 
+def test_forward_at_the_row_limit(dsa):
+    """65535 query rows (257 sequences x 255 queries), the most one call takes:
+    every grid's row dimension at its limit (generic indexer, top-K, generic
+    attention), integer inputs, selection and scores exact."""
+    cfg = g.CONFIGS["tiny"].replace(B=257, T=255)
+    assert cfg.B * cfg.T == 65535
+    x = _inputs(cfg)
+    o, lse, idx = _forward(dsa, cfg, x)
+    rows = cfg.B * cfg.T
+    rb, rt = _rows(cfg)
+    ref_sc = oracle.indexer_scores(cfg, rb, rt, g.full(cfg, "q_idx").reshape(rows, cfg.HI, cfg.DI),
+                                   g.full(cfg, "w").reshape(rows, cfg.HI), g.full(cfg, "k_idx"))
+    ref_idx = oracle.topk(cfg, ref_sc)
+    assert np.array_equal(idx.cpu().numpy().reshape(rows, -1), ref_idx)
+    ro, rl = oracle.sparse_mla(cfg, rb, g.full(cfg, "q").reshape(rows, cfg.H, cfg.D), g.full(cfg, "kv"), ref_idx)
+    U.assert_rows_close(o.cpu().numpy().reshape(rows, cfg.H, cfg.Dc), ro, U.RTOL["f32"], "row limit o")
+
+
 def test_forward_dense_when_k_covers_causal(dsa):
     """K >= causal length: the sparse path is plain causal attention."""
     cfg = g.CONFIGS["tiny"].replace(K=256)
