@@ -21,7 +21,11 @@
 //    exp2 against a fixed reference max, and O^T += V^T . P^T (latent dims on
 //    M, heads on N) with P^T taken straight from the logit accumulators.  A
 //    ring of 4 LDS tiles holds the tile of the value product, the tile of the
-//    logits and two tiles whose copies are in flight.
+//    logits and two tiles whose copies are in flight.  With too few query
+//    rows to give every CU a workgroup even at the finest split, a workgroup
+//    of 2 waves takes 64 heads instead (two workgroups per split, on one XCD,
+//    gathering the same rows): twice the workgroups, half the query block
+//    and half the partials per workgroup.
 //  * mla_combine: merges split partials (o_s, lse_s) with weights
 //    exp(lse_s - lse), deterministically (fixed split order, no atomics).
 //  * mla_generic: any shape, fp32 VALU loops, two passes over the index row.
@@ -162,18 +166,16 @@ mla_generic(int T, int S, int H, int Dc, int Dr, int W, float sm_scale,
 //
 // Tiles are filled by direct global->LDS copies (global_load_lds_dwordx4:
 // lane l of a wave writes 16 B at the wave's LDS base + 16 l): wave w copies
-// the latent parts of rows 8w .. 8w+7 (one 1 KiB run each) and the rotary
-// parts of the same rows.  A ring of 4 tiles holds the tile of the value
+// the latent parts of rows R w .. R w + R - 1 (R = 8 with 4 waves, 16 with
+// 2; one 1 KiB run each) and the rotary parts of the same rows (8 rows per
+// copy), spread over its logits steps.  A ring of 4 tiles holds the tile of the value
 // product, the tile of the logits and two tiles in flight.  Before the first
 // tile the ring stages the query (one buffer per wave), after the last one
 // the output (bf16 [head][dims], stored as whole 1 KiB head rows).
 // ---------------------------------------------------------------------------
 constexpr int kH = 128, kDc = 512, kDr = 64, kD = kDc + kDr;
-constexpr int kMlaWaves = 4;                 // wave w owns heads 32w .. 32w+31
-constexpr int kMlaThreads = kMlaWaves * 64;
 constexpr int kTileKeys = 32;
 constexpr int kBuffers = 4;                  // LDS tile ring
-constexpr int kCopiesPerTile = 9;            // copies per wave per tile: 8 latent rows + rotary parts
 constexpr int kLatStride = 1088;             // bytes per latent row in LDS (1024 + 64 pad)
 constexpr int kRopeBase = kTileKeys * kLatStride;            // byte offset of the rotary region
 constexpr int kTileBytes = kRopeBase + kTileKeys * kDr * 2;  // 38912
@@ -184,9 +186,7 @@ constexpr int kPvSteps = 2 * kDimBlocks;     // value MFMAs per tile (2 key step
 constexpr int kReadAhead = 4;                // logits A-operand reads issued ahead of their MFMAs
 constexpr int kVAhead = 4;                   // value A operands (2 reads each) issued ahead
 constexpr float kRefSlack = 32.0f;           // log2 units: p <= 2^32 against the reference max
-constexpr int kIdxWin = 1024;                // index entries staged in LDS at a time
-constexpr int kWinTiles = kIdxWin / kTileKeys;
-constexpr int kWinPerThread = kIdxWin / kMlaThreads;
+constexpr int kIdxWin = 1024;                // index entries staged in LDS at a time (4 waves)
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef short short8_t __attribute__((ext_vector_type(8)));
@@ -244,21 +244,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v_t{a, b}, bf16x2v_t));
 }
 
-// 1-D grid of rows * nsplit workgroups.  With xcd_map, the splits of one query
-// row share an XCD (workgroups are dealt to the 8 XCDs round-robin), so its
-// 147 KB query block is fetched once into that XCD's L2.
+// NW waves (4: heads 0..127; 2: a head half, 64 heads from head0).  1-D grid
+// of rows * nsplit * (4 / NW) workgroups.  With xcd_map, the workgroups of
+// one query row share an XCD (workgroups are dealt to the 8 XCDs
+// round-robin), so its 147 KB query block and, with 2 waves, the key rows
+// both head halves gather are fetched once into that XCD's L2.
 // nsplit == 1: writes o (bf16) and lse directly; otherwise writes bf16
 // partials part_o [rows, nsplit, H, Dc] (already divided by the split's own
 // sum) and part_lse [rows, H, nsplit] (natural log; -inf for an empty split).
-__global__ void __launch_bounds__(kMlaThreads, 1)
+template <int NW>
+__global__ void __launch_bounds__(NW * 64, 1)
 mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
          const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
          const int32_t* __restrict__ idx, uint16_t* __restrict__ o, float* __restrict__ lse,
          uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(1024))) MlaTile tiles[kBuffers];
   // a window of the split's index entries as key rows (-1: skipped entry)
-  __shared__ __attribute__((aligned(16))) int32_t idxw[kIdxWin];
-  __shared__ int32_t last_valid[kMlaWaves];  // per wave: the split's last valid entry it saw
+  // index window: 4 entries per thread (4 waves: 1024, 2 waves: 512)
+  constexpr int kWin = kIdxWin * NW / 4;
+  constexpr int kWinTiles = kWin / kTileKeys;
+  __shared__ __attribute__((aligned(16))) int32_t idxw[kWin];
+  static_assert(NW == 4 || NW == 2, "4 waves (128 heads) or 2 waves (64 heads) per workgroup");
+  constexpr int kThreads = NW * 64;
+  constexpr int kRowsPerWave = kTileKeys / NW;        // tile rows each wave copies: 8 or 16
+  constexpr int kRopeCopies = kRowsPerWave / 8;       // their rotary parts, 8 rows per 1 KiB copy
+  constexpr int kCopies = kRowsPerWave + kRopeCopies; // copies per wave per tile: 9 or 18
+  constexpr int kCopyStep = kKSteps / kCopies;        // logits steps per copy: 4 or 2
+  constexpr int kWinPer = kWin / kThreads;            // index window entries per thread
+  static_assert(kCopyStep * kCopies == kKSteps && kCopyStep >= 2, "copies spread over the logits steps");
+  __shared__ int32_t last_valid[NW];  // per wave: the split's last valid entry it saw
   debug_poison_lds<sizeof(tiles)>(tiles);
   debug_poison_lds<sizeof(idxw)>(idxw);
   const int tid = threadIdx.x;
@@ -266,15 +280,20 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, m = lane & 31;
   const int L = blockIdx.x;
-  int sp;
+  // workgroups per query row: the splits, times 2 head halves with 2 waves
+  constexpr int kHalves = 4 / NW;
+  const int nsh = nsplit * kHalves;
+  int sh;
   int64_t row;
   if (xcd_map) {
-    sp = (L >> 3) % nsplit;
-    row = static_cast<int64_t>(L / (8 * nsplit)) * 8 + (L & 7);
+    sh = (L >> 3) % nsh;
+    row = static_cast<int64_t>(L / (8 * nsh)) * 8 + (L & 7);
   } else {
-    sp = L % nsplit;
-    row = L / nsplit;
+    sh = L % nsh;
+    row = L / nsh;
   }
+  const int sp = sh / kHalves;
+  const int head0 = (sh % kHalves) * 32 * NW;  // the workgroup's first head
   const int b = static_cast<int>(row / T);
   const int j0 = sp * kps;
   const int nj = max(0, min(W, j0 + kps) - j0);
@@ -285,18 +304,18 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   // loads entries i, i + 256, ... of the window (past the split's end: -1).
   const int32_t* idx_row = idx + row * W;
   const int j_end = j0 + nj;
-  int win[kWinPerThread];
+  int win[kWinPer];
   auto load_window = [&](int w) {
 #pragma unroll
-    for (int u = 0; u < kWinPerThread; ++u) {
-      const int j = j0 + w * kIdxWin + tid + u * kMlaThreads;
+    for (int u = 0; u < kWinPer; ++u) {
+      const int j = j0 + w * kWin + tid + u * kThreads;
       win[u] = j < j_end ? idx_row[j] : -1;
     }
   };
   auto store_window = [&]() {
 #pragma unroll
-    for (int u = 0; u < kWinPerThread; ++u)
-      idxw[tid + u * kMlaThreads] = (win[u] >= 0 && win[u] < S) ? win[u] : -1;
+    for (int u = 0; u < kWinPer; ++u)
+      idxw[tid + u * kThreads] = (win[u] >= 0 && win[u] < S) ? win[u] : -1;
   };
 
   // Query operand (B of logits^T): qf[ks] = head 32w + m, dims 16ks + 8h .. +8,
@@ -308,7 +327,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   // the 8 splits of a query row share an XCD and 7 of them find it in L2.
   bf16x8_t qf[kKSteps];
   {
-    const char* qsrc = reinterpret_cast<const char*>(q + (row * kH + 32 * wave) * kD);
+    const char* qsrc = reinterpret_cast<const char*>(q + (row * kH + head0 + 32 * wave) * kD);
     const uint32_t qlds = lds_addr(tiles[wave].bytes);
     int ln = __lane_id();
     asm volatile("" : "+v"(ln));
@@ -327,9 +346,9 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   {
     int last = -1;
 #pragma unroll
-    for (int u = 0; u < kWinPerThread; ++u)
-      if (win[u] >= 0 && win[u] < S) last = j0 + tid + u * kMlaThreads;
-    for (int j = j0 + kIdxWin + tid; j < j_end; j += kMlaThreads) {
+    for (int u = 0; u < kWinPer; ++u)
+      if (win[u] >= 0 && win[u] < S) last = j0 + tid + u * kThreads;
+    for (int j = j0 + kWin + tid; j < j_end; j += kThreads) {
       const int e = idx_row[j];
       if (e >= 0 && e < S) last = j;
     }
@@ -342,7 +361,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   {
     int last = last_valid[0];
 #pragma unroll
-    for (int w = 1; w < kMlaWaves; ++w) last = max(last, last_valid[w]);
+    for (int w = 1; w < NW; ++w) last = max(last, last_valid[w]);
     const int nj_used = last >= j0 ? last - j0 + 1 : 0;
     ntiles = __builtin_amdgcn_readfirstlane((nj_used + kTileKeys - 1) / kTileKeys);
   }
@@ -362,9 +381,8 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
   float l_run = 0.f;
   const float scale2 = sm_scale * kLog2e;
 
-  // Wave w copies tile rows 8w .. 8w+7 (latent and rotary parts), reading
-  // their key rows from the index window; wave 0 also publishes the tile's
-  // validity mask.  Skipped entries copy key row 0 of the sequence: their
+  // Wave w copies tile rows R w .. R w + R - 1 (R = kRowsPerWave; latent and
+  // rotary parts), reading their key rows from the index window.  Skipped entries copy key row 0 of the sequence: their
   // logits are replaced by -inf, so their probabilities are exactly zero and
   // (finite) rows add nothing to O.
   // the sequence's base address, wave-uniform (the copies take it in SGPRs)
@@ -375,12 +393,19 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
     kvb = reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
   }
-  // latent copy of row 8w + k: lane ln's 16-byte slot holds piece swz4(ln, f),
-  // f = lat_f(8w + k) = (2w + k/4) & 3
-  const int lat_lo[2] = {16 * swz4(lane, (2 * wave) & 3), 16 * swz4(lane, (2 * wave + 1) & 3)};
-  // rotary copy: lane ln takes row 8w + ln/8, slot ln % 8
-  const int rope_r = 8 * wave + (lane >> 3);
-  const int rope_lo = 2 * kDc + 16 * ((lane & 7) ^ rope_swz(rope_r));
+  // latent copy of row R w + k: lane ln's 16-byte slot holds piece swz4(ln, f),
+  // f = lat_f(R w + k), the same for each group of 4 rows
+  int lat_lo[kRowsPerWave / 4];
+#pragma unroll
+  for (int g4 = 0; g4 < kRowsPerWave / 4; ++g4)
+    lat_lo[g4] = 16 * swz4(lane, lat_f(kRowsPerWave * wave + 4 * g4));
+  // rotary copy c: lane ln takes row R w + 8c + ln/8, slot ln % 8
+  int rope_r[kRopeCopies], rope_lo[kRopeCopies];
+#pragma unroll
+  for (int c = 0; c < kRopeCopies; ++c) {
+    rope_r[c] = kRowsPerWave * wave + 8 * c + (lane >> 3);
+    rope_lo[c] = 2 * kDc + 16 * ((lane & 7) ^ rope_swz(rope_r[c]));
+  }
   struct TileCopies {
     const int32_t* wrow;  // the tile's 32 index entries in the window
     uint32_t lds;
@@ -396,10 +421,11 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     c.lds = lds_addr(tiles[(t + 2) % kBuffers].bytes);
     return c;
   };
-  // key row of copy k (0..7: tile row 8w + k, all lanes; 8: row 8w + lane/8),
-  // read from the index window just before the copy goes out (skipped: row 0)
+  // key row of copy k (k < R: tile row R w + k, all lanes; then the rotary
+  // copies, row rope_r[k - R] per lane), read from the index window just
+  // before the copy goes out (skipped: row 0)
   auto copy_key = [&](const TileCopies& c, int k) {
-    return k < 8 ? c.wrow[8 * wave + k] : c.wrow[rope_r & 31];
+    return k < kRowsPerWave ? c.wrow[kRowsPerWave * wave + k] : c.wrow[rope_r[k - kRowsPerWave] & 31];
   };
   // byte offsets within the sequence fit 32 bits (S * 1152 < 2^32, checked on the host)
   auto copy_row = [&](const TileCopies& c, int k, int s) {
@@ -407,30 +433,31 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     // and the row offset is formed per lane on the VALU, not the scalar unit
     asm volatile("" : "+v"(s));
     s = max(s, 0);
-    const int lo = k < 8 ? lat_lo[k >> 2] : rope_lo;
+    const int lo = k < kRowsPerWave ? lat_lo[k >> 2] : rope_lo[k - kRowsPerWave];
     // (wave-uniform; readfirstlane keeps it in a scalar register for m0)
     const uint32_t dst = __builtin_amdgcn_readfirstlane(
-        k < 8 ? c.lds + kLatStride * (8 * wave + k) : c.lds + kRopeBase + 1024 * wave);
+        k < kRowsPerWave ? c.lds + kLatStride * (kRowsPerWave * wave + k)
+                         : c.lds + kRopeBase + 1024 * (kRopeCopies * wave + k - kRowsPerWave));
     lds_dma_16_sbase(kvb, static_cast<uint32_t>(s) * static_cast<uint32_t>(kD * 2) + lo, dst);
   };
   // all of a tile's copies at once (start-up): the key reads go out together
   auto issue_tile = [&](int t) {
     const TileCopies c = prep_tile(t);
-    int keys[kCopiesPerTile];
+    int keys[kCopies];
 #pragma unroll
-    for (int k = 0; k < kCopiesPerTile; ++k) keys[k] = copy_key(c, k);
+    for (int k = 0; k < kCopies; ++k) keys[k] = copy_key(c, k);
     const uint32_t vm = tile_mask(c.wrow[lane & 31]);
 #pragma unroll
-    for (int k = 0; k < kCopiesPerTile; ++k) copy_row(c, k, keys[k]);
+    for (int k = 0; k < kCopies; ++k) copy_row(c, k, keys[k]);
     return vm;
   };
   // wait until at most `pending` later tiles' copies of this wave are in flight
   auto wait_tiles = [&](int pending) {
-    static_assert(kCopiesPerTile == 9, "vmcnt immediates");
+    static_assert(kCopies < 64, "vmcnt immediate");
     if (pending <= 0)
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     else
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCopies) : "memory");
   };
 
   // LDS byte offsets.  Logits A operand of step ks: row m, piece 2ks + h:
@@ -509,10 +536,12 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
         else
           mfma32_acc(sacc, ka[ks % kReadAhead], qf[ks]);
         if (ks + kReadAhead < kKSteps) ka[ks % kReadAhead] = aload(ks + kReadAhead);
-        // copy k of the tile two ahead goes out with step 4k + 1, its key row
-        // is read with step 4k - 1
-        if (ks % 4 == 3 && ks / 4 + 1 < kCopiesPerTile && copies) key = copy_key(nxt, ks / 4 + 1);
-        if (ks % 4 == 1 && ks / 4 < kCopiesPerTile && copies) copy_row(nxt, ks / 4, key);
+        // copy k of the tile two ahead goes out with step C k + 1 (C =
+        // kCopyStep), the key row of copy k + 1 is read right after, with
+        // step C k + C - 1 (the same step when C = 2)
+        if (ks % kCopyStep == 1 && ks / kCopyStep < kCopies && copies) copy_row(nxt, ks / kCopyStep, key);
+        if (ks % kCopyStep == kCopyStep - 1 && ks / kCopyStep + 1 < kCopies && copies)
+          key = copy_key(nxt, ks / kCopyStep + 1);
         if (ks == 6 && copies) vm_nxt = tile_mask(entry);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -615,7 +644,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
       TileCopies nxt;
       if (copies) {
         const int t = it + 2;
-        if (t % kWinTiles == 0) {  // next index window (splits longer than kIdxWin)
+        if (t % kWinTiles == 0) {  // next index window (splits longer than one window)
           load_window(t / kWinTiles);
           store_window();
           __syncthreads();
@@ -675,7 +704,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
                            pack_bf16x2(a[4 * u + 2] * inv_l, a[4 * u + 3] * inv_l)};
         *reinterpret_cast<u32x2_t*>(srow + 64 * db + 16 * u) = v;
       }
-    uint16_t* dst = nsplit == 1 ? o + row * kH * kDc : part_o + (row * nsplit + sp) * kH * kDc;
+    uint16_t* dst = (nsplit == 1 ? o + row * kH * kDc : part_o + (row * nsplit + sp) * kH * kDc) + head0 * kDc;
 #pragma unroll 4
     for (int k = 0; k < 32; ++k) {
       const int hh = 32 * wave + k;
@@ -684,7 +713,7 @@ mla_mfma(int T, int S, int W, int kps, int nsplit, int xcd_map, float sm_scale,
     }
   }
   if (hl == 0) {
-    const int h = 32 * wave + m;
+    const int h = head0 + 32 * wave + m;
     const float v = l_run > 0.f ? (m_ref + __log2f(l_run)) * kLn2 : -__builtin_inff();
     if (nsplit > 1)
       part_lse[(row * kH + h) * nsplit + sp] = v;
@@ -758,10 +787,11 @@ struct MlaPlan {
   bool mfma;
   int splits;
   int kps;  // index entries per split (multiple of the tile)
+  int nw;   // waves per workgroup: 4 (128 heads) or 2 (64 heads, two workgroups per split)
 };
 
 MlaPlan plan(const dsa_shape_t& s) {
-  MlaPlan p{false, 1, k_eff(s)};
+  MlaPlan p{false, 1, k_eff(s), 4};
   if (!(s.H == kH && s.Dc == kDc && s.Dr == kDr && s.mla_dtype == DSA_BF16)) return p;
   p.mfma = true;
   const int W = k_eff(s);
@@ -776,6 +806,9 @@ MlaPlan plan(const dsa_shape_t& s) {
   splits = (W + kps - 1) / kps;
   p.splits = splits < 1 ? 1 : splits;
   p.kps = kps;
+  // still fewer workgroups than CUs: split the heads as well, two workgroups
+  // of 64 heads per split, placed on one XCD (each gathers the same rows)
+  if (rows * p.splits * 2 <= cus) p.nw = 2;
   return p;
 }
 
@@ -833,11 +866,18 @@ dsa_status_t launch_sparse_mla(const dsa_shape_t& s, const void* q, const void* 
       part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + (po + 255) / 256 * 256);
     }
     const int xcd_map = (p.splits > 1 && rows % 8 == 0) ? 1 : 0;
+    const unsigned wgs = static_cast<unsigned>(rows * p.splits * (4 / p.nw));
     LaunchTimer timer;
-    hipExtLaunchKernelGGL(mla_mfma, dim3(static_cast<unsigned>(rows * p.splits)), dim3(kMlaThreads), 0,
-                          stream, timer.start(), timer.stop(), 0, s.T, s.S, W, p.kps, p.splits, xcd_map,
-                          s.sm_scale, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
-                          idx, static_cast<uint16_t*>(o), lse, part_o, part_lse);
+    auto attend = [&](auto kernel) {
+      hipExtLaunchKernelGGL(kernel, dim3(wgs), dim3(p.nw * 64), 0, stream, timer.start(), timer.stop(), 0,
+                            s.T, s.S, W, p.kps, p.splits, xcd_map, s.sm_scale,
+                            static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv), idx,
+                            static_cast<uint16_t*>(o), lse, part_o, part_lse);
+    };
+    if (p.nw == 2)
+      attend(mla_mfma<2>);
+    else
+      attend(mla_mfma<4>);
     dsa_status_t st = timer.done("mla_mfma");
     if (st != DSA_OK || p.splits == 1) return st;
     const int64_t total_heads = rows * kH;
