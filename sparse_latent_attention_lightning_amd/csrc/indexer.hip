@@ -120,11 +120,12 @@ constexpr int kIdxDim = 128;
 // 64 heads] x [128 dims] x [S keys], with the ReLU-weighted head sum applied
 // to every 64-head column.  Streaming the key rows once per query (as the
 // decode kernel does) would make the kernel bound by key traffic, so here a
-// block of 4 waves takes 4 consecutive queries of one sequence, one per wave,
-// and streams every key the 4 of them see through LDS once (two such blocks
-// share a CU, so one block's MFMAs run while the other waits at a barrier):
-//  * keys move in 64-key chunks (16 KB) through a ring of 4 LDS buffers,
-//    copied global -> LDS by the DMA path, four 1 KB copies per wave per chunk;
+// block of 8 waves (two per SIMD, one block per CU) takes 8 consecutive
+// queries of one sequence, one per wave, and streams every key the 8 of them
+// see through LDS once:
+//  * keys move in 64-key chunks (16 KB) through a ring of 8 LDS buffers (six
+//    chunks in flight while one is scored), copied global -> LDS by the DMA
+//    path, two 1 KB copies per wave per chunk;
 //    a key row is 256 bytes = 16 pieces of 16 bytes, and piece c of row r sits
 //    in slot c ^ ((r & 7) << 1) of the row, so that the operand reads (lane
 //    (g, n): row n, piece 4 ks + g) touch all 64 banks in every cycle;
@@ -140,21 +141,23 @@ constexpr int kIdxDim = 128;
 // Blocks run longest first (the causal key range grows with the query index),
 // which balances the triangular work over the CUs.
 // ---------------------------------------------------------------------------
-constexpr int kPfWaves = 4;                                  // queries per block
+constexpr int kPfWaves = 4;                                  // e4m3: queries per block
 constexpr int kPfChunkKeys = 64;
 constexpr int kPfRowBytes = kIdxDim * 2;                     // 256
 constexpr int kPfChunkBytes = kPfChunkKeys * kPfRowBytes;    // 16 KB
-constexpr int kPfBuffers = 4;
+constexpr int kPfBuffers = 4;                                // e4m3: chunks in the LDS ring
 constexpr int kPfMinQueries = 8;   // fewer queries per sequence use the per-query kernel
-constexpr int kPfCopies = kPfChunkBytes / 1024 / kPfWaves;  // 1 KB copies per wave per chunk
-static_assert(kPfCopies * kPfWaves * 1024 == kPfChunkBytes, "whole copies per wave");
+constexpr int kPfQueries = 8;      // bf16: queries (waves) per block, one block per CU
+constexpr int kPfRing = 8;         // bf16: chunks in the LDS ring (128 KB)
+constexpr int kPfCopies = kPfChunkBytes / 1024 / kPfQueries;  // 1 KB copies per wave per chunk
+static_assert(kPfCopies * kPfQueries * 1024 == kPfChunkBytes, "whole copies per wave");
 
 template <int WDT>
-__global__ void __launch_bounds__(kPfWaves * 64)
+__global__ void __launch_bounds__(kPfQueries * 64)
 indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __restrict__ q_idx,
                 const uint16_t* __restrict__ k_idx, const void* __restrict__ w,
                 const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPfBuffers * kPfChunkBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPfRing * kPfChunkBytes];
   debug_poison_lds<sizeof(kbuf)>(kbuf);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -163,22 +166,22 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
   const int nb = gridDim.x / n_qblk;                 // sequences
   const int qb = n_qblk - 1 - static_cast<int>(blockIdx.x) / nb;   // longest first
   const int b = static_cast<int>(blockIdx.x) % nb;
-  const int t0 = qb * kPfWaves;
+  const int t0 = qb * kPfQueries;
   const int t = t0 + wave;
   const bool has_q = t < T;
   const int tq = min(t, T - 1);
   const int L = seq_len(seq_lens, b, S);
   const int q_pos = L - T + tq;
-  const int kend = max(0, L - T + min(t0 + kPfWaves, T));  // keys [0, kend) are visible to some query
+  const int kend = max(0, L - T + min(t0 + kPfQueries, T));  // keys [0, kend) are visible to some query
   const int nchunks = (kend + kPfChunkKeys - 1) / kPfChunkKeys;
   const int64_t kbase = static_cast<int64_t>(b) * S;
   const uint32_t kb_lds = lds_addr(kbuf);
 
-  // chunk c -> buffer c % kPfBuffers; this wave copies chunk rows
+  // chunk c -> buffer c % kPfRing; this wave copies chunk rows
   // 4 kPfCopies wave .. 4 kPfCopies (wave + 1) - 1
   // (keys past S - 1 load row S - 1: every address stays in bounds)
   auto issue_chunk = [&](int c) {
-    const uint32_t dst = kb_lds + (c % kPfBuffers) * kPfChunkBytes + wave * kPfCopies * 1024;
+    const uint32_t dst = kb_lds + (c % kPfRing) * kPfChunkBytes + wave * kPfCopies * 1024;
 #pragma unroll
     for (int i = 0; i < kPfCopies; ++i) {
       const int r = (wave * kPfCopies + i) * 4 + (lane >> 4);
@@ -188,7 +191,7 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
     }
   };
 #pragma unroll
-  for (int c = 0; c < kPfBuffers - 1; ++c)
+  for (int c = 0; c < kPfRing - 1; ++c)
     if (c < nchunks) issue_chunk(c);
 
   // ---- the query tile (A operands) and head weights, in registers ----
@@ -251,18 +254,21 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
   float part[4];
   for (int c = 0; c < nchunks; ++c) {
     // chunk c has landed: the copies issued after it are those of chunks
-    // c + 1 .. min(c + kPfBuffers - 2, nchunks - 1), two per chunk (the first
+    // c + 1 .. min(c + kPfRing - 2, nchunks - 1), two per chunk (the first
     // chunk also waits for the query loads, issued after the copies)
-    const int later = min(kPfBuffers - 2, nchunks - 1 - c);
-    if (c == 0 || later <= 0)
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if (later == 1)
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPfCopies) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPfCopies) : "memory");
+    const int later = c == 0 ? 0 : max(0, min(kPfRing - 2, nchunks - 1 - c));
+    switch (later) {
+      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPfCopies) : "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPfCopies) : "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kPfCopies) : "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * kPfCopies) : "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * kPfCopies) : "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * kPfCopies) : "memory"); break;
+    }
     __syncthreads();   // every wave's copies of chunk c are in; chunk c - 1 is consumed
-    if (c + kPfBuffers - 1 < nchunks) issue_chunk(c + kPfBuffers - 1);
-    const uint8_t* buf = kbuf + (c % kPfBuffers) * kPfChunkBytes;
+    if (c + kPfRing - 1 < nchunks) issue_chunk(c + kPfRing - 1);
+    const uint8_t* buf = kbuf + (c % kPfRing) * kPfChunkBytes;
     tile_mfma(buf, 0, acc0);
     if (c > 0) {
       part[3] = tile_part(acc1);
@@ -881,13 +887,13 @@ template <int WDT>
 dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_idx,
                          const void* w, const int32_t* seq_lens, float* scores,
                          hipStream_t stream) {
-  const int n_qblk = (s.T + kPfWaves - 1) / kPfWaves;
+  const int n_qblk = (s.T + kPfQueries - 1) / kPfQueries;
   const int64_t blocks = static_cast<int64_t>(n_qblk) * s.B;
   if (blocks > 0x7fffffff)
     return fail(DSA_ERR_UNSUPPORTED, "indexer: %lld query blocks", static_cast<long long>(blocks));
   LaunchTimer timer;
   hipExtLaunchKernelGGL(indexer_prefill<WDT>, dim3(static_cast<unsigned>(blocks)),
-                        dim3(kPfWaves * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
+                        dim3(kPfQueries * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
                         n_qblk, s.idx_scale, static_cast<const uint16_t*>(q_idx),
                         static_cast<const uint16_t*>(k_idx), w, seq_lens, scores);
   return timer.done("indexer_prefill");
