@@ -281,6 +281,16 @@ def test_mla_mfma_decode(dsa, B):
     _mla_check(dsa, cfg, _random_idx(cfg, np.random.default_rng(B)), rb)
 
 
+@pytest.mark.parametrize("B,K", [(8, 64), (3, 2048)])
+def test_mla_mfma_head_halves(dsa, B, K):
+    """Few query rows: two 2-wave workgroups of 64 heads per split (B=8, K=64:
+    one split, so each writes its heads of o directly; B=3: 16 splits and the
+    merge)."""
+    cfg = g.CONFIGS["decode_8k"].replace(B=B, K=K)
+    rb, _ = _rows(cfg)
+    _mla_check(dsa, cfg, _random_idx(cfg, np.random.default_rng(100 + B)), rb)
+
+
 def test_mla_mfma_prefill_rows(dsa):
     """MFMA kernel without splits (many query rows), causal-style short rows."""
     cfg = g.CONFIGS["prefill_16k"].replace(T=300, S=2500)
