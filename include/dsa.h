@@ -131,7 +131,9 @@ dsa_status_t dsa_indexer_scores_ragged(const dsa_shape_t* shape, const int32_t* 
  * indices in ascending order and is padded with -1 when fewer than K_eff
  * scores are selectable.  The result is exact (no approximation).
  * ws/ws_bytes: workspace of at least dsa_workspace_bytes(shape, DSA_ENTRY_TOPK)
- * bytes (may be NULL/0 when that is 0).
+ * bytes (may be NULL/0 when that is 0); its contents before the call do not
+ * matter, and calls sharing one workspace must not overlap.  B*T <= 65535 and
+ * S <= 8388608, else DSA_ERR_UNSUPPORTED before any launch.
  */
 dsa_status_t dsa_topk(const dsa_shape_t* shape, const float* scores, int32_t* idx,
                       void* ws, size_t ws_bytes, void* stream);

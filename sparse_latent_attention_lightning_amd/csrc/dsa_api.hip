@@ -122,8 +122,10 @@ size_t indexer_topk_total_bytes(const dsa_shape_t& s) {
   return indexer_topk_scores_bytes(s) + align_up(indexer_select_workspace_bytes(s));
 }
 
-// A tag per call of the fused selection: distinct across calls of this
-// process (a random start plus a counter), 39 bits.
+}  // namespace
+
+// A tag per call of a launch whose workgroups meet through the workspace:
+// distinct across calls of this process (a random start plus a counter), 39 bits.
 uint64_t next_call_tag() {
   static std::atomic<uint64_t> counter{0};
   static const uint64_t salt = [] {
@@ -132,8 +134,6 @@ uint64_t next_call_tag() {
   }();
   return (salt + counter.fetch_add(1, std::memory_order_relaxed)) & ((uint64_t(1) << 39) - 1);
 }
-
-}  // namespace
 
 dsa_status_t fail(dsa_status_t st, const char* fmt, ...) {
   va_list ap;

@@ -49,6 +49,15 @@ __device__ __forceinline__ float ue8m0_to_f32(uint8_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 23);
 }
 
+// Workgroups of one launch that meet through words of the caller's
+// workspace tag those words with the call's own 39-bit tag; a word holding
+// another tag is stale and counts as zero.  The meeting's last workgroup
+// marks the words stale (tag with bit 39 set) so that a replay of the same
+// call starts afresh.  A workgroup that waits for another, already running,
+// one polls at most kSelWaitSpins rounds of about 256 cycles.
+constexpr uint64_t kTagStale = uint64_t(1) << 39;
+constexpr int kSelWaitSpins = 1 << 20;
+
 // Order-preserving key of an fp32 score: larger score -> larger key.
 // -0 is folded into +0; NaN and -inf map to 0, which no selectable score
 // reaches (the smallest selectable key, that of -FLT_MAX, is 0x00800000).

@@ -39,6 +39,10 @@ class LaunchTimer {
   long gen_ = 0;    // the session the slot belongs to
 };
 
+// A tag per call of a launch whose workgroups meet through the workspace:
+// distinct across calls of this process (39 bits).
+uint64_t next_call_tag();
+
 inline int32_t k_eff(const dsa_shape_t& s) { return s.K < s.S ? s.K : s.S; }
 
 // ---- index scores -------------------------------------------------------

@@ -524,8 +524,6 @@ struct StreamShape {
 // has the whole row: it selects the row's top-K (select_row.h) and writes
 // idx, then marks both words stale (tag with bit 39 set), so that a replay
 // of the same call starts afresh.  The scores never leave the workspace.
-constexpr uint64_t kTagStale = uint64_t(1) << 39;
-constexpr int kSelWaitSpins = 1 << 20;  // rounds of about 256 cycles
 
 struct SelectArgs {
   int32_t* idx;       // [rows, K]

@@ -320,29 +320,382 @@ dsa_status_t run_select(int per_wg, bool vec, dim3 grid, int n_in, int64_t in_st
   return timer.done(SRC_CAND ? "topk_merge" : OUT_CAND ? "topk_chunk" : "topk_select");
 }
 
+// ---------------------------------------------------------------------------
+// Long rows (more keys than one workgroup holds), in two launches over the
+// row's chunks of kLongChunk keys, one workgroup per chunk.  The chunks of a
+// row meet through per-row words of the workspace guarded by the call's tag,
+// so nothing needs zeroing beforehand:
+//   meet[0] = tag << 24 | arrivals of launch 1 << 12   (12-bit counts)
+//   meet[1] = the tag once the row's histogram has been zeroed for this call
+//   meet[2] = tag << 24 | arrivals of launch 2         (24-bit count)
+// A word holding another tag is stale (an earlier call, or whatever the
+// workspace held) and counts as zero.
+//  1. topk_long_hist: a chunk's 12-bit histogram of its selectable keys is
+//     added into the row's with device-scope atomics; the row's first
+//     arriving workgroup zeroes the row's histogram first and publishes the
+//     tag in meet[1], which later arrivals wait for (the first one is
+//     already running, so the wait ends).
+//  2. topk_long_gather: every workgroup finds the bin holding the row's K-th
+//     key from the complete histogram and stores its chunk's selectable keys
+//     in that bin or above it (every selectable key when the row has at most
+//     K) as (key, index) pairs, in index order, into the chunk's slot (device-
+//     scope stores).  The row's last arriving workgroup narrows the K-th key
+//     k_T from the pairs inside the boundary bin (two 10-bit levels) and,
+//     where keys equal to k_T must be split by index, the highest index taken
+//     i_T (three 9-bit levels, lowest index first); it writes the indices of
+//     the pairs with key > k_T, or key == k_T and index <= i_T, in chunk
+//     order (so ascending), pads the row with -1, and marks the row's words
+//     stale so that a replay of the same call starts afresh.
+// The same (score, index) order as the single-workgroup select.
+// ---------------------------------------------------------------------------
+constexpr int kLongThreads = 1024;
+constexpr int kLongWaves = kLongThreads / 64;
+constexpr int kLongE = 4;                             // keys per thread
+constexpr int kLongChunk = kLongThreads * kLongE;     // 4096 keys per workgroup
+constexpr int kLongBins = 4096;                       // 12-bit first level
+constexpr int kLongBins2 = 1024;                      // 10-bit key levels
+constexpr int kLongBins3 = 512;                       // 9-bit index levels
+constexpr int kLongMaxChunks = 2048;                  // chunk offsets in the tail's LDS
+constexpr int kLongMeetWords = 4;                     // uint64 per row
+constexpr int kLongHeld = 8;                          // pairs per thread in the tail's registers
+
+// exclusive prefix sum over the workgroup's threads; *total gets the sum.
+// One barrier; wave_tot must not be written again before the next barrier.
+__device__ __forceinline__ uint32_t long_scan(uint32_t v, uint32_t* wave_tot, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_inclusive_scan(v);
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kLongWaves; ++w) {
+    const uint32_t t = wave_tot[w];
+    before += w < wave ? t : 0u;
+    tot += t;
+  }
+  *total = tot;
+  return before + inc - v;
+}
+
+// The bin where the running count reaches k (from the top bin down when DESC,
+// from bin 0 up otherwise) and the count before it, into sel[0], sel[1]
+// (published by the caller's next barrier); returns the histogram's total.
+template <int NB, bool DESC>
+__device__ __forceinline__ uint32_t long_boundary(const uint32_t* h, uint32_t k, uint32_t* wave_tot,
+                                                  uint32_t* sel) {
+  constexpr int per = NB / kLongThreads > 0 ? NB / kLongThreads : 1;
+  const int t = static_cast<int>(threadIdx.x);
+  uint32_t c[per];
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    const int i = t * per + j;
+    c[j] = i < NB ? h[DESC ? NB - 1 - i : i] : 0u;
+    local += c[j];
+  }
+  uint32_t tot;
+  uint32_t acc = long_scan(local, wave_tot, &tot);
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    if (acc < k && k <= acc + c[j]) {
+      const int i = t * per + j;
+      sel[0] = static_cast<uint32_t>(DESC ? NB - 1 - i : i);
+      sel[1] = acc;
+    }
+    acc += c[j];
+  }
+  return tot;
+}
+
+// This thread's kLongE keys of the chunk starting at c0 (keys past the row
+// are 0: never selectable); thread t holds keys [kLongE t, kLongE t + kLongE).
+template <bool VEC>
+__device__ __forceinline__ void long_load(const float* row_scores, int S, int c0, uint32_t (&key)[kLongE]) {
+  const int i0 = c0 + static_cast<int>(threadIdx.x) * kLongE;
+  if (VEC && i0 + kLongE <= S) {
+    const float4 f4 = *reinterpret_cast<const float4*>(row_scores + i0);  // read again by the second launch
+    key[0] = score_key(f4.x); key[1] = score_key(f4.y); key[2] = score_key(f4.z); key[3] = score_key(f4.w);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kLongE; ++j) key[j] = i0 + j < S ? score_key(row_scores[i0 + j]) : 0u;
+  }
+}
+
+// Arrival on a tagged word: returns the arrival count including this one
+// (1 for the arrival that installs the call's tag).  A compare and swap is
+// retried only while the word is stale.
+__device__ __forceinline__ uint32_t long_arrive(uint64_t* word, uint64_t tag, uint64_t one, uint64_t count_mask) {
+  uint64_t old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    if ((old >> 24) == tag) {
+      const uint64_t prev = __hip_atomic_fetch_add(word, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return static_cast<uint32_t>(((prev / one) & count_mask) + 1);
+    }
+    if (__hip_atomic_compare_exchange_strong(word, &old, (tag << 24) | one, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return 1u;
+  }
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kLongThreads)
+topk_long_hist(int S, const float* __restrict__ scores, uint64_t* __restrict__ meet, uint32_t* __restrict__ hist,
+               uint64_t tag) {
+  __shared__ uint32_t h[kLongBins];
+  __shared__ uint32_t first;
+  debug_poison_lds<sizeof(h)>(h);
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.y;
+  uint32_t key[kLongE];
+  long_load<VEC>(scores + row * S, S, blockIdx.x * kLongChunk, key);
+  for (int i = tid; i < kLongBins; i += kLongThreads) h[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kLongE; ++j)
+    if (key[j] != 0u) atomicAdd(&h[key[j] >> 20], 1u);
+  uint64_t* st = meet + row * kLongMeetWords;
+  uint32_t* gh = hist + row * kLongBins;
+  if (tid == 0) first = long_arrive(st, tag, uint64_t(1) << 12, 0xfffu) == 1u ? 1u : 0u;
+  __syncthreads();
+  if (first) {  // the first arrival: a zeroed row histogram, then the tag
+    for (int i = tid; i < kLongBins; i += kLongThreads)
+      __hip_atomic_store(gh + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(st + 1, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (tid == 0) {  // wait for the first arrival's zeroing (it is running)
+    for (int spin = 0; spin < kSelWaitSpins &&
+                       __hip_atomic_load(st + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != tag;
+         ++spin)
+      __builtin_amdgcn_s_sleep(4);
+  }
+  __syncthreads();
+  for (int i = tid; i < kLongBins; i += kLongThreads) {
+    const uint32_t c = h[i];
+    if (c != 0u) __hip_atomic_fetch_add(gh + i, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(kLongThreads)
+topk_long_gather(int S, int K, int nchunk, const float* __restrict__ scores, uint64_t* __restrict__ meet,
+                 const uint32_t* __restrict__ hist, uint32_t* __restrict__ counts, uint64_t* __restrict__ pairs,
+                 int32_t* __restrict__ idx_out, uint64_t tag) {
+  // the row histogram; in the tail, [0, 1024) the narrowing histograms and
+  // [1024, 1024 + nchunk] the chunks' pair offsets
+  __shared__ __attribute__((aligned(16))) uint32_t h[kLongBins];
+  __shared__ uint32_t wave_tot[2][kLongWaves];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t last;
+  debug_poison_lds<sizeof(h)>(h);
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.y;
+  const int chunk = blockIdx.x;
+  const int c0 = chunk * kLongChunk;
+  uint32_t key[kLongE];
+  long_load<VEC>(scores + row * S, S, c0, key);
+  reinterpret_cast<u32x4_t*>(h)[tid] = reinterpret_cast<const u32x4_t*>(hist + row * kLongBins)[tid];
+  __syncthreads();
+  const uint32_t nvalid = long_boundary<kLongBins, true>(h, static_cast<uint32_t>(K), wave_tot[0], sel);
+  __syncthreads();
+  const bool all = nvalid <= static_cast<uint32_t>(K);
+  const uint32_t b1 = all ? 0u : sel[0];
+  const uint32_t above1 = all ? 0u : sel[1];
+  // the chunk's pairs: selectable keys in the boundary bin or above, index order
+  uint32_t in = 0u;
+#pragma unroll
+  for (int j = 0; j < kLongE; ++j) in |= static_cast<uint32_t>(key[j] != 0u && (key[j] >> 20) >= b1) << j;
+  uint32_t m;
+  uint32_t pos = long_scan(static_cast<uint32_t>(__builtin_popcount(in)), wave_tot[1], &m);
+  uint64_t* slot = pairs + (row * nchunk + chunk) * static_cast<int64_t>(kLongChunk);
+  const int i0 = c0 + tid * kLongE;
+#pragma unroll
+  for (int j = 0; j < kLongE; ++j)
+    if ((in >> j) & 1u)
+      __hip_atomic_store(slot + pos++, (static_cast<uint64_t>(key[j]) << 32) | static_cast<uint32_t>(i0 + j),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(counts + row * nchunk + chunk, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's pair stores are complete
+  __syncthreads();
+  uint64_t* st = meet + row * kLongMeetWords;
+  if (tid == 0) last = long_arrive(st + 2, tag, 1u, 0xffffffu) == static_cast<uint32_t>(nchunk) ? 1u : 0u;
+  __syncthreads();
+  if (!last) return;
+
+  // ---- the row's last workgroup: every chunk's pairs are stored ----
+  uint32_t* offs = h + kLongBins2;  // offs[c] = pairs before chunk c, offs[nchunk] = all
+  {
+    uint32_t cnt[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = 2 * tid + q;
+      cnt[q] = c < nchunk ? __hip_atomic_load(counts + row * nchunk + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : 0u;
+    }
+    uint32_t tot;
+    const uint32_t before = long_scan(cnt[0] + cnt[1], wave_tot[0], &tot);
+    if (2 * tid < nchunk) offs[2 * tid] = before;
+    if (2 * tid + 1 < nchunk) offs[2 * tid + 1] = before + cnt[0];
+    if (tid == 0) offs[nchunk] = tot;
+  }
+  __syncthreads();
+  const uint32_t M = offs[nchunk];
+  const uint64_t* row_pairs = pairs + row * nchunk * static_cast<int64_t>(kLongChunk);
+  // Pairs in chunk order are visited in rounds of kLongHeld * kLongThreads:
+  // thread t holds pairs base + kLongHeld t + r in registers.  A row with at
+  // most one round of pairs (the usual case) loads them once; a larger one
+  // reloads its rounds on every pass.  A pair's chunk: binary search over
+  // offs, all of a thread's searches in lockstep.
+  constexpr uint32_t kRound = kLongHeld * kLongThreads;
+  int top = nchunk > 1 ? 1 : 0;   // the largest power of two <= nchunk - 1
+  while (top != 0 && 2 * top <= nchunk - 1) top *= 2;
+  uint64_t held[kLongHeld];
+  auto load_round = [&](uint32_t base) {
+    int c[kLongHeld];
+#pragma unroll
+    for (int r = 0; r < kLongHeld; ++r) c[r] = 0;
+    const uint32_t v0 = base + static_cast<uint32_t>(tid) * kLongHeld;
+    for (int step = top; step > 0; step >>= 1)
+#pragma unroll
+      for (int r = 0; r < kLongHeld; ++r) {
+        const int nc = c[r] + step;
+        if (nc < nchunk && offs[nc] <= v0 + r) c[r] = nc;
+      }
+#pragma unroll
+    for (int r = 0; r < kLongHeld; ++r) {
+      const uint32_t v = v0 + r;
+      held[r] = v < M ? __hip_atomic_load(row_pairs + static_cast<int64_t>(c[r]) * kLongChunk + (v - offs[c[r]]),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                      : 0u;
+    }
+  };
+  const bool one_round = M <= kRound;
+  if (one_round) load_round(0);
+  // f(pair) for every pair (pairs past M are 0: key 0, never counted)
+  auto visit = [&](auto&& f) {
+    for (uint32_t base = 0; base < M; base += kRound) {
+      if (!one_round) load_round(base);
+#pragma unroll
+      for (int r = 0; r < kLongHeld; ++r) f(held[r]);
+    }
+  };
+  uint32_t k_t = 1u;               // selected: key > k_t, or key == k_t and index <= i_t
+  uint32_t i_t = 0xffffffffu;
+  const uint32_t ksel = all ? nvalid : static_cast<uint32_t>(K);
+  if (!all) {
+    uint32_t k_rem = static_cast<uint32_t>(K) - above1;   // from the boundary bin: 1 .. its size
+    uint32_t prefix = b1 << 20;
+#pragma unroll 1
+    for (int lvl = 0; lvl < 2; ++lvl) {
+      const int shift = lvl == 0 ? 10 : 0;
+      const uint32_t mask = lvl == 0 ? 0xfff00000u : 0xfffffc00u;
+      h[tid] = 0u;
+      __syncthreads();
+      visit([&](uint64_t pr) {
+        const uint32_t kk = static_cast<uint32_t>(pr >> 32);
+        if (kk != 0u && (kk & mask) == prefix) atomicAdd(&h[(kk >> shift) & (kLongBins2 - 1)], 1u);
+      });
+      __syncthreads();
+      (void)long_boundary<kLongBins2, true>(h, k_rem, wave_tot[lvl], sel);
+      __syncthreads();
+      prefix |= sel[0] << shift;
+      k_rem -= sel[1];
+    }
+    k_t = prefix;                                 // the exact K-th key; k_rem of its equals are taken
+    const uint32_t n_eq = h[k_t & (kLongBins2 - 1)];
+    if (n_eq > k_rem) {
+      // equal keys split by index: the k_rem-th smallest index among them
+      uint32_t iprefix = 0u, imask = 0u, i_rem = k_rem;
+#pragma unroll 1
+      for (int lvl = 0; lvl < 3; ++lvl) {
+        const int shift = 18 - 9 * lvl;
+        __syncthreads();
+        if (tid < kLongBins3) h[tid] = 0u;
+        __syncthreads();
+        visit([&](uint64_t pr) {
+          const uint32_t ii = static_cast<uint32_t>(pr);
+          if (static_cast<uint32_t>(pr >> 32) == k_t && (ii & imask) == iprefix)
+            atomicAdd(&h[(ii >> shift) & (kLongBins3 - 1)], 1u);
+        });
+        __syncthreads();
+        (void)long_boundary<kLongBins3, false>(h, i_rem, wave_tot[lvl & 1], sel);
+        __syncthreads();
+        iprefix |= sel[0] << shift;
+        imask |= static_cast<uint32_t>(kLongBins3 - 1) << shift;
+        i_rem -= sel[1];
+      }
+      i_t = iprefix;
+    }
+  }
+  // the selected pairs in chunk order: ascending indices
+  int32_t* out = idx_out + row * K;
+  uint32_t written = 0u;
+  int it = 0;
+#pragma unroll 1
+  for (uint32_t base = 0; base < M; base += kRound, ++it) {
+    if (!one_round) load_round(base);
+    uint32_t take = 0u;
+#pragma unroll
+    for (int r = 0; r < kLongHeld; ++r) {
+      const uint32_t kk = static_cast<uint32_t>(held[r] >> 32);
+      const uint32_t ii = static_cast<uint32_t>(held[r]);
+      const bool t = kk != 0u && (all || kk > k_t || (kk == k_t && ii <= i_t));
+      take |= static_cast<uint32_t>(t) << r;
+    }
+    uint32_t tot;
+    uint32_t p = written + long_scan(static_cast<uint32_t>(__builtin_popcount(take)), wave_tot[it & 1], &tot);
+#pragma unroll
+    for (int r = 0; r < kLongHeld; ++r)
+      if (((take >> r) & 1u) && p < static_cast<uint32_t>(K))  // p < ksel by construction
+        out[p++] = static_cast<int32_t>(static_cast<uint32_t>(held[r]));
+    written += tot;
+  }
+  for (int j = static_cast<int>(ksel) + tid; j < K; j += kLongThreads) out[j] = -1;
+  if (tid == 0) {
+    __hip_atomic_store(st, (tag | kTagStale) << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(st + 1, tag | kTagStale, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(st + 2, (tag | kTagStale) << 24, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 struct TopkPlan {
-  int chunks;      // stage-1 chunks per row (1 = single stage)
+  int chunks;      // chunks per row (1 = one workgroup per row)
   int chunk_elems;
+  bool long_rows;  // the two-launch long-row select
 };
 
-// Rows longer than one workgroup's capacity: the smaller chunk (16 K
-// elements) when its candidate lists still fit one merge workgroup, since it
-// spreads stage 1 over twice the workgroups; else 32 K.
+// Rows longer than one workgroup's capacity: exact per-chunk candidates and
+// one merge workgroup per row, with the smaller chunk (16 K elements) when
+// its candidate lists still fit the merge, since it spreads stage 1 over
+// twice the workgroups, else 32 K.  Rows whose candidates fit neither (more
+// than 16 chunks of K, or K of a chunk or more) take the long-row select.
 TopkPlan plan(const dsa_shape_t& s) {
-  TopkPlan p{1, s.S};
-  if (s.S > kChunkElems) {
-    const int64_t K = k_eff(s);
-    p.chunk_elems = kChunkElems;
-    for (int ce = kChunkElems / 2; ce <= kChunkElems; ce *= 2) {
-      const int64_t chunks = (s.S + ce - 1) / ce;
-      if (chunks * K <= kChunkElems && K < ce) {
-        p.chunk_elems = ce;
-        break;
-      }
+  TopkPlan p{1, s.S, false};
+  if (s.S <= kChunkElems) return p;
+  const int64_t K = k_eff(s);
+  for (int ce = kChunkElems / 2; ce <= kChunkElems; ce *= 2) {
+    const int64_t chunks = (s.S + ce - 1) / ce;
+    if (chunks * K <= kChunkElems && K < ce) {
+      p.chunk_elems = ce;
+      p.chunks = static_cast<int>(chunks);
+      return p;
     }
-    p.chunks = (s.S + p.chunk_elems - 1) / p.chunk_elems;
   }
+  p.long_rows = true;
+  p.chunk_elems = kLongChunk;
+  p.chunks = (s.S + kLongChunk - 1) / kLongChunk;
   return p;
+}
+
+// long-row workspace: per row the meeting words, the 12-bit histogram, the
+// chunks' pair counts and a slot of kLongChunk pairs per chunk
+struct LongWs {
+  size_t meet_words, hist_words, cnt_words, pair_words;  // uint64, uint32, uint32, uint64
+};
+LongWs long_ws(const dsa_shape_t& s, const TopkPlan& p) {
+  const size_t rows = static_cast<size_t>(s.B) * s.T;
+  return LongWs{rows * kLongMeetWords, rows * kLongBins, (rows * p.chunks + 63) / 64 * 64,
+                rows * p.chunks * static_cast<size_t>(kLongChunk)};
 }
 
 }  // namespace
@@ -350,6 +703,10 @@ TopkPlan plan(const dsa_shape_t& s) {
 size_t topk_workspace_bytes(const dsa_shape_t& s) {
   const TopkPlan p = plan(s);
   if (p.chunks == 1) return 0;
+  if (p.long_rows) {
+    const LongWs w = long_ws(s, p);
+    return (w.meet_words + w.pair_words) * sizeof(uint64_t) + (w.hist_words + w.cnt_words) * sizeof(uint32_t);
+  }
   const size_t rows = static_cast<size_t>(s.B) * s.T;
   return rows * p.chunks * k_eff(s) * (sizeof(uint32_t) + sizeof(int32_t));
 }
@@ -360,13 +717,46 @@ dsa_status_t topk_check(const dsa_shape_t& s) {
     return fail(DSA_ERR_UNSUPPORTED, "topk: B*T = %lld exceeds 65535 rows",
                 static_cast<long long>(rows));
   const TopkPlan p = plan(s);
-  const int K = k_eff(s);
-  if (p.chunks > 1 && (static_cast<int64_t>(p.chunks) * K > kChunkElems || K >= p.chunk_elems))
-    return fail(DSA_ERR_UNSUPPORTED, "topk: S = %d with K = %d needs more than two stages", s.S, K);
+  if (p.long_rows && p.chunks > kLongMaxChunks)
+    return fail(DSA_ERR_UNSUPPORTED, "topk: S = %d exceeds the long-row select's %d keys", s.S,
+                kLongMaxChunks * kLongChunk);
   return DSA_OK;
 }
 
 namespace {
+dsa_status_t long_rows_launch(const dsa_shape_t& s, const TopkPlan& p, const float* scores, int32_t* idx,
+                              void* ws, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(s.B) * s.T;
+  const int K = k_eff(s);
+  const LongWs w = long_ws(s, p);
+  uint64_t* meet = static_cast<uint64_t*>(ws);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(meet + w.meet_words);
+  uint32_t* counts = hist + w.hist_words;
+  uint64_t* pairs = reinterpret_cast<uint64_t*>(counts + w.cnt_words);
+  const uint64_t tag = next_call_tag();
+  const bool vec = s.S % 4 == 0;
+  const dim3 grid(p.chunks, rows), block(kLongThreads);
+  {
+    LaunchTimer t;
+    if (vec)
+      hipExtLaunchKernelGGL(topk_long_hist<true>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, scores, meet,
+                            hist, tag);
+    else
+      hipExtLaunchKernelGGL(topk_long_hist<false>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, scores, meet,
+                            hist, tag);
+    const dsa_status_t st = t.done("topk_long_hist");
+    if (st != DSA_OK) return st;
+  }
+  LaunchTimer t;
+  if (vec)
+    hipExtLaunchKernelGGL(topk_long_gather<true>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, K, p.chunks,
+                          scores, meet, hist, counts, pairs, idx, tag);
+  else
+    hipExtLaunchKernelGGL(topk_long_gather<false>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, K, p.chunks,
+                          scores, meet, hist, counts, pairs, idx, tag);
+  return t.done("topk_long_gather");
+}
+
 dsa_status_t topk_launches(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
   dsa_status_t st = topk_check(s);
@@ -378,10 +768,11 @@ dsa_status_t topk_launches(const dsa_shape_t& s, const float* scores, int32_t* i
     return run_select<false, false>(s.S, s.S % 4 == 0, dim3(1, rows), s.S, s.S, s.S, scores,
                                     nullptr, nullptr, K, idx, nullptr, stream);
   }
-  const int64_t n2 = static_cast<int64_t>(p.chunks) * K;
   const size_t need = topk_workspace_bytes(s);
   if (ws == nullptr || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "topk: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (p.long_rows) return long_rows_launch(s, p, scores, idx, ws, stream);
+  const int64_t n2 = static_cast<int64_t>(p.chunks) * K;
   int32_t* cand_idx = static_cast<int32_t*>(ws);
   uint32_t* cand_key = reinterpret_cast<uint32_t*>(cand_idx + rows * n2);
   st = run_select<false, true>(p.chunk_elems, s.S % 4 == 0, dim3(p.chunks, rows), s.S,

@@ -67,6 +67,11 @@ def test_workspace_sizes(dsa):
     assert dsa.workspace_bytes(long, dsa.ENTRY_TOPK) == 8 * 8 * 2048 * 8  # 8 chunks of 16 K keys
     longer = _v32(dsa, B=1, S=300000)  # 19 chunks of 16 K would overflow one merge: 10 of 32 K
     assert dsa.workspace_bytes(longer, dsa.ENTRY_TOPK) == 10 * 2048 * 8
+    # candidates that fit no merge (19 chunks of 32 K): the long-row select, per
+    # row 4 meeting words, a 4096-bin histogram, one pair count per 4096-key
+    # chunk (rounded up to 64 over all rows) and 4096 (key, index) pairs per chunk
+    longest = _v32(dsa, B=1, S=600000)  # 147 chunks, the last one ragged
+    assert dsa.workspace_bytes(longest, dsa.ENTRY_TOPK) == 32 + 4096 * 4 + 192 * 4 + 147 * 4096 * 8
     prefill = _v32(dsa, B=1, T=16384, S=16384)
     assert dsa.workspace_bytes(prefill, dsa.ENTRY_SPARSE_MLA) == 0         # no splits
     with pytest.raises(dsa.DsaError):
@@ -147,7 +152,7 @@ def test_forward_workspace_too_small(dsa):
 
 @pytest.mark.parametrize("over,msg", [
     (dict(B=65536), "65535 rows"),                 # one grid row per query row in top-K and attention
-    (dict(B=1, S=600000), "two stages"),           # top-K candidates of more than 16 chunks of 32768
+    (dict(B=1, S=2048 * 4096 + 1), "long-row select's 8388608 keys"),  # the top-K's 2048 chunks of 4096
 ])
 def test_forward_shape_limits_fail_before_any_launch(dsa, over, msg):
     """dsa_forward checks every step's limits before its first launch: without a

@@ -203,11 +203,12 @@ def _special_rows(S, K, rng):
 
 
 # rows up to 32768 keys: one workgroup; longer rows: 16 K-key chunks (40000,
-# 131072), or 32 K-key chunks when the candidates of the 16 K chunks would not
-# fit one merge workgroup (300000: 19 chunks x 2048 > 32768)
+# 40001, 131072) or 32 K-key chunks (300000: 19 chunks x 2048 > 32768) and a
+# merge; candidates that fit no merge: the long-row select over 4096-key
+# chunks (600000 keys; K of 30000 over 100003 keys)
 @pytest.mark.parametrize("S,K", [(256, 32), (1000, 64), (3000, 2048), (8192, 2048),
-                                 (16384, 2048), (40000, 2048), (131072, 2048), (300000, 2048),
-                                 (100, 300)])
+                                 (16384, 2048), (40000, 2048), (40001, 2048), (131072, 2048),
+                                 (300000, 2048), (600000, 2048), (100003, 30000), (100, 300)])
 def test_topk_bit_exact(dsa, S, K):
     print(f"[topk] S={S} K={K}", flush=True)
     torch = U.torch()
@@ -219,6 +220,72 @@ def test_topk_bit_exact(dsa, S, K):
     ref = oracle.topk(cfg, sc)
     for r in range(cfg.B):
         assert np.array_equal(got[r], ref[r]), f"row {r} differs"
+
+
+def _long_rows(S, rng):
+    rows = [rng.standard_normal(S).astype(np.float32)]                     # real-valued
+    rows.append(rng.integers(-3, 4, S).astype(np.float32))                # heavy ties: split by index
+    r = np.full(S, -np.inf, np.float32)
+    r[rng.choice(S, size=1500, replace=False)] = rng.standard_normal(1500)  # fewer than K selectable
+    rows.append(r)
+    rows.append(np.full(S, 0.25, np.float32))                              # one value everywhere
+    return np.stack(rows)
+
+
+def test_topk_long_rows_reuse_workspace(dsa):
+    """The long-row select's workgroups meet through tagged words of the
+    workspace: from arbitrary bytes, three calls in a row on one workspace,
+    each on other rows, each give the oracle's selection.  (K = 8192 over
+    131077 keys: candidates that fit no merge; more pairs than the last
+    workgroup holds in registers.)"""
+    torch = U.torch()
+    S, K = 131072 + 5, 8192
+    cfg = g.CONFIGS["decode_8k"].replace(B=4, T=1, S=S, K=K)
+    shape = U.shape_of(cfg)
+    ws = torch.empty(dsa.workspace_bytes(shape, dsa.ENTRY_TOPK), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)
+    for rep in range(3):
+        print(f"[topk_long] reuse call {rep}", flush=True)
+        sc = np.roll(_long_rows(S, np.random.default_rng(100 + rep)), rep, axis=0)
+        got = dsa.dsa_topk(shape, torch.from_numpy(sc).cuda().view(cfg.B, 1, S), ws=ws)
+        got = got.cpu().numpy().reshape(cfg.B, -1)
+        assert np.array_equal(got, oracle.topk(cfg, sc)), f"call {rep} differs"
+
+
+def test_topk_long_rows_graph_replay(dsa):
+    """Captured once in a HIP graph (the call's tag fixed at capture), the
+    long-row select gives the oracle's selection on every replay, with eager
+    calls in between: the row's last workgroup marks its words stale.
+    (K = 12000 over 70000 keys takes the long-row select.)"""
+    torch = U.torch()
+    S, K = 70000, 12000
+    cfg = g.CONFIGS["decode_8k"].replace(B=4, T=1, S=S, K=K)
+    shape = U.shape_of(cfg)
+    sc = torch.from_numpy(_long_rows(S, np.random.default_rng(7))).cuda().view(cfg.B, 1, S)
+    ws = torch.empty(dsa.workspace_bytes(shape, dsa.ENTRY_TOPK), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)
+    out = torch.empty((cfg.B, 1, K), dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dsa.dsa_topk(shape, sc, out=out, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dsa.dsa_topk(shape, sc, out=out, ws=ws)
+    for rep in range(3):
+        print(f"[topk_long] replay {rep}", flush=True)
+        rows = np.roll(_long_rows(S, np.random.default_rng(200 + rep)), rep, axis=0)
+        sc.copy_(torch.from_numpy(rows).view(cfg.B, 1, S))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.topk(cfg, rows)
+        assert np.array_equal(out.cpu().numpy().reshape(cfg.B, -1), ref), f"replay {rep} differs"
+        eager = dsa.dsa_topk(shape, sc)                  # the program's own work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(eager.cpu().numpy().reshape(cfg.B, -1), ref)
 
 
 def test_topk_on_gpu_scores(dsa):
