@@ -166,9 +166,12 @@ dsa_status_t forward_on(const dsa_shape_t& s, const int32_t* seq_lens, const voi
   if ((st = check_mla_args(q, kv, idx, o)) != DSA_OK) return st;
   // every step's shape limits before the first launch: a failing call enqueues nothing
   if ((st = topk_check(s)) != DSA_OK || (st = mla_check(s)) != DSA_OK) return st;
-  if ((st = launch_indexer(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, hs)) != DSA_OK)
+  // the scores stay in the workspace: the top-K ignores each row past its
+  // query's position, so the indexer need not write the keys there
+  if ((st = launch_indexer(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, false, hs)) != DSA_OK)
     return st;
-  if ((st = launch_topk(s, scores, idx, base + L.topk_ws, L.mla_ws - L.topk_ws, hs)) != DSA_OK)
+  if ((st = launch_topk(s, scores, seq_lens, true, idx, base + L.topk_ws, L.mla_ws - L.topk_ws, hs)) !=
+      DSA_OK)
     return st;
   return launch_sparse_mla(s, q, kv, idx, o, lse, base + L.mla_ws, L.total - L.mla_ws, hs);
 }
@@ -315,7 +318,7 @@ dsa_status_t dsa_indexer_scores_ragged(const dsa_shape_t* shape, const int32_t* 
   if (st != DSA_OK) return st;
   if ((st = check_indexer_args(*shape, q_idx, q_sf, k_idx, k_sf, w, scores)) != DSA_OK) return st;
   if ((st = check_seq_lens(seq_lens)) != DSA_OK) return st;
-  return launch_indexer(*shape, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores,
+  return launch_indexer(*shape, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, true,
                         static_cast<hipStream_t>(stream));
 }
 
@@ -332,7 +335,7 @@ dsa_status_t dsa_topk(const dsa_shape_t* shape, const float* scores, int32_t* id
   if (st != DSA_OK) return st;
   if ((st = need(scores, "scores")) || (st = need(idx, "idx"))) return st;
   if (ws != nullptr && !aligned16(ws)) return fail(DSA_ERR_INVALID_ARG, "ws is not 16-byte aligned");
-  return launch_topk(*shape, scores, idx, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return launch_topk(*shape, scores, nullptr, false, idx, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 dsa_status_t dsa_indexer_topk(const dsa_shape_t* shape, const int32_t* seq_lens,

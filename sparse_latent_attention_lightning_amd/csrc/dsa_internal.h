@@ -46,10 +46,15 @@ uint64_t next_call_tag();
 inline int32_t k_eff(const dsa_shape_t& s) { return s.K < s.S ? s.K : s.S; }
 
 // ---- index scores -------------------------------------------------------
-// seq_lens: device int32 [B] context lengths of a ragged batch, or nullptr
+// seq_lens: device int32 [B] context lengths of a ragged batch, or nullptr.
+// full_rows: every score of a row is written (keys past the query's position
+// get -inf); false lets the many-query kernels leave the keys past a query
+// block's last visible one unwritten, for a consumer that ignores each row
+// past its query's position (launch_topk with causal_rows).
 dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                             const void* k_idx, const uint8_t* k_sf, const void* w,
-                            const int32_t* seq_lens, float* scores, hipStream_t stream);
+                            const int32_t* seq_lens, float* scores, bool full_rows,
+                            hipStream_t stream);
 
 // The index scores with the top-K selection fused in (decode: fewer than 8
 // queries per sequence, V3.2 indexer shapes): scores go to `scores` (scratch),
@@ -67,8 +72,12 @@ dsa_status_t launch_indexer_select(const dsa_shape_t& s, const void* q_idx, cons
 // with fail) it would return; launches nothing.
 dsa_status_t topk_check(const dsa_shape_t& s);
 size_t topk_workspace_bytes(const dsa_shape_t& s);
-dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
-                         size_t ws_bytes, hipStream_t stream);
+// causal_rows: row (b, t) holds scores only for its causally visible keys
+// [0, L_b - T + t + 1) (L_b = seq_lens[b] clamped to [0, S], or S without
+// seq_lens; the length clamped to [0, S]); whatever the rest of the row's
+// memory holds is ignored.  Else every row holds S scores.
+dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, const int32_t* seq_lens,
+                         bool causal_rows, int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // ---- cache fill and indexer inputs ---------------------------------------
 size_t cache_fill_workspace_bytes(int N, int D);

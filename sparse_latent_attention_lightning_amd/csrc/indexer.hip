@@ -156,7 +156,8 @@ template <int WDT>
 __global__ void __launch_bounds__(kPfQueries * 64)
 indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __restrict__ q_idx,
                 const uint16_t* __restrict__ k_idx, const void* __restrict__ w,
-                const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
+                const int32_t* __restrict__ seq_lens, float* __restrict__ scores,
+                int full_rows) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPfRing * kPfChunkBytes];
   debug_poison_lds<sizeof(kbuf)>(kbuf);
   const int lane = threadIdx.x & 63;
@@ -286,7 +287,7 @@ indexer_prefill(int T, int S, int n_qblk, float idx_scale, const uint16_t* __res
     chunk_store(nchunks - 1, part);
   }
   // keys past the block's last chunk are in every query's future
-  if (has_q) {
+  if (has_q && full_rows) {
     const int k0 = nchunks * kPfChunkKeys;
     if ((S & 3) == 0) {
       const f32x4_t ninf = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
@@ -333,7 +334,8 @@ __global__ void __launch_bounds__(kPfWaves * 64)
 indexer_prefill_fp8(int T, int S, int n_qblk, float idx_scale, const uint8_t* __restrict__ q_idx,
                     const uint8_t* __restrict__ q_sf, const uint8_t* __restrict__ k_idx,
                     const uint8_t* __restrict__ k_sf, const void* __restrict__ w,
-                    const int32_t* __restrict__ seq_lens, float* __restrict__ scores) {
+                    const int32_t* __restrict__ seq_lens, float* __restrict__ scores,
+                    int full_rows) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[kPfBuffers * kPf8Stride];
   debug_poison_lds<sizeof(kbuf)>(kbuf);
   const int lane = threadIdx.x & 63;
@@ -460,7 +462,7 @@ indexer_prefill_fp8(int T, int S, int n_qblk, float idx_scale, const uint8_t* __
     half_store(buf, c, 1, part);
   }
   // keys past the block's last chunk are in every query's future
-  if (has_q) {
+  if (has_q && full_rows) {
     const int k0 = nchunks * kPf8ChunkKeys;
     for (int k = k0 + lane; k < S; k += 64) __builtin_nontemporal_store(-__builtin_inff(), out_row + k);
   }
@@ -868,7 +870,7 @@ dsa_status_t run_stream(const dsa_shape_t& s, const void* q_idx, const uint8_t* 
 template <int WDT>
 dsa_status_t run_prefill_fp8(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                              const void* k_idx, const uint8_t* k_sf, const void* w,
-                             const int32_t* seq_lens, float* scores, hipStream_t stream) {
+                             const int32_t* seq_lens, float* scores, bool full_rows, hipStream_t stream) {
   const int n_qblk = (s.T + kPfWaves - 1) / kPfWaves;
   const int64_t blocks = static_cast<int64_t>(n_qblk) * s.B;
   if (blocks > 0x7fffffff)
@@ -877,13 +879,13 @@ dsa_status_t run_prefill_fp8(const dsa_shape_t& s, const void* q_idx, const uint
   hipExtLaunchKernelGGL(indexer_prefill_fp8<WDT>, dim3(static_cast<unsigned>(blocks)),
                         dim3(kPfWaves * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
                         n_qblk, s.idx_scale, static_cast<const uint8_t*>(q_idx), q_sf,
-                        static_cast<const uint8_t*>(k_idx), k_sf, w, seq_lens, scores);
+                        static_cast<const uint8_t*>(k_idx), k_sf, w, seq_lens, scores, full_rows ? 1 : 0);
   return timer.done("indexer_prefill_fp8");
 }
 
 template <int WDT>
 dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_idx,
-                         const void* w, const int32_t* seq_lens, float* scores,
+                         const void* w, const int32_t* seq_lens, float* scores, bool full_rows,
                          hipStream_t stream) {
   const int n_qblk = (s.T + kPfQueries - 1) / kPfQueries;
   const int64_t blocks = static_cast<int64_t>(n_qblk) * s.B;
@@ -893,7 +895,7 @@ dsa_status_t run_prefill(const dsa_shape_t& s, const void* q_idx, const void* k_
   hipExtLaunchKernelGGL(indexer_prefill<WDT>, dim3(static_cast<unsigned>(blocks)),
                         dim3(kPfQueries * 64), 0, stream, timer.start(), timer.stop(), 0, s.T, s.S,
                         n_qblk, s.idx_scale, static_cast<const uint16_t*>(q_idx),
-                        static_cast<const uint16_t*>(k_idx), w, seq_lens, scores);
+                        static_cast<const uint16_t*>(k_idx), w, seq_lens, scores, full_rows ? 1 : 0);
   return timer.done("indexer_prefill");
 }
 
@@ -933,18 +935,19 @@ dsa_status_t launch_indexer_select(const dsa_shape_t& s, const void* q_idx, cons
 
 dsa_status_t launch_indexer(const dsa_shape_t& s, const void* q_idx, const uint8_t* q_sf,
                             const void* k_idx, const uint8_t* k_sf, const void* w,
-                            const int32_t* seq_lens, float* scores, hipStream_t stream) {
+                            const int32_t* seq_lens, float* scores, bool full_rows,
+                            hipStream_t stream) {
   const bool v32 = s.HI == kIdxHeads && s.DI == kIdxDim;
   const bool wbf = s.w_dtype == DSA_BF16;
   if (v32 && s.idx_dtype == DSA_BF16 && s.T >= kPfMinQueries)
-    return wbf ? run_prefill<DSA_BF16>(s, q_idx, k_idx, w, seq_lens, scores, stream)
-               : run_prefill<DSA_F32>(s, q_idx, k_idx, w, seq_lens, scores, stream);
+    return wbf ? run_prefill<DSA_BF16>(s, q_idx, k_idx, w, seq_lens, scores, full_rows, stream)
+               : run_prefill<DSA_F32>(s, q_idx, k_idx, w, seq_lens, scores, full_rows, stream);
   if (v32 && s.idx_dtype == DSA_BF16)
     return wbf ? run_stream<false, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
                : run_stream<false, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);
   if (v32 && s.idx_dtype == DSA_FP8_E4M3 && s.T >= kPfMinQueries && s.S % 4 == 0)
-    return wbf ? run_prefill_fp8<DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
-               : run_prefill_fp8<DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);
+    return wbf ? run_prefill_fp8<DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, full_rows, stream)
+               : run_prefill_fp8<DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, full_rows, stream);
   if (v32 && s.idx_dtype == DSA_FP8_E4M3)
     return wbf ? run_stream<true, DSA_BF16>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream)
                : run_stream<true, DSA_F32>(s, q_idx, q_sf, k_idx, k_sf, w, seq_lens, scores, stream);

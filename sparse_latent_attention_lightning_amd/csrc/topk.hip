@@ -105,12 +105,24 @@ __device__ __forceinline__ uint32_t find_boundary(const uint32_t* hist, uint32_t
   return tot;
 }
 
+// The keys row `row` holds: n_in; with causal_T > 0 (rows of causal queries,
+// causal_T of them per sequence) only the ones its query sees, [0, L_b - T +
+// t + 1) for row (b, t), L_b the sequence's length (seq_lens[b] clamped to
+// [0, n_in], or n_in), the count clamped to [0, n_in]; whatever the rest of
+// the row's memory holds counts as key 0.
+__device__ __forceinline__ int row_keys(int64_t row, int n_in, int causal_T, const int32_t* seq_lens) {
+  if (causal_T <= 0) return n_in;
+  const int t = static_cast<int>(row % causal_T);
+  const int L = seq_lens == nullptr ? n_in : min(max(seq_lens[row / causal_T], 0), n_in);
+  return min(max(L - causal_T + t + 1, 0), n_in);
+}
+
 // SRC_CAND: elements come from a candidate list (key, index) instead of fp32
 // scores.  OUT_CAND: the result is a candidate list (key and index written).
 // VEC: every thread's run of E inputs starts 16-byte aligned (16-byte loads).
 template <int E, bool SRC_CAND, bool OUT_CAND, bool VEC>
 __global__ void __launch_bounds__(kTopkThreads, (E <= 16 && !SRC_CAND && !OUT_CAND) ? 8 : 1)
-topk_select(int n_in, int64_t in_stride, int chunk_elems,
+topk_select(int n_in, int causal_T, const int32_t* __restrict__ seq_lens, int64_t in_stride, int chunk_elems,
             const float* __restrict__ scores, const uint32_t* __restrict__ cand_key_in,
             const int32_t* __restrict__ cand_idx_in, int K_out, int32_t* __restrict__ idx_out,
             uint32_t* __restrict__ cand_key_out) {
@@ -119,9 +131,11 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.y;
   const int chunk = blockIdx.x;
-  // this workgroup's elements: [elem0, elem0 + n) of the row's input
+  // this workgroup's elements: [elem0, elem0 + n) of the row's input, of the
+  // [elem0, elem0 + n_mem) it holds in memory
   const int elem0 = chunk * chunk_elems;
-  const int n = min(chunk_elems, n_in - elem0);
+  const int n_mem = min(chunk_elems, n_in - elem0);
+  const int n = min(n_mem, row_keys(row, n_in, causal_T, seq_lens) - elem0);
   const int64_t in_base = row * in_stride + elem0;
   const int64_t out_base = (row * gridDim.x + chunk) * static_cast<int64_t>(K_out);
 
@@ -129,7 +143,7 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
   uint32_t key[E];
   int32_t id[SRC_CAND ? E : 1];  // candidate indices; a score's index is its position
   const int i0 = tid * E;
-  if (VEC && i0 + E <= n) {
+  if (VEC && i0 + E <= n_mem) {
 #pragma unroll
     for (int j = 0; j < E; j += 4) {
       if constexpr (SRC_CAND) {
@@ -143,22 +157,30 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
         key[j + 2] = score_key(f4.z); key[j + 3] = score_key(f4.w);
       }
     }
+    // a run that reaches past the row's n elements (what the memory holds
+    // there is not a score of this row): those count as key 0
+    if (i0 + E > n) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) key[j] &= 0u - static_cast<uint32_t>(i0 + j < n);
+    }
   } else {
+    // the chunk's ragged end (or rows not 16-byte aligned): every load issued
+    // before any is used, at positions clamped into the chunk's memory,
+    // elements past n masked to key 0 (a branch per element would wait for
+    // each load in turn)
+    const int last = max(n, 1) - 1;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      const int i = i0 + j;
-      if (i < n) {
-        if constexpr (SRC_CAND) {
-          key[j] = cand_key_in[in_base + i];
-          id[j] = cand_idx_in[in_base + i];
-        } else {
-          key[j] = score_key(scores[in_base + i]);
-        }
+      const int i = min(i0 + j, last);
+      if constexpr (SRC_CAND) {
+        key[j] = cand_key_in[in_base + i];
+        id[j] = cand_idx_in[in_base + i];
       } else {
-        key[j] = 0u;
-        if constexpr (SRC_CAND) id[j] = -1;
+        key[j] = score_key(scores[in_base + i]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < E; ++j) key[j] &= 0u - static_cast<uint32_t>(i0 + j < n);
   }
   // the row index of element j of this thread (keys of elements past the
   // input are 0, so they are never taken and their index is never used)
@@ -300,14 +322,16 @@ topk_select(int n_in, int64_t in_stride, int chunk_elems,
 }
 
 template <bool SRC_CAND, bool OUT_CAND>
-dsa_status_t run_select(int per_wg, bool vec, dim3 grid, int n_in, int64_t in_stride,
+dsa_status_t run_select(int per_wg, bool vec, dim3 grid, int n_in, int causal_T, const int32_t* seq_lens,
+                        int64_t in_stride,
                         int chunk_elems, const float* scores, const uint32_t* ck_in,
                         const int32_t* ci_in, int K_out, int32_t* idx_out, uint32_t* ck_out,
                         hipStream_t stream) {
   LaunchTimer timer;
 #define DSA_TOPK_LAUNCH(EV, VEC)                                                                \
   hipExtLaunchKernelGGL(topk_select<EV, SRC_CAND, OUT_CAND, VEC>, grid, dim3(kTopkThreads), 0,  \
-                        stream, timer.start(), timer.stop(), 0, n_in, in_stride, chunk_elems,   \
+                        stream, timer.start(), timer.stop(), 0, n_in, causal_T, seq_lens,       \
+                        in_stride, chunk_elems,                                                 \
                         scores, ck_in, ci_in, K_out, idx_out, ck_out)
   if (per_wg <= 8 * kTopkThreads) {
     if (vec) DSA_TOPK_LAUNCH(8, true); else DSA_TOPK_LAUNCH(8, false);
@@ -407,18 +431,22 @@ __device__ __forceinline__ uint32_t long_boundary(const uint32_t* h, uint32_t k,
   return tot;
 }
 
-// This thread's kLongE keys of the chunk starting at c0 (keys past the row
-// are 0: never selectable); thread t holds keys [kLongE t, kLongE t + kLongE).
+// This thread's kLongE keys of the chunk starting at c0 of a row of S scores
+// in memory, of which the first n count (the rest are key 0: never
+// selectable); thread t holds keys [kLongE t, kLongE t + kLongE).  Loads are
+// all issued before any is used (positions clamped into the row), then masked.
 template <bool VEC>
-__device__ __forceinline__ void long_load(const float* row_scores, int S, int c0, uint32_t (&key)[kLongE]) {
+__device__ __forceinline__ void long_load(const float* row_scores, int S, int n, int c0, uint32_t (&key)[kLongE]) {
   const int i0 = c0 + static_cast<int>(threadIdx.x) * kLongE;
   if (VEC && i0 + kLongE <= S) {
     const float4 f4 = *reinterpret_cast<const float4*>(row_scores + i0);  // read again by the second launch
     key[0] = score_key(f4.x); key[1] = score_key(f4.y); key[2] = score_key(f4.z); key[3] = score_key(f4.w);
   } else {
 #pragma unroll
-    for (int j = 0; j < kLongE; ++j) key[j] = i0 + j < S ? score_key(row_scores[i0 + j]) : 0u;
+    for (int j = 0; j < kLongE; ++j) key[j] = score_key(row_scores[min(i0 + j, S - 1)]);
   }
+#pragma unroll
+  for (int j = 0; j < kLongE; ++j) key[j] &= 0u - static_cast<uint32_t>(i0 + j < n);
 }
 
 // Arrival on a tagged word: returns the arrival count including this one
@@ -439,15 +467,15 @@ __device__ __forceinline__ uint32_t long_arrive(uint64_t* word, uint64_t tag, ui
 
 template <bool VEC>
 __global__ void __launch_bounds__(kLongThreads)
-topk_long_hist(int S, const float* __restrict__ scores, uint64_t* __restrict__ meet, uint32_t* __restrict__ hist,
-               uint64_t tag) {
+topk_long_hist(int S, int causal_T, const int32_t* __restrict__ seq_lens, const float* __restrict__ scores,
+               uint64_t* __restrict__ meet, uint32_t* __restrict__ hist, uint64_t tag) {
   __shared__ uint32_t h[kLongBins];
   __shared__ uint32_t first;
   debug_poison_lds<sizeof(h)>(h);
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.y;
   uint32_t key[kLongE];
-  long_load<VEC>(scores + row * S, S, blockIdx.x * kLongChunk, key);
+  long_load<VEC>(scores + row * S, S, row_keys(row, S, causal_T, seq_lens), blockIdx.x * kLongChunk, key);
   for (int i = tid; i < kLongBins; i += kLongThreads) h[i] = 0u;
   __syncthreads();
 #pragma unroll
@@ -478,7 +506,8 @@ topk_long_hist(int S, const float* __restrict__ scores, uint64_t* __restrict__ m
 
 template <bool VEC>
 __global__ void __launch_bounds__(kLongThreads)
-topk_long_gather(int S, int K, int nchunk, const float* __restrict__ scores, uint64_t* __restrict__ meet,
+topk_long_gather(int S, int causal_T, const int32_t* __restrict__ seq_lens, int K, int nchunk,
+                 const float* __restrict__ scores, uint64_t* __restrict__ meet,
                  const uint32_t* __restrict__ hist, uint32_t* __restrict__ counts, uint64_t* __restrict__ pairs,
                  int32_t* __restrict__ idx_out, uint64_t tag) {
   // the row histogram; in the tail, [0, 1024) the narrowing histograms and
@@ -493,7 +522,7 @@ topk_long_gather(int S, int K, int nchunk, const float* __restrict__ scores, uin
   const int chunk = blockIdx.x;
   const int c0 = chunk * kLongChunk;
   uint32_t key[kLongE];
-  long_load<VEC>(scores + row * S, S, c0, key);
+  long_load<VEC>(scores + row * S, S, row_keys(row, S, causal_T, seq_lens), c0, key);
   reinterpret_cast<u32x4_t*>(h)[tid] = reinterpret_cast<const u32x4_t*>(hist + row * kLongBins)[tid];
   __syncthreads();
   const uint32_t nvalid = long_boundary<kLongBins, true>(h, static_cast<uint32_t>(K), wave_tot[0], sel);
@@ -724,8 +753,8 @@ dsa_status_t topk_check(const dsa_shape_t& s) {
 }
 
 namespace {
-dsa_status_t long_rows_launch(const dsa_shape_t& s, const TopkPlan& p, const float* scores, int32_t* idx,
-                              void* ws, hipStream_t stream) {
+dsa_status_t long_rows_launch(const dsa_shape_t& s, const TopkPlan& p, const float* scores, int causal_T,
+                              const int32_t* seq_lens, int32_t* idx, void* ws, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(s.B) * s.T;
   const int K = k_eff(s);
   const LongWs w = long_ws(s, p);
@@ -739,55 +768,54 @@ dsa_status_t long_rows_launch(const dsa_shape_t& s, const TopkPlan& p, const flo
   {
     LaunchTimer t;
     if (vec)
-      hipExtLaunchKernelGGL(topk_long_hist<true>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, scores, meet,
-                            hist, tag);
+      hipExtLaunchKernelGGL(topk_long_hist<true>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, causal_T,
+                            seq_lens, scores, meet, hist, tag);
     else
-      hipExtLaunchKernelGGL(topk_long_hist<false>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, scores, meet,
-                            hist, tag);
+      hipExtLaunchKernelGGL(topk_long_hist<false>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, causal_T,
+                            seq_lens, scores, meet, hist, tag);
     const dsa_status_t st = t.done("topk_long_hist");
     if (st != DSA_OK) return st;
   }
   LaunchTimer t;
   if (vec)
-    hipExtLaunchKernelGGL(topk_long_gather<true>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, K, p.chunks,
-                          scores, meet, hist, counts, pairs, idx, tag);
+    hipExtLaunchKernelGGL(topk_long_gather<true>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, causal_T,
+                          seq_lens, K, p.chunks, scores, meet, hist, counts, pairs, idx, tag);
   else
-    hipExtLaunchKernelGGL(topk_long_gather<false>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, K, p.chunks,
-                          scores, meet, hist, counts, pairs, idx, tag);
+    hipExtLaunchKernelGGL(topk_long_gather<false>, grid, block, 0, stream, t.start(), t.stop(), 0, s.S, causal_T,
+                          seq_lens, K, p.chunks, scores, meet, hist, counts, pairs, idx, tag);
   return t.done("topk_long_gather");
 }
 
-dsa_status_t topk_launches(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
-                           size_t ws_bytes, hipStream_t stream) {
+dsa_status_t topk_launches(const dsa_shape_t& s, const float* scores, int causal_T, const int32_t* seq_lens,
+                           int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
   dsa_status_t st = topk_check(s);
   if (st != DSA_OK) return st;
   const int64_t rows = static_cast<int64_t>(s.B) * s.T;
   const int K = k_eff(s);
   const TopkPlan p = plan(s);
   if (p.chunks == 1) {
-    return run_select<false, false>(s.S, s.S % 4 == 0, dim3(1, rows), s.S, s.S, s.S, scores,
-                                    nullptr, nullptr, K, idx, nullptr, stream);
+    return run_select<false, false>(s.S, s.S % 4 == 0, dim3(1, rows), s.S, causal_T, seq_lens, s.S, s.S,
+                                    scores, nullptr, nullptr, K, idx, nullptr, stream);
   }
   const size_t need = topk_workspace_bytes(s);
   if (ws == nullptr || ws_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "topk: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  if (p.long_rows) return long_rows_launch(s, p, scores, idx, ws, stream);
+  if (p.long_rows) return long_rows_launch(s, p, scores, causal_T, seq_lens, idx, ws, stream);
   const int64_t n2 = static_cast<int64_t>(p.chunks) * K;
   int32_t* cand_idx = static_cast<int32_t*>(ws);
   uint32_t* cand_key = reinterpret_cast<uint32_t*>(cand_idx + rows * n2);
-  st = run_select<false, true>(p.chunk_elems, s.S % 4 == 0, dim3(p.chunks, rows), s.S,
-                                            s.S, p.chunk_elems, scores, nullptr, nullptr, K,
-                                            cand_idx, cand_key, stream);
+  st = run_select<false, true>(p.chunk_elems, s.S % 4 == 0, dim3(p.chunks, rows), s.S, causal_T, seq_lens,
+                               s.S, p.chunk_elems, scores, nullptr, nullptr, K, cand_idx, cand_key, stream);
   if (st != DSA_OK) return st;
-  return run_select<true, false>(static_cast<int>(n2), n2 % 4 == 0, dim3(1, rows),
-                                 static_cast<int>(n2), n2, static_cast<int>(n2), nullptr, cand_key,
-                                 cand_idx, K, idx, nullptr, stream);
+  return run_select<true, false>(static_cast<int>(n2), n2 % 4 == 0, dim3(1, rows), static_cast<int>(n2), 0,
+                                 nullptr, n2, static_cast<int>(n2), nullptr, cand_key, cand_idx, K, idx, nullptr,
+                                 stream);
 }
 }  // namespace
 
-dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, int32_t* idx, void* ws,
-                         size_t ws_bytes, hipStream_t stream) {
-  dsa_status_t st = topk_launches(s, scores, idx, ws, ws_bytes, stream);
+dsa_status_t launch_topk(const dsa_shape_t& s, const float* scores, const int32_t* seq_lens, bool causal_rows,
+                         int32_t* idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  dsa_status_t st = topk_launches(s, scores, causal_rows ? s.T : 0, seq_lens, idx, ws, ws_bytes, stream);
 #ifdef DSA_DEBUG
   if (st == DSA_OK)
     st = debug_check_idx(static_cast<int64_t>(s.B) * s.T, k_eff(s), s.S, true, idx, stream, "top-K output");

@@ -537,6 +537,33 @@ def test_forward_ragged(dsa):
     np.testing.assert_allclose(lse.cpu().numpy().reshape(cfg.B, cfg.H), rl, rtol=1e-4, atol=1e-4)
 
 
+@pytest.mark.parametrize("name,over,lens", [
+    ("prefill_16k", dict(T=300, S=300), None),                       # T = S: row t sees t + 1 keys
+    ("prefill_16k", dict(T=40, S=2500), None),                       # S > T: row t sees S - T + t + 1
+    ("prefill_16k_fp8", dict(T=40, S=2500), None),
+    ("prefill_16k", dict(B=3, T=40, S=2500), [2500, 1200, 20]),      # ragged: the last has rows that see nothing
+])
+def test_forward_reads_only_visible_scores(dsa, name, over, lens):
+    """Inside dsa_forward the many-query indexer leaves a causal row's
+    invisible keys unwritten and the top-K ignores each row past its query's
+    position: with the workspace filled with 0x7f bytes (each an unwritten
+    score of 3.4e38, which would be selected if it counted), the selection is
+    still the oracle's, exactly (integer twins)."""
+    torch = U.torch()
+    cfg = g.CONFIGS[name].replace(integer=True, **over)
+    print(f"[forward_visible] {cfg.name} {over} lens={lens}", flush=True)
+    x = _inputs(cfg)
+    shape = U.shape_of(cfg)
+    ws = torch.full((dsa.workspace_bytes(shape, dsa.ENTRY_FORWARD),), 0x7F, dtype=torch.uint8, device="cuda")
+    lens_dev = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    _, _, idx = dsa.dsa_forward_ragged(shape, lens_dev, x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"],
+                                       x["q_sf"], x["k_sf"], ws=ws)
+    rb, rt = _rows(cfg)
+    ref_sc = _oracle_scores(cfg, rb, rt, seq_lens=None if lens is None else np.array(lens, np.int32))
+    got = idx.cpu().numpy().reshape(cfg.B * cfg.T, -1)
+    assert np.array_equal(got, oracle.topk(cfg, ref_sc))
+
+
 FORWARD_CASES = {
     "decode_int": g.CONFIGS["decode_8k"].replace(B=4, integer=True),
     "decode_real": g.CONFIGS["decode_8k"].replace(B=4),
