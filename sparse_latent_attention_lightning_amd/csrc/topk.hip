@@ -22,6 +22,12 @@
 // index order, and a second pass selects the top-K of the candidates.  This is
 // exact: an element of the row's top-K has fewer than K elements ahead of it
 // in the (score, index) order within its chunk, so it survives its chunk.
+// Rows whose candidates would not fit one merge workgroup (more than 16
+// chunks of K, or K of a chunk or more) take the two-launch long-row select
+// described before its kernels.
+//
+// Inside the whole path, causal query rows hold scores only up to their
+// query's position; the rest of such a row's memory is masked to key 0.
 #include "dsa_device.h"
 #include "dsa_internal.h"
 

@@ -288,6 +288,51 @@ def test_topk_long_rows_graph_replay(dsa):
         assert np.array_equal(eager.cpu().numpy().reshape(cfg.B, -1), ref)
 
 
+def _random_topk_case(rng):
+    """One seeded (S, K, rows) case: lengths across the one-workgroup,
+    two-stage and long-row plans, K from 1 to past S, value patterns from
+    spread reals to heavy ties, NaN, -inf and +inf."""
+    S = int(rng.choice([int(rng.integers(1, 4097)), int(rng.integers(4097, 32769)),
+                        int(rng.integers(32769, 140000)), int(rng.integers(140000, 700000))]))
+    K = int(rng.choice([int(rng.integers(1, 65)), 2048, int(rng.integers(1, 40000)), S + int(rng.integers(0, 9))]))
+    B = int(rng.integers(1, 4))
+    rows = []
+    for _ in range(B):
+        kind = int(rng.integers(0, 5))
+        if kind == 0:
+            r = rng.standard_normal(S).astype(np.float32)
+        elif kind == 1:
+            r = rng.integers(-4, 5, S).astype(np.float32)
+        elif kind == 2:
+            r = (rng.standard_normal(S) * 10 ** rng.uniform(-30, 30)).astype(np.float32)
+        elif kind == 3:
+            r = rng.standard_normal(S).astype(np.float32)
+            r[rng.random(S) < 0.3] = -np.inf
+            r[rng.random(S) < 0.1] = np.nan
+            r[rng.random(S) < 0.001] = np.inf
+        else:
+            r = np.full(S, -np.inf, np.float32)
+            n = int(rng.integers(0, min(S, 3000) + 1))
+            r[rng.choice(S, size=n, replace=False)] = rng.integers(-2, 3, n).astype(np.float32)
+        rows.append(r)
+    return S, K, np.stack(rows)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_topk_random_shapes(dsa, seed):
+    """Seeded random shapes and value patterns: the selection equals the
+    oracle's bit for bit whichever plan the shape takes."""
+    torch = U.torch()
+    S, K, sc = _random_topk_case(np.random.default_rng(1000 + seed))
+    cfg = g.CONFIGS["decode_8k"].replace(B=sc.shape[0], T=1, S=S, K=K)
+    print(f"[topk_random] seed={seed} B={cfg.B} S={S} K={K}", flush=True)
+    got = dsa.dsa_topk(U.shape_of(cfg), torch.from_numpy(sc).cuda().view(cfg.B, 1, S))
+    got = got.cpu().numpy().reshape(cfg.B, -1)
+    ref = oracle.topk(cfg, sc)
+    for r in range(cfg.B):
+        assert np.array_equal(got[r], ref[r]), f"row {r} differs"
+
+
 def test_topk_on_gpu_scores(dsa):
     """Selection from the GPU's own fp32 scores matches the oracle's selection
     of those same scores exactly (decode 8k shape, real-valued)."""
