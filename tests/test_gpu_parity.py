@@ -587,6 +587,8 @@ def test_forward_ragged(dsa):
     ("prefill_16k", dict(T=40, S=2500), None),                       # S > T: row t sees S - T + t + 1
     ("prefill_16k_fp8", dict(T=40, S=2500), None),
     ("prefill_16k", dict(B=3, T=40, S=2500), [2500, 1200, 20]),      # ragged: the last has rows that see nothing
+    ("prefill_16k", dict(T=8, S=70000), None),                       # rows past one workgroup: two-stage top-K
+    ("prefill_16k", dict(T=8, S=70000, K=12000), None),              # candidates that fit no merge: long rows
 ])
 def test_forward_reads_only_visible_scores(dsa, name, over, lens):
     """Inside dsa_forward the many-query indexer leaves a causal row's
