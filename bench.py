@@ -733,7 +733,7 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calibration_mib, args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     if args.workload in FILL_WORKLOADS:
