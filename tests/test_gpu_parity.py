@@ -611,6 +611,45 @@ def test_forward_reads_only_visible_scores(dsa, name, over, lens):
     assert np.array_equal(got, oracle.topk(cfg, ref_sc))
 
 
+def _random_forward_case(rng, seed):
+    """One seeded dsa_forward shape: bf16 or e4m3 indexer, T from 1 (the
+    streaming kernels) to 48 (the many-query kernels), S up to 45000 (past
+    one top-K workgroup), K small, 2048 or past S, full or ragged contexts
+    (lengths 0 .. S); integer twins, so the selection is exact."""
+    base = "prefill_16k_fp8" if rng.random() < 0.4 else "prefill_16k"
+    B = int(rng.integers(1, 4))
+    S = int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(600, 5000)),
+                        int(rng.integers(33000, 45000))]))
+    T = int(rng.integers(1, min(S, 48) + 1))
+    K = int(rng.choice([int(rng.integers(1, 64)), 2048, S + 3]))
+    if S > 30000:
+        B, T = 1, int(rng.integers(1, 9))
+    cfg = g.CONFIGS[base].replace(B=B, T=T, S=S, K=K, integer=True, seed=seed + 1)
+    lens = [int(rng.integers(0, S + 1)) for _ in range(B)] if rng.random() < 0.5 else None
+    return cfg, lens
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_forward_random_shapes(dsa, seed):
+    """Seeded random dsa_forward shapes over a workspace of 0x7f bytes: the
+    selection equals the oracle's top-K of the oracle's scores, exactly."""
+    torch = U.torch()
+    cfg, lens = _random_forward_case(np.random.default_rng(70000 + seed), seed)
+    print(f"[forward_random] seed={seed} {cfg.name} B={cfg.B} T={cfg.T} S={cfg.S} K={cfg.K} lens={lens}",
+          flush=True)
+    x = _inputs(cfg)
+    shape = U.shape_of(cfg)
+    ws = torch.full((max(1, dsa.workspace_bytes(shape, dsa.ENTRY_FORWARD)),), 0x7F, dtype=torch.uint8,
+                    device="cuda")
+    lens_dev = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    _, _, idx = dsa.dsa_forward_ragged(shape, lens_dev, x["q_idx"], x["k_idx"], x["w"], x["q"], x["kv"],
+                                       x["q_sf"], x["k_sf"], ws=ws)
+    rb, rt = _rows(cfg)
+    ref_sc = _oracle_scores(cfg, rb, rt, seq_lens=None if lens is None else np.array(lens, np.int32))
+    got = idx.cpu().numpy().reshape(cfg.B * cfg.T, -1)
+    assert np.array_equal(got, oracle.topk(cfg, ref_sc))
+
+
 FORWARD_CASES = {
     "decode_int": g.CONFIGS["decode_8k"].replace(B=4, integer=True),
     "decode_real": g.CONFIGS["decode_8k"].replace(B=4),
