@@ -378,6 +378,49 @@ def _random_idx(cfg, rng, frac_invalid=0.0):
     return np.stack(rows)
 
 
+def _random_mla_case(rng, seed):
+    """One seeded attention case: the generic fp32 kernels (tiny shapes) or
+    the V3.2 MFMA kernel, B x T rows with K_eff from 1 to past 4096, each row
+    sorted distinct keys, unsorted with duplicates, with out-of-range
+    entries, empty, or ending in -1 padding."""
+    base = "tiny" if rng.random() < 0.15 else "decode_8k"
+    B, T = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+    S = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(300, 9000)), int(rng.integers(9000, 40000))]))
+    K = int(rng.choice([int(rng.integers(1, 65)), int(rng.integers(65, 2049)), 2048, S + 2]))
+    if base == "tiny":
+        S, K = min(S, 3000), min(K, 300)
+    if min(K, S) > 4096:
+        B, T = 1, min(T, 2)
+    cfg = g.CONFIGS[base].replace(B=B, T=T, S=S, K=K, seed=seed + 3)
+    W = cfg.K_eff
+    rows = []
+    for _ in range(B * T):
+        kind = int(rng.integers(0, 5))
+        if kind == 0:
+            r = np.sort(rng.choice(S, size=W, replace=False)).astype(np.int32)
+        elif kind == 1:
+            r = rng.integers(0, S, W).astype(np.int32)
+        elif kind == 2:
+            r = rng.integers(-3, S + 3, W).astype(np.int32)
+        elif kind == 3:
+            r = np.full(W, -1, np.int32)
+        else:
+            r = np.sort(rng.choice(S, size=W, replace=False)).astype(np.int32)
+            r[int(rng.integers(0, W + 1)):] = -1
+        rows.append(r)
+    return cfg, np.stack(rows)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_mla_random_shapes(dsa, seed):
+    """Seeded random attention shapes and index rows: o and lse within the
+    bar of the oracle's."""
+    cfg, idx_np = _random_mla_case(np.random.default_rng(90000 + seed), seed)
+    print(f"[mla_random] seed={seed} {cfg.name} B={cfg.B} T={cfg.T} S={cfg.S} K={cfg.K}", flush=True)
+    rb, _ = _rows(cfg)
+    _mla_check(dsa, cfg, idx_np, rb, x={n: U.upload(cfg, n) for n in ("q", "kv")})
+
+
 def test_mla_tiny_fp32(dsa):
     cfg = g.CONFIGS["tiny"]
     rb, rt = _rows(cfg)
