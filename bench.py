@@ -55,6 +55,10 @@ def parse():
                          "GRBM_GUI_ACTIVE and one of MfmaUtil")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="no GPU: the kernel table of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-stalls", metavar="DIR",
+                    help="no GPU: wave-cycle shares per kernel from a rocprofv3 --pmc run of "
+                         "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY "
+                         "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_INSTS_LDS")
     return ap.parse_args()
 
 
@@ -181,6 +185,31 @@ def summarize_pmc(fetch_dir, write_dir, mib, workload, out_path=None):
     json.dump(d, open(p, "w"), indent=1, sort_keys=True)
     print(f"calibration: {ck} copying {mib} MiB (last 5 dispatches) reads FETCH_SIZE {cf:,.0f} KiB "
           f"and WRITE_SIZE {cw:,.0f} KiB: factors {f_fetch:.4f} (fetch), {f_write:.4f} (write)\n")
+    print("\n".join(lines))
+
+
+def summarize_stalls(d):
+    """Per kernel, each SQ counter of the run as a share of the waves' cycles
+    (SQ_WAVE_CYCLES: cycles summed over the kernel's resident waves), plus
+    the LDS instructions per dispatch; values are the mean over dispatches."""
+    shares = ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+              "SQ_ACTIVE_INST_LDS")
+    base = _pmc_rows(d, "SQ_WAVE_CYCLES")
+    cols = {c: _pmc_rows(d, c) for c in shares + ("SQ_INSTS_LDS", "SQ_BUSY_CYCLES")}
+    lines = ["| kernel | dispatches | wave cycles | " + " | ".join(c[3:].lower() for c in shares) + " | LDS instructions |",
+             "|---|---|---|" + "---|" * len(shares) + "---|"]
+    for k in sorted(base):
+        if not k or k.startswith("__amd") or "elementwise" in k:
+            continue
+        n = len(base[k])
+        wc = sum(base[k].values()) / n
+        row = [k, str(n), f"{wc:,.0f}"]
+        for c in shares:
+            v = cols[c].get(k)
+            row.append(f"{100.0 * sum(v.values()) / n / wc:.1f} %" if v and wc else "—")
+        v = cols["SQ_INSTS_LDS"].get(k)
+        row.append(f"{sum(v.values()) / n:,.0f}" if v else "—")
+        lines.append("| " + " | ".join(row) + " |")
     print("\n".join(lines))
 
 
@@ -728,6 +757,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_stalls:
+        summarize_stalls(args.summarize_stalls)
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.calibration_mib, args.workload)
