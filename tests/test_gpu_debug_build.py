@@ -73,7 +73,8 @@ def _forward_check(dsa, cfg):
     ("decode_8k", dict(B=2, S=4096, integer=True)),                  # split attention + combine
     ("decode_64k_fp8", dict(B=2, S=4096, integer=True)),             # e4m3 streaming indexer
     ("prefill_16k", dict(T=40, S=2500, integer=True)),               # prefill indexer, no splits
-    ("decode_128k", dict(B=1, S=40000, cluster=0, integer=True)),    # long-row top-K (two launches)
+    ("decode_128k", dict(B=1, S=40000, cluster=0, integer=True)),    # two-stage top-K
+    ("decode_128k", dict(B=1, S=40000, K=20000, cluster=0, integer=True)),  # long-row top-K
 ])
 def test_debug_build_path_matches_oracle(debug_build, name, over):
     _forward_check(debug_build, g.CONFIGS[name].replace(**over))
