@@ -11,7 +11,7 @@
  *    nnterp deepseek_v32 page, section 03, gives the result's layout, int32
  *    [batch, query, min(index_topk, keys)];
  *  - sparse latent attention: the same step list (k^C = c^KV W_UK, v = c^KV
- *    W_UV, K_i = [K^C_i ; k^R], one rotary key shared by all heads), taken in
+ *    W_UV, K_i = [K^C_i ; k^R], the same rotary key for every head), taken in
  *    absorbed form (q_lat_h = W_UK,h q^C_h, output = per-head 512-wide latent
  *    context before W_UV), with the nnterp deepseek_v32 semantics of section
  *    03/04: zero probability outside the selection, rows summing to one over
@@ -336,7 +336,7 @@ dsa_status_t dsa_absorb_query(int32_t N, int32_t H, const void* qb, const void* 
  *   o_lat [N, H, 512] bf16: dsa_sparse_mla_fwd's o
  *   out   [N, H * 128] out_dtype (BF16 or F32): out[n, 128 h + d] =
  *         sum_c o_lat[n, h, c] kv_b[256 h + 128 + d][c] (fp32 accumulation),
- *         every head's output side by side, as o_proj / wo takes it
+ *         the heads' outputs concatenated, the input o_proj / wo takes
  * Device pointers, 16-byte aligned; no workspace.
  */
 dsa_status_t dsa_absorb_output(int32_t N, int32_t H, const void* o_lat, const void* kv_b,

@@ -358,7 +358,7 @@ int orc_cache_fill(int32_t n, int32_t D, const uint16_t* x, const uint16_t* W,
     const double inv_rms = 1.0 / sqrt(ms + ORC_NORM_EPS);
     for (int32_t i = 0; i < ORC_FILL_LAT; ++i) kv[i] = p[i] * inv_rms * kv_gamma[i];
     /* k^pe: pair (2i, 2i + 1) is turned by angle i of this token and lands in
-     * dims i and i + 32 of the rotary part */
+     * rotary dims i and i + 32 */
     const double* kpe = p + ORC_FILL_LAT;
     for (int32_t i = 0; i < ORC_FILL_ROPE / 2; ++i) {
       const double c = rope_cos[(int64_t)t * (ORC_FILL_ROPE / 2) + i];

@@ -13,8 +13,9 @@
 //   k^I  = p[576:704]   -> LayerNorm (eps 1e-6), gain and bias      -> indexer key row
 //                          (bf16, or E4M3 codes with one ue8m0 scale)
 //   w    = p[704:768]   -> the head weights of the token's query
-// The nnterp page states the rotary layout for this model: pair (2i, 2i+1)
-// of the projection lands in dims i and i + 32.
+// The rotary layout for this model (the nnterp deepseek_v32 page, section
+// 03): the projection's dims 2i and 2i+1 form a pair that lands in rotary
+// dims i and i + 32.
 //
 // Kernels:
 //  * fill_gemm_skinny (few tokens, a decode step): p = x W^T on 32x32x16

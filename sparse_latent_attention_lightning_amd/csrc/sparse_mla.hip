@@ -5,7 +5,7 @@
 //   logit_j = sm_scale * (q[h, 0:Dc] . c_j + q[h, Dc:Dc+Dr] . r_j),  kv_j = [c_j ; r_j]
 //   o[h, :] = sum_j softmax(logit)_j c_j,   lse[h] = log sum_j exp(logit_j)
 // (atlas.klimoza.dev, DeepSeek-V3.2-Exp MoE block, "All 43 steps": keys
-// [K^C ; k^R] with one rotary key shared by all heads, values c W_UV; taken in
+// [K^C ; k^R] with the same rotary key for every head, values c W_UV; taken in
 // absorbed form, q_lat = W_UK q^C, so every head reads the same 576-wide
 // row.  nnterp deepseek_v32, sections 03/04: zero probability outside the
 // selection, each row sums to one over it.)
